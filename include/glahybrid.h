@@ -1,0 +1,150 @@
+/*
+ * glahybrid.h -- C ABI of the MI355X (gfx950) hybrid gated-linear + sliding-window
+ * attention library.
+ *
+ * The layer is the hybrid attention of Lizard ("Lizard" technical summary,
+ * gist.science paper 2507.09025, Methodology section A; Lizard abstract on
+ * chatpaper.ai):
+ *
+ *   gated linear attention (Methodology A.1):
+ *     phi(x)  = [softmax(x Wphi), softmax(-x Wphi)]     Hedgehog map, non-negative
+ *                                                        (Methodology C)
+ *     Gamma_t = sigmoid(g_t)        g_t = W_gamma x_t, supplied by the caller
+ *     S_t     = diag(Gamma_t) S_{t-1} + phi(k_t)^T v_t   f x d_v state, fp32
+ *     o_gla,t = phi(q_t) S_t
+ *   sliding-window attention with meta-memory sinks (Methodology A.2):
+ *     s_tj    = scale * q_t . k_j      for j in [t-w+1, t]
+ *     o_swa,t = sum_j e^{s_tj} v_j / (sum_j e^{s_tj} + sum_m e^{t_m})
+ *   hybrid:  o_t = o_gla,t + o_swa,t
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory) unless
+ *    stated otherwise; the caller owns every buffer.  The library never allocates
+ *    or frees memory and never synchronises the stream.
+ *  - All tensors are dense, C-contiguous, row-major:
+ *      q, k            [B][H][L][d_qk]        (decode: [B][H][d_qk])
+ *      v, o            [B][H][L][d_v]         (decode: [B][H][d_v])
+ *      gate            [B][H][L][f]           (decode: [B][H][f])
+ *      wphi_q, wphi_k  [H][d_qk][f/2]         Hedgehog projections, per head
+ *      meta            [H][n_meta]            fp32 sink logits t_m
+ *      state           [B][H][f][d_v]         fp32
+ *      kcache, vcache  [B][H][window][d_qk|d_v]  ring: token p lives in slot p % window
+ *    The element type of q, k, v, gate, wphi_*, o and the caches is desc->dtype;
+ *    meta and state are always fp32.  Every pointer must be 16-byte aligned.
+ *  - Work is enqueued on `stream` (0 = the null stream) and returns immediately.
+ *  - Argument errors are reported synchronously, before anything is launched;
+ *    no entry point throws.  GLAH_EHIP means a HIP launch error was reported.
+ *  - Outputs must not alias inputs, except state_in == state_out (prefill).
+ */
+#ifndef GLAHYBRID_H
+#define GLAHYBRID_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *glah_stream_t; /* = hipStream_t */
+
+typedef enum {
+  GLAH_OK = 0,
+  GLAH_EINVAL = 1,     /* null required pointer, bad size, misaligned pointer */
+  GLAH_ENOTSUP = 2,    /* valid but unsupported combination of sizes/dtype   */
+  GLAH_EWORKSPACE = 3, /* workspace missing or smaller than required         */
+  GLAH_EHIP = 4        /* the HIP runtime reported an error                  */
+} glah_status;
+
+typedef enum { GLAH_BF16 = 0, GLAH_F32 = 1 } glah_dtype;
+
+typedef enum {
+  GLAH_GATE_LOGITS = 0, /* gate holds g = W_gamma x; the layer applies sigmoid  */
+  GLAH_GATE_LOG = 1     /* gate holds log Gamma <= 0 directly (-inf allowed)    */
+} glah_gate_kind;
+
+typedef struct glah_desc {
+  int32_t B, H, L;      /* batch, heads, tokens (L is ignored by the decode step)  */
+  int32_t d_qk, d_v, f; /* q/k head dim, value dim, feature dim (f even)            */
+  int32_t chunk;        /* token chunk of the prefill state pass; 0 = default (64)  */
+  int32_t window;       /* SWA window w >= 1 (keys including the query's own);
+                           gla_decode_step: 0 = no window part                      */
+  int32_t n_meta;       /* number of meta-memory sink scalars per head, >= 0        */
+  float scale;          /* SWA score scale; <= 0 selects 1/sqrt(d_qk)               */
+  int32_t dtype;        /* glah_dtype                                               */
+  int32_t gate_kind;    /* glah_gate_kind                                           */
+} glah_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char *glah_status_str(int status);
+
+/* Library version, (major << 16) | minor. */
+int glah_version(void);
+
+/* Bytes of device workspace that gla_prefill / hybrid_layer_fwd need for `desc`
+ * on the current device (segment states of the parallel state pass).  0 means
+ * none.  Returns (size_t)-1 when `desc` is invalid. */
+size_t glah_workspace_bytes(const glah_desc *desc);
+
+/*
+ * gla_prefill -- gated linear attention over whole sequences (Methodology A.1 and
+ * C): chunkwise-parallel form with the cumulative log-gates folded into phi(q)
+ * and phi(k), an fp32 inter-chunk state pass, o = o_gla.
+ *   state_in   nullable; [B][H][f][d_v] fp32 state before token 0 (0 if NULL)
+ *   state_out  nullable; receives S_{L-1}; may equal state_in
+ *   ws         device workspace of ws_bytes >= glah_workspace_bytes(desc)
+ */
+glah_status gla_prefill(const glah_desc *desc, const void *q, const void *k,
+                        const void *v, const void *gate, const void *wphi_q,
+                        const void *wphi_k, const float *state_in,
+                        float *state_out, void *o, void *ws, size_t ws_bytes,
+                        glah_stream_t stream);
+
+/*
+ * swa_meta_attn -- sliding-window softmax attention with meta-memory sinks
+ * (Methodology A.2), o = o_swa.  meta is [H][n_meta] fp32 and may be NULL only
+ * when n_meta == 0.  Positions start at 0 (no keys before the sequence).
+ */
+glah_status swa_meta_attn(const glah_desc *desc, const void *q, const void *k,
+                          const void *v, const float *meta, void *o,
+                          glah_stream_t stream);
+
+/*
+ * hybrid_layer_fwd -- the whole hybrid layer in one pass over q, k, v and gate:
+ * o = o_gla + o_swa (Lizard abstract: gated linear attention for global context
+ * plus meta-memory window attention for local detail).
+ *   state_in/state_out  as in gla_prefill (state_in continues the gated part only;
+ *                       the window part starts at token 0 of this call)
+ *   kcache_out/vcache_out  nullable; receive the ring of the last `window` keys and
+ *                       values (slot p % window holds token p; slots of tokens
+ *                       before 0 are zero-filled), ready for gla_decode_step
+ */
+glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k,
+                             const void *v, const void *gate, const void *wphi_q,
+                             const void *wphi_k, const float *meta,
+                             const float *state_in, float *state_out,
+                             void *kcache_out, void *vcache_out, void *o,
+                             void *ws, size_t ws_bytes, glah_stream_t stream);
+
+/*
+ * gla_decode_step -- one token of constant-memory recurrent inference
+ * (Methodology A.1: the state is updated token by token instead of keeping a KV
+ * cache; A.2 for the window part).  For every (b, h):
+ *   S <- diag(Gamma) S + phi(k_t)^T v_t   in place in `state`
+ *   ring slot pos[b] % window <- (k_t, v_t)       (when window > 0)
+ *   o_t = phi(q_t) S + window attention over positions [pos-w+1, pos] and sinks
+ *   pos     DEVICE int32 [B]: tokens already consumed by sequence b (= the new
+ *           token's position); read only, the caller advances it
+ *   kcache, vcache  may be NULL only when desc->window == 0
+ */
+glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
+                            const void *k_t, const void *v_t, const void *gate_t,
+                            const void *wphi_q, const void *wphi_k,
+                            const float *meta, float *state, void *kcache,
+                            void *vcache, const int32_t *pos, void *o_t,
+                            glah_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLAHYBRID_H */
