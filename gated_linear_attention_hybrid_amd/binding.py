@@ -1,0 +1,180 @@
+"""Python binding of ``libglahybrid.so`` (C ABI in ``include/glahybrid.h``).
+
+Argument marshalling only: each function reads shapes from torch tensors, fills
+the ``glah_desc`` descriptor, passes raw device pointers and the current HIP
+stream, and raises :class:`GlahError` on a non-zero status.  Every step of the
+layer runs in the library's HIP kernels; torch only provides device memory
+(outputs and workspace are allocated with ``torch.empty`` when not given) and
+the stream.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libglahybrid.so")
+
+GLAH_OK, GLAH_EINVAL, GLAH_ENOTSUP, GLAH_EWORKSPACE, GLAH_EHIP = range(5)
+GLAH_BF16, GLAH_F32 = 0, 1
+GLAH_GATE_LOGITS, GLAH_GATE_LOG = 0, 1
+
+EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
+           "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step")
+
+
+class GlahError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+class GlahDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("f", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("window", ctypes.c_int32), ("n_meta", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate_kind", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIBRARY):
+    """Load the HIP library (raises when it is missing: there is no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("libglahybrid.so is not built (run __graft_entry__.build() or "
+                                   "python -m gated_linear_attention_hybrid_amd.build_lib)")
+            lib = ctypes.CDLL(path)
+            vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+            dp = ctypes.POINTER(GlahDesc)
+            lib.glah_status_str.argtypes = [i32]
+            lib.glah_status_str.restype = ctypes.c_char_p
+            lib.glah_version.restype = i32
+            lib.glah_workspace_bytes.argtypes = [dp]
+            lib.glah_workspace_bytes.restype = sz
+            lib.gla_prefill.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
+            lib.gla_prefill.restype = i32
+            lib.swa_meta_attn.argtypes = [dp] + [vp] * 5 + [vp]
+            lib.swa_meta_attn.restype = i32
+            lib.hybrid_layer_fwd.argtypes = [dp] + [vp] * 12 + [vp, sz, vp]
+            lib.hybrid_layer_fwd.restype = i32
+            lib.gla_decode_step.argtypes = [dp] + [vp] * 12 + [vp]
+            lib.gla_decode_step.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _check(fn, status):
+    if status != GLAH_OK:
+        raise GlahError(fn, status, load().glah_status_str(status).decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return GLAH_BF16
+    if t.dtype == torch.float32:
+        return GLAH_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def make_desc(B, H, L, d, dv, f, *, window=0, n_meta=0, chunk=0, scale=0.0, dtype=GLAH_BF16,
+              gate_is_log=False) -> GlahDesc:
+    return GlahDesc(B, H, L, d, dv, f, chunk, window, n_meta, float(scale or 0.0), dtype,
+                    GLAH_GATE_LOG if gate_is_log else GLAH_GATE_LOGITS)
+
+
+def workspace_bytes(desc: GlahDesc) -> int:
+    n = load().glah_workspace_bytes(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlahError("glah_workspace_bytes", GLAH_EINVAL, "invalid argument")
+    return n
+
+
+def _workspace(desc, ws, device):
+    n = workspace_bytes(desc)
+    if ws is None and n:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def gla_prefill(q, k, v, gate, wq, wk, *, chunk=0, gate_is_log=False, state_in=None,
+                state_out=None, o=None, ws=None, stream=None):
+    """Gated linear attention prefill; returns o [B,H,L,dv]."""
+    B, H, L, d = q.shape
+    dv, f = v.shape[-1], gate.shape[-1]
+    desc = make_desc(B, H, L, d, dv, f, chunk=chunk, dtype=_dtype_code(q), gate_is_log=gate_is_log)
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    ws, nbytes = _workspace(desc, ws, q.device)
+    st = load().gla_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
+                            _p(state_in), _p(state_out), _p(o), _p(ws), nbytes, _stream(stream))
+    _check("gla_prefill", st)
+    return o
+
+
+def swa_meta_attn(q, k, v, meta, *, window, scale=0.0, o=None, stream=None):
+    """Sliding-window attention with meta-memory sinks; returns o [B,H,L,dv]."""
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    n_meta = 0 if meta is None else meta.shape[-1]
+    desc = make_desc(B, H, L, d, dv, 2, window=window, n_meta=n_meta, scale=scale,
+                     dtype=_dtype_code(q))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    st = load().swa_meta_attn(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(meta), _p(o),
+                              _stream(stream))
+    _check("swa_meta_attn", st)
+    return o
+
+
+def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
+                     gate_is_log=False, state_in=None, state_out=None, kcache_out=None,
+                     vcache_out=None, o=None, ws=None, stream=None):
+    """Whole hybrid layer (gated linear + window attention); returns o [B,H,L,dv]."""
+    B, H, L, d = q.shape
+    dv, f = v.shape[-1], gate.shape[-1]
+    n_meta = 0 if meta is None else meta.shape[-1]
+    desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log)
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    ws, nbytes = _workspace(desc, ws, q.device)
+    st = load().hybrid_layer_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq),
+                                 _p(wk), _p(meta), _p(state_in), _p(state_out), _p(kcache_out),
+                                 _p(vcache_out), _p(o), _p(ws), nbytes, _stream(stream))
+    _check("hybrid_layer_fwd", st)
+    return o
+
+
+def gla_decode_step(q, k, v, gate, wq, wk, meta, state, kcache, vcache, pos, *, window,
+                    scale=0.0, gate_is_log=False, o=None, stream=None):
+    """One decode step (state and ring updated in place); returns o [B,H,dv].
+    ``pos`` is a device int32 tensor [B] of tokens already consumed."""
+    B, H, d = q.shape
+    dv, f = v.shape[-1], gate.shape[-1]
+    n_meta = 0 if meta is None else meta.shape[-1]
+    desc = make_desc(B, H, 1, d, dv, f, window=window, n_meta=n_meta, scale=scale,
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    st = load().gla_decode_step(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
+                                _p(meta), _p(state), _p(kcache), _p(vcache), _p(pos), _p(o),
+                                _stream(stream))
+    _check("gla_decode_step", st)
+    return o

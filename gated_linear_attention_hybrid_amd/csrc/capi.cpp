@@ -1,0 +1,206 @@
+// capi.cpp -- the C ABI of the library (include/glahybrid.h): argument checks,
+// choice of kernel path, launches on the caller's stream.  No entry point
+// allocates memory, synchronises, or lets an exception cross the boundary.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "glahybrid.h"
+#include "launch.hpp"
+
+using namespace glah;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Entry-point kinds: which parts of the layer they compute.
+enum class Op { kGlaPrefill, kSwa, kHybrid, kDecode };
+
+int parts_of(Op op, const glah_desc *d) {
+  switch (op) {
+    case Op::kGlaPrefill: return PART_GLA;
+    case Op::kSwa: return PART_SWA;
+    case Op::kHybrid: return PART_BOTH;
+    case Op::kDecode: return PART_GLA | (d->window > 0 ? PART_SWA : 0);
+  }
+  return 0;
+}
+
+// Size and enum checks shared by every entry point.
+glah_status check_desc(const glah_desc *d, Op op, LayerArgs &a) {
+  if (!d) return GLAH_EINVAL;
+  const int parts = parts_of(op, d);
+  if (d->B < 0 || d->H < 0 || d->d_qk <= 0 || d->d_v <= 0 || d->n_meta < 0) return GLAH_EINVAL;
+  if (op != Op::kDecode && d->L < 0) return GLAH_EINVAL;
+  if ((parts & PART_GLA) && (d->f <= 0 || (d->f & 1))) return GLAH_EINVAL;
+  if ((parts & PART_SWA) && d->window < 1) return GLAH_EINVAL;
+  if (op == Op::kDecode && d->window < 0) return GLAH_EINVAL;
+  if (d->dtype != GLAH_BF16 && d->dtype != GLAH_F32) return GLAH_EINVAL;
+  if (d->gate_kind != GLAH_GATE_LOGITS && d->gate_kind != GLAH_GATE_LOG) return GLAH_EINVAL;
+  if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
+    return GLAH_EINVAL;
+  // element counts must stay far from overflow of 64-bit offsets and of the
+  // 32-bit grid sizes used by the kernels
+  const double L = op == Op::kDecode ? 1.0 : (double)d->L;
+  const double rows = (double)d->B * d->H * L;
+  const double widest = fmax(fmax((double)d->d_qk, (double)d->d_v), (double)d->f);
+  if (rows * widest > 9.0e15 || (double)d->B * d->H * (d->window + 1.0) > 1.0e9) return GLAH_EINVAL;
+  if ((double)d->f * d->d_v > 1.0e8) return GLAH_EINVAL;
+
+  a.B = d->B; a.H = d->H; a.L = op == Op::kDecode ? 1 : d->L;
+  a.d = d->d_qk; a.dv = d->d_v; a.f = (parts & PART_GLA) ? d->f : 2;
+  a.window = (parts & PART_SWA) ? d->window : 0;
+  a.n_meta = (parts & PART_SWA) ? d->n_meta : 0;
+  a.chunk = d->chunk == 0 ? 64 : d->chunk;
+  a.scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)d->d_qk);
+  a.bf16 = d->dtype == GLAH_BF16;
+  a.gate_is_log = d->gate_kind == GLAH_GATE_LOG;
+  return GLAH_OK;
+}
+
+// A required pointer must be non-null (unless the call has no work) and
+// 16-byte aligned; an optional one must be aligned when given.
+bool req(const void *p, bool has_work) { return has_work ? (p && aligned16(p)) : aligned16(p); }
+bool opt(const void *p) { return aligned16(p); }
+
+glah_status finish(hipError_t e) { return e == hipSuccess ? GLAH_OK : GLAH_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *glah_status_str(int status) {
+  switch (status) {
+    case GLAH_OK: return "ok";
+    case GLAH_EINVAL: return "invalid argument";
+    case GLAH_ENOTSUP: return "unsupported size or dtype combination";
+    case GLAH_EWORKSPACE: return "workspace missing or too small";
+    case GLAH_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int glah_version(void) { return (0 << 16) | 1; }
+
+size_t glah_workspace_bytes(const glah_desc *desc) {
+  LayerArgs a;
+  if (!desc) return (size_t)-1;
+  // the hybrid call needs the most: the state pass of the gated part
+  if (check_desc(desc, Op::kHybrid, a) != GLAH_OK && check_desc(desc, Op::kGlaPrefill, a) != GLAH_OK)
+    return (size_t)-1;
+  if (!chunked_supported(a, PART_GLA)) return 0;
+  return chunked_workspace_bytes(a, PART_GLA);
+}
+
+glah_status gla_prefill(const glah_desc *desc, const void *q, const void *k, const void *v,
+                        const void *gate, const void *wphi_q, const void *wphi_k,
+                        const float *state_in, float *state_out, void *o, void *ws,
+                        size_t ws_bytes, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kGlaPrefill, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    const bool heads = (size_t)a.B * a.H > 0;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work) || !req(o, work) ||
+        !req(wphi_q, heads) || !req(wphi_k, heads) || !opt(state_in) || !opt(state_out) || !opt(ws))
+      return GLAH_EINVAL;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k;
+    a.state_in = state_in; a.state_out = state_out; a.o = o;
+    a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
+    if (chunked_supported(a, PART_GLA)) {
+      if (ws_bytes < chunked_workspace_bytes(a, PART_GLA) || (!ws && chunked_workspace_bytes(a, PART_GLA)))
+        return GLAH_EWORKSPACE;
+      return finish(launch_chunked_prefill(a, PART_GLA));
+    }
+    if (!recurrent_supported(a, PART_GLA)) return GLAH_ENOTSUP;
+    return finish(launch_recurrent_prefill(a, PART_GLA));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status swa_meta_attn(const glah_desc *desc, const void *q, const void *k, const void *v,
+                          const float *meta, void *o, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kSwa, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(o, work) ||
+        !req(meta, a.n_meta > 0 && a.H > 0))
+      return GLAH_EINVAL;
+    a.q = q; a.k = k; a.v = v; a.meta = meta; a.o = o; a.stream = (hipStream_t)stream;
+    if (swa_mfma_supported(a)) return finish(launch_swa_mfma(a));
+    if (!recurrent_supported(a, PART_SWA)) return GLAH_ENOTSUP;
+    return finish(launch_recurrent_prefill(a, PART_SWA));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k, const void *v,
+                             const void *gate, const void *wphi_q, const void *wphi_k,
+                             const float *meta, const float *state_in, float *state_out,
+                             void *kcache_out, void *vcache_out, void *o, void *ws,
+                             size_t ws_bytes, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kHybrid, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    const bool heads = (size_t)a.B * a.H > 0;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work) || !req(o, work) ||
+        !req(wphi_q, heads) || !req(wphi_k, heads) || !req(meta, a.n_meta > 0 && a.H > 0) ||
+        !opt(state_in) || !opt(state_out) || !opt(ws) || !opt(kcache_out) || !opt(vcache_out))
+      return GLAH_EINVAL;
+    if ((kcache_out == nullptr) != (vcache_out == nullptr)) return GLAH_EINVAL;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
+    a.state_in = state_in; a.state_out = state_out; a.o = o;
+    a.kcache = kcache_out; a.vcache = vcache_out;
+    a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
+    hipError_t e;
+    if (chunked_supported(a, PART_BOTH)) {
+      if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
+        return GLAH_EWORKSPACE;
+      e = launch_chunked_prefill(a, PART_BOTH);
+    } else {
+      if (!recurrent_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
+      e = launch_recurrent_prefill(a, PART_BOTH);
+    }
+    if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
+    return finish(e);
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status gla_decode_step(const glah_desc *desc, const void *q_t, const void *k_t,
+                            const void *v_t, const void *gate_t, const void *wphi_q,
+                            const void *wphi_k, const float *meta, float *state, void *kcache,
+                            void *vcache, const int32_t *pos, void *o_t, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kDecode, a);
+    if (st != GLAH_OK) return st;
+    const int parts = parts_of(Op::kDecode, desc);
+    const bool work = (size_t)a.B * a.H > 0;
+    if (!req(q_t, work) || !req(k_t, work) || !req(v_t, work) || !req(gate_t, work) ||
+        !req(wphi_q, work) || !req(wphi_k, work) || !req(state, work) || !req(pos, work) ||
+        !req(o_t, work))
+      return GLAH_EINVAL;
+    if ((parts & PART_SWA) && (!req(kcache, work) || !req(vcache, work) ||
+                               !req(meta, a.n_meta > 0 && work)))
+      return GLAH_EINVAL;
+    if (a.dv % 4 != 0 || !recurrent_supported(a, parts)) return GLAH_ENOTSUP;
+    a.q = q_t; a.k = k_t; a.v = v_t; a.gate = gate_t; a.wq = wphi_q; a.wk = wphi_k;
+    a.meta = meta; a.state = state; a.kcache = kcache; a.vcache = vcache; a.pos = pos;
+    a.o = o_t; a.stream = (hipStream_t)stream;
+    return finish(launch_decode_step(a, parts));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+}  // extern "C"

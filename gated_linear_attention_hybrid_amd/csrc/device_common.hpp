@@ -1,0 +1,66 @@
+// device_common.hpp -- small gfx950 device helpers shared by the HIP kernels of
+// the hybrid gated-linear + window attention library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glah {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float exp_fast(float x) { return exp2_fast(x * kLog2e); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Element loads/stores with conversion to/from fp32 (bf16 stores round to
+// nearest even through v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+template <class T> __device__ __forceinline__ float ld(const T *p) { return to_f32(*p); }
+
+// Gate value Gamma in [0,1] from a logit (sigmoid) or from a log-gate (exp).
+__device__ __forceinline__ float gate_from(float g, bool gate_is_log) {
+  if (gate_is_log) return exp_fast(g);
+  return rcp_fast(1.0f + exp_fast(-g));
+}
+
+// log Gamma <= 0 from a logit (log-sigmoid = -softplus(-g)) or a log-gate.
+__device__ __forceinline__ float log_gate_from(float g, bool gate_is_log) {
+  if (gate_is_log) return g;
+  // -softplus(-g) = min(g, 0) - log(1 + e^{-|g|})
+  const float e = exp_fast(-fabsf(g));
+  return fminf(g, 0.0f) - kLn2 * log2_fast(1.0f + e);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+}  // namespace glah

@@ -1,0 +1,55 @@
+// launch.hpp -- host-side launchers of the HIP kernels (internal to the library;
+// the public interface is include/glahybrid.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace glah {
+
+enum { PART_GLA = 1, PART_SWA = 2, PART_BOTH = 3 };
+
+// One call's arguments after validation (sizes checked, scale resolved).
+struct LayerArgs {
+  int B = 0, H = 0, L = 0, d = 0, dv = 0, f = 0;
+  int window = 0, n_meta = 0, chunk = 64;
+  float scale = 1.0f;
+  bool bf16 = true;
+  bool gate_is_log = false;
+  const void *q = nullptr, *k = nullptr, *v = nullptr, *gate = nullptr;
+  const void *wq = nullptr, *wk = nullptr;
+  const float *meta = nullptr;
+  const float *state_in = nullptr;
+  float *state_out = nullptr;
+  float *state = nullptr;            // decode: in/out
+  void *o = nullptr;
+  void *kcache = nullptr, *vcache = nullptr;
+  const int32_t *pos = nullptr;      // decode
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t stream = nullptr;
+};
+
+// Limits of the token-recurrent VALU kernels (any dtype, general sizes).
+constexpr int kRecMaxD = 256;
+constexpr int kRecMaxF = 256;
+constexpr int kRecMaxWindow = 4096;
+constexpr int kRecMaxMeta = 64;
+
+bool recurrent_supported(const LayerArgs &a, int parts);
+hipError_t launch_recurrent_prefill(const LayerArgs &a, int parts);
+hipError_t launch_decode_step(const LayerArgs &a, int parts);
+hipError_t launch_window_cache(const LayerArgs &a);
+
+// Chunkwise MFMA path (bf16, d = f = d_v = 128).
+bool chunked_supported(const LayerArgs &a, int parts);
+size_t chunked_workspace_bytes(const LayerArgs &a, int parts);
+hipError_t launch_chunked_prefill(const LayerArgs &a, int parts);
+
+// Banded MFMA window attention (bf16, d = d_v = 128).
+bool swa_mfma_supported(const LayerArgs &a);
+hipError_t launch_swa_mfma(const LayerArgs &a);
+
+int device_cu_count();
+
+}  // namespace glah

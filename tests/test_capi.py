@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/glahybrid.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_linear_attention_hybrid_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "glahybrid.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIBRARY):
+        from gated_linear_attention_hybrid_amd import build_lib
+        build_lib.build()
+    return binding.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gla_prefill", "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step",
+              "glah_workspace_bytes", "glah_status_str", "glah_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+    assert set(binding.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.glah_status_str(code)
+    assert lib.glah_status_str(99) == b"unknown status"
+    assert lib.glah_version() >= 1
+
+
+FAKE = 0x10000  # an aligned, non-null address: never dereferenced by these calls
+
+
+def _desc(**kw):
+    base = dict(B=1, H=2, L=16, d=64, dv=64, f=64, window=8, n_meta=4, chunk=0, scale=0.0,
+                dtype=binding.GLAH_F32, gate_is_log=False)
+    base.update(kw)
+    return binding.make_desc(base["B"], base["H"], base["L"], base["d"], base["dv"], base["f"],
+                             window=base["window"], n_meta=base["n_meta"], chunk=base["chunk"],
+                             scale=base["scale"], dtype=base["dtype"],
+                             gate_is_log=base["gate_is_log"])
+
+
+def _hybrid(lib, desc, **ptrs):
+    names = ["q", "k", "v", "gate", "wq", "wk", "meta", "state_in", "state_out", "kc", "vc", "o", "ws"]
+    p = {n: FAKE for n in ("q", "k", "v", "gate", "wq", "wk", "meta", "o")}
+    p.update(ptrs)
+    args = [ctypes.c_void_p(p.get(n)) if p.get(n) else None for n in names]
+    return lib.hybrid_layer_fwd(ctypes.byref(desc) if desc is not None else None, *args[:12],
+                                args[12], ptrs.get("ws_bytes", 0), None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(f=63), dict(f=0), dict(B=-1), dict(H=-2), dict(L=-1), dict(d=0), dict(dv=0),
+    dict(window=0), dict(n_meta=-1), dict(chunk=48), dict(dtype=7),
+])
+def test_bad_descriptor_is_einval(lib, bad):
+    d = _desc(**bad)
+    if "gate_is_log" not in bad and bad.get("dtype") is None:
+        pass
+    assert _hybrid(lib, d) == binding.GLAH_EINVAL
+
+
+def test_bad_gate_kind_is_einval(lib):
+    d = _desc()
+    d.gate_kind = 5
+    assert _hybrid(lib, d) == binding.GLAH_EINVAL
+
+
+def test_null_descriptor_is_einval(lib):
+    assert _hybrid(lib, None) == binding.GLAH_EINVAL
+    assert lib.glah_workspace_bytes(None) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("missing", ["q", "k", "v", "gate", "wq", "wk", "meta", "o"])
+def test_missing_required_pointer_is_einval(lib, missing):
+    assert _hybrid(lib, _desc(), **{missing: 0}) == binding.GLAH_EINVAL
+
+
+@pytest.mark.parametrize("which", ["q", "o", "state_in", "kc"])
+def test_misaligned_pointer_is_einval(lib, which):
+    extra = {"vc": FAKE} if which == "kc" else {}
+    assert _hybrid(lib, _desc(), **{which: FAKE + 4}, **extra) == binding.GLAH_EINVAL
+
+
+def test_one_sided_window_cache_is_einval(lib):
+    assert _hybrid(lib, _desc(), kc=FAKE) == binding.GLAH_EINVAL
+
+
+def test_meta_may_be_null_only_without_sinks(lib):
+    assert _hybrid(lib, _desc(n_meta=4), meta=0) == binding.GLAH_EINVAL
+
+
+def _decode(lib, desc, **ptrs):
+    names = ["q", "k", "v", "gate", "wq", "wk", "meta", "state", "kc", "vc", "pos", "o"]
+    p = {n: FAKE for n in names}
+    p.update(ptrs)
+    args = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
+    return lib.gla_decode_step(ctypes.byref(desc), *args, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, _desc(dv=66)) == binding.GLAH_ENOTSUP
+    assert _decode(lib, _desc(), pos=0) == binding.GLAH_EINVAL
+    assert _decode(lib, _desc(), state=0) == binding.GLAH_EINVAL
+    assert _decode(lib, _desc(), kc=0) == binding.GLAH_EINVAL
+    assert _decode(lib, _desc(window=-1)) == binding.GLAH_EINVAL
+    assert _decode(lib, _desc(d=1024)) == binding.GLAH_ENOTSUP
+
+
+def test_prefill_rejects_unsupported_sizes(lib):
+    # a head dim beyond every kernel's limit is a valid but unsupported request
+    assert _hybrid(lib, _desc(d=1024)) == binding.GLAH_ENOTSUP
+    assert _hybrid(lib, _desc(window=100000)) == binding.GLAH_ENOTSUP
+
+
+def test_swa_and_gla_prefill_argument_checks(lib):
+    d = _desc()
+    f = ctypes.c_void_p(FAKE)
+    assert lib.swa_meta_attn(ctypes.byref(d), f, f, None, f, f, None) == binding.GLAH_EINVAL
+    assert lib.gla_prefill(ctypes.byref(_desc(f=7)), f, f, f, f, f, f, None, None, f, None, 0,
+                           None) == binding.GLAH_EINVAL
+    assert lib.gla_prefill(ctypes.byref(d), f, f, f, None, f, f, None, None, f, None, 0,
+                           None) == binding.GLAH_EINVAL

@@ -1,0 +1,177 @@
+"""GPU parity of the token-recurrent kernels (fp32 mode, general sizes) and of the
+decode step, against the fp64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_linear_attention_hybrid_amd import binding as G
+from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_decode_token, make_prefill, to_f64
+from parity import TOL_BF16, TOL_F32, assert_finite, gpu_f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print("[case]", msg, flush=True)
+
+
+def ref_layer(x, wl, parts=oracle.PART_BOTH, gate_is_log=False, state_in=None, return_state=False,
+              window=None):
+    o = {k: to_f64(v) for k, v in x.items()}
+    return oracle.layer_fwd(o["q"], o["k"], o["v"], o["gate"], o["wq"], o["wk"], o["meta"],
+                            window=wl.window if window is None else window, gate_is_log=gate_is_log,
+                            parts=parts, state_in=state_in, return_state=return_state)
+
+
+def tiny(**kw):
+    return WORKLOADS["tiny_fp32"].with_(**kw)
+
+
+@pytest.mark.parametrize("variant", ["base", "slow_decay", "gate_one", "strong_decay"])
+def test_fp32_hybrid_tiny(variant):
+    wl = tiny()
+    gate_is_log = False
+    if variant == "slow_decay":
+        wl = wl.with_(gate_mean=6.0)
+    elif variant == "strong_decay":
+        wl = wl.with_(gate_mean=-2.0, gate_std=1.5)
+    say("fp32 hybrid tiny %s" % variant)
+    x = make_prefill(wl, DEV, gate_log_zero=(variant == "gate_one"))
+    gate_is_log = variant == "gate_one"
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                           window=wl.window, gate_is_log=gate_is_log, state_out=st)
+    ref, sref = ref_layer(x, wl, gate_is_log=gate_is_log, return_state=True)
+    assert row_rel_err(gpu_f64(o), ref) <= TOL_F32
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), sref.reshape(-1, wl.dv)) <= TOL_F32
+
+
+def test_fp32_parts_separately():
+    wl = tiny()
+    say("fp32 gla_prefill / swa_meta_attn tiny")
+    x = make_prefill(wl, DEV)
+    o = G.gla_prefill(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"])
+    assert row_rel_err(gpu_f64(o), ref_layer(x, wl, parts=oracle.PART_GLA)) <= TOL_F32
+    o = G.swa_meta_attn(x["q"], x["k"], x["v"], x["meta"], window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref_layer(x, wl, parts=oracle.PART_SWA)) <= TOL_F32
+
+
+@pytest.mark.parametrize("L", [0, 1, 5, 77])
+def test_fp32_ragged_lengths(L):
+    wl = tiny(L=L, H=3, B=2)
+    say("fp32 ragged L=%d" % L)
+    x = make_prefill(wl, DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                           window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref_layer(x, wl)) <= TOL_F32
+
+
+def test_fp32_odd_sizes_and_no_sinks():
+    wl = tiny(d=40, f=22, dv=72, window=5, n_meta=0, L=50)
+    say("fp32 odd sizes d=40 f=22 dv=72 no sinks")
+    x = make_prefill(wl, DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], None,
+                           window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref_layer(x, wl)) <= TOL_F32
+
+
+def test_fp32_state_continuation():
+    wl = tiny(L=96)
+    say("fp32 state_in continuation")
+    x = make_prefill(wl, DEV)
+    L1 = 37
+    first = {k: (v[:, :, :L1].contiguous() if v.dim() == 4 else v) for k, v in x.items()}
+    rest = {k: (v[:, :, L1:].contiguous() if v.dim() == 4 else v) for k, v in x.items()}
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    G.gla_prefill(first["q"], first["k"], first["v"], first["gate"], first["wq"], first["wk"],
+                  state_out=st)
+    o2 = G.gla_prefill(rest["q"], rest["k"], rest["v"], rest["gate"], rest["wq"], rest["wk"],
+                       state_in=st, state_out=st)
+    full, sfull = ref_layer(x, wl, parts=oracle.PART_GLA, return_state=True)
+    assert row_rel_err(gpu_f64(o2), full[:, :, L1:]) <= TOL_F32
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), sfull.reshape(-1, wl.dv)) <= TOL_F32
+
+
+def test_bf16_general_sizes_recurrent():
+    # a bf16 size outside the MFMA kernels (head dim 64) runs the recurrent form
+    wl = WORKLOADS["prefill_2k"].with_(H=4, L=200, d=64, f=64, dv=64, w_std=1.0)
+    say("bf16 recurrent d=64")
+    x = make_prefill(wl, DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                           window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref_layer(x, wl)) <= TOL_BF16
+
+
+def test_window_cache_out():
+    wl = tiny(L=37, window=16)
+    say("window cache out")
+    x = make_prefill(wl, DEV)
+    kc = torch.full((wl.B, wl.H, wl.window, wl.d), 7.0, device=DEV)
+    vc = torch.full((wl.B, wl.H, wl.window, wl.dv), 7.0, device=DEV)
+    G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                       window=wl.window, kcache_out=kc, vcache_out=vc)
+    torch.cuda.synchronize()
+    for p in range(wl.L - wl.window, wl.L):
+        assert torch.equal(kc[:, :, p % wl.window], x["k"][:, :, p])
+        assert torch.equal(vc[:, :, p % wl.window], x["v"][:, :, p])
+    short = tiny(L=5, window=16)
+    xs = make_prefill(short, DEV)
+    G.hybrid_layer_fwd(xs["q"], xs["k"], xs["v"], xs["gate"], xs["wq"], xs["wk"], xs["meta"],
+                       window=16, kcache_out=kc, vcache_out=vc)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :, :5], xs["k"]) and bool((kc[:, :, 5:] == 0).all())
+
+
+def _decode_case(wl, L0, steps, dtype_tol):
+    x = make_prefill(wl.with_(L=L0), DEV)
+    B, H = wl.B, wl.H
+    st = torch.zeros((B, H, wl.f, wl.dv), device=DEV)
+    kc = torch.zeros((B, H, wl.window, wl.d), device=DEV, dtype=wl.torch_dtype)
+    vc = torch.zeros((B, H, wl.window, wl.dv), device=DEV, dtype=wl.torch_dtype)
+    G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                       window=wl.window, state_out=st, kcache_out=kc, vcache_out=vc)
+    # oracle: same prefix, then the same tokens step by step
+    ox = {k: to_f64(v) for k, v in x.items()}
+    _, ost = oracle.layer_fwd(ox["q"], ox["k"], ox["v"], ox["gate"], ox["wq"], ox["wk"], ox["meta"],
+                              window=wl.window, return_state=True)
+    ost = np.ascontiguousarray(ost)
+    okc = np.zeros((B, H, wl.window, wl.d))
+    ovc = np.zeros((B, H, wl.window, wl.dv))
+    for p in range(max(0, L0 - wl.window), L0):
+        okc[:, :, p % wl.window] = ox["k"][:, :, p]
+        ovc[:, :, p % wl.window] = ox["v"][:, :, p]
+    pos = torch.full((B,), L0, dtype=torch.int32, device=DEV)
+    worst = 0.0
+    for s in range(steps):
+        t = make_decode_token(wl, s, DEV)
+        o = G.gla_decode_step(t["q"], t["k"], t["v"], t["gate"], x["wq"], x["wk"], x["meta"], st,
+                              kc, vc, pos, window=wl.window)
+        ot = {k: to_f64(v) for k, v in t.items()}
+        oref = oracle.decode_step(ot["q"], ot["k"], ot["v"], ot["gate"], ox["wq"], ox["wk"],
+                                  ox["meta"], ost, okc, ovc, np.full(B, L0 + s), window=wl.window)
+        worst = max(worst, row_rel_err(gpu_f64(o), oref))
+        pos += 1
+    assert_finite(st, "state")
+    assert worst <= dtype_tol, worst
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), ost.reshape(-1, wl.dv)) <= dtype_tol
+    return worst
+
+
+def test_decode_fp32_tiny():
+    say("decode fp32 tiny")
+    _decode_case(tiny(B=2), L0=40, steps=20, dtype_tol=TOL_F32)
+
+
+def test_decode_fp32_short_prefix():
+    # prefix shorter than the window: the ring is still filling
+    say("decode fp32 short prefix")
+    _decode_case(tiny(B=2, window=16), L0=3, steps=20, dtype_tol=TOL_F32)
+
+
+def test_decode_bf16_llama_shape():
+    say("decode bf16 d=f=dv=128 w=64")
+    wl = WORKLOADS["decode_b8"].with_(B=2, H=8)
+    _decode_case(wl, L0=150, steps=12, dtype_tol=TOL_BF16)
