@@ -1,20 +1,806 @@
-// chunked.hip -- chunkwise-parallel MFMA prefill (placeholder until the kernels land).
+// chunked.hip -- chunkwise-parallel MFMA prefill of the hybrid layer for gfx950
+// (bf16 inputs, fp32 accumulation, d = f = d_v = 128, 64-token chunks).
+//
+// Method ("Lizard" technical summary, gist.science 2507.09025, Methodology C,
+// hardware-aware algorithm): the Hedgehog features are non-negative, so the
+// cumulative log-gates can be moved into phi(q) and phi(k) and every product
+// inside a chunk becomes a plain low-precision GEMM instead of a cumulative
+// product that underflows.  With b_t the in-chunk inclusive cumsum of
+// a = log Gamma (per feature):
+//   intra:  A[t][s] = sum_f phi_q[t,f] e^{b_t,f - r_f} * phi_k[s,f] e^{r_f - b_s,f}
+//   inter:  o_t    += (phi_q[t] e^{b_t}) S_c
+//   state:  S_{c+1} = diag(e^{B_c}) S_c + sum_s (phi_k[s] e^{B_c - b_s})^T v_s
+// The reference r is taken per 16-token tile, in the middle of the tile's decay
+// (r_w = P_w + T_w/2 with P_w the log-gate sum of the earlier tiles and T_w the
+// tile's own), so every exponent stays inside the fp32/bf16 range even when the
+// gate product over a whole chunk underflows; cross-tile factors
+// e^{r_qt - r_kt} <= 1, and q-bar / k-hat are formed from summed exponents that
+// are never positive.
+// The window part (Methodology A.2) reuses the same tiles: band scores over the
+// 5 key tiles that can reach a 16-query tile, a one-shot softmax whose
+// denominator starts from the meta-memory sinks, and the probabilities are added
+// to the intra-chunk weights so one GEMM with V yields both parts.
+//
+// Parallel structure over one head: the sequence is cut into P segments.
+//   chunk_kernel<MODE_STATE>   each segment's end state from a zero state and its
+//                              total log-decay (segments 0..P-2)
+//   segment_scan_kernel        start state of every segment (fp32, sequential in p)
+//   chunk_kernel<MODE_HYBRID>  (or MODE_GLA) the outputs, one block per segment,
+//                              starting from that segment's state
+//   chunk_kernel<MODE_SWA>     window attention alone, one block per chunk
+//
+// Block = 256 threads = 4 waves.  Row phase: wave w owns query/key tile w (16
+// tokens).  Column phase: wave w owns d_v columns [32w, 32w+32) for all 64
+// tokens and the matching 128 x 32 slice of the fp32 state, which stays in
+// MFMA accumulators for the whole segment.  Operands are exchanged through LDS
+// as ready-made MFMA fragments (1 KiB: 64 lanes x 16 B).
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace glah {
 
+namespace {
+
+constexpr int kC = 64;      // chunk (tokens)
+constexpr int kD = 128;     // q/k head dim
+constexpr int kF = 128;     // feature dim
+constexpr int kF2 = 64;     // Hedgehog half
+constexpr int kDV = 128;    // value dim
+constexpr int kNT = 256;    // threads per block
+constexpr int kFrag = 1024; // bytes of one MFMA operand fragment
+constexpr int kHalf = 512;  // bytes of a half fragment (4 bf16 per lane)
+
+enum { MODE_STATE = 0, MODE_GLA = 1, MODE_HYBRID = 2, MODE_SWA = 3 };
+
+struct ChunkParams {
+  const bf16 *q, *k, *v, *gate, *wq, *wk;
+  const float *meta;
+  const float *state_in;  // [BH][F][DV] state before token 0 (segment 0), or null
+  float *state_out;       // [BH][F][DV] written by the last segment, or null
+  bf16 *o;
+  float *seg_state;       // [BH][P-1][F][DV]: end state of segment p from zero (state
+                          // pass), overwritten by the scan with the start state of p+1
+  float *seg_decay;       // [BH][P-1][F]: total log-decay of segment p
+  int B, H, L, window, n_meta;
+  int nchunks, P, seg_chunks;
+  float scale;
+  int gate_is_log;
+};
+
+// ---------------------------------------------------------------- LDS layout
+template <int MODE>
+struct Lds {
+  static constexpr bool Q = MODE != MODE_STATE;
+  static constexpr bool GLA = MODE != MODE_SWA;
+  static constexpr bool SWA = MODE == MODE_HYBRID || MODE == MODE_SWA;
+  static constexpr int VSLOTS = SWA ? 2 : 1;
+  static constexpr int NKS = SWA ? 3 : 2;  // k-steps of the (weights x V) GEMM
+  static constexpr int WQ = 0;                                   // Wphi_q^T frags [4][4]
+  static constexpr int WK = WQ + ((Q && GLA) ? 16 * kFrag : 0);  // Wphi_k^T frags [4][4]
+  static constexpr int RK = WK + (GLA ? 16 * kFrag : 0);         // raw k frags [2][4][4]
+  static constexpr int VT = RK + (SWA ? 32 * kFrag : 0);         // V^T half frags [slot][4][8]
+  static constexpr int KT = VT + VSLOTS * 32 * kHalf;            // k-tilde frags [4][4]
+  static constexpr int QB = KT + ((Q && GLA) ? 16 * kFrag : 0);  // q-bar frags [4][4]
+  static constexpr int KH = QB + ((Q && GLA) ? 16 * kFrag : 0);  // k-hat^T frags [8][2]
+  static constexpr int W = KH + (GLA ? 16 * kFrag : 0);          // weight frags [4][NKS]
+  static constexpr int T = W + (Q ? 4 * NKS * kFrag : 0);        // tile log-gate totals [4][128]
+  static constexpr int BYTES = T + (GLA ? 4 * kF * 4 : 0);
+};
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = (bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack44(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (bf16)lo[j];
+    r[4 + j] = (bf16)hi[j];
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds8(const char *base) { return *(const bf16x8 *)base; }
+__device__ __forceinline__ void sts8(char *base, bf16x8 x) { *(bf16x8 *)base = x; }
+
+__device__ __forceinline__ bf16x8 join44(bf16x4 lo, bf16x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = lo[j];
+    r[4 + j] = hi[j];
+  }
+  return r;
+}
+
+// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48)
+__device__ __forceinline__ float grp_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float grp_min(float x) {
+  x = fminf(x, __shfl_xor(x, 16, 64));
+  return fminf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float grp_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// inclusive scan over the 16 lanes of a row (the 16 tokens of a tile)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x110 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+// broadcast lane 15 of each 16-lane row (the tile's last token) to the row
+__device__ __forceinline__ float row_bcast15(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15F,
+                                                               0xF, 0xF, false));
+}
+
+// Smallest per-token log-gate used by the chunkwise path.  A 16-token tile then
+// spans at most 160 in log space, so with the mid-tile reference every fold
+// factor stays within e^{+-80}.  Gates below e^{-10} (~4.5e-5) act as 4.5e-5:
+// any term they touch is already below 4.5e-5 of its undecayed size, so the
+// change is bounded by that factor.
+constexpr float kMinLogGate = -10.0f;
+
+// feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
+__device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
+
+// d_v column held by lane n, column-tile dt, of wave w (8 contiguous per lane group)
+__device__ __forceinline__ int dvcol(int w, int dt, int n) {
+  return 32 * w + 8 * (n >> 2) + 4 * dt + (n & 3);
+}
+
+// One chunk's inputs held in registers (prefetched one chunk ahead).
+struct ChunkRegs {
+  bf16x8 xq[4];  // q[token 16w+n][32g + 8s + j]
+  bf16x8 xk[4];  // k, same layout
+  bf16x8 xg[4];  // gate[token][feat(g, 8s + j)]
+  bf16x8 xv[4];  // v[token 4kg + i][8dc + j] (V^T staging)
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_chunk(const ChunkParams &p, size_t bh, int c, ChunkRegs &r) {
+  constexpr bool Q = Lds<MODE>::Q, GLA = Lds<MODE>::GLA, SWA = Lds<MODE>::SWA;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int t = c * kC + 16 * wave + n;
+  const bool ok = c >= 0 && t < p.L;
+  const size_t row = bh * p.L + t;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (Q) r.xq[s] = ok ? *(const bf16x8 *)(p.q + row * kD + 32 * g + 8 * s) : zero8();
+    if (GLA || SWA) r.xk[s] = ok ? *(const bf16x8 *)(p.k + row * kD + 32 * g + 8 * s) : zero8();
+    if (GLA) r.xg[s] = ok ? *(const bf16x8 *)(p.gate + row * kF + feat(g, 8 * s)) : zero8();
+  }
+  const int kg = tid >> 4, dc = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tv = c * kC + 4 * kg + i;
+    r.xv[i] = (c >= 0 && tv < p.L) ? *(const bf16x8 *)(p.v + (bh * p.L + tv) * kDV + 8 * dc) : zero8();
+  }
+}
+
+// V^T half fragments of one chunk into ring slot `slot`: for key tile kt and
+// d_v tile (2w + dt), lane 16g + r holds v[16kt + 4g + j][dvcol(w, dt, r)].
+template <int MODE>
+__device__ __forceinline__ void store_vt(char *smem, int slot, const ChunkRegs &r) {
+  const int tid = threadIdx.x, kg = tid >> 4, dc = tid & 15;
+  const int kt = kg >> 2, ga = kg & 3;
+  char *base = smem + Lds<MODE>::VT + slot * 32 * kHalf + kt * 8 * kHalf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int dv = 8 * dc + e;
+    const int w = dv >> 5, within = dv & 31;
+    const int rr = 4 * (within >> 3) + (within & 3);
+    const int dt = (within >> 2) & 1;
+    bf16x4 col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) col[i] = r.xv[i][e];
+    *(bf16x4 *)(base + (2 * w + dt) * kHalf + (16 * ga + rr) * 8) = col;
+  }
+}
+
+// ---------------------------------------------------------------- the kernel
+template <int MODE>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_kernel(ChunkParams p) {
+  using LD = Lds<MODE>;
+  constexpr bool Q = LD::Q, GLA = LD::GLA, SWA = LD::SWA;
+  constexpr bool INTRA = Q && GLA;
+  constexpr int NKS = LD::NKS;
+  extern __shared__ __align__(16) char smem[];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int nseg = MODE == MODE_STATE ? p.P - 1 : p.P;
+  const size_t bh = blockIdx.x / nseg;
+  const int seg = blockIdx.x % nseg;
+  const int h = (int)(bh % p.H);
+  const int c_begin = seg * p.seg_chunks;
+  const int c_end = min(c_begin + p.seg_chunks, p.nchunks);
+
+  // ---- Hedgehog projections as MFMA A fragments: frag (mt, s), lane (r, g)
+  // holds W[32g + 8s + j][m] with m = 16(r/4) + 4mt + (r%4), so that the
+  // accumulator of tile mt gives lane (n, g) the u-values m = 16g + 4mt + j.
+  if (GLA) {
+    for (int idx = tid; idx < 16 * 64; idx += kNT) {
+      const int fi = idx >> 6, l = idx & 63, rr = l & 15, gg = l >> 4;
+      const int mt = fi >> 2, s = fi & 3;
+      const int m = 16 * (rr >> 2) + 4 * mt + (rr & 3);
+      const bf16 *wk = p.wk + (size_t)h * kD * kF2;
+      bf16x8 fk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fk[j] = wk[(32 * gg + 8 * s + j) * kF2 + m];
+      sts8(smem + LD::WK + fi * kFrag + l * 16, fk);
+      if (Q) {
+        const bf16 *wq = p.wq + (size_t)h * kD * kF2;
+        bf16x8 fq;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fq[j] = wq[(32 * gg + 8 * s + j) * kF2 + m];
+        sts8(smem + LD::WQ + fi * kFrag + l * 16, fq);
+      }
+    }
+  }
+
+  // ---- state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvcol(wave, dt, n)]
+  f32x4 S[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) S[mt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  if (GLA && MODE != MODE_STATE) {
+    const float *src = nullptr;
+    if (seg == 0)
+      src = p.state_in ? p.state_in + bh * kF * kDV : nullptr;
+    else
+      src = p.seg_state + (bh * (p.P - 1) + (seg - 1)) * (size_t)(kF * kDV);
+    if (src) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)];
+    }
+  }
+  float dsum[32];  // total log-decay of the segment (state pass)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dsum[i] = 0.0f;
+
+  // ---- window part: keys and values of the chunk before the segment
+  if (SWA) {
+    ChunkRegs pr;
+    load_chunk<MODE>(p, bh, c_begin - 1, pr);
+    const int slot = (c_begin - 1) & 1;
+    store_vt<MODE>(smem, slot, pr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sts8(smem + LD::RK + ((slot * 4 + wave) * 4 + s) * kFrag + lane * 16, pr.xk[s]);
+  }
+
+  ChunkRegs cur;
+  load_chunk<MODE>(p, bh, c_begin, cur);
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    ChunkRegs nxt;
+    if (c + 1 < c_end) load_chunk<MODE>(p, bh, c + 1, nxt);
+    const int c0 = c * kC;
+    const int slot = LD::VSLOTS == 2 ? (c & 1) : 0;
+    const int pslot = slot ^ 1;
+    const int tq = c0 + 16 * wave + n;  // this lane's token in the row phase
+    const bool tok_ok = tq < p.L;
+
+    store_vt<MODE>(smem, slot, cur);
+    if (SWA) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sts8(smem + LD::RK + ((slot * 4 + wave) * 4 + s) * kFrag + lane * 16, cur.xk[s]);
+    }
+
+    // ================= row phase 1: features, gates, folds =================
+    // Fold exponents (base 2) of this lane's token for the 32 features F_g:
+    //   lq = log2 phi_q + (b_loc - T_w/2) log2e,  lk = log2 phi_k + (T_w/2 - b_loc) log2e
+    // b_loc: in-tile inclusive cumsum of the log-gates, T_w: the tile total.  The
+    // reference sits at the middle of the tile's decay, so |exponent| <= |T_w|/2.
+    float lq[32], lk[32];
+    bf16x8 kb[4];  // k~ = 2^lk of this lane's token, as MFMA operands
+    if (GLA) {
+      f32x4 uk[4], uq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        uk[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        uq[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uk[mt] = mfma(lds8(smem + LD::WK + (mt * 4 + s) * kFrag + lane * 16), cur.xk[s], uk[mt]);
+          if (Q) uq[mt] = mfma(lds8(smem + LD::WQ + (mt * 4 + s) * kFrag + lane * 16), cur.xq[s], uq[mt]);
+        }
+      // log-gates (clamped at kMinLogGate) and their in-tile inclusive cumsum
+      float bl[32], half[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float a = tok_ok ? fmaxf(log_gate_from((float)cur.xg[i >> 3][i & 7], p.gate_is_log), kMinLogGate)
+                               : 0.0f;
+        bl[i] = row_scan(a);
+        half[i] = 0.5f * row_bcast15(bl[i]);
+      }
+      if (n == 15) {
+        float *T = (float *)(smem + LD::T) + wave * kF;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) T[feat(g, i)] = bl[i];
+      }
+      // log-softmax of +u and -u over the 64 u-values of each token, plus the fold
+      auto fold = [&](const f32x4 *u, float *out, float sgn) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            mx = fmaxf(mx, u[mt][j]);
+            mn = fminf(mn, u[mt][j]);
+          }
+        mx = grp_max(mx);
+        mn = grp_min(mn);
+        float zp = 0.0f, zn = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            zp += exp2_fast((u[mt][j] - mx) * kLog2e);
+            zn += exp2_fast((mn - u[mt][j]) * kLog2e);
+          }
+        zp = grp_sum(zp);
+        zn = grp_sum(zn);
+        // log2 phi+ = (u - mx) log2e - log2 zp ; log2 phi- = (mn - u) log2e - log2 zn
+        const float lp = log2_fast(zp), ln_ = log2_fast(zn);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * mt + j;
+            out[e] = (u[mt][j] - mx) * kLog2e - lp + sgn * (bl[e] - half[e]) * kLog2e;
+            out[16 + e] = (mn - u[mt][j]) * kLog2e - ln_ + sgn * (bl[16 + e] - half[16 + e]) * kLog2e;
+          }
+      };
+      fold(uk, lk, -1.0f);
+      if (!tok_ok) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lk[i] = -INFINITY;  // padded tokens carry no key
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = exp2_fast(lk[8 * s + j]);
+        kb[s] = pack8(tmp);
+      }
+      if (INTRA) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (wave * 4 + s) * kFrag + lane * 16, kb[s]);
+      }
+      if (Q) fold(uq, lq, 1.0f);
+    }
+    __syncthreads();  // B1: tile totals, k~ and raw-k fragments visible
+
+    // ================= row phase 2: cross-tile factors, scores =================
+    f32x4 Wt[5];  // weights^T for key tiles wave-4 .. wave (index kt - wave + 4)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    float btot[32];
+    if (GLA) {
+      const float *T = (const float *)(smem + LD::T);
+      float pre[32], tw[32];  // P_w (log-gate sum of earlier tiles), T_w
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        pre[i] = 0.0f;
+        btot[i] = 0.0f;
+        tw[i] = 0.0f;
+      }
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float tv = T[w2 * kF + feat(g, i)];
+          btot[i] += tv;
+          if (w2 < wave) pre[i] += tv;
+          if (w2 == wave) tw[i] = tv;
+        }
+      }
+      if (MODE == MODE_STATE) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dsum[i] += btot[i];
+      }
+      // q-bar = phi_q e^{b} (inter-chunk readout): exponent lq + (P_w + T_w/2)
+      if (Q) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float tmp[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * s + j;
+            tmp[j] = exp2_fast(lq[i] + (pre[i] + 0.5f * tw[i]) * kLog2e);
+          }
+          sts8(smem + LD::QB + (wave * 4 + s) * kFrag + lane * 16, pack8(tmp));
+        }
+      }
+      {  // k-hat = phi_k e^{B - b} (state update): exponent lk + (B - P_w - T_w/2) <= 0
+        const int sp = wave >> 1, hh = wave & 1, ga = n >> 2, jj = 4 * hh + (n & 3);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float khat = exp2_fast(lk[i] + (btot[i] - pre[i] - 0.5f * tw[i]) * kLog2e);
+          const int hf = i >> 4, e = i & 15;
+          const int mt = 4 * hf + (e >> 2), rr = 4 * g + (e & 3);
+          *(bf16 *)(smem + LD::KH + (mt * 2 + sp) * kFrag + (16 * ga + rr) * 16 + jj * 2) = (bf16)khat;
+        }
+      }
+      // intra-chunk scores A^T for key tiles 0..wave
+      if (INTRA) {
+        {  // diagonal tile: q~ k~^T with the tile's own reference
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            float tmp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) tmp[j] = exp2_fast(lq[8 * s + j]);
+            acc = mfma(kb[s], pack8(tmp), acc);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
+          Wt[4] = acc;
+        }
+        // earlier tiles: q~ scaled by e^{r_w - r_kt} <= 1, r_x = P_x + T_x/2
+        float run[32];  // sum of tile totals kt .. wave-1
+#pragma unroll
+        for (int i = 0; i < 32; ++i) run[i] = 0.0f;
+#pragma unroll
+        for (int kt = 3; kt >= 0; --kt) {
+          if (kt < wave) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              float tmp[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int i = 8 * s + j;
+                const float tk = T[kt * kF + feat(g, i)];
+                run[i] += tk;
+                tmp[j] = exp2_fast(lq[i] + (run[i] + 0.5f * (tw[i] - tk)) * kLog2e);
+              }
+              acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), pack8(tmp), acc);
+            }
+            Wt[kt - wave + 4] = acc;
+          }
+        }
+      }
+    }
+
+    if (SWA) {
+      // band scores for key tiles wave-4 .. wave, one-shot softmax with sinks
+      f32x4 sc[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int kt = wave - 4 + i;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 a;
+          if (i == 4)
+            a = cur.xk[s];
+          else if (kt >= 0)
+            a = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
+          else
+            a = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
+          acc = mfma(a, cur.xq[s], acc);
+        }
+        sc[i] = acc;
+      }
+      const int tqa = c0 + 16 * wave + n;  // query position
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ka = c0 + 16 * (wave - 4 + i) + 4 * g + j;
+          const bool ok = ka <= tqa && ka > tqa - p.window && ka >= 0;
+          sc[i][j] = ok ? sc[i][j] * p.scale : -INFINITY;
+          mx = fmaxf(mx, sc[i][j]);
+        }
+      mx = grp_max(mx);
+      const float *meta = p.meta + (size_t)h * p.n_meta;
+      for (int m = 0; m < p.n_meta; ++m) mx = fmaxf(mx, meta[m]);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = sc[i][j] == -INFINITY ? 0.0f : exp2_fast((sc[i][j] - mx) * kLog2e);
+          sc[i][j] = e;
+          sum += e;
+        }
+      sum = grp_sum(sum);
+      for (int m = 0; m < p.n_meta; ++m) sum += exp2_fast((meta[m] - mx) * kLog2e);
+      const float inv = 1.0f / sum;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) Wt[i] += sc[i] * inv;
+    }
+
+    if (Q) {
+      // weight fragments for the (weights x V) GEMM
+      if (SWA) {
+        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(Wt[0], Wt[1]));
+        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(Wt[2], Wt[3]));
+        sts8(smem + LD::W + (wave * NKS + 2) * kFrag + lane * 16,
+             pack44(Wt[4], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}));
+      } else {
+        // key tiles 0..3 of the chunk: Wt[kt - wave + 4], zero beyond the diagonal
+        f32x4 wk4[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          wk4[kt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int i = 0; i < 5; ++i)
+            if (kt <= wave && i == kt - wave + 4) wk4[kt] = Wt[i];
+        }
+        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(wk4[0], wk4[1]));
+        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(wk4[2], wk4[3]));
+      }
+    }
+    __syncthreads();  // B2: q-bar, k-hat^T, weight fragments visible
+
+    // ================= column phase: outputs and state =================
+    if (Q) {
+      f32x4 O[4][2];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) O[qt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      if (GLA) {  // inter-chunk readout: O^T += S^T q-bar^T
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 a = pack44(S[2 * s][dt], S[2 * s + 1][dt]);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt)
+              O[qt][dt] = mfma(a, lds8(smem + LD::QB + (qt * 4 + s) * kFrag + lane * 16), O[qt][dt]);
+          }
+      }
+      // weights x V over the key tiles of each query tile
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 b = lds8(smem + LD::W + (qt * NKS + ks) * kFrag + lane * 16);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            bf16x4 lo, hi;
+            auto vt_half = [&](int kt) -> bf16x4 {
+              const int sl = kt >= 0 ? slot : pslot;
+              const int tile = kt >= 0 ? kt : kt + 4;
+              return *(const bf16x4 *)(smem + LD::VT + (sl * 4 + tile) * 8 * kHalf +
+                                       (2 * wave + dt) * kHalf + lane * 8);
+            };
+            if (SWA) {
+              const int ka = qt - 4 + 2 * ks;
+              lo = vt_half(ka);
+              if (ks < 2) {
+                hi = vt_half(ka + 1);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hi[j] = (bf16)0.0f;
+              }
+            } else {
+              lo = vt_half(2 * ks);
+              hi = vt_half(2 * ks + 1);
+            }
+            O[qt][dt] = mfma(join44(lo, hi), b, O[qt][dt]);
+          }
+        }
+      // store o: lane (n, g) of query tile qt holds d_v 32w + 8g + (4dt + j)
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int t = c0 + 16 * qt + n;
+        if (t < p.L)
+          *(bf16x8 *)(p.o + (bh * p.L + t) * kDV + 32 * wave + 8 * g) = pack44(O[qt][0], O[qt][1]);
+      }
+    }
+
+    if (GLA) {  // S <- diag(e^{B}) S + k-hat^T V
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float eb = exp2_fast(btot[4 * mt + j] * kLog2e);
+          S[mt][0][j] *= eb;
+          S[mt][1][j] *= eb;
+        }
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        bf16x8 bv[2];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const char *vb = smem + LD::VT + slot * 32 * kHalf + (2 * wave + dt) * kHalf + lane * 8;
+          bv[dt] = join44(*(const bf16x4 *)(vb + (2 * sp) * 8 * kHalf),
+                          *(const bf16x4 *)(vb + (2 * sp + 1) * 8 * kHalf));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const bf16x8 a = lds8(smem + LD::KH + (mt * 2 + sp) * kFrag + lane * 16);
+          S[mt][0] = mfma(a, bv[0], S[mt][0]);
+          S[mt][1] = mfma(a, bv[1], S[mt][1]);
+        }
+      }
+    }
+    __syncthreads();  // B3: the next chunk may overwrite LDS
+    if (c + 1 < c_end) cur = nxt;
+  }
+
+  // ---- epilogue
+  if (MODE == MODE_STATE) {
+    float *dst = p.seg_state + (bh * (p.P - 1) + seg) * (size_t)(kF * kDV);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
+    if (wave == 0 && n == 0) {
+      float *dd = p.seg_decay + (bh * (p.P - 1) + seg) * (size_t)kF;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[feat(g, i)] = dsum[i];
+    }
+  } else if (GLA && p.state_out && seg == p.P - 1) {
+    float *dst = p.state_out + bh * kF * kDV;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
+  }
+}
+
+// Start state of every segment: S_1 = e^{D_0} S_in + dS_0, S_{p+1} = e^{D_p} S_p + dS_p.
+// Thread = one state element of one head; the segment slots are overwritten in
+// place (slot p receives the start state of segment p + 1).
+__global__ __launch_bounds__(kNT) void segment_scan_kernel(float *seg_state, const float *seg_decay,
+                                                           const float *state_in, int BH, int P) {
+  const size_t idx = (size_t)blockIdx.x * kNT + threadIdx.x;
+  const size_t per = (size_t)kF * kDV;
+  if (idx >= (size_t)BH * per) return;
+  const size_t bh = idx / per, e = idx % per;
+  const int f = (int)(e / kDV);
+  float s = state_in ? state_in[idx] : 0.0f;
+  for (int q = 0; q < P - 1; ++q) {
+    float *slot = seg_state + (bh * (P - 1) + q) * per;
+    const float dec = exp2_fast(seg_decay[(bh * (P - 1) + q) * kF + f] * kLog2e);
+    s = dec * s + slot[e];
+    slot[e] = s;
+  }
+}
+
+int choose_segments(const LayerArgs &a, int nchunks) {
+  const int bh = a.B * a.H;
+  const int cus = device_cu_count();
+  // about one block per compute unit; at least 4 chunks per segment
+  int P = (cus + bh - 1) / bh;
+  P = max(1, min(P, nchunks / 4));
+  return P;
+}
+
+ChunkParams make_params(const LayerArgs &a, int P, int seg_chunks, int nchunks) {
+  ChunkParams p;
+  p.q = (const bf16 *)a.q; p.k = (const bf16 *)a.k; p.v = (const bf16 *)a.v;
+  p.gate = (const bf16 *)a.gate; p.wq = (const bf16 *)a.wq; p.wk = (const bf16 *)a.wk;
+  p.meta = a.meta; p.state_in = a.state_in; p.state_out = a.state_out; p.o = (bf16 *)a.o;
+  p.seg_state = nullptr; p.seg_decay = nullptr;
+  p.B = a.B; p.H = a.H; p.L = a.L; p.window = a.window; p.n_meta = a.n_meta;
+  p.nchunks = nchunks; p.P = P; p.seg_chunks = seg_chunks;
+  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0;
+  return p;
+}
+
+template <int MODE>
+hipError_t launch_mode(const ChunkParams &p, int blocks, hipStream_t stream) {
+  const int bytes = Lds<MODE>::BYTES;
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_kernel<MODE>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_kernel<MODE>, dim3((unsigned)blocks), dim3(kNT), bytes, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
   return n;
 }
 
-bool chunked_supported(const LayerArgs &, int) { return false; }
-size_t chunked_workspace_bytes(const LayerArgs &, int) { return 0; }
-hipError_t launch_chunked_prefill(const LayerArgs &, int) { return hipErrorNotSupported; }
-bool swa_mfma_supported(const LayerArgs &) { return false; }
-hipError_t launch_swa_mfma(const LayerArgs &) { return hipErrorNotSupported; }
+bool chunked_supported(const LayerArgs &a, int parts) {
+  if (!a.bf16 || a.d != kD || a.dv != kDV) return false;
+  if ((parts & PART_GLA) && (a.f != kF || a.chunk != kC)) return false;
+  if ((parts & PART_SWA) && (a.window < 1 || a.window > kC)) return false;
+  return true;
+}
+
+size_t chunked_workspace_bytes(const LayerArgs &a, int parts) {
+  if (!(parts & PART_GLA) || a.L <= 0) return 0;
+  const int nchunks = (a.L + kC - 1) / kC;
+  const int P = choose_segments(a, nchunks);
+  if (P <= 1) return 0;
+  const size_t bh = (size_t)a.B * a.H;
+  return bh * (P - 1) * ((size_t)kF * kDV + kF) * sizeof(float);
+}
+
+hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
+  if ((size_t)a.B * a.H * a.L == 0) return hipSuccess;
+  const int nchunks = (a.L + kC - 1) / kC;
+  const int bh = a.B * a.H;
+  const int P = choose_segments(a, nchunks);
+  const int seg_chunks = (nchunks + P - 1) / P;
+  // every segment must own at least one chunk
+  const int Peff = (nchunks + seg_chunks - 1) / seg_chunks;
+  ChunkParams p = make_params(a, Peff, seg_chunks, nchunks);
+  if (Peff > 1) {
+    p.seg_state = (float *)a.ws;
+    p.seg_decay = p.seg_state + (size_t)bh * (Peff - 1) * kF * kDV;
+    hipError_t e = launch_mode<MODE_STATE>(p, bh * (Peff - 1), a.stream);
+    if (e != hipSuccess) return e;
+    const size_t elems = (size_t)bh * kF * kDV;
+    hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((elems + kNT - 1) / kNT)), dim3(kNT), 0,
+                       a.stream, p.seg_state, (const float *)p.seg_decay, a.state_in, bh, Peff);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (parts == PART_GLA) return launch_mode<MODE_GLA>(p, bh * Peff, a.stream);
+  return launch_mode<MODE_HYBRID>(p, bh * Peff, a.stream);
+}
+
+bool swa_mfma_supported(const LayerArgs &a) {
+  return a.bf16 && a.d == kD && a.dv == kDV && a.window >= 1 && a.window <= kC;
+}
+
+hipError_t launch_swa_mfma(const LayerArgs &a) {
+  if ((size_t)a.B * a.H * a.L == 0) return hipSuccess;
+  const int nchunks = (a.L + kC - 1) / kC;
+  ChunkParams p = make_params(a, nchunks, 1, nchunks);
+  return launch_mode<MODE_SWA>(p, a.B * a.H * nchunks, a.stream);
+}
 
 }  // namespace glah

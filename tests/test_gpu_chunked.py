@@ -1,0 +1,214 @@
+"""GPU parity of the chunkwise MFMA path (bf16, d = f = d_v = 128, 64-token
+chunks) against the fp64 oracle on the same seeded inputs.
+
+The base workloads (2K and 32K-token LLaMA-3-8B-shaped layers, the batch-8
+strong-decay layer) barely exercise the inter-chunk state pass, because their
+gates decay the state within a few chunks; the slow-decay, gate=1 and
+state-continuation cases make the state pass carry real signal, and the peaked
+case makes the window softmax far from uniform."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_linear_attention_hybrid_amd import binding as G
+from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_prefill, to_f64
+from parity import TOL_BF16, assert_finite, gpu_f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print("[case]", msg, flush=True)
+
+
+def run_hybrid(x, wl, gate_is_log=False, **kw):
+    return G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                              window=wl.window, chunk=64, gate_is_log=gate_is_log, **kw)
+
+
+def ref(x, wl, parts=oracle.PART_BOTH, gate_is_log=False, heads=None, **kw):
+    """Oracle output; ``heads`` = list of (b, h) pairs restricts it to those heads."""
+    if heads is None:
+        o = {k: to_f64(v) for k, v in x.items()}
+        return oracle.layer_fwd(o["q"], o["k"], o["v"], o["gate"], o["wq"], o["wk"], o["meta"],
+                                window=wl.window, gate_is_log=gate_is_log, parts=parts, **kw)
+    outs = []
+    for b, h in heads:
+        o = {k: to_f64(v[b:b + 1, h:h + 1]) for k, v in x.items() if v.dim() == 4}
+        w = {k: to_f64(x[k][h:h + 1]) for k in ("wq", "wk", "meta")}
+        outs.append(oracle.layer_fwd(o["q"], o["k"], o["v"], o["gate"], w["wq"], w["wk"], w["meta"],
+                                     window=wl.window, gate_is_log=gate_is_log, parts=parts)[0, 0])
+    return np.stack(outs)
+
+
+def base(H=4, **kw):
+    return WORKLOADS["prefill_2k"].with_(H=H, **kw)
+
+
+def test_prefill_2k_full():
+    wl = WORKLOADS["prefill_2k"]
+    say("hybrid prefill_2k all 32 heads")
+    x = make_prefill(wl, DEV)
+    o = run_hybrid(x, wl)
+    assert_finite(o, "o")
+    assert row_rel_err(gpu_f64(o), ref(x, wl)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("variant", ["slow_decay", "gate_one", "peaked", "strong_decay"])
+def test_hybrid_variants(variant):
+    wl = base(L=1024)
+    gate_is_log = False
+    if variant == "slow_decay":
+        wl = wl.with_(gate_mean=6.0)
+    elif variant == "peaked":
+        wl = wl.with_(x_std=1.0, w_std=1.0 / np.sqrt(128.0))
+    elif variant == "strong_decay":
+        wl = wl.with_(gate_mean=-2.0, gate_std=1.5)
+    say("hybrid variant %s" % variant)
+    x = make_prefill(wl, DEV, gate_log_zero=(variant == "gate_one"))
+    gate_is_log = variant == "gate_one"
+    o = run_hybrid(x, wl, gate_is_log=gate_is_log)
+    assert_finite(o, "o")
+    assert row_rel_err(gpu_f64(o), ref(x, wl, gate_is_log=gate_is_log)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("extreme", ["logits_plus30", "logits_minus30", "log_minus_inf", "mixed"])
+def test_extreme_gates(extreme):
+    wl = base(H=2, L=300)
+    say("extreme gates %s" % extreme)
+    x = make_prefill(wl, DEV)
+    gate_is_log = False
+    g = x["gate"]
+    if extreme == "logits_plus30":
+        g = torch.full_like(g, 30.0)
+    elif extreme == "logits_minus30":
+        g = torch.full_like(g, -30.0)
+    elif extreme == "log_minus_inf":
+        gate_is_log = True
+        g = torch.full_like(g, float("-inf"))
+    else:  # random mix of open, shut and ordinary gates
+        gen = torch.Generator(device=DEV).manual_seed(7)
+        r = torch.rand(g.shape, generator=gen, device=DEV)
+        g = torch.where(r < 0.1, torch.full_like(g, -30.0), torch.where(r > 0.8, torch.full_like(g, 30.0), g))
+    x = dict(x, gate=g.contiguous())
+    o = run_hybrid(x, wl, gate_is_log=gate_is_log)
+    assert_finite(o, "o")
+    assert row_rel_err(gpu_f64(o), ref(x, wl, gate_is_log=gate_is_log)) <= TOL_BF16
+
+
+def test_gla_and_swa_parts():
+    wl = base(L=700, gate_mean=5.0)
+    say("gla_prefill and swa_meta_attn (MFMA)")
+    x = make_prefill(wl, DEV)
+    o = G.gla_prefill(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], chunk=64)
+    assert row_rel_err(gpu_f64(o), ref(x, wl, parts=oracle.PART_GLA)) <= TOL_BF16
+    o = G.swa_meta_attn(x["q"], x["k"], x["v"], x["meta"], window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref(x, wl, parts=oracle.PART_SWA)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("L", [1, 15, 63, 64, 65, 200, 1000])
+def test_ragged_lengths(L):
+    wl = base(H=3, B=2, L=L, gate_mean=4.0)
+    say("ragged L=%d" % L)
+    x = make_prefill(wl, DEV)
+    o = run_hybrid(x, wl)
+    assert row_rel_err(gpu_f64(o), ref(x, wl)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("window", [1, 2, 17, 63])
+def test_windows(window):
+    wl = base(H=2, L=333, window=window, x_std=0.5)
+    say("window %d" % window)
+    x = make_prefill(wl, DEV)
+    o = run_hybrid(x, wl)
+    assert row_rel_err(gpu_f64(o), ref(x, wl)) <= TOL_BF16
+
+
+def test_no_sinks():
+    wl = base(H=2, L=256, n_meta=0)
+    say("no meta sinks")
+    x = make_prefill(wl, DEV)
+    x["meta"] = torch.zeros((wl.H, 0), device=DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], None,
+                           window=wl.window)
+    assert row_rel_err(gpu_f64(o), ref(x, wl)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("H", [1, 8, 40])
+def test_segment_splits(H):
+    # the number of heads changes how many sequence segments run in parallel
+    wl = base(H=H, L=1536, gate_mean=6.0)
+    say("segment split H=%d" % H)
+    x = make_prefill(wl, DEV)
+    o = run_hybrid(x, wl)
+    heads = [(0, h) for h in sorted(set([0, H // 2, H - 1]))]
+    got = gpu_f64(o)
+    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), ref(x, wl, heads=heads)) <= TOL_BF16
+
+
+def test_state_in_out_continuation():
+    wl = base(H=4, L=1280, gate_mean=6.0)
+    say("state continuation")
+    x = make_prefill(wl, DEV)
+    L1 = 512
+    first = {k: (v[:, :, :L1].contiguous() if v.dim() == 4 else v) for k, v in x.items()}
+    rest = {k: (v[:, :, L1:].contiguous() if v.dim() == 4 else v) for k, v in x.items()}
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    G.gla_prefill(first["q"], first["k"], first["v"], first["gate"], first["wq"], first["wk"],
+                  state_out=st)
+    o2 = G.gla_prefill(rest["q"], rest["k"], rest["v"], rest["gate"], rest["wq"], rest["wk"],
+                       state_in=st, state_out=st)
+    full, sfull = ref(x, wl, parts=oracle.PART_GLA, return_state=True)
+    assert row_rel_err(gpu_f64(o2), full[:, :, L1:]) <= TOL_BF16
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), sfull.reshape(-1, wl.dv)) <= TOL_BF16
+
+
+def test_window_cache_out_mfma():
+    wl = base(H=2, L=200)
+    say("window cache out (MFMA path)")
+    x = make_prefill(wl, DEV)
+    kc = torch.full((wl.B, wl.H, wl.window, wl.d), 3.0, device=DEV, dtype=torch.bfloat16)
+    vc = torch.full((wl.B, wl.H, wl.window, wl.dv), 3.0, device=DEV, dtype=torch.bfloat16)
+    run_hybrid(x, wl, kcache_out=kc, vcache_out=vc)
+    torch.cuda.synchronize()
+    for p in range(wl.L - wl.window, wl.L):
+        assert torch.equal(kc[:, :, p % wl.window], x["k"][:, :, p])
+        assert torch.equal(vc[:, :, p % wl.window], x["v"][:, :, p])
+
+
+def test_deterministic():
+    wl = base(H=4, L=640)
+    say("bitwise determinism")
+    x = make_prefill(wl, DEV)
+    a = run_hybrid(x, wl).clone()
+    b = run_hybrid(x, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_prefill_32k_sampled_heads():
+    wl = WORKLOADS["prefill_32k"]
+    say("hybrid prefill_32k, oracle on 3 sampled heads")
+    x = make_prefill(wl, DEV)
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    o = run_hybrid(x, wl, state_out=st)
+    assert_finite(o, "o")
+    heads = [(0, 0), (0, 17), (0, 31)]
+    got = gpu_f64(o)
+    exp = ref(x, wl, heads=heads)
+    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), exp) <= TOL_BF16
+
+
+def test_strong_decay_8k_sampled_heads():
+    wl = WORKLOADS["strong_decay_8k"]
+    say("strong decay B=8 L=8192, oracle on 4 sampled heads")
+    x = make_prefill(wl, DEV)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                           window=wl.window, chunk=64)
+    assert_finite(o, "o")
+    heads = [(0, 0), (3, 9), (5, 20), (7, 31)]
+    got = gpu_f64(o)
+    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), ref(x, wl, heads=heads)) <= TOL_BF16
