@@ -1,0 +1,268 @@
+// decode.hip -- one recurrent decode step of the hybrid layer at d = f = d_v = 128
+// (window <= 64), bf16 or fp32 tokens, fp32 state updated in place.
+//
+// Constant-memory inference ("Lizard" technical summary, gist.science
+// 2507.09025, Methodology A.1): per (b, h) the step reads the f x d_v fp32 state
+// once and writes it once; everything else is small.  The step is bound by HBM
+// bandwidth, so the block issues its share of the state loads first (16-byte
+// vector loads, 2 x 32 KiB in flight per block) and does the Hedgehog GEMVs and
+// the window scores while they are in flight:
+//   * Hedgehog GEMV: each thread loads 4 rows x 8 columns of each projection
+//     with 16-byte loads, partial sums are reduced across lanes and waves.
+//   * window scores: 4 threads per key, 32 dimensions each, 16-byte loads.
+//   * window values and ring slots: loaded up front with the state.
+// Block = (b, h, 64-column slice of d_v); blocks of one head share an XCD.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace glah {
+
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kD = 128, kF = 128, kF2 = 64, kDV = 128, kMaxW = 64;
+constexpr int kDVS = 64;                 // state columns per block
+constexpr int kC4 = kDVS / 4;            // float4 column groups per block
+constexpr int kNRG = kNT / kC4;          // row groups
+constexpr int kRPT = kF / kNRG;          // state rows per thread
+constexpr int kNSL = kDV / kDVS;         // blocks per head
+constexpr int kKPT = kMaxW / kNRG;       // window keys per thread (values)
+
+struct DecParams {
+  const void *q, *k, *v, *gate, *wq, *wk;
+  const float *meta;
+  float *state;
+  void *kcache, *vcache;
+  const int32_t *pos;
+  void *o;
+  int B, H, window, n_meta;
+  float scale;
+  int gate_is_log;
+};
+
+template <class T> struct Vec;
+template <> struct Vec<bf16> {
+  static __device__ __forceinline__ f32x4 ld4(const bf16 *p) {
+    const bf16x4 x = *(const bf16x4 *)p;
+    return (f32x4){(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+  }
+  static __device__ __forceinline__ void ld8(const bf16 *p, float *o) {
+    const bf16x8 x = *(const bf16x8 *)p;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (float)x[j];
+  }
+  static __device__ __forceinline__ void st4(bf16 *p, f32x4 v) {
+    bf16x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (bf16)v[j];
+    *(bf16x4 *)p = x;
+  }
+};
+template <> struct Vec<float> {
+  static __device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
+  static __device__ __forceinline__ void ld8(const float *p, float *o) {
+    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = a[j];
+      o[4 + j] = b[j];
+    }
+  }
+  static __device__ __forceinline__ void st4(float *p, f32x4 v) { *(f32x4 *)p = v; }
+};
+
+template <class T, int PARTS>
+__global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
+  constexpr bool SWA = PARTS & PART_SWA;
+  using V = Vec<T>;
+  __shared__ float s_uw[4][2][kF2];  // per-wave Hedgehog partial sums
+  __shared__ float s_ph[2][kF];      // phi(q), phi(k)
+  __shared__ float s_gam[kF];
+  __shared__ float s_p[kMaxW];       // window weights
+  __shared__ f32x4 s_red[kNRG][kC4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int bh, slice;
+  {
+    const int bid = blockIdx.x, nbh = p.B * p.H;
+    if ((nbh & 7) == 0) {
+      const int xcd = bid & 7, local = bid >> 3;
+      slice = local % kNSL;
+      bh = (local / kNSL) * 8 + xcd;
+    } else {
+      bh = bid / kNSL;
+      slice = bid % kNSL;
+    }
+  }
+  const int b = bh / p.H, h = bh % p.H;
+  const int w = p.window;
+  const int pos = max(p.pos[b], 0);
+  const int c4 = tid % kC4, rg = tid / kC4;
+  const int col = slice * kDVS + 4 * c4;
+
+  // (1) state slice, first: rows rg + kNRG * ii, four columns per thread
+  float *Sg = p.state + (size_t)bh * kF * kDV;
+  f32x4 S[kRPT];
+#pragma unroll
+  for (int ii = 0; ii < kRPT; ++ii) S[ii] = *(const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col);
+
+  const T *qt = (const T *)p.q + (size_t)bh * kD;
+  const T *kt = (const T *)p.k + (size_t)bh * kD;
+  const T *vt = (const T *)p.v + (size_t)bh * kDV;
+  T *kc = SWA ? (T *)p.kcache + (size_t)bh * w * kD : nullptr;
+  T *vc = SWA ? (T *)p.vcache + (size_t)bh * w * kDV : nullptr;
+  const int n = SWA ? min(pos + 1, w) : 0;  // window keys: tokens pos, pos-1, ..., pos-n+1
+
+  // (2) window values this thread will weight: keys j = rg + kNRG * jj
+  f32x4 vv[kKPT];
+  if (SWA) {
+#pragma unroll
+    for (int jj = 0; jj < kKPT; ++jj) {
+      const int j = rg + kNRG * jj;
+      vv[jj] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      if (j < n) vv[jj] = V::ld4(j == 0 ? vt + col : vc + (size_t)((pos - j) % w) * kDV + col);
+    }
+  }
+  const f32x4 v4 = V::ld4(vt + col);
+
+  // (3) Hedgehog GEMV partials: rows 4*rgw .. 4*rgw+3, columns 8*cb .. 8*cb+7
+  {
+    const int cb = tid & 7, rgw = tid >> 3;
+    const T *Wq = (const T *)p.wq + (size_t)h * kD * kF2;
+    const T *Wk = (const T *)p.wk + (size_t)h * kD * kF2;
+    float pq[8], pk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pq[e] = pk[e] = 0.0f;
+    const f32x4 xq = V::ld4(qt + 4 * rgw), xk = V::ld4(kt + 4 * rgw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float wq[8], wk[8];
+      V::ld8(Wq + (size_t)(4 * rgw + i) * kF2 + 8 * cb, wq);
+      V::ld8(Wk + (size_t)(4 * rgw + i) * kF2 + 8 * cb, wk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pq[e] += xq[i] * wq[e];
+        pk[e] += xk[i] * wk[e];
+      }
+    }
+    // reduce the 8 row groups of this wave (lane bits 3..5)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        pq[e] += __shfl_xor(pq[e], o, 64);
+        pk[e] += __shfl_xor(pk[e], o, 64);
+      }
+    }
+    if ((lane >> 3) == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_uw[wave][0][8 * cb + e] = pq[e];
+        s_uw[wave][1][8 * cb + e] = pk[e];
+      }
+    }
+  }
+  // (4) gates
+  if (tid < kF) s_gam[tid] = gate_from(to_f32(((const T *)p.gate)[(size_t)bh * kF + tid]), p.gate_is_log);
+  // (5) window scores: 4 threads per key, 32 dimensions each
+  if (SWA) {
+    const int j = tid >> 2, qd = tid & 3;
+    float acc = 0.0f;
+    if (j < n) {
+      const T *kr = j == 0 ? kt : kc + (size_t)((pos - j) % w) * kD;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float a8[8], b8[8];
+        V::ld8(qt + 32 * qd + 8 * s, a8);
+        V::ld8(kr + 32 * qd + 8 * s, b8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += a8[e] * b8[e];
+      }
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (qd == 0 && j < kMaxW) s_p[j] = acc * p.scale;
+  }
+  __syncthreads();
+
+  // (6) wave 0 / 1: log-softmax of +u and -u for q / k; wave 2: window softmax
+  if (wave < 2) {
+    const float u = s_uw[0][wave][lane] + s_uw[1][wave][lane] + s_uw[2][wave][lane] + s_uw[3][wave][lane];
+    const float mx = wave_max(u), mn = wave_min(u);
+    const float ep = exp_fast(u - mx), en = exp_fast(mn - u);
+    const float zp = wave_sum(ep), zn = wave_sum(en);
+    s_ph[wave][lane] = ep / zp;
+    s_ph[wave][kF2 + lane] = en / zn;
+  } else if (SWA && wave == 2) {
+    const float s = lane < n ? s_p[lane] : -INFINITY;
+    float m = wave_max(s);
+    const float *meta = p.meta + (size_t)h * p.n_meta;
+    float tm = lane < p.n_meta ? meta[lane] : -INFINITY;
+    m = fmaxf(m, wave_max(tm));
+    const float e = lane < n ? exp_fast(s - m) : 0.0f;
+    const float es = lane < p.n_meta ? exp_fast(tm - m) : 0.0f;
+    const float den = wave_sum(e) + wave_sum(es);
+    s_p[lane] = e / den;
+  }
+  __syncthreads();
+
+  // (7) state update, readout, window weights x values
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ii = 0; ii < kRPT; ++ii) {
+    const int r = rg + kNRG * ii;
+    S[ii] = s_gam[r] * S[ii] + s_ph[1][r] * v4;
+    acc += s_ph[0][r] * S[ii];
+    *(f32x4 *)(Sg + (size_t)r * kDV + col) = S[ii];
+  }
+  if (SWA) {
+#pragma unroll
+    for (int jj = 0; jj < kKPT; ++jj) {
+      const int j = rg + kNRG * jj;
+      if (j < n) acc += s_p[j] * vv[jj];
+    }
+  }
+  s_red[rg][c4] = acc;
+  __syncthreads();
+  if (tid < kC4) {
+    f32x4 s = s_red[0][tid];
+#pragma unroll
+    for (int r2 = 1; r2 < kNRG; ++r2) s += s_red[r2][tid];
+    V::st4((T *)p.o + (size_t)bh * kDV + slice * kDVS + 4 * tid, s);
+  }
+  // (8) ring append: slot pos % w holds token pos - w, which no block reads now
+  if (SWA) {
+    const int slot = pos % w;
+    if (slice == 0 && tid < kD / 4) V::st4(kc + (size_t)slot * kD + 4 * tid, V::ld4(kt + 4 * tid));
+    if (tid < kC4) V::st4(vc + (size_t)slot * kDV + slice * kDVS + 4 * tid, V::ld4(vt + slice * kDVS + 4 * tid));
+  }
+}
+
+template <class T>
+hipError_t dispatch(const LayerArgs &a, int parts) {
+  DecParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.wq = a.wq; p.wk = a.wk; p.meta = a.meta;
+  p.state = a.state; p.kcache = a.kcache; p.vcache = a.vcache; p.pos = a.pos; p.o = a.o;
+  p.B = a.B; p.H = a.H; p.window = a.window; p.n_meta = a.n_meta; p.scale = a.scale;
+  p.gate_is_log = a.gate_is_log ? 1 : 0;
+  const dim3 grid((unsigned)(a.B * a.H * kNSL)), block(kNT);
+  if (parts & PART_SWA)
+    hipLaunchKernelGGL((decode128_kernel<T, PART_BOTH>), grid, block, 0, a.stream, p);
+  else
+    hipLaunchKernelGGL((decode128_kernel<T, PART_GLA>), grid, block, 0, a.stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode128_supported(const LayerArgs &a, int parts) {
+  return a.d == kD && a.f == kF && a.dv == kDV && (parts & PART_GLA) &&
+         (!(parts & PART_SWA) || (a.window >= 1 && a.window <= kMaxW && a.n_meta <= 64));
+}
+
+hipError_t launch_decode128(const LayerArgs &a, int parts) {
+  if (a.B * a.H == 0) return hipSuccess;
+  return a.bf16 ? dispatch<bf16>(a, parts) : dispatch<float>(a, parts);
+}
+
+}  // namespace glah

@@ -41,6 +41,10 @@ hipError_t launch_recurrent_prefill(const LayerArgs &a, int parts);
 hipError_t launch_decode_step(const LayerArgs &a, int parts);
 hipError_t launch_window_cache(const LayerArgs &a);
 
+// Bandwidth-oriented decode step at d = f = d_v = 128, window <= 64.
+bool decode128_supported(const LayerArgs &a, int parts);
+hipError_t launch_decode128(const LayerArgs &a, int parts);
+
 // Chunkwise MFMA path (bf16, d = f = d_v = 128).
 bool chunked_supported(const LayerArgs &a, int parts);
 size_t chunked_workspace_bytes(const LayerArgs &a, int parts);

@@ -423,6 +423,7 @@ hipError_t launch_recurrent_prefill(const LayerArgs &a, int parts) {
 
 hipError_t launch_decode_step(const LayerArgs &a, int parts) {
   if (a.B * a.H == 0) return hipSuccess;
+  if (decode128_supported(a, parts)) return launch_decode128(a, parts);
   // 32 state columns per block: 4 blocks per head at d_v = 128, so a batch of
   // 8 x 32 heads spreads over 1024 blocks.
   return a.bf16 ? decode_dispatch<bf16, 32>(a, parts) : decode_dispatch<float, 32>(a, parts);

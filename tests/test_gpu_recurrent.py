@@ -175,3 +175,38 @@ def test_decode_bf16_llama_shape():
     say("decode bf16 d=f=dv=128 w=64")
     wl = WORKLOADS["decode_b8"].with_(B=2, H=8)
     _decode_case(wl, L0=150, steps=12, dtype_tol=TOL_BF16)
+
+
+def test_decode_fp32_llama_shape():
+    say("decode fp32 d=f=dv=128 w=64")
+    wl = WORKLOADS["decode_b8"].with_(B=2, H=4, dtype="f32")
+    _decode_case(wl, L0=70, steps=8, dtype_tol=TOL_F32)
+
+
+def test_decode_bf16_short_prefix_and_small_window():
+    say("decode bf16 d=128 w=7 prefix 2")
+    wl = WORKLOADS["decode_b8"].with_(B=3, H=2, window=7)
+    _decode_case(wl, L0=2, steps=12, dtype_tol=TOL_BF16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_gated_part_only(dtype):
+    # window 0: the step advances the gated state only; no ring is touched
+    say("decode GLA only %s" % dtype)
+    wl = WORKLOADS["decode_b8"].with_(B=2, H=4, dtype=dtype)
+    x = make_prefill(wl.with_(L=5), DEV)
+    st = torch.randn((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    ost = np.ascontiguousarray(to_f64(st))
+    t = make_decode_token(wl, 0, DEV)
+    pos = torch.full((wl.B,), 9, dtype=torch.int32, device=DEV)
+    o = G.gla_decode_step(t["q"], t["k"], t["v"], t["gate"], x["wq"], x["wk"], None, st, None,
+                          None, pos, window=0)
+    ot = {k: to_f64(v) for k, v in t.items()}
+    dummy_k = np.zeros((wl.B, wl.H, 1, wl.d))
+    dummy_v = np.zeros((wl.B, wl.H, 1, wl.dv))
+    oref = oracle.decode_step(ot["q"], ot["k"], ot["v"], ot["gate"], to_f64(x["wq"]), to_f64(x["wk"]),
+                              None, ost, dummy_k, dummy_v, np.full(wl.B, 9), window=1,
+                              parts=oracle.PART_GLA)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert row_rel_err(gpu_f64(o), oref) <= tol
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), ost.reshape(-1, wl.dv)) <= tol
