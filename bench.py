@@ -202,6 +202,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a reference kernel "
+                         "of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer shards by heads or by sequence segments "
@@ -251,6 +254,15 @@ def main():
                      "mfma_frac": round(nflops / (per_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "nonfinite_outputs": bad,
     }
+    if args.copy_calibration_mib > 0:
+        nel = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": nel * 4, "written": nel * 4}
+        del src, dst
     if not args.no_decode:
         out["decode"] = bench_decode(G, torch)
     if not args.no_cpu_baseline:

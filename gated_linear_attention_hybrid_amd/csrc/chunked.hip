@@ -60,7 +60,7 @@ struct ChunkParams {
   bf16 *o;
   float *seg_state;       // [BH][P-1][F][DV]: end state of segment p from zero (state
                           // pass), overwritten by the scan with the start state of p+1
-  float *seg_decay;       // [BH][P-1][F]: total log-decay of segment p
+  float *seg_decay;       // [BH][P-1][F]: total base-2 log-decay of segment p
   int B, H, L, window, n_meta;
   int nchunks, P, seg_chunks;
   float scale;
@@ -168,7 +168,40 @@ __device__ __forceinline__ float row_bcast15(float x) {
 // factor stays within e^{+-80}.  Gates below e^{-10} (~4.5e-5) act as 4.5e-5:
 // any term they touch is already below 4.5e-5 of its undecayed size, so the
 // change is bounded by that factor.
-constexpr float kMinLogGate = -10.0f;
+constexpr float kMinLog2Gate = -10.0f * kLog2e;
+
+// log2 sigmoid(g) = min(g, 0) log2e - log2(1 + 2^{-|g| log2e})
+__device__ __forceinline__ float log2_sigmoid(float g) {
+  return fminf(g, 0.0f) * kLog2e - log2_fast(1.0f + exp2_fast(-fabsf(g) * kLog2e));
+}
+
+// value of x in lane SRC (0..15) of this lane's 16-lane row (DPP row_newbcast)
+template <int SRC>
+__device__ __forceinline__ float row_bcast_c(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x150 + SRC, 0xF, 0xF, false));
+}
+// the same for an index that is a constant after unrolling (the switch folds)
+__device__ __forceinline__ float row_bcast(float x, int src) {
+  switch (src & 15) {
+    case 0: return row_bcast_c<0>(x);
+    case 1: return row_bcast_c<1>(x);
+    case 2: return row_bcast_c<2>(x);
+    case 3: return row_bcast_c<3>(x);
+    case 4: return row_bcast_c<4>(x);
+    case 5: return row_bcast_c<5>(x);
+    case 6: return row_bcast_c<6>(x);
+    case 7: return row_bcast_c<7>(x);
+    case 8: return row_bcast_c<8>(x);
+    case 9: return row_bcast_c<9>(x);
+    case 10: return row_bcast_c<10>(x);
+    case 11: return row_bcast_c<11>(x);
+    case 12: return row_bcast_c<12>(x);
+    case 13: return row_bcast_c<13>(x);
+    case 14: return row_bcast_c<14>(x);
+    default: return row_bcast_c<15>(x);
+  }
+}
 
 // feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
 __device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
@@ -189,7 +222,8 @@ struct ChunkRegs {
 template <int MODE>
 __device__ __forceinline__ void load_chunk(const ChunkParams &p, size_t bh, int c, ChunkRegs &r) {
   constexpr bool Q = Lds<MODE>::Q, GLA = Lds<MODE>::GLA, SWA = Lds<MODE>::SWA;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int t = c * kC + 16 * wave + n;
   const bool ok = c >= 0 && t < p.L;
   const size_t row = bh * p.L + t;
@@ -237,7 +271,8 @@ void chunk_kernel(ChunkParams p) {
   constexpr int NKS = LD::NKS;
   extern __shared__ __align__(16) char smem[];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int nseg = MODE == MODE_STATE ? p.P - 1 : p.P;
   const size_t bh = blockIdx.x / nseg;
   const int seg = blockIdx.x % nseg;
@@ -290,9 +325,8 @@ void chunk_kernel(ChunkParams p) {
             S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)];
     }
   }
-  float dsum[32];  // total log-decay of the segment (state pass)
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dsum[i] = 0.0f;
+  // total base-2 log-decay of the segment (state pass): features 2n and 2n+1
+  float dsum2[2] = {0.0f, 0.0f};
 
   // ---- window part: keys and values of the chunk before the segment
   if (SWA) {
@@ -310,8 +344,6 @@ void chunk_kernel(ChunkParams p) {
   __syncthreads();
 
   for (int c = c_begin; c < c_end; ++c) {
-    ChunkRegs nxt;
-    if (c + 1 < c_end) load_chunk<MODE>(p, bh, c + 1, nxt);
     const int c0 = c * kC;
     const int slot = LD::VSLOTS == 2 ? (c & 1) : 0;
     const int pslot = slot ^ 1;
@@ -326,12 +358,11 @@ void chunk_kernel(ChunkParams p) {
     }
 
     // ================= row phase 1: features, gates, folds =================
-    // Fold exponents (base 2) of this lane's token for the 32 features F_g:
-    //   lq = log2 phi_q + (b_loc - T_w/2) log2e,  lk = log2 phi_k + (T_w/2 - b_loc) log2e
-    // b_loc: in-tile inclusive cumsum of the log-gates, T_w: the tile total.  The
-    // reference sits at the middle of the tile's decay, so |exponent| <= |T_w|/2.
-    float lq[32], lk[32];
-    bf16x8 kb[4];  // k~ = 2^lk of this lane's token, as MFMA operands
+    // For the 32 features F_g of this lane's token (fold slot i):
+    //   d_i = b_i - T_i/2  (base 2; b: in-tile inclusive log-gate cumsum, T: tile total)
+    //   q~ = phi_q 2^{d},  k~ = phi_k 2^{-d}        |d| <= 80 ln... (|d| <= 115.4 in log2)
+    float qf[32];  // q~ in fp32
+    bf16x8 kb[4];  // k~ as MFMA operands
     if (GLA) {
       f32x4 uk[4], uq[4];
 #pragma unroll
@@ -346,22 +377,24 @@ void chunk_kernel(ChunkParams p) {
           uk[mt] = mfma(lds8(smem + LD::WK + (mt * 4 + s) * kFrag + lane * 16), cur.xk[s], uk[mt]);
           if (Q) uq[mt] = mfma(lds8(smem + LD::WQ + (mt * 4 + s) * kFrag + lane * 16), cur.xq[s], uq[mt]);
         }
-      // log-gates (clamped at kMinLogGate) and their in-tile inclusive cumsum
-      float bl[32], half[32];
+      float dd[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const float a = tok_ok ? fmaxf(log_gate_from((float)cur.xg[i >> 3][i & 7], p.gate_is_log), kMinLogGate)
-                               : 0.0f;
-        bl[i] = row_scan(a);
-        half[i] = 0.5f * row_bcast15(bl[i]);
+        const float gv = (float)cur.xg[i >> 3][i & 7];
+        float a2 = p.gate_is_log ? gv * kLog2e : log2_sigmoid(gv);
+        a2 = tok_ok ? fmaxf(a2, kMinLog2Gate) : 0.0f;
+        dd[i] = row_scan(a2);
       }
       if (n == 15) {
         float *T = (float *)(smem + LD::T) + wave * kF;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) T[feat(g, i)] = bl[i];
+        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
       }
-      // log-softmax of +u and -u over the 64 u-values of each token, plus the fold
-      auto fold = [&](const f32x4 *u, float *out, float sgn) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] -= 0.5f * row_bcast15(dd[i]);
+
+      // Hedgehog softmaxes of +u and -u, scaled by the fold factors
+      auto features = [&](const f32x4 *u, float *out, float sgn) {
         float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -370,95 +403,92 @@ void chunk_kernel(ChunkParams p) {
             mx = fmaxf(mx, u[mt][j]);
             mn = fminf(mn, u[mt][j]);
           }
-        mx = grp_max(mx);
-        mn = grp_min(mn);
+        mx = grp_max(mx) * kLog2e;
+        mn = grp_min(mn) * kLog2e;
         float zp = 0.0f, zn = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            zp += exp2_fast((u[mt][j] - mx) * kLog2e);
-            zn += exp2_fast((mn - u[mt][j]) * kLog2e);
-          }
-        zp = grp_sum(zp);
-        zn = grp_sum(zn);
-        // log2 phi+ = (u - mx) log2e - log2 zp ; log2 phi- = (mn - u) log2e - log2 zn
-        const float lp = log2_fast(zp), ln_ = log2_fast(zn);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
             const int e = 4 * mt + j;
-            out[e] = (u[mt][j] - mx) * kLog2e - lp + sgn * (bl[e] - half[e]) * kLog2e;
-            out[16 + e] = (mn - u[mt][j]) * kLog2e - ln_ + sgn * (bl[16 + e] - half[16 + e]) * kLog2e;
+            out[e] = exp2_fast(u[mt][j] * kLog2e - mx);
+            out[16 + e] = exp2_fast(mn - u[mt][j] * kLog2e);
+            zp += out[e];
+            zn += out[16 + e];
           }
+        const float izp = rcp_fast(grp_sum(zp)), izn = rcp_fast(grp_sum(zn));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          out[e] *= izp * exp2_fast(sgn * dd[e]);
+          out[16 + e] *= izn * exp2_fast(sgn * dd[16 + e]);
+        }
       };
-      fold(uk, lk, -1.0f);
-      if (!tok_ok) {
+      {
+        float kf[32];
+        features(uk, kf, -1.0f);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) lk[i] = -INFINITY;  // padded tokens carry no key
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float tmp[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = exp2_fast(lk[8 * s + j]);
-        kb[s] = pack8(tmp);
+        for (int s = 0; s < 4; ++s) kb[s] = tok_ok ? pack8(kf + 8 * s) : zero8();
       }
       if (INTRA) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (wave * 4 + s) * kFrag + lane * 16, kb[s]);
       }
-      if (Q) fold(uq, lq, 1.0f);
+      if (Q) features(uq, qf, 1.0f);
     }
     __syncthreads();  // B1: tile totals, k~ and raw-k fragments visible
 
     // ================= row phase 2: cross-tile factors, scores =================
+    // Per-tile factors depend on the feature only; lane n computes them for
+    // features 2n, 2n+1 of its group and the others broadcast them (DPP).
     f32x4 Wt[5];  // weights^T for key tiles wave-4 .. wave (index kt - wave + 4)
 #pragma unroll
     for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    float btot[32];
+    float fdec[2];  // 2^{B}: state decay over the chunk
     if (GLA) {
       const float *T = (const float *)(smem + LD::T);
-      float pre[32], tw[32];  // P_w (log-gate sum of earlier tiles), T_w
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        pre[i] = 0.0f;
-        btot[i] = 0.0f;
-        tw[i] = 0.0f;
-      }
+      const int f0 = feat(g, 2 * n);
+      float tt[4][2];
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
+        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
+        tt[w2][0] = v2.x;
+        tt[w2][1] = v2.y;
+      }
+      float pre[2], btot[2], tw[2];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float tv = T[w2 * kF + feat(g, i)];
-          btot[i] += tv;
-          if (w2 < wave) pre[i] += tv;
-          if (w2 == wave) tw[i] = tv;
+      for (int e = 0; e < 2; ++e) {
+        pre[e] = 0.0f;
+        btot[e] = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          btot[e] += tt[w2][e];
+          if (w2 < wave) pre[e] += tt[w2][e];
         }
+        tw[e] = wave == 0 ? tt[0][e] : wave == 1 ? tt[1][e] : wave == 2 ? tt[2][e] : tt[3][e];
+        fdec[e] = exp2_fast(btot[e]);
+        dsum2[e] += btot[e];
       }
-      if (MODE == MODE_STATE) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) dsum[i] += btot[i];
-      }
-      // q-bar = phi_q e^{b} (inter-chunk readout): exponent lq + (P_w + T_w/2)
+      // q-bar = q~ 2^{P + T/2} (inter-chunk readout)
       if (Q) {
+        float fq[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fq[e] = exp2_fast(pre[e] + 0.5f * tw[e]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           float tmp[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * s + j;
-            tmp[j] = exp2_fast(lq[i] + (pre[i] + 0.5f * tw[i]) * kLog2e);
-          }
+          for (int j = 0; j < 8; ++j) tmp[j] = qf[8 * s + j] * row_bcast(fq[j & 1], (8 * s + j) >> 1);
           sts8(smem + LD::QB + (wave * 4 + s) * kFrag + lane * 16, pack8(tmp));
         }
       }
-      {  // k-hat = phi_k e^{B - b} (state update): exponent lk + (B - P_w - T_w/2) <= 0
+      {  // k-hat = k~ 2^{B - P - T/2} (state update), scattered into k-hat^T fragments
+        float fk[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fk[e] = exp2_fast(btot[e] - pre[e] - 0.5f * tw[e]);
         const int sp = wave >> 1, hh = wave & 1, ga = n >> 2, jj = 4 * hh + (n & 3);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const float khat = exp2_fast(lk[i] + (btot[i] - pre[i] - 0.5f * tw[i]) * kLog2e);
+          const float khat = (float)kb[i >> 3][i & 7] * row_bcast(fk[i & 1], i >> 1);
           const int hf = i >> 4, e = i & 15;
           const int mt = 4 * hf + (e >> 2), rr = 4 * g + (e & 3);
           *(bf16 *)(smem + LD::KH + (mt * 2 + sp) * kFrag + (16 * ga + rr) * 16 + jj * 2) = (bf16)khat;
@@ -469,35 +499,29 @@ void chunk_kernel(ChunkParams p) {
         {  // diagonal tile: q~ k~^T with the tile's own reference
           f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            float tmp[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) tmp[j] = exp2_fast(lq[8 * s + j]);
-            acc = mfma(kb[s], pack8(tmp), acc);
-          }
+          for (int s = 0; s < 4; ++s) acc = mfma(kb[s], pack8(qf + 8 * s), acc);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
           Wt[4] = acc;
         }
-        // earlier tiles: q~ scaled by e^{r_w - r_kt} <= 1, r_x = P_x + T_x/2
-        float run[32];  // sum of tile totals kt .. wave-1
-#pragma unroll
-        for (int i = 0; i < 32; ++i) run[i] = 0.0f;
+        // earlier tiles: q~ scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
+        float run[2] = {0.0f, 0.0f};  // log-gate sum of tiles kt .. wave-1
 #pragma unroll
         for (int kt = 3; kt >= 0; --kt) {
           if (kt < wave) {
+            float fo[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              run[e] += tt[kt][e];
+              fo[e] = exp2_fast(run[e] + 0.5f * (tw[e] - tt[kt][e]));
+            }
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               float tmp[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const int i = 8 * s + j;
-                const float tk = T[kt * kF + feat(g, i)];
-                run[i] += tk;
-                tmp[j] = exp2_fast(lq[i] + (run[i] + 0.5f * (tw[i] - tk)) * kLog2e);
-              }
+              for (int j = 0; j < 8; ++j) tmp[j] = qf[8 * s + j] * row_bcast(fo[j & 1], (8 * s + j) >> 1);
               acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), pack8(tmp), acc);
             }
             Wt[kt - wave + 4] = acc;
@@ -526,32 +550,35 @@ void chunk_kernel(ChunkParams p) {
         }
         sc[i] = acc;
       }
-      const int tqa = c0 + 16 * wave + n;  // query position
+      // key position minus query position: 16(i-4) + 4g + j - n; valid when in
+      // (-window, 0] and the key exists (position >= 0)
+      const float sl2 = p.scale * kLog2e;
+      const int qpos = c0 + 16 * wave + n;
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 5; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int ka = c0 + 16 * (wave - 4 + i) + 4 * g + j;
-          const bool ok = ka <= tqa && ka > tqa - p.window && ka >= 0;
-          sc[i][j] = ok ? sc[i][j] * p.scale : -INFINITY;
+          const int rel = 16 * (i - 4) + 4 * g + j - n;
+          const bool ok = rel <= 0 && rel > -p.window && qpos + rel >= 0;
+          sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
           mx = fmaxf(mx, sc[i][j]);
         }
       mx = grp_max(mx);
       const float *meta = p.meta + (size_t)h * p.n_meta;
-      for (int m = 0; m < p.n_meta; ++m) mx = fmaxf(mx, meta[m]);
+      for (int m = 0; m < p.n_meta; ++m) mx = fmaxf(mx, meta[m] * kLog2e);
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 5; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float e = sc[i][j] == -INFINITY ? 0.0f : exp2_fast((sc[i][j] - mx) * kLog2e);
+          const float e = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
           sc[i][j] = e;
           sum += e;
         }
       sum = grp_sum(sum);
-      for (int m = 0; m < p.n_meta; ++m) sum += exp2_fast((meta[m] - mx) * kLog2e);
-      const float inv = 1.0f / sum;
+      for (int m = 0; m < p.n_meta; ++m) sum += exp2_fast(meta[m] * kLog2e - mx);
+      const float inv = rcp_fast(sum);
 #pragma unroll
       for (int i = 0; i < 5; ++i) Wt[i] += sc[i] * inv;
     }
@@ -577,6 +604,9 @@ void chunk_kernel(ChunkParams p) {
         sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(wk4[2], wk4[3]));
       }
     }
+    // the next chunk's inputs: issued now so they arrive during the column phase
+    ChunkRegs nxt;
+    if (c + 1 < c_end) load_chunk<MODE>(p, bh, c + 1, nxt);
     __syncthreads();  // B2: q-bar, k-hat^T, weight fragments visible
 
     // ================= column phase: outputs and state =================
@@ -637,12 +667,13 @@ void chunk_kernel(ChunkParams p) {
       }
     }
 
-    if (GLA) {  // S <- diag(e^{B}) S + k-hat^T V
+    if (GLA) {  // S <- diag(2^{B}) S + k-hat^T V
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float eb = exp2_fast(btot[4 * mt + j] * kLog2e);
+          const int i = 4 * mt + j;
+          const float eb = row_bcast(fdec[i & 1], i >> 1);
           S[mt][0][j] *= eb;
           S[mt][1][j] *= eb;
         }
@@ -676,10 +707,9 @@ void chunk_kernel(ChunkParams p) {
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
-    if (wave == 0 && n == 0) {
+    if (wave == 0) {
       float *dd = p.seg_decay + (bh * (p.P - 1) + seg) * (size_t)kF;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) dd[feat(g, i)] = dsum[i];
+      *(float2 *)(dd + feat(g, 2 * n)) = make_float2(dsum2[0], dsum2[1]);
     }
   } else if (GLA && p.state_out && seg == p.P - 1) {
     float *dst = p.state_out + bh * kF * kDV;
@@ -705,7 +735,7 @@ __global__ __launch_bounds__(kNT) void segment_scan_kernel(float *seg_state, con
   float s = state_in ? state_in[idx] : 0.0f;
   for (int q = 0; q < P - 1; ++q) {
     float *slot = seg_state + (bh * (P - 1) + q) * per;
-    const float dec = exp2_fast(seg_decay[(bh * (P - 1) + q) * kF + f] * kLog2e);
+    const float dec = exp2_fast(seg_decay[(bh * (P - 1) + q) * kF + f]);  // base-2 log-decay
     s = dec * s + slot[e];
     slot[e] = s;
   }
