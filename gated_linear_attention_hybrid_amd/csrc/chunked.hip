@@ -170,9 +170,10 @@ __device__ __forceinline__ float row_bcast15(float x) {
 // change is bounded by that factor.
 constexpr float kMinLog2Gate = -10.0f * kLog2e;
 
-// log2 sigmoid(g) = min(g, 0) log2e - log2(1 + 2^{-|g| log2e})
+// log2 sigmoid(g) = -log2(1 + 2^{-g log2e}).  For g below about -88 the power
+// overflows and the result is -inf, which the log-gate floor below replaces.
 __device__ __forceinline__ float log2_sigmoid(float g) {
-  return fminf(g, 0.0f) * kLog2e - log2_fast(1.0f + exp2_fast(-fabsf(g) * kLog2e));
+  return -log2_fast(1.0f + exp2_fast(-g * kLog2e));
 }
 
 // value of x in lane SRC (0..15) of this lane's 16-lane row (DPP row_newbcast)
@@ -216,54 +217,74 @@ struct ChunkRegs {
   bf16x8 xq[4];  // q[token 16w+n][32g + 8s + j]
   bf16x8 xk[4];  // k, same layout
   bf16x8 xg[4];  // gate[token][feat(g, 8s + j)]
-  bf16x8 xv[4];  // v[token 4kg + i][8dc + j] (V^T staging)
+  bf16x8 xv[4];  // v[token 16w+n][32s + 8g + j]
 };
 
-template <int MODE>
+// Parts of a chunk's inputs, loaded separately so that each part of the next
+// chunk can be requested as soon as this chunk's copy has been consumed.
+enum { LOAD_V = 1, LOAD_QK = 2, LOAD_G = 4, LOAD_ALL = 7 };
+
+template <int MODE, int PARTS>
 __device__ __forceinline__ void load_chunk(const ChunkParams &p, size_t bh, int c, ChunkRegs &r) {
   constexpr bool Q = Lds<MODE>::Q, GLA = Lds<MODE>::GLA, SWA = Lds<MODE>::SWA;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int t = c * kC + 16 * wave + n;
-  const bool ok = c >= 0 && t < p.L;
+  // Rows outside [0, L) are read from a clamped, valid row instead of being
+  // zero-filled: every consumer masks such tokens (gates and keys of tokens >= L,
+  // window keys before 0, outputs not stored), and unconditional loads let the
+  // prefetch stay in flight (a conditional zero-fill would have to wait for it).
+  const int t = min(max(c * kC + 16 * wave + n, 0), p.L - 1);
   const size_t row = bh * p.L + t;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (Q) r.xq[s] = ok ? *(const bf16x8 *)(p.q + row * kD + 32 * g + 8 * s) : zero8();
-    if (GLA || SWA) r.xk[s] = ok ? *(const bf16x8 *)(p.k + row * kD + 32 * g + 8 * s) : zero8();
-    if (GLA) r.xg[s] = ok ? *(const bf16x8 *)(p.gate + row * kF + feat(g, 8 * s)) : zero8();
-  }
-  const int kg = tid >> 4, dc = tid & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tv = c * kC + 4 * kg + i;
-    r.xv[i] = (c >= 0 && tv < p.L) ? *(const bf16x8 *)(p.v + (bh * p.L + tv) * kDV + 8 * dc) : zero8();
+    if (Q && (PARTS & LOAD_QK)) r.xq[s] = *(const bf16x8 *)(p.q + row * kD + 32 * g + 8 * s);
+    if ((GLA || SWA) && (PARTS & LOAD_QK)) r.xk[s] = *(const bf16x8 *)(p.k + row * kD + 32 * g + 8 * s);
+    if (GLA && (PARTS & LOAD_G)) r.xg[s] = *(const bf16x8 *)(p.gate + row * kF + feat(g, 8 * s));
+    if (PARTS & LOAD_V) r.xv[s] = *(const bf16x8 *)(p.v + row * kDV + 32 * s + 8 * g);
   }
 }
 
-// V^T half fragments of one chunk into ring slot `slot`: for key tile kt and
-// d_v tile (2w + dt), lane 16g + r holds v[16kt + 4g + j][dvcol(w, dt, r)].
+// 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
+// picks K-slot (group n/4, element 4*dt + n%4).  A x sel(dt) re-lays a
+// row-per-lane operand (lane = row, 8 K-values) into accumulator form
+// (lane = column, 4 consecutive rows): a transpose on the matrix core, exact
+// for bf16 inputs since every output is one input times 1.
+__device__ __forceinline__ bf16x8 select_operand(int dt) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  bf16x8 b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = (bf16)((g == (n >> 2) && j == 4 * dt + (n & 3)) ? 1.0f : 0.0f);
+  return b;
+}
+
+__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
+  bf16x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+// V^T half fragments of this wave's 16 tokens into ring slot `slot`: for d_v
+// tile (2w' + dt), lane 16g + r holds v[16*wave + 4g + j][dvcol(w', dt, r)].
+// K-step s of xv covers d_v [32s, 32s+32), i.e. the two d_v tiles of w' = s.
 template <int MODE>
-__device__ __forceinline__ void store_vt(char *smem, int slot, const ChunkRegs &r) {
-  const int tid = threadIdx.x, kg = tid >> 4, dc = tid & 15;
-  const int kt = kg >> 2, ga = kg & 3;
-  char *base = smem + Lds<MODE>::VT + slot * 32 * kHalf + kt * 8 * kHalf;
+__device__ __forceinline__ void store_vt(char *smem, int slot, const ChunkRegs &r, const bf16x8 *sel) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char *base = smem + Lds<MODE>::VT + (slot * 4 + wave) * 8 * kHalf + lane * 8;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int dv = 8 * dc + e;
-    const int w = dv >> 5, within = dv & 31;
-    const int rr = 4 * (within >> 3) + (within & 3);
-    const int dt = (within >> 2) & 1;
-    bf16x4 col;
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) col[i] = r.xv[i][e];
-    *(bf16x4 *)(base + (2 * w + dt) * kHalf + (16 * ga + rr) * 8) = col;
-  }
+    for (int dt = 0; dt < 2; ++dt) {
+      const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
+                                                            0, 0, 0);
+      *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t);
+    }
 }
 
 // ---------------------------------------------------------------- the kernel
 template <int MODE>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MODE == MODE_STATE ? 2 : 1, MODE == MODE_STATE ? 2 : 1)))
 void chunk_kernel(ChunkParams p) {
   using LD = Lds<MODE>;
   constexpr bool Q = LD::Q, GLA = LD::GLA, SWA = LD::SWA;
@@ -325,303 +346,55 @@ void chunk_kernel(ChunkParams p) {
             S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)];
     }
   }
+  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
+  // meta-memory sinks of this head, base 2: max_m t_m log2e and
+  // sum_m 2^{t_m log2e - max}, so a query's denominator needs one power of two
+  float meta_max = -INFINITY, meta_sum = 0.0f;
+  if (SWA) {
+    const float *meta = p.meta + (size_t)h * p.n_meta;
+    for (int m = 0; m < p.n_meta; ++m) meta_max = fmaxf(meta_max, meta[m] * kLog2e);
+    for (int m = 0; m < p.n_meta; ++m) meta_sum += exp2_fast(meta[m] * kLog2e - meta_max);
+    if (p.n_meta == 0) meta_max = 0.0f;  // meta_sum = 0: no sink mass
+  }
   // total base-2 log-decay of the segment (state pass): features 2n and 2n+1
   float dsum2[2] = {0.0f, 0.0f};
 
   // ---- window part: keys and values of the chunk before the segment
   if (SWA) {
     ChunkRegs pr;
-    load_chunk<MODE>(p, bh, c_begin - 1, pr);
+    load_chunk<MODE, LOAD_ALL>(p, bh, c_begin - 1, pr);
     const int slot = (c_begin - 1) & 1;
-    store_vt<MODE>(smem, slot, pr);
+    store_vt<MODE>(smem, slot, pr, sel);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       sts8(smem + LD::RK + ((slot * 4 + wave) * 4 + s) * kFrag + lane * 16, pr.xk[s]);
   }
 
-  ChunkRegs cur;
-  load_chunk<MODE>(p, bh, c_begin, cur);
-  __syncthreads();
-
-  for (int c = c_begin; c < c_end; ++c) {
-    const int c0 = c * kC;
-    const int slot = LD::VSLOTS == 2 ? (c & 1) : 0;
+  // ================= column phase of chunk cc: outputs and state =================
+  // Runs while the next chunk's inputs are in flight (software pipelining).
+  float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
+  auto column = [&](int cc) {
+    const int c0 = cc * kC;
+    const int slot = LD::VSLOTS == 2 ? (cc & 1) : 0;
     const int pslot = slot ^ 1;
-    const int tq = c0 + 16 * wave + n;  // this lane's token in the row phase
-    const bool tok_ok = tq < p.L;
-
-    store_vt<MODE>(smem, slot, cur);
-    if (SWA) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sts8(smem + LD::RK + ((slot * 4 + wave) * 4 + s) * kFrag + lane * 16, cur.xk[s]);
-    }
-
-    // ================= row phase 1: features, gates, folds =================
-    // For the 32 features F_g of this lane's token (fold slot i):
-    //   d_i = b_i - T_i/2  (base 2; b: in-tile inclusive log-gate cumsum, T: tile total)
-    //   q~ = phi_q 2^{d},  k~ = phi_k 2^{-d}        |d| <= 80 ln... (|d| <= 115.4 in log2)
-    float qf[32];  // q~ in fp32
-    bf16x8 kb[4];  // k~ as MFMA operands
-    if (GLA) {
-      f32x4 uk[4], uq[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        uk[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        uq[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uk[mt] = mfma(lds8(smem + LD::WK + (mt * 4 + s) * kFrag + lane * 16), cur.xk[s], uk[mt]);
-          if (Q) uq[mt] = mfma(lds8(smem + LD::WQ + (mt * 4 + s) * kFrag + lane * 16), cur.xq[s], uq[mt]);
-        }
-      float dd[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float gv = (float)cur.xg[i >> 3][i & 7];
-        float a2 = p.gate_is_log ? gv * kLog2e : log2_sigmoid(gv);
-        a2 = tok_ok ? fmaxf(a2, kMinLog2Gate) : 0.0f;
-        dd[i] = row_scan(a2);
-      }
-      if (n == 15) {
-        float *T = (float *)(smem + LD::T) + wave * kF;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) dd[i] -= 0.5f * row_bcast15(dd[i]);
-
-      // Hedgehog softmaxes of +u and -u, scaled by the fold factors
-      auto features = [&](const f32x4 *u, float *out, float sgn) {
-        float mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            mx = fmaxf(mx, u[mt][j]);
-            mn = fminf(mn, u[mt][j]);
-          }
-        mx = grp_max(mx) * kLog2e;
-        mn = grp_min(mn) * kLog2e;
-        float zp = 0.0f, zn = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * mt + j;
-            out[e] = exp2_fast(u[mt][j] * kLog2e - mx);
-            out[16 + e] = exp2_fast(mn - u[mt][j] * kLog2e);
-            zp += out[e];
-            zn += out[16 + e];
-          }
-        const float izp = rcp_fast(grp_sum(zp)), izn = rcp_fast(grp_sum(zn));
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          out[e] *= izp * exp2_fast(sgn * dd[e]);
-          out[16 + e] *= izn * exp2_fast(sgn * dd[16 + e]);
-        }
-      };
-      {
-        float kf[32];
-        features(uk, kf, -1.0f);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kb[s] = tok_ok ? pack8(kf + 8 * s) : zero8();
-      }
-      if (INTRA) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (wave * 4 + s) * kFrag + lane * 16, kb[s]);
-      }
-      if (Q) features(uq, qf, 1.0f);
-    }
-    __syncthreads();  // B1: tile totals, k~ and raw-k fragments visible
-
-    // ================= row phase 2: cross-tile factors, scores =================
-    // Per-tile factors depend on the feature only; lane n computes them for
-    // features 2n, 2n+1 of its group and the others broadcast them (DPP).
-    f32x4 Wt[5];  // weights^T for key tiles wave-4 .. wave (index kt - wave + 4)
-#pragma unroll
-    for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    float fdec[2];  // 2^{B}: state decay over the chunk
-    if (GLA) {
-      const float *T = (const float *)(smem + LD::T);
-      const int f0 = feat(g, 2 * n);
-      float tt[4][2];
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
-        tt[w2][0] = v2.x;
-        tt[w2][1] = v2.y;
-      }
-      float pre[2], btot[2], tw[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        pre[e] = 0.0f;
-        btot[e] = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          btot[e] += tt[w2][e];
-          if (w2 < wave) pre[e] += tt[w2][e];
-        }
-        tw[e] = wave == 0 ? tt[0][e] : wave == 1 ? tt[1][e] : wave == 2 ? tt[2][e] : tt[3][e];
-        fdec[e] = exp2_fast(btot[e]);
-        dsum2[e] += btot[e];
-      }
-      // q-bar = q~ 2^{P + T/2} (inter-chunk readout)
-      if (Q) {
-        float fq[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) fq[e] = exp2_fast(pre[e] + 0.5f * tw[e]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float tmp[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) tmp[j] = qf[8 * s + j] * row_bcast(fq[j & 1], (8 * s + j) >> 1);
-          sts8(smem + LD::QB + (wave * 4 + s) * kFrag + lane * 16, pack8(tmp));
-        }
-      }
-      {  // k-hat = k~ 2^{B - P - T/2} (state update), scattered into k-hat^T fragments
-        float fk[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) fk[e] = exp2_fast(btot[e] - pre[e] - 0.5f * tw[e]);
-        const int sp = wave >> 1, hh = wave & 1, ga = n >> 2, jj = 4 * hh + (n & 3);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float khat = (float)kb[i >> 3][i & 7] * row_bcast(fk[i & 1], i >> 1);
-          const int hf = i >> 4, e = i & 15;
-          const int mt = 4 * hf + (e >> 2), rr = 4 * g + (e & 3);
-          *(bf16 *)(smem + LD::KH + (mt * 2 + sp) * kFrag + (16 * ga + rr) * 16 + jj * 2) = (bf16)khat;
-        }
-      }
-      // intra-chunk scores A^T for key tiles 0..wave
-      if (INTRA) {
-        {  // diagonal tile: q~ k~^T with the tile's own reference
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma(kb[s], pack8(qf + 8 * s), acc);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
-          Wt[4] = acc;
-        }
-        // earlier tiles: q~ scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
-        float run[2] = {0.0f, 0.0f};  // log-gate sum of tiles kt .. wave-1
-#pragma unroll
-        for (int kt = 3; kt >= 0; --kt) {
-          if (kt < wave) {
-            float fo[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              run[e] += tt[kt][e];
-              fo[e] = exp2_fast(run[e] + 0.5f * (tw[e] - tt[kt][e]));
-            }
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              float tmp[8];
-#pragma unroll
-              for (int j = 0; j < 8; ++j) tmp[j] = qf[8 * s + j] * row_bcast(fo[j & 1], (8 * s + j) >> 1);
-              acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), pack8(tmp), acc);
-            }
-            Wt[kt - wave + 4] = acc;
-          }
-        }
-      }
-    }
-
-    if (SWA) {
-      // band scores for key tiles wave-4 .. wave, one-shot softmax with sinks
-      f32x4 sc[5];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int kt = wave - 4 + i;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 a;
-          if (i == 4)
-            a = cur.xk[s];
-          else if (kt >= 0)
-            a = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
-          else
-            a = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
-          acc = mfma(a, cur.xq[s], acc);
-        }
-        sc[i] = acc;
-      }
-      // key position minus query position: 16(i-4) + 4g + j - n; valid when in
-      // (-window, 0] and the key exists (position >= 0)
-      const float sl2 = p.scale * kLog2e;
-      const int qpos = c0 + 16 * wave + n;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rel = 16 * (i - 4) + 4 * g + j - n;
-          const bool ok = rel <= 0 && rel > -p.window && qpos + rel >= 0;
-          sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
-          mx = fmaxf(mx, sc[i][j]);
-        }
-      mx = grp_max(mx);
-      const float *meta = p.meta + (size_t)h * p.n_meta;
-      for (int m = 0; m < p.n_meta; ++m) mx = fmaxf(mx, meta[m] * kLog2e);
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
-          sc[i][j] = e;
-          sum += e;
-        }
-      sum = grp_sum(sum);
-      for (int m = 0; m < p.n_meta; ++m) sum += exp2_fast(meta[m] * kLog2e - mx);
-      const float inv = rcp_fast(sum);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) Wt[i] += sc[i] * inv;
-    }
-
-    if (Q) {
-      // weight fragments for the (weights x V) GEMM
-      if (SWA) {
-        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(Wt[0], Wt[1]));
-        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(Wt[2], Wt[3]));
-        sts8(smem + LD::W + (wave * NKS + 2) * kFrag + lane * 16,
-             pack44(Wt[4], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}));
-      } else {
-        // key tiles 0..3 of the chunk: Wt[kt - wave + 4], zero beyond the diagonal
-        f32x4 wk4[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          wk4[kt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int i = 0; i < 5; ++i)
-            if (kt <= wave && i == kt - wave + 4) wk4[kt] = Wt[i];
-        }
-        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(wk4[0], wk4[1]));
-        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(wk4[2], wk4[3]));
-      }
-    }
-    // the next chunk's inputs: issued now so they arrive during the column phase
-    ChunkRegs nxt;
-    if (c + 1 < c_end) load_chunk<MODE>(p, bh, c + 1, nxt);
-    __syncthreads();  // B2: q-bar, k-hat^T, weight fragments visible
-
-    // ================= column phase: outputs and state =================
     if (Q) {
       f32x4 O[4][2];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) O[qt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      if (GLA) {  // inter-chunk readout: O^T += S^T q-bar^T
+      if (GLA) {  // inter-chunk readout: O^T += S^T q-bar^T; the state is decayed
+                  // (S <- diag(2^{B}) S) right after it is read for the readout
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const bf16x8 a = pack44(S[2 * s][dt], S[2 * s + 1][dt]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              S[2 * s][dt][j] *= row_bcast(fdec[j & 1], (8 * s + j) >> 1);
+              S[2 * s + 1][dt][j] *= row_bcast(fdec[j & 1], (8 * s + 4 + j) >> 1);
+            }
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt)
               O[qt][dt] = mfma(a, lds8(smem + LD::QB + (qt * 4 + s) * kFrag + lane * 16), O[qt][dt]);
@@ -667,16 +440,19 @@ void chunk_kernel(ChunkParams p) {
       }
     }
 
-    if (GLA) {  // S <- diag(2^{B}) S + k-hat^T V
+    if (GLA) {  // S <- diag(2^{B}) S + k-hat^T V (the decay is already applied in the
+                // readout when there are queries)
+      if (!Q) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * mt + j;
-          const float eb = row_bcast(fdec[i & 1], i >> 1);
-          S[mt][0][j] *= eb;
-          S[mt][1][j] *= eb;
-        }
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * mt + j;
+            const float eb = row_bcast(fdec[i & 1], i >> 1);
+            S[mt][0][j] *= eb;
+            S[mt][1][j] *= eb;
+          }
+      }
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         bf16x8 bv[2];
@@ -694,8 +470,315 @@ void chunk_kernel(ChunkParams p) {
         }
       }
     }
-    __syncthreads();  // B3: the next chunk may overwrite LDS
-    if (c + 1 < c_end) cur = nxt;
+  };
+
+  ChunkRegs cur;
+  load_chunk<MODE, LOAD_ALL>(p, bh, c_begin, cur);
+  __syncthreads();
+
+  for (int c = c_begin; c <= c_end; ++c) {
+    if (c > c_begin) column(c - 1);
+    __syncthreads();  // B3: LDS fragments of chunk c-1 consumed
+    if (c == c_end) break;
+    const int c0 = c * kC;
+    const int slot = LD::VSLOTS == 2 ? (c & 1) : 0;
+    const int pslot = slot ^ 1;
+    const int tq = c0 + 16 * wave + n;  // this lane's token in the row phase
+    const bool tok_ok = tq < p.L;
+    const bool full = c0 + kC <= p.L;  // every token of the chunk exists (uniform)
+
+    const bool more = c + 1 < c_end;
+    store_vt<MODE>(smem, slot, cur, sel);
+    if (more) load_chunk<MODE, LOAD_V>(p, bh, c + 1, cur);
+    f32x4 Wt[5];  // weights^T for key tiles wave-4+i, i = 0..4 (i = 4: the diagonal tile)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (SWA) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sts8(smem + LD::RK + ((slot * 4 + wave) * 4 + s) * kFrag + lane * 16, cur.xk[s]);
+      __syncthreads();  // B0: raw-k fragments of this chunk visible
+      // band scores for key tiles wave-4 .. wave, one-shot softmax with sinks
+      f32x4 sc[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int kt = wave - 4 + i;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 a;
+          if (i == 4)
+            a = cur.xk[s];
+          else if (kt >= 0)
+            a = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
+          else
+            a = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
+          acc = mfma(a, cur.xq[s], acc);
+        }
+        sc[i] = acc;
+      }
+      // key position minus query position: 16(i-4) + 4g + j - n; valid when in
+      // (-window, 0] and the key exists (position >= 0)
+      const float sl2 = p.scale * kLog2e;
+      const int qpos = c0 + 16 * wave + n;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rel = 16 * (i - 4) + 4 * g + j - n;
+          const bool ok = rel <= 0 && rel > -p.window && qpos + rel >= 0;
+          sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
+          mx = fmaxf(mx, sc[i][j]);
+        }
+      mx = grp_max(mx);
+      mx = fmaxf(mx, meta_max);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
+          sc[i][j] = e;
+          sum += e;
+        }
+      sum = grp_sum(sum);
+      sum += meta_sum * exp2_fast(meta_max - mx);  // sum_m 2^{t_m log2e - mx}
+      const float inv = rcp_fast(sum);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) Wt[i] = sc[i] * inv;
+      if (!GLA && more) load_chunk<MODE, LOAD_QK>(p, bh, c + 1, cur);
+    }
+
+    // ================= row phase 1: features, gates, folds =================
+    // For the 32 features F_g of this lane's token (fold slot i):
+    //   d_i = b_i - T_i/2  (base 2; b: in-tile inclusive log-gate cumsum, T: tile total)
+    //   q~ = phi_q 2^{d},  k~ = phi_k 2^{-d},  |d| <= 10 log2(e) * 16 / 2
+    bf16x8 qb[4];  // q~ as MFMA operands
+    bf16x8 kb[4];  // k~ as MFMA operands
+    if (GLA) {
+      f32x4 uk[4], uq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        uk[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        uq[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uk[mt] = mfma(lds8(smem + LD::WK + (mt * 4 + s) * kFrag + lane * 16), cur.xk[s], uk[mt]);
+          if (Q) uq[mt] = mfma(lds8(smem + LD::WQ + (mt * 4 + s) * kFrag + lane * 16), cur.xq[s], uq[mt]);
+        }
+      if (more) load_chunk<MODE, LOAD_QK>(p, bh, c + 1, cur);
+      float dd[32];
+      if (p.gate_is_log) {  // one uniform branch around the whole loop
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dd[i] = (float)cur.xg[i >> 3][i & 7] * kLog2e;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dd[i] = log2_sigmoid((float)cur.xg[i >> 3][i & 7]);
+      }
+      if (more) load_chunk<MODE, LOAD_G>(p, bh, c + 1, cur);
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dd[i] = fmaxf(dd[i], kMinLog2Gate);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dd[i] = tok_ok ? fmaxf(dd[i], kMinLog2Gate) : 0.0f;
+      }
+      // in-tile inclusive cumsum over the 16 tokens: one scan step across all 32
+      // features at a time, so consecutive DPP reads never wait on each other
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] += row_shr<1>(dd[i]);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] += row_shr<2>(dd[i]);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] += row_shr<4>(dd[i]);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] += row_shr<8>(dd[i]);
+      if (n == 15) {
+        float *T = (float *)(smem + LD::T) + wave * kF;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] -= 0.5f * row_bcast15(dd[i]);
+
+      // Hedgehog softmaxes of +u and -u, scaled by the fold factors
+      auto features = [&](const f32x4 *u, bf16x8 *outb, float sgn) {
+        float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            mx = fmaxf(mx, u[mt][j]);
+            mn = fminf(mn, u[mt][j]);
+          }
+        mx = grp_max(mx) * kLog2e;
+        mn = grp_min(mn) * kLog2e;
+        float out[32];
+        float zp = 0.0f, zn = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * mt + j;
+            out[e] = exp2_fast(u[mt][j] * kLog2e - mx);
+            out[16 + e] = exp2_fast(mn - u[mt][j] * kLog2e);
+            zp += out[e];
+            zn += out[16 + e];
+          }
+        const float izp = rcp_fast(grp_sum(zp)), izn = rcp_fast(grp_sum(zn));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          out[e] *= izp * exp2_fast(sgn * dd[e]);
+          out[16 + e] *= izn * exp2_fast(sgn * dd[16 + e]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) outb[s] = pack8(out + 8 * s);
+      };
+      features(uk, kb, -1.0f);
+      if (!full && !tok_ok) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kb[s] = zero8();
+      }
+      if (INTRA) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (wave * 4 + s) * kFrag + lane * 16, kb[s]);
+      }
+      if (Q) features(uq, qb, 1.0f);
+    }
+    __syncthreads();  // B1: tile totals and k~ fragments visible
+
+    // ================= row phase 2: cross-tile factors, intra scores =================
+    // Per-tile factors depend on the feature only; lane n computes them for
+    // features 2n, 2n+1 of its group and the others broadcast them (DPP).
+    if (GLA) {
+      const float *T = (const float *)(smem + LD::T);
+      const int f0 = feat(g, 2 * n);
+      float tt[4][2];
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
+        tt[w2][0] = v2.x;
+        tt[w2][1] = v2.y;
+      }
+      float pre[2], btot[2], tw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pre[e] = 0.0f;
+        btot[e] = 0.0f;
+        tw[e] = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          btot[e] += tt[w2][e];
+          if (w2 < wave) pre[e] += tt[w2][e];
+          if (w2 == wave) tw[e] = tt[w2][e];
+        }
+        fdec[e] = exp2_fast(btot[e]);
+        dsum2[e] += btot[e];
+      }
+      // q-bar = q~ 2^{P + T/2} (inter-chunk readout)
+      if (Q) {
+        float fq[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fq[e] = exp2_fast(pre[e] + 0.5f * tw[e]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float tmp[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) tmp[j] = (float)qb[s][j] * row_bcast(fq[j & 1], (8 * s + j) >> 1);
+          sts8(smem + LD::QB + (wave * 4 + s) * kFrag + lane * 16, pack8(tmp));
+        }
+      }
+      {  // k-hat = k~ 2^{B - P - T/2} (state update) -> k-hat^T fragments: state
+         // tile mt takes its 16 features from K-step s(mt) = 2(mt/4) + (mt%4)/2 of
+         // the token-row operand, transposed on the matrix core
+        float fk[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) fk[e] = exp2_fast(btot[e] - pre[e] - 0.5f * tw[e]);
+        bf16x8 kh[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          float tmp[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) tmp[j] = (float)kb[s2][j] * row_bcast(fk[j & 1], (8 * s2 + j) >> 1);
+          kh[s2] = pack8(tmp);
+        }
+        const int sp = wave >> 1, hh = wave & 1;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const int s2 = 2 * (mt >> 2) + ((mt & 3) >> 1);
+          const f32x4 t = mfma(kh[s2], sel[mt & 1], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+          *(bf16x4 *)(smem + LD::KH + (mt * 2 + sp) * kFrag + lane * 16 + hh * 8) = pack4(t);
+        }
+      }
+      // intra-chunk scores A^T for key tiles kt = wave-4+i, i = 1..4, kt >= 0
+      if (INTRA) {
+        {  // diagonal tile: q~ k~^T with the tile's own reference
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mfma(kb[s], qb[s], acc);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
+          Wt[4] += acc;
+        }
+        // earlier tiles: q~ scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          const int kt = wave - 4 + i;
+          if (kt >= 0) {
+            float fo[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float run = 0.0f, tk = 0.0f;  // log-gate sum of tiles kt .. wave-1
+#pragma unroll
+              for (int w2 = 0; w2 < 4; ++w2) {
+                if (w2 >= kt && w2 < wave) run += tt[w2][e];
+                if (w2 == kt) tk = tt[w2][e];
+              }
+              fo[e] = exp2_fast(run + 0.5f * (tw[e] - tk));
+            }
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              float tmp[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) tmp[j] = (float)qb[s][j] * row_bcast(fo[j & 1], (8 * s + j) >> 1);
+              acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), pack8(tmp), acc);
+            }
+            Wt[i] += acc;
+          }
+        }
+      }
+    }
+
+    if (Q) {
+      // weight fragments for the (weights x V) GEMM
+      if (SWA) {
+        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(Wt[0], Wt[1]));
+        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(Wt[2], Wt[3]));
+        sts8(smem + LD::W + (wave * NKS + 2) * kFrag + lane * 16,
+             pack44(Wt[4], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}));
+      } else {
+        // absolute key tiles 0..3 of the chunk: tile kt is Wt[kt - wave + 4]
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 w0 = z, w1 = z, w2 = z, w3 = z;
+        switch (wave) {
+          case 0: w0 = Wt[4]; break;
+          case 1: w0 = Wt[3]; w1 = Wt[4]; break;
+          case 2: w0 = Wt[2]; w1 = Wt[3]; w2 = Wt[4]; break;
+          default: w0 = Wt[1]; w1 = Wt[2]; w2 = Wt[3]; w3 = Wt[4]; break;
+        }
+        sts8(smem + LD::W + (wave * NKS + 0) * kFrag + lane * 16, pack44(w0, w1));
+        sts8(smem + LD::W + (wave * NKS + 1) * kFrag + lane * 16, pack44(w2, w3));
+      }
+    }
+    __syncthreads();  // B2: q-bar, k-hat^T, weight fragments visible
+
   }
 
   // ---- epilogue
