@@ -1,0 +1,196 @@
+// chunk_common.hpp -- shared pieces of the chunkwise MFMA prefill kernels for
+// gfx950 (bf16 inputs, fp32 accumulation, d = f = d_v = 128, 64-token chunks):
+// call parameters, sizes and the small device helpers (MFMA operand packing,
+// lane-group reductions, DPP scans and broadcasts, the log-gate).
+#pragma once
+#include "device_common.hpp"
+
+namespace glah {
+
+struct ChunkParams {
+  const bf16 *q, *k, *v, *gate, *wq, *wk;
+  const float *meta;
+  const float *state_in;  // [BH][F][DV] state before token 0 (segment 0), or null
+  float *state_out;       // [BH][F][DV] written by the last segment, or null
+  bf16 *o;
+  float *seg_state;       // [BH][NS][F][DV]: end state of state slice q from zero (state
+                          // pass), overwritten by the scan with the state after slice q
+  float *seg_decay;       // [BH][NS][F]: total base-2 log-decay of state slice q
+  int B, H, L, window, n_meta;
+  int nchunks, P, seg_chunks;
+  // The state pass cuts each of the segments 0..P-2 into R slices of sub_chunks
+  // chunks (NS = (P-1) R slices per head) so that it runs more blocks than the
+  // output pass; segment p >= 1 starts from the state after slice pR - 1.
+  int R, sub_chunks;
+  float scale;
+  int gate_is_log;
+};
+
+// Output pass with two waves per 16-token tile (chunk_out.hip); `swa` adds the
+// window part.  blocks = heads x segments.
+hipError_t launch_chunk_out(const ChunkParams &p, bool swa, int blocks, hipStream_t stream);
+
+namespace {
+
+constexpr int kC = 64;      // chunk (tokens)
+constexpr int kD = 128;     // q/k head dim
+constexpr int kF = 128;     // feature dim
+constexpr int kF2 = 64;     // Hedgehog half
+constexpr int kDV = 128;    // value dim
+constexpr int kFrag = 1024; // bytes of one MFMA operand fragment
+constexpr int kHalf = 512;  // bytes of a half fragment (4 bf16 per lane)
+
+enum { MODE_STATE = 0, MODE_GLA = 1, MODE_HYBRID = 2, MODE_SWA = 3 };
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = (bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack44(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (bf16)lo[j];
+    r[4 + j] = (bf16)hi[j];
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds8(const char *base) { return *(const bf16x8 *)base; }
+
+// Compiler-only ordering point for memory operations: loads written before it are
+// issued before it, so a group of LDS operand loads is in flight together rather
+// than one load per MFMA.  Emits no instruction.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ void sts8(char *base, bf16x8 x) { *(bf16x8 *)base = x; }
+
+__device__ __forceinline__ bf16x8 join44(bf16x4 lo, bf16x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = lo[j];
+    r[4 + j] = hi[j];
+  }
+  return r;
+}
+
+// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48)
+__device__ __forceinline__ float grp_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float grp_min(float x) {
+  x = fminf(x, __shfl_xor(x, 16, 64));
+  return fminf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float grp_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// inclusive scan over the 16 lanes of a row (the 16 tokens of a tile)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x110 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+// broadcast lane 15 of each 16-lane row (the tile's last token) to the row
+__device__ __forceinline__ float row_bcast15(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15F,
+                                                               0xF, 0xF, false));
+}
+
+// Smallest per-token log-gate used by the chunkwise path.  A 16-token tile then
+// spans at most 160 in log space, so with the mid-tile reference every fold
+// factor stays within e^{+-80}.  Gates below e^{-10} (~4.5e-5) act as 4.5e-5:
+// any term they touch is already below 4.5e-5 of its undecayed size, so the
+// change is bounded by that factor.
+constexpr float kMinLog2Gate = -10.0f * kLog2e;
+
+// Largest |chunk log2-decay| for which one chunk-wide fold reference is used:
+// the fold exponents then stay within 2^{+-100}.
+constexpr float kChunkRefLimit = 200.0f;
+
+// log2 sigmoid(g) = -log2(1 + 2^{-g log2e}).  For g below about -88 the power
+// overflows and the result is -inf, which the log-gate floor below replaces.
+__device__ __forceinline__ float log2_sigmoid(float g) {
+  return -log2_fast(1.0f + exp2_fast(-g * kLog2e));
+}
+
+// value of x in lane SRC (0..15) of this lane's 16-lane row (DPP row_newbcast)
+template <int SRC>
+__device__ __forceinline__ float row_bcast_c(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x150 + SRC, 0xF, 0xF, false));
+}
+// the same for an index that is a constant after unrolling (the switch folds)
+__device__ __forceinline__ float row_bcast(float x, int src) {
+  switch (src & 15) {
+    case 0: return row_bcast_c<0>(x);
+    case 1: return row_bcast_c<1>(x);
+    case 2: return row_bcast_c<2>(x);
+    case 3: return row_bcast_c<3>(x);
+    case 4: return row_bcast_c<4>(x);
+    case 5: return row_bcast_c<5>(x);
+    case 6: return row_bcast_c<6>(x);
+    case 7: return row_bcast_c<7>(x);
+    case 8: return row_bcast_c<8>(x);
+    case 9: return row_bcast_c<9>(x);
+    case 10: return row_bcast_c<10>(x);
+    case 11: return row_bcast_c<11>(x);
+    case 12: return row_bcast_c<12>(x);
+    case 13: return row_bcast_c<13>(x);
+    case 14: return row_bcast_c<14>(x);
+    default: return row_bcast_c<15>(x);
+  }
+}
+
+// feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
+__device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
+
+// 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
+// picks K-slot (group n/4, element 4*dt + n%4).  A x sel(dt) re-lays a
+// row-per-lane operand (lane = row, 8 K-values) into accumulator form
+// (lane = column, 4 consecutive rows): a transpose on the matrix core, exact
+// for bf16 inputs since every output is one input times 1.
+__device__ __forceinline__ bf16x8 select_operand(int dt) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  bf16x8 b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = (bf16)((g == (n >> 2) && j == 4 * dt + (n & 3)) ? 1.0f : 0.0f);
+  return b;
+}
+
+__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
+  bf16x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+}  // namespace
+
+}  // namespace glah

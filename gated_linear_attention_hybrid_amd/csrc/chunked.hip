@@ -34,38 +34,14 @@
 // tokens and the matching 128 x 32 slice of the fp32 state, which stays in
 // MFMA accumulators for the whole segment.  Operands are exchanged through LDS
 // as ready-made MFMA fragments (1 KiB: 64 lanes x 16 B).
-#include "device_common.hpp"
+#include "chunk_common.hpp"
 #include "launch.hpp"
 
 namespace glah {
 
 namespace {
 
-constexpr int kC = 64;      // chunk (tokens)
-constexpr int kD = 128;     // q/k head dim
-constexpr int kF = 128;     // feature dim
-constexpr int kF2 = 64;     // Hedgehog half
-constexpr int kDV = 128;    // value dim
 constexpr int kNT = 256;    // threads per block
-constexpr int kFrag = 1024; // bytes of one MFMA operand fragment
-constexpr int kHalf = 512;  // bytes of a half fragment (4 bf16 per lane)
-
-enum { MODE_STATE = 0, MODE_GLA = 1, MODE_HYBRID = 2, MODE_SWA = 3 };
-
-struct ChunkParams {
-  const bf16 *q, *k, *v, *gate, *wq, *wk;
-  const float *meta;
-  const float *state_in;  // [BH][F][DV] state before token 0 (segment 0), or null
-  float *state_out;       // [BH][F][DV] written by the last segment, or null
-  bf16 *o;
-  float *seg_state;       // [BH][P-1][F][DV]: end state of segment p from zero (state
-                          // pass), overwritten by the scan with the start state of p+1
-  float *seg_decay;       // [BH][P-1][F]: total base-2 log-decay of segment p
-  int B, H, L, window, n_meta;
-  int nchunks, P, seg_chunks;
-  float scale;
-  int gate_is_log;
-};
 
 // ---------------------------------------------------------------- LDS layout
 template <int MODE>
@@ -86,126 +62,6 @@ struct Lds {
   static constexpr int T = W + (Q ? 4 * NKS * kFrag : 0);        // tile log-gate totals [4][128]
   static constexpr int BYTES = T + (GLA ? 4 * kF * 4 : 0);
 };
-
-// ---------------------------------------------------------------- helpers
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) z[j] = (bf16)0.0f;
-  return z;
-}
-
-__device__ __forceinline__ bf16x8 pack8(const float *x) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 pack44(f32x4 lo, f32x4 hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = (bf16)lo[j];
-    r[4 + j] = (bf16)hi[j];
-  }
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 lds8(const char *base) { return *(const bf16x8 *)base; }
-__device__ __forceinline__ void sts8(char *base, bf16x8 x) { *(bf16x8 *)base = x; }
-
-__device__ __forceinline__ bf16x8 join44(bf16x4 lo, bf16x4 hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = lo[j];
-    r[4 + j] = hi[j];
-  }
-  return r;
-}
-
-// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48)
-__device__ __forceinline__ float grp_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
-}
-__device__ __forceinline__ float grp_min(float x) {
-  x = fminf(x, __shfl_xor(x, 16, 64));
-  return fminf(x, __shfl_xor(x, 32, 64));
-}
-__device__ __forceinline__ float grp_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
-}
-
-// inclusive scan over the 16 lanes of a row (the 16 tokens of a tile)
-template <int N>
-__device__ __forceinline__ float row_shr(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x110 + N, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row_scan(float x) {
-  x += row_shr<1>(x);
-  x += row_shr<2>(x);
-  x += row_shr<4>(x);
-  x += row_shr<8>(x);
-  return x;
-}
-
-// broadcast lane 15 of each 16-lane row (the tile's last token) to the row
-__device__ __forceinline__ float row_bcast15(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x15F,
-                                                               0xF, 0xF, false));
-}
-
-// Smallest per-token log-gate used by the chunkwise path.  A 16-token tile then
-// spans at most 160 in log space, so with the mid-tile reference every fold
-// factor stays within e^{+-80}.  Gates below e^{-10} (~4.5e-5) act as 4.5e-5:
-// any term they touch is already below 4.5e-5 of its undecayed size, so the
-// change is bounded by that factor.
-constexpr float kMinLog2Gate = -10.0f * kLog2e;
-
-// log2 sigmoid(g) = -log2(1 + 2^{-g log2e}).  For g below about -88 the power
-// overflows and the result is -inf, which the log-gate floor below replaces.
-__device__ __forceinline__ float log2_sigmoid(float g) {
-  return -log2_fast(1.0f + exp2_fast(-g * kLog2e));
-}
-
-// value of x in lane SRC (0..15) of this lane's 16-lane row (DPP row_newbcast)
-template <int SRC>
-__device__ __forceinline__ float row_bcast_c(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x150 + SRC, 0xF, 0xF, false));
-}
-// the same for an index that is a constant after unrolling (the switch folds)
-__device__ __forceinline__ float row_bcast(float x, int src) {
-  switch (src & 15) {
-    case 0: return row_bcast_c<0>(x);
-    case 1: return row_bcast_c<1>(x);
-    case 2: return row_bcast_c<2>(x);
-    case 3: return row_bcast_c<3>(x);
-    case 4: return row_bcast_c<4>(x);
-    case 5: return row_bcast_c<5>(x);
-    case 6: return row_bcast_c<6>(x);
-    case 7: return row_bcast_c<7>(x);
-    case 8: return row_bcast_c<8>(x);
-    case 9: return row_bcast_c<9>(x);
-    case 10: return row_bcast_c<10>(x);
-    case 11: return row_bcast_c<11>(x);
-    case 12: return row_bcast_c<12>(x);
-    case 13: return row_bcast_c<13>(x);
-    case 14: return row_bcast_c<14>(x);
-    default: return row_bcast_c<15>(x);
-  }
-}
-
-// feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
-__device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
 
 // d_v column held by lane n, column-tile dt, of wave w (8 contiguous per lane group)
 __device__ __forceinline__ int dvcol(int w, int dt, int n) {
@@ -244,26 +100,6 @@ __device__ __forceinline__ void load_chunk(const ChunkParams &p, size_t bh, int 
   }
 }
 
-// 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
-// picks K-slot (group n/4, element 4*dt + n%4).  A x sel(dt) re-lays a
-// row-per-lane operand (lane = row, 8 K-values) into accumulator form
-// (lane = column, 4 consecutive rows): a transpose on the matrix core, exact
-// for bf16 inputs since every output is one input times 1.
-__device__ __forceinline__ bf16x8 select_operand(int dt) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  bf16x8 b;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) b[j] = (bf16)((g == (n >> 2) && j == 4 * dt + (n & 3)) ? 1.0f : 0.0f);
-  return b;
-}
-
-__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
-  bf16x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
-  return r;
-}
-
 // V^T half fragments of this wave's 16 tokens into ring slot `slot`: for d_v
 // tile (2w' + dt), lane 16g + r holds v[16*wave + 4g + j][dvcol(w', dt, r)].
 // K-step s of xv covers d_v [32s, 32s+32), i.e. the two d_v tiles of w' = s.
@@ -294,12 +130,21 @@ void chunk_kernel(ChunkParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int nseg = MODE == MODE_STATE ? p.P - 1 : p.P;
+  const int NS = (p.P - 1) * p.R;
+  const int nseg = MODE == MODE_STATE ? NS : p.P;
   const size_t bh = blockIdx.x / nseg;
-  const int seg = blockIdx.x % nseg;
+  const int seg = blockIdx.x % nseg;  // state slice (state pass) or segment
   const int h = (int)(bh % p.H);
-  const int c_begin = seg * p.seg_chunks;
-  const int c_end = min(c_begin + p.seg_chunks, p.nchunks);
+  int c_begin, c_end;
+  if (MODE == MODE_STATE) {
+    const int ps = seg / p.R, r = seg % p.R;
+    const int seg_end = min((ps + 1) * p.seg_chunks, p.nchunks);
+    c_begin = min(ps * p.seg_chunks + r * p.sub_chunks, seg_end);
+    c_end = min(c_begin + p.sub_chunks, seg_end);  // may be empty: zero state, zero decay
+  } else {
+    c_begin = seg * p.seg_chunks;
+    c_end = min(c_begin + p.seg_chunks, p.nchunks);
+  }
 
   // ---- Hedgehog projections as MFMA A fragments: frag (mt, s), lane (r, g)
   // holds W[32g + 8s + j][m] with m = 16(r/4) + 4mt + (r%4), so that the
@@ -335,7 +180,7 @@ void chunk_kernel(ChunkParams p) {
     if (seg == 0)
       src = p.state_in ? p.state_in + bh * kF * kDV : nullptr;
     else
-      src = p.seg_state + (bh * (p.P - 1) + (seg - 1)) * (size_t)(kF * kDV);
+      src = p.seg_state + (bh * NS + (seg * p.R - 1)) * (size_t)(kF * kDV);
     if (src) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
@@ -557,8 +402,9 @@ void chunk_kernel(ChunkParams p) {
     //   q~ = phi_q 2^{d},  k~ = phi_k 2^{-d},  |d| <= 10 log2(e) * 16 / 2
     bf16x8 qb[4];  // q~ as MFMA operands
     bf16x8 kb[4];  // k~ as MFMA operands
+    f32x4 uk[4], uq[4];
+    float dd[32];
     if (GLA) {
-      f32x4 uk[4], uq[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         uk[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
@@ -572,7 +418,6 @@ void chunk_kernel(ChunkParams p) {
           if (Q) uq[mt] = mfma(lds8(smem + LD::WQ + (mt * 4 + s) * kFrag + lane * 16), cur.xq[s], uq[mt]);
         }
       if (more) load_chunk<MODE, LOAD_QK>(p, bh, c + 1, cur);
-      float dd[32];
       if (p.gate_is_log) {  // one uniform branch around the whole loop
 #pragma unroll
         for (int i = 0; i < 32; ++i) dd[i] = (float)cur.xg[i >> 3][i & 7] * kLog2e;
@@ -603,8 +448,48 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
       }
+    }
+    __syncthreads();  // B1a: tile log-gate totals visible
+
+    // Fold reference r (base 2, per feature).  Chunk mode: r = B/2, one
+    // reference for the whole chunk, so cross-tile factors are 1; used when every
+    // feature's chunk total satisfies |B| <= kChunkRefLimit, which keeps
+    // |b - r| <= |B|/2 in range.  Tile mode otherwise: r_w = P_w + T_w/2.
+    // Per-tile quantities are computed for features 2n, 2n+1 of the lane's group
+    // and broadcast to the row (DPP) where needed.
+    float tt[4][2], pre[2], btot[2], tw[2], rr2[2];
+    bool chunk_mode = true;
+    if (GLA) {
+      const float *T = (const float *)(smem + LD::T);
+      const int f0 = feat(g, 2 * n);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) dd[i] -= 0.5f * row_bcast15(dd[i]);
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
+        tt[w2][0] = v2.x;
+        tt[w2][1] = v2.y;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pre[e] = 0.0f;
+        btot[e] = 0.0f;
+        tw[e] = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          btot[e] += tt[w2][e];
+          if (w2 < wave) pre[e] += tt[w2][e];
+          if (w2 == wave) tw[e] = tt[w2][e];
+        }
+      }
+      // every wave sees all 128 features, so the vote is the same in all waves
+      chunk_mode = __all(fabsf(btot[0]) <= kChunkRefLimit && fabsf(btot[1]) <= kChunkRefLimit);
+      float off[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        rr2[e] = chunk_mode ? 0.5f * btot[e] : pre[e] + 0.5f * tw[e];
+        off[e] = pre[e] - rr2[e];  // b_chunk - r = b_loc + off
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dd[i] += row_bcast(off[i & 1], i >> 1);
 
       // Hedgehog softmaxes of +u and -u, scaled by the fold factors
       auto features = [&](const f32x4 *u, bf16x8 *outb, float sgn) {
@@ -650,41 +535,22 @@ void chunk_kernel(ChunkParams p) {
       }
       if (Q) features(uq, qb, 1.0f);
     }
-    __syncthreads();  // B1: tile totals and k~ fragments visible
+    __syncthreads();  // B1: k~ fragments visible
 
     // ================= row phase 2: cross-tile factors, intra scores =================
     // Per-tile factors depend on the feature only; lane n computes them for
     // features 2n, 2n+1 of its group and the others broadcast them (DPP).
     if (GLA) {
-      const float *T = (const float *)(smem + LD::T);
-      const int f0 = feat(g, 2 * n);
-      float tt[4][2];
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
-        tt[w2][0] = v2.x;
-        tt[w2][1] = v2.y;
-      }
-      float pre[2], btot[2], tw[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        pre[e] = 0.0f;
-        btot[e] = 0.0f;
-        tw[e] = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          btot[e] += tt[w2][e];
-          if (w2 < wave) pre[e] += tt[w2][e];
-          if (w2 == wave) tw[e] = tt[w2][e];
-        }
         fdec[e] = exp2_fast(btot[e]);
         dsum2[e] += btot[e];
       }
-      // q-bar = q~ 2^{P + T/2} (inter-chunk readout)
+      // q-bar = phi_q 2^{b_chunk} = q~ 2^{r} (inter-chunk readout), r <= 0
       if (Q) {
         float fq[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) fq[e] = exp2_fast(pre[e] + 0.5f * tw[e]);
+        for (int e = 0; e < 2; ++e) fq[e] = exp2_fast(rr2[e]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           float tmp[8];
@@ -693,12 +559,12 @@ void chunk_kernel(ChunkParams p) {
           sts8(smem + LD::QB + (wave * 4 + s) * kFrag + lane * 16, pack8(tmp));
         }
       }
-      {  // k-hat = k~ 2^{B - P - T/2} (state update) -> k-hat^T fragments: state
+      {  // k-hat = phi_k 2^{B - b_chunk} = k~ 2^{B - r} (state update) -> k-hat^T fragments: state
          // tile mt takes its 16 features from K-step s(mt) = 2(mt/4) + (mt%4)/2 of
          // the token-row operand, transposed on the matrix core
         float fk[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) fk[e] = exp2_fast(btot[e] - pre[e] - 0.5f * tw[e]);
+        for (int e = 0; e < 2; ++e) fk[e] = exp2_fast(btot[e] - rr2[e]);
         bf16x8 kh[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
@@ -726,11 +592,18 @@ void chunk_kernel(ChunkParams p) {
             if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
           Wt[4] += acc;
         }
-        // earlier tiles: q~ scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
+        // earlier tiles: in chunk mode both sides share the reference; in tile mode
+        // q~ is scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
 #pragma unroll
         for (int i = 1; i < 4; ++i) {
           const int kt = wave - 4 + i;
-          if (kt >= 0) {
+          if (kt >= 0 && chunk_mode) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), qb[s], acc);
+            Wt[i] += acc;
+          } else if (kt >= 0) {
             float fo[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -783,7 +656,7 @@ void chunk_kernel(ChunkParams p) {
 
   // ---- epilogue
   if (MODE == MODE_STATE) {
-    float *dst = p.seg_state + (bh * (p.P - 1) + seg) * (size_t)(kF * kDV);
+    float *dst = p.seg_state + (bh * NS + seg) * (size_t)(kF * kDV);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -791,7 +664,7 @@ void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
     if (wave == 0) {
-      float *dd = p.seg_decay + (bh * (p.P - 1) + seg) * (size_t)kF;
+      float *dd = p.seg_decay + (bh * NS + seg) * (size_t)kF;
       *(float2 *)(dd + feat(g, 2 * n)) = make_float2(dsum2[0], dsum2[1]);
     }
   } else if (GLA && p.state_out && seg == p.P - 1) {
@@ -805,32 +678,51 @@ void chunk_kernel(ChunkParams p) {
   }
 }
 
-// Start state of every segment: S_1 = e^{D_0} S_in + dS_0, S_{p+1} = e^{D_p} S_p + dS_p.
-// Thread = one state element of one head; the segment slots are overwritten in
-// place (slot p receives the start state of segment p + 1).
+// State after every state slice: S_(0) = e^{D_0} S_in + dS_0,
+// S_(q) = e^{D_q} S_(q-1) + dS_q.  Thread = one state element of one head; the
+// slots are overwritten in place (slot q receives S_(q)).
 __global__ __launch_bounds__(kNT) void segment_scan_kernel(float *seg_state, const float *seg_decay,
-                                                           const float *state_in, int BH, int P) {
+                                                           const float *state_in, int BH, int NS) {
   const size_t idx = (size_t)blockIdx.x * kNT + threadIdx.x;
   const size_t per = (size_t)kF * kDV;
   if (idx >= (size_t)BH * per) return;
   const size_t bh = idx / per, e = idx % per;
   const int f = (int)(e / kDV);
   float s = state_in ? state_in[idx] : 0.0f;
-  for (int q = 0; q < P - 1; ++q) {
-    float *slot = seg_state + (bh * (P - 1) + q) * per;
-    const float dec = exp2_fast(seg_decay[(bh * (P - 1) + q) * kF + f]);  // base-2 log-decay
+  for (int q = 0; q < NS; ++q) {
+    float *slot = seg_state + (bh * NS + q) * per;
+    const float dec = exp2_fast(seg_decay[(bh * NS + q) * kF + f]);  // base-2 log-decay
     s = dec * s + slot[e];
     slot[e] = s;
   }
 }
 
-int choose_segments(const LayerArgs &a, int nchunks) {
+// How one call is cut: P output segments of seg_chunks chunks; the state pass
+// cuts segments 0..P-2 into R slices of sub_chunks chunks.
+struct SegPlan {
+  int nchunks = 0, P = 1, seg_chunks = 0, R = 1, sub_chunks = 0;
+  int slices() const { return (P - 1) * R; }
+};
+
+SegPlan plan_segments(const LayerArgs &a) {
+  SegPlan s;
+  s.nchunks = (a.L + kC - 1) / kC;
   const int bh = a.B * a.H;
   const int cus = device_cu_count();
-  // about one block per compute unit; at least 4 chunks per segment
+  // output pass: about one block per compute unit (its LDS allows one), at least
+  // 4 chunks per segment, and every segment owns at least one chunk
   int P = (cus + bh - 1) / bh;
-  P = max(1, min(P, nchunks / 4));
-  return P;
+  P = max(1, min(P, s.nchunks / 4));
+  s.seg_chunks = (s.nchunks + P - 1) / P;
+  s.P = (s.nchunks + s.seg_chunks - 1) / s.seg_chunks;
+  // state pass: two blocks fit on a compute unit, so aim at two per unit, with
+  // at least 2 chunks per slice
+  if (s.P > 1) {
+    int R = (2 * cus) / (bh * (s.P - 1));
+    s.R = max(1, min(R, s.seg_chunks / 2));
+  }
+  s.sub_chunks = (s.seg_chunks + s.R - 1) / s.R;
+  return s;
 }
 
 ChunkParams make_params(const LayerArgs &a, int P, int seg_chunks, int nchunks) {
@@ -841,6 +733,7 @@ ChunkParams make_params(const LayerArgs &a, int P, int seg_chunks, int nchunks) 
   p.seg_state = nullptr; p.seg_decay = nullptr;
   p.B = a.B; p.H = a.H; p.L = a.L; p.window = a.window; p.n_meta = a.n_meta;
   p.nchunks = nchunks; p.P = P; p.seg_chunks = seg_chunks;
+  p.R = 1; p.sub_chunks = seg_chunks;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0;
   return p;
 }
@@ -874,35 +767,31 @@ bool chunked_supported(const LayerArgs &a, int parts) {
 
 size_t chunked_workspace_bytes(const LayerArgs &a, int parts) {
   if (!(parts & PART_GLA) || a.L <= 0) return 0;
-  const int nchunks = (a.L + kC - 1) / kC;
-  const int P = choose_segments(a, nchunks);
-  if (P <= 1) return 0;
+  const SegPlan s = plan_segments(a);
   const size_t bh = (size_t)a.B * a.H;
-  return bh * (P - 1) * ((size_t)kF * kDV + kF) * sizeof(float);
+  return bh * s.slices() * ((size_t)kF * kDV + kF) * sizeof(float);
 }
 
 hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
   if ((size_t)a.B * a.H * a.L == 0) return hipSuccess;
-  const int nchunks = (a.L + kC - 1) / kC;
   const int bh = a.B * a.H;
-  const int P = choose_segments(a, nchunks);
-  const int seg_chunks = (nchunks + P - 1) / P;
-  // every segment must own at least one chunk
-  const int Peff = (nchunks + seg_chunks - 1) / seg_chunks;
-  ChunkParams p = make_params(a, Peff, seg_chunks, nchunks);
-  if (Peff > 1) {
+  const SegPlan s = plan_segments(a);
+  ChunkParams p = make_params(a, s.P, s.seg_chunks, s.nchunks);
+  p.R = s.R;
+  p.sub_chunks = s.sub_chunks;
+  if (s.P > 1) {
+    const int NS = s.slices();
     p.seg_state = (float *)a.ws;
-    p.seg_decay = p.seg_state + (size_t)bh * (Peff - 1) * kF * kDV;
-    hipError_t e = launch_mode<MODE_STATE>(p, bh * (Peff - 1), a.stream);
+    p.seg_decay = p.seg_state + (size_t)bh * NS * kF * kDV;
+    hipError_t e = launch_mode<MODE_STATE>(p, bh * NS, a.stream);
     if (e != hipSuccess) return e;
     const size_t elems = (size_t)bh * kF * kDV;
     hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((elems + kNT - 1) / kNT)), dim3(kNT), 0,
-                       a.stream, p.seg_state, (const float *)p.seg_decay, a.state_in, bh, Peff);
+                       a.stream, p.seg_state, (const float *)p.seg_decay, a.state_in, bh, NS);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (parts == PART_GLA) return launch_mode<MODE_GLA>(p, bh * Peff, a.stream);
-  return launch_mode<MODE_HYBRID>(p, bh * Peff, a.stream);
+  return launch_chunk_out(p, parts != PART_GLA, bh * s.P, a.stream);
 }
 
 bool swa_mfma_supported(const LayerArgs &a) {

@@ -149,6 +149,31 @@ def test_segment_splits(H):
     assert row_rel_err(np.stack([got[b, h] for b, h in heads]), ref(x, wl, heads=heads)) <= TOL_BF16
 
 
+def test_state_slices_with_empty_slice():
+    # 128 sequences of 18 chunks on 256 compute units: 2 output segments of 9
+    # chunks, and the state pass cuts segment 0 into 4 slices of 3 chunks, the
+    # last of which is empty (zero state, zero decay)
+    wl = base(B=2, H=64, L=18 * 64, gate_mean=6.0)
+    say("state slices B=2 H=64 L=1152")
+    x = make_prefill(wl, DEV)
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    o = run_hybrid(x, wl, state_out=st)
+    heads = [(0, 0), (0, 37), (1, 63)]
+    got = gpu_f64(o)
+    want, wst = [], []
+    for b, h in heads:
+        oo = {k: to_f64(v[b:b + 1, h:h + 1]) for k, v in x.items() if v.dim() == 4}
+        w = {k: to_f64(x[k][h:h + 1]) for k in ("wq", "wk", "meta")}
+        r, s = oracle.layer_fwd(oo["q"], oo["k"], oo["v"], oo["gate"], w["wq"], w["wk"], w["meta"],
+                                window=wl.window, return_state=True)
+        want.append(r[0, 0])
+        wst.append(s[0, 0])
+    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), np.stack(want)) <= TOL_BF16
+    sg = gpu_f64(st)
+    assert row_rel_err(np.stack([sg[b, h] for b, h in heads]).reshape(-1, wl.dv),
+                       np.stack(wst).reshape(-1, wl.dv)) <= TOL_BF16
+
+
 def test_state_in_out_continuation():
     wl = base(H=4, L=1280, gate_mean=6.0)
     say("state continuation")
