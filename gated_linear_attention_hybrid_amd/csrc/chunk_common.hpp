@@ -89,18 +89,27 @@ __device__ __forceinline__ bf16x8 join44(bf16x4 lo, bf16x4 hi) {
   return r;
 }
 
-// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48)
+// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48) with the
+// gfx950 row swaps: v_permlane16_swap with both operands x yields rows
+// (x0, x0, x2, x2) and (x1, x1, x3, x3), v_permlane32_swap yields (x0, x1, x0, x1)
+// and (x2, x3, x2, x3); combining each pair reduces over the rows without LDS.
+template <class Op>
+__device__ __forceinline__ float grp_reduce(float x, Op op) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = op(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, x);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return op(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
+}
 __device__ __forceinline__ float grp_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  return grp_reduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float grp_min(float x) {
-  x = fminf(x, __shfl_xor(x, 16, 64));
-  return fminf(x, __shfl_xor(x, 32, 64));
+  return grp_reduce(x, [](float a, float b) { return fminf(a, b); });
 }
 __device__ __forceinline__ float grp_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+  return grp_reduce(x, [](float a, float b) { return a + b; });
 }
 
 // inclusive scan over the 16 lanes of a row (the 16 tokens of a tile)
@@ -170,6 +179,11 @@ __device__ __forceinline__ float row_bcast(float x, int src) {
 
 // feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
 __device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
+
+// d_v column held by lane n, column-tile dt, of wave w (8 contiguous per lane group)
+__device__ __forceinline__ int dvcol(int w, int dt, int n) {
+  return 32 * w + 8 * (n >> 2) + 4 * dt + (n & 3);
+}
 
 // 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
 // picks K-slot (group n/4, element 4*dt + n%4).  A x sel(dt) re-lays a

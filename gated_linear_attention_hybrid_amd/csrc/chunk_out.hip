@@ -12,22 +12,23 @@
 //   state  S  <- diag(2^{B}) S + k-hat^T V,  k-hat = phi_k 2^{B-b}
 // and the window probabilities are added to A^T so one GEMM with V gives both.
 //
-// A block of 512 threads runs 8 waves, two per SIMD, so that the dependency and
-// issue stalls of one wave are filled by the other's work (a lone wave issues
-// vector instructions at about half the rate of two).  Row phase, tile t = w & 3:
-//   key wave   (w = 0..3): V^T fragments, u_k = k Wphi_k, log-gates and in-tile
-//                          cumsums of the phi+ half, phi(k), k~ and k-hat^T
-//   query wave (w = 4..7): raw-k fragments, u_q, log-gates and cumsums of the
-//                          phi- half, phi(q), q-bar, window scores and softmax,
-//                          intra-chunk scores, weight fragments
-// The two halves of the cumsums are swapped through LDS (over the q-bar and
-// k-hat^T buffers, which are free at that point of the chunk).  Column phase:
-// wave w owns d_v columns [16w, 16w + 16) and the matching 128 x 16 slice of the
-// fp32 state, which stays in MFMA accumulators for the whole segment.
-//
-// Per chunk: B3 (column phase of the previous chunk done) -> phase A -> B1a
-// (cumsum halves, tile totals, raw k visible) -> phase B -> B1 (k~ visible) ->
-// phase C -> B2 (q-bar, k-hat^T, weights visible).
+// A block of 512 threads runs 8 waves, two per SIMD, so that the stalls of one
+// wave are filled by the other's work (a lone wave issues vector instructions at
+// about half the rate of two).  Tile t = w & 3:
+//   key wave   (w = 0..3): holds d_v columns [32t, 32t + 32) of the fp32 state in
+//                          MFMA accumulators and runs the column phase (readout,
+//                          weights x V, state update) of the previous chunk; then
+//                          u_k = k Wphi_k, the log-gates of its tile, phi(k), k~,
+//                          k-hat^T and V^T fragments
+//   query wave (w = 4..7): raw-k fragments, window scores and softmax, u_q,
+//                          phi(q), q~, q-bar, intra-chunk scores, weight
+//                          fragments; and the log-gates of the NEXT chunk, whose
+//                          tile totals it publishes one chunk ahead, so every
+//                          wave knows the chunk-wide fold reference when a chunk
+//                          starts
+// Per chunk there are two barriers: B1 (raw-k and k~ fragments visible, column
+// phase of the previous chunk done) and B2 (q-bar, k-hat^T, V^T and weights
+// visible).
 #include "chunk_common.hpp"
 
 namespace glah {
@@ -47,60 +48,52 @@ struct Lds8 {
   static constexpr int QB = KT + 16 * kFrag;              // q-bar frags [4 tile][4 s]
   static constexpr int KH = QB + 16 * kFrag;              // k-hat^T frags [8 mt][2 sp]
   static constexpr int W = KH + 16 * kFrag;               // weight frags [4 qt][NKS]
-  static constexpr int T = W + 4 * NKS * kFrag;           // tile log-gate totals [4 tile][128]
-  static constexpr int BYTES = T + 4 * kF * 4;
-  // in-tile cumsums [4 tile][8 slot group][64 lanes][4] (32 KiB) over QB and KH:
-  // written after B3, read before B1, while QB and KH hold nothing live
-  static constexpr int DD = QB;
+  // per query tile: window part 2 full fragments + the diagonal tile as a half
+  // fragment (its upper K half is zero); no window: 2 full fragments
+  static constexpr int WQT = SWA ? 2 * kFrag + kHalf : 2 * kFrag;
+  static constexpr int T = W + 4 * WQT;                   // tile log-gate totals [2 slot][4 tile][128]
+  static constexpr int BYTES = T + 2 * 4 * kF * 4;
 };
-static_assert(Lds8<true>::DD + 4 * 8 * 64 * 16 <= Lds8<true>::W, "cumsum exchange overlaps the weights");
 static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
 
-// One chunk's inputs of one wave, prefetched one chunk ahead.
-struct Regs8 {
-  bf16x8 xa[4];  // key wave: k, query wave: q   [token 16t + n][32g + 8s + j]
-  bf16x8 xb[4];  // key wave: v [token][32s + 8g + j]; query wave: raw k [token][32g + 8s + j]
-  bf16x8 xg[2];  // gate[token][feat(g, 16h + 8s + j)], h = 0 key wave, 1 query wave
+// Per-head buffer resources over the [L][128] bf16 rows of q, k, v, gate and o.
+// Loads past the last row return zeros and stores there are dropped by the range
+// check of the buffer instructions (offsets are unsigned, so rows before 0 are
+// past the end too); every consumer masks such tokens anyway.
+struct HeadBufs {
+  __amdgpu_buffer_rsrc_t q, k, v, g, o;
 };
-enum { L8_A = 1, L8_B = 2, L8_G = 4, L8_ALL = 7 };
-
-template <bool SWA, int PARTS>
-__device__ __forceinline__ void load8(const ChunkParams &p, size_t bh, int c, int tile, bool kw, Regs8 &r) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  // rows outside [0, L) come from a clamped valid row; every consumer masks them
-  const int t = min(max(c * kC + 16 * tile + n, 0), p.L - 1);
-  const size_t row = bh * p.L + t;
-  if (PARTS & L8_A) {
-    const bf16 *src = (kw ? p.k : p.q) + row * kD + 32 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) r.xa[s] = *(const bf16x8 *)(src + 8 * s);
-  }
-  if (PARTS & L8_B) {
-    if (kw) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) r.xb[s] = *(const bf16x8 *)(p.v + row * kDV + 32 * s + 8 * g);
-    } else if (SWA) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) r.xb[s] = *(const bf16x8 *)(p.k + row * kD + 32 * g + 8 * s);
-    }
-  }
-  if (PARTS & L8_G) {
-    const bf16 *src = p.gate + row * kF + feat(g, kw ? 0 : 16);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) r.xg[s] = *(const bf16x8 *)(src + 8 * s);
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16 *base, size_t bh, int L) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + bh * (size_t)L * kD), (short)0, L * kD * 2,
+                                           0x00020000);
 }
-
-// 0/1 selection operand: output column n picks K-slot 16 dt + n, so for a
-// token-row operand A (lane = token, K = 32 value dims 32s + k),
-// A x select16(dt) is the accumulator tile (row = token 4g + j, column n) of
-// value dims 32s + 16dt + n: an exact transpose on the matrix core.
-__device__ __forceinline__ bf16x8 select16(int dt) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  bf16x8 b;
+__device__ __forceinline__ HeadBufs head_bufs(const ChunkParams &p, size_t bh) {
+  return {head_rsrc(p.q, bh, p.L), head_rsrc(p.k, bh, p.L), head_rsrc(p.v, bh, p.L),
+          head_rsrc(p.gate, bh, p.L), head_rsrc(p.o, bh, p.L)};
+}
+__device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// byte offset of chunk c's rows (wraps for c < 0, which reads zeros)
+__device__ __forceinline__ unsigned chunk_off(int c) { return (unsigned)c * (unsigned)(kC * kD * 2); }
+// Per-lane byte offsets within a chunk, lane (n, g) of tile t on token 16t + n:
+// token-row operand x[token][32g + 8s + j], values v[token][32s + 8g + j] and
+// gates gate[token][feat(g, 8s + j)]
+__device__ __forceinline__ unsigned row_off(int tile) { return (unsigned)(16 * tile + (threadIdx.x & 15)) * (kD * 2); }
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
+  const unsigned g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) b[j] = (bf16)((g == ((16 * dt + n) >> 3) && j == (n & 7)) ? 1.0f : 0.0f);
-  return b;
+  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 64 * g + 16 * s);
+}
+__device__ __forceinline__ void load_vals(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
+  const unsigned g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 16 * g + 64 * s);
+}
+__device__ __forceinline__ void load_gates(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
+  const unsigned g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 2 * feat(g, 8 * s));
 }
 
 // Unnormalised Hedgehog exponentials of the lane's token: e[4mt + j] =
@@ -133,6 +126,117 @@ __device__ __forceinline__ void hedgehog_exp(const f32x4 *u, float *e, float &iz
   izn = rcp_fast(grp_sum(zn));
 }
 
+// u = x Wphi for a 16-token tile (A = Wphi^T fragments in LDS, B = the tile's
+// token rows); the 4 fragments of tile mt+1 are requested before the MFMAs of mt
+__device__ __forceinline__ void project(const char *wb, const bf16x8 *x, f32x4 *u) {
+  bf16x8 wf[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) u[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) wf[0][s] = lds8(wb + s * kFrag);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt + 1 < 4) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wf[(mt + 1) & 1][s] = lds8(wb + ((mt + 1) * 4 + s) * kFrag);
+    }
+    issue_fence();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) u[mt] = mfma(wf[mt & 1][s], x[s], u[mt]);
+  }
+}
+
+// In-tile inclusive cumsums of the base-2 log-gates of the lane's token for all
+// 32 fold slots (feature feat(g, i)), floored at kMinLog2Gate, zero for tokens
+// past the end.
+__device__ __forceinline__ void tile_cumsum(const bf16x8 *xg, bool gate_is_log, bool tok_ok, float *dd) {
+  if (gate_is_log) {  // one uniform branch around the whole loop
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dd[i] = (float)xg[i >> 3][i & 7] * kLog2e;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dd[i] = log2_sigmoid((float)xg[i >> 3][i & 7]);
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dd[i] = tok_ok ? fmaxf(dd[i], kMinLog2Gate) : 0.0f;
+  // one scan step across all 32 slots at a time, so consecutive DPP reads
+  // never wait on each other
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dd[i] += row_shr<1>(dd[i]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dd[i] += row_shr<2>(dd[i]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dd[i] += row_shr<4>(dd[i]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dd[i] += row_shr<8>(dd[i]);
+}
+
+// Per-feature chunk quantities for features 2n, 2n+1 of the lane's group from
+// the tile totals of the chunk (base 2): fold reference rr2, offset off = P_w - r
+// of this wave's tile, total B, and the per-tile totals tt (tile mode).
+struct FoldRef {
+  float tt[4][2], tw[2], btot[2], rr2[2], off[2];
+  bool chunk_mode;
+};
+__device__ __forceinline__ FoldRef fold_ref(const float *T, int tile) {
+  FoldRef r;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int f0 = feat(g, 2 * n);
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
+    r.tt[w2][0] = v2.x;
+    r.tt[w2][1] = v2.y;
+  }
+  float pre[2];
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    pre[e2] = 0.0f;
+    r.btot[e2] = 0.0f;
+    r.tw[e2] = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      r.btot[e2] += r.tt[w2][e2];
+      if (w2 < tile) pre[e2] += r.tt[w2][e2];
+      if (w2 == tile) r.tw[e2] = r.tt[w2][e2];
+    }
+  }
+  // Chunk mode: r = B/2 for the whole chunk, so cross-tile factors are 1; used
+  // when every feature's chunk total has |B| <= kChunkRefLimit.  Tile mode
+  // otherwise: r_w = P_w + T_w/2.  Every wave sees all 128 features, so the vote
+  // is the same in all waves.
+  r.chunk_mode = __all(fabsf(r.btot[0]) <= kChunkRefLimit && fabsf(r.btot[1]) <= kChunkRefLimit);
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) {
+    r.rr2[e2] = r.chunk_mode ? 0.5f * r.btot[e2] : pre[e2] + 0.5f * r.tw[e2];
+    r.off[e2] = pre[e2] - r.rr2[e2];  // b_chunk - r = b_loc + off
+  }
+  return r;
+}
+
+// Folded feature operands: xr = phi 2^{sgn (b - r)} (k~ with sgn = -1, q~ with
+// sgn = +1) and xs = xr 2^{fs} (per feature: k-hat with fs = B - r, q-bar with
+// fs = r), as MFMA token-row operands (slot i = 8s + j).
+__device__ __forceinline__ void fold(const float *e, float izp, float izn, const float *dd, const FoldRef &r,
+                                     float sgn, const float *fs, bf16x8 *xr, bf16x8 *xs) {
+  float fsx[2];
+#pragma unroll
+  for (int e2 = 0; e2 < 2; ++e2) fsx[e2] = exp2_fast(fs[e2]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float a8[8], b8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = 8 * s + j;
+      const float d = dd[i] + row_bcast(r.off[i & 1], i >> 1);
+      a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(sgn * d);
+      b8[j] = a8[j] * row_bcast(fsx[i & 1], i >> 1);
+    }
+    xr[s] = pack8(a8);
+    xs[s] = pack8(b8);
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 template <bool SWA>
 __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
@@ -149,6 +253,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
   const int h = (int)(bh % p.H);
   const int c_begin = seg * p.seg_chunks;
   const int c_end = min(c_begin + p.seg_chunks, p.nchunks);
+  const bool gate_is_log = p.gate_is_log != 0;
 
   // ---- Hedgehog projections as MFMA A fragments: frag (mt, s), lane (r, g)
   // holds W[32g + 8s + j][m] with m = 16(r/4) + 4mt + (r%4), so that the
@@ -163,365 +268,189 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
     for (int j = 0; j < 8; ++j) f[j] = w[(32 * gg + 8 * s + j) * kF2 + m];
     sts8(smem + (which ? LD::WK : LD::WQ) + fi * kFrag + l * 16, f);
   }
+  // The column phase of the chunk before the segment runs on zero operands (its
+  // outputs are not stored), so the loop needs no first-iteration branch.  The
+  // window part's V^T slot of that chunk is staged below.
+  for (int off = LD::KT + tid * 16; off < LD::T; off += kNT8 * 16) sts8(smem + off, zero8());
+  for (int off = LD::VT + tid * 16; off < LD::KT; off += kNT8 * 16) sts8(smem + off, zero8());
+  __syncthreads();  // zero fill before the staged fragments below
 
-  // ---- state slice: S[mt][j] = S[feat(g, 4mt + j)][16 wave + n]
-  f32x4 S[8];
+  if (kw) {
+    // =============================== key waves ===============================
+    const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
+    // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvcol(tile, dt, n)]
+    f32x4 S[8][2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) S[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  {
-    const float *src = nullptr;
-    if (seg == 0)
-      src = p.state_in ? p.state_in + bh * kF * kDV : nullptr;
-    else
-      src = p.seg_state + (bh * ((p.P - 1) * p.R) + (seg * p.R - 1)) * (size_t)(kF * kDV);
-    if (src) {
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int dt = 0; dt < 2; ++dt) S[mt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      const float *src = nullptr;
+      if (seg == 0)
+        src = p.state_in ? p.state_in + bh * kF * kDV : nullptr;
+      else
+        src = p.seg_state + (bh * ((p.P - 1) * p.R) + (seg * p.R - 1)) * (size_t)(kF * kDV);
+      if (src) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S[mt][j] = src[feat(g, 4 * mt + j) * kDV + 16 * wave + n];
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvcol(tile, dt, n)];
+      }
     }
-  }
-  const bf16x8 selv[2] = {select16(0), select16(1)};
-  const bf16x8 selk[2] = {select_operand(0), select_operand(1)};
-  // meta-memory sinks of this head, base 2 (query waves)
-  float meta_max = -INFINITY, meta_sum = 0.0f;
-  if (SWA && !kw) {
-    const float *meta = p.meta + (size_t)h * p.n_meta;
-    for (int m = 0; m < p.n_meta; ++m) meta_max = fmaxf(meta_max, meta[m] * kLog2e);
-    for (int m = 0; m < p.n_meta; ++m) meta_sum += exp2_fast(meta[m] * kLog2e - meta_max);
-    if (p.n_meta == 0) meta_max = 0.0f;  // meta_sum = 0: no sink mass
-  }
-
-  // V^T half fragments (key waves) or raw-k fragments (query waves) of this
-  // wave's tile of chunk c into ring slot `slot`
-  auto stage = [&](const Regs8 &r, int slot) {
-    if (kw) {
+    // V^T half fragments of token tile `tile` into ring slot `slot`: for d_v tile
+    // (2w' + dt), lane 16g + r holds v[16 tile + 4g + j][dvcol(w', dt, r)]
+    auto stage_vt = [&](const bf16x8 *xv, int slot) {
       char *base = smem + LD::VT + (slot * 4 + tile) * 8 * kHalf + lane * 8;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s) {
+        f32x4 t2[2];
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const f32x4 t = mfma(r.xb[s], selv[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
-          *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t);
-        }
-    } else if (SWA) {
+        for (int dt = 0; dt < 2; ++dt) t2[dt] = mfma(xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sts8(smem + LD::RK + ((slot * 4 + tile) * 4 + s) * kFrag + lane * 16, r.xb[s]);
-    }
-  };
-
-  // ---- window part: keys and values of the chunk before the segment
-  if (SWA) {
-    Regs8 pr;
-    load8<SWA, L8_B>(p, bh, c_begin - 1, tile, kw, pr);
-    stage(pr, (c_begin - 1) & 1);
-  }
-
-  // ================= column phase of chunk cc: outputs and state =================
-  float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
-  auto column = [&](int cc) {
-    const int c0 = cc * kC;
-    const int slot = SWA ? (cc & 1) : 0;
-    const int pslot = slot ^ 1;
-    f32x4 O[4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) O[qt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    // inter-chunk readout O^T += S^T q-bar^T; the state is decayed right after
-    // it is read (S <- diag(2^{B}) S).  The q-bar fragments of k-step s+1 are
-    // requested before the MFMAs of step s.
-    bf16x8 qf[2][4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) qf[0][qt] = lds8(smem + LD::QB + (qt * 4) * kFrag + lane * 16);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) {
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
-          qf[(s + 1) & 1][qt] = lds8(smem + LD::QB + (qt * 4 + s + 1) * kFrag + lane * 16);
-      }
-      issue_fence();
-      const bf16x8 a = pack44(S[2 * s], S[2 * s + 1]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        S[2 * s][j] *= row_bcast(fdec[j & 1], (8 * s + j) >> 1);
-        S[2 * s + 1][j] *= row_bcast(fdec[j & 1], (8 * s + 4 + j) >> 1);
-      }
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) O[qt] = mfma(a, qf[s & 1][qt], O[qt]);
-    }
-    // weights x V over the key tiles of each query tile; the operands of query
-    // tile qt+1 are requested before the MFMAs of qt
-    auto vt_half = [&](int kt) -> bf16x4 {
-      const int sl = kt >= 0 ? slot : pslot;
-      const int tl = kt >= 0 ? kt : kt + 4;
-      return *(const bf16x4 *)(smem + LD::VT + ((sl * 4 + tl) * 8 + wave) * kHalf + lane * 8);
-    };
-    bf16x8 wf[2][NKS], vf[2][NKS];
-    auto wv_load = [&](int qt, int buf) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        wf[buf][ks] = lds8(smem + LD::W + (qt * NKS + ks) * kFrag + lane * 16);
-        bf16x4 lo, hi;
-        if (SWA) {
-          const int ka = qt - 4 + 2 * ks;
-          lo = vt_half(ka);
-          if (ks < 2) {
-            hi = vt_half(ka + 1);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hi[j] = (bf16)0.0f;
-          }
-        } else {
-          lo = vt_half(2 * ks);
-          hi = vt_half(2 * ks + 1);
-        }
-        vf[buf][ks] = join44(lo, hi);
+        for (int dt = 0; dt < 2; ++dt) *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t2[dt]);
       }
     };
-    wv_load(0, 0);
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      if (qt + 1 < 4) wv_load(qt + 1, (qt + 1) & 1);
-      issue_fence();
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) O[qt] = mfma(vf[qt & 1][ks], wf[qt & 1][ks], O[qt]);
+    const HeadBufs hb = head_bufs(p, bh);
+    const unsigned ro = row_off(tile);
+    bf16x8 xk[4], xv[4], xg[4];  // this chunk's keys, values, gates
+    if (SWA) {  // values of the chunk before the segment (window part)
+      load_vals(hb.v, ro + chunk_off(c_begin - 1), xv);
+      stage_vt(xv, (c_begin - 1) & 1);
     }
-    // store o: lane (n, g) of query tile qt holds o[16qt + n][16 wave + 4g + j]
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const int t = c0 + 16 * qt + n;
-      if (t < p.L) *(bf16x4 *)(p.o + (bh * p.L + t) * kDV + 16 * wave + 4 * g) = pack4(O[qt]);
-    }
-    // S += k-hat^T V, in groups of 4 state tiles; group i+1 requested before the
-    // MFMAs of group i
-    const char *vb = smem + LD::VT + (slot * 32 + wave) * kHalf + lane * 8;
-    const bf16x8 bv[2] = {join44(*(const bf16x4 *)vb, *(const bf16x4 *)(vb + 8 * kHalf)),
-                          join44(*(const bf16x4 *)(vb + 16 * kHalf), *(const bf16x4 *)(vb + 24 * kHalf))};
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) kf[0][m4] = lds8(smem + LD::KH + (m4 * 2) * kFrag + lane * 16);
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {  // grp = 2 sp + (mt / 4)
-      if (grp + 1 < 4) {
-        const int sp1 = (grp + 1) >> 1, mb1 = 4 * ((grp + 1) & 1);
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4)
-          kf[(grp + 1) & 1][m4] = lds8(smem + LD::KH + ((mb1 + m4) * 2 + sp1) * kFrag + lane * 16);
-      }
-      issue_fence();
-      const int sp = grp >> 1, mb = 4 * (grp & 1);
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) S[mb + m4] = mfma(kf[grp & 1][m4], bv[sp], S[mb + m4]);
-    }
-  };
+    load_rows(hb.k, ro + chunk_off(c_begin), xk);
+    load_vals(hb.v, ro + chunk_off(c_begin), xv);
+    load_gates(hb.g, ro + chunk_off(c_begin), xg);
+    float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
+    __syncthreads();               // staged fragments and the first chunk's totals
 
-  Regs8 cur;
-  load8<SWA, L8_ALL>(p, bh, c_begin, tile, kw, cur);
-  __syncthreads();
-
-  const float sl2 = p.scale * kLog2e;
-  for (int c = c_begin; c <= c_end; ++c) {
-    if (c > c_begin) column(c - 1);
-    __syncthreads();  // B3: LDS fragments of chunk c-1 consumed
-    if (c == c_end) break;
-    const int c0 = c * kC;
-    const int slot = SWA ? (c & 1) : 0;
-    const int pslot = slot ^ 1;
-    const int tq = c0 + 16 * tile + n;  // this lane's token in the row phase
-    const bool tok_ok = tq < p.L;
-    const bool full = c0 + kC <= p.L;  // every token of the chunk exists (uniform)
-    const bool more = c + 1 < c_end;
-    const int hh = kw ? 0 : 16;  // first fold slot of this wave's log-gate half
-
-    // ================= phase A =================
-    stage(cur, slot);
-    if (more && kw) load8<SWA, L8_B>(p, bh, c + 1, tile, kw, cur);
-
-    // band scores (query waves): sc[i] for key tile tile-4+i; tiles of the
-    // previous chunk and the diagonal now, the others after B1a
-    f32x4 sc[5];
+    // column phase of chunk cc: outputs and state
+    auto column = [&](int cc) {
+      const int c0 = cc * kC;
+      const int slot = SWA ? (cc & 1) : 0;
+      const int pslot = slot ^ 1;
+      f32x4 O[4][2];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) sc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    auto band = [&](int i) {
-      const int kt = tile - 4 + i;
-      bf16x8 a[4];
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) O[qt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      // inter-chunk readout O^T += S^T q-bar^T; the state is decayed right after
+      // it is read (S <- diag(2^{B}) S).  The 4 q-bar fragments of a k-step are
+      // requested together.
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if (i == 4)
-          a[s] = cur.xb[s];
-        else if (kt >= 0)
-          a[s] = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
-        else
-          a[s] = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
+        bf16x8 qf[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) qf[qt] = lds8(smem + LD::QB + (qt * 4 + s) * kFrag + lane * 16);
+        issue_fence();
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16x8 a = pack44(S[2 * s][dt], S[2 * s + 1][dt]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            S[2 * s][dt][j] *= row_bcast(fdec[j & 1], (8 * s + j) >> 1);
+            S[2 * s + 1][dt][j] *= row_bcast(fdec[j & 1], (8 * s + 4 + j) >> 1);
+          }
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) O[qt][dt] = mfma(a, qf[qt], O[qt][dt]);
+        }
       }
-      issue_fence();
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      // weights x V over the key tiles of each query tile
+      auto vt_half = [&](int kt, int dt) -> bf16x4 {
+        const int sl = kt >= 0 ? slot : pslot;
+        const int tl = kt >= 0 ? kt : kt + 4;
+        return *(const bf16x4 *)(smem + LD::VT + ((sl * 4 + tl) * 8 + 2 * tile + dt) * kHalf + lane * 8);
+      };
+      const bf16x4 z4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma(a[s], cur.xa[s], acc);
-      sc[i] = acc;
-    };
-    if (SWA && !kw) {
+      for (int qt = 0; qt < 4; ++qt) {
+        bf16x8 wf[NKS], vf[NKS][2];
 #pragma unroll
-      for (int i = 0; i < 5; ++i)
-        if (i == 4 || tile - 4 + i < 0) band(i);
-      if (more) load8<SWA, L8_B>(p, bh, c + 1, tile, kw, cur);
-    }
-
-    // u = x Wphi (16 x 64 per tile)
-    f32x4 u[4];
+        for (int ks = 0; ks < NKS; ++ks) {
+          const char *wb = smem + LD::W + qt * LD::WQT + ks * kFrag;
+          if (SWA && ks == 2)
+            wf[ks] = join44(*(const bf16x4 *)(wb + lane * 8), z4);
+          else
+            wf[ks] = lds8(wb + lane * 16);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) u[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    {  // the 4 fragments of tile mt+1 are requested before the MFMAs of tile mt
-      const char *wb = smem + (kw ? LD::WK : LD::WQ) + lane * 16;
-      bf16x8 wfr[2][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wfr[0][s] = lds8(wb + s * kFrag);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt + 1 < 4) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) wfr[(mt + 1) & 1][s] = lds8(wb + ((mt + 1) * 4 + s) * kFrag);
+          for (int dt = 0; dt < 2; ++dt) {
+            bf16x4 lo, hi;
+            if (SWA) {
+              const int ka = qt - 4 + 2 * ks;
+              lo = vt_half(ka, dt);
+              hi = ks < 2 ? vt_half(ka + 1, dt) : z4;
+            } else {
+              lo = vt_half(2 * ks, dt);
+              hi = vt_half(2 * ks + 1, dt);
+            }
+            vf[ks][dt] = join44(lo, hi);
+          }
         }
         issue_fence();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) u[mt] = mfma(wfr[mt & 1][s], cur.xa[s], u[mt]);
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) O[qt][dt] = mfma(vf[ks][dt], wf[ks], O[qt][dt]);
       }
-    }
-    if (more && kw) load8<SWA, L8_A>(p, bh, c + 1, tile, kw, cur);
-
-    // log-gates of this wave's half (fold slots hh .. hh+15), base 2, floored,
-    // zero for tokens past the end; in-tile inclusive cumsum over the 16 tokens
-    float dh[16];
-    if (p.gate_is_log) {  // one uniform branch around the whole loop
+      // store o: lane (n, g) of query tile qt holds d_v 32 tile + 8g + (4dt + j);
+      // rows past the end are dropped by the range check
+      if (cc >= c_begin) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dh[i] = (float)cur.xg[i >> 3][i & 7] * kLog2e;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dh[i] = log2_sigmoid((float)cur.xg[i >> 3][i & 7]);
-    }
-    if (more) load8<SWA, L8_G>(p, bh, c + 1, tile, kw, cur);
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dh[i] = fmaxf(dh[i], kMinLog2Gate);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dh[i] = tok_ok ? fmaxf(dh[i], kMinLog2Gate) : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dh[i] += row_shr<1>(dh[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dh[i] += row_shr<2>(dh[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dh[i] += row_shr<4>(dh[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dh[i] += row_shr<8>(dh[i]);
-    {
-      char *xd = smem + LD::DD + tile * 8 * 1024 + lane * 16;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(f32x4 *)(xd + ((hh >> 2) + q4) * 1024) =
-            (f32x4){dh[4 * q4], dh[4 * q4 + 1], dh[4 * q4 + 2], dh[4 * q4 + 3]};
-      if (n == 15) {
-        float *T = (float *)(smem + LD::T) + tile * kF;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) T[feat(g, hh + i)] = dh[i];
+        for (int qt = 0; qt < 4; ++qt)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4, pack44(O[qt][0], O[qt][1])), hb.o,
+              (int)(chunk_off(cc) + (unsigned)(16 * qt + n) * (kDV * 2) + 64 * tile + 16 * g), 0, 0);
       }
-    }
-    // unnormalised Hedgehog exponentials
-    float e[32], izp, izn;
-    hedgehog_exp(u, e, izp, izn);
-    __syncthreads();  // B1a: cumsum halves, tile totals, raw-k fragments visible
-
-    // ================= phase B =================
-    // Fold reference r (base 2, per feature).  Chunk mode: r = B/2 for the whole
-    // chunk, so cross-tile factors are 1; used when every feature's chunk total
-    // has |B| <= kChunkRefLimit.  Tile mode otherwise: r_w = P_w + T_w/2.
-    // Per-tile quantities are computed for features 2n, 2n+1 of the lane's group
-    // and broadcast to the row (DPP) where needed.
-    float tt[4][2], pre[2], btot[2], tw[2], rr2[2], dd[32];
-    bool chunk_mode = true;
-    {
-      const float *T = (const float *)(smem + LD::T);
-      const int f0 = feat(g, 2 * n);
+      // S += k-hat^T V in groups of 4 state tiles (fragments of a group requested
+      // together)
+      bf16x8 bv[2][2];
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
-        tt[w2][0] = v2.x;
-        tt[w2][1] = v2.y;
-      }
+      for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        pre[e2] = 0.0f;
-        btot[e2] = 0.0f;
-        tw[e2] = 0.0f;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          btot[e2] += tt[w2][e2];
-          if (w2 < tile) pre[e2] += tt[w2][e2];
-          if (w2 == tile) tw[e2] = tt[w2][e2];
+        for (int dt = 0; dt < 2; ++dt) {
+          const char *vb = smem + LD::VT + ((slot * 4 + 2 * sp) * 8 + 2 * tile + dt) * kHalf + lane * 8;
+          bv[sp][dt] = join44(*(const bf16x4 *)vb, *(const bf16x4 *)(vb + 8 * kHalf));
         }
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {  // grp = 2 sp + (mt / 4)
+        const int sp = grp >> 1, mb = 4 * (grp & 1);
+        bf16x8 kf[4];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) kf[m4] = lds8(smem + LD::KH + ((mb + m4) * 2 + sp) * kFrag + lane * 16);
+        issue_fence();
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) S[mb + m4][dt] = mfma(kf[m4], bv[sp][dt], S[mb + m4][dt]);
       }
-      // every wave sees all 128 features, so the vote is the same in all waves
-      chunk_mode = __all(fabsf(btot[0]) <= kChunkRefLimit && fabsf(btot[1]) <= kChunkRefLimit);
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        rr2[e2] = chunk_mode ? 0.5f * btot[e2] : pre[e2] + 0.5f * tw[e2];
-        fdec[e2] = exp2_fast(btot[e2]);
-      }
-      // the other wave's cumsum half
-      const char *xd = smem + LD::DD + tile * 8 * 1024 + lane * 16;
-      float oth[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = *(const f32x4 *)(xd + ((4 - (hh >> 2)) + q4) * 1024);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oth[4 * q4 + j] = v4[j];
-      }
-      if (kw) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          dd[i] = dh[i];
-          dd[16 + i] = oth[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          dd[i] = oth[i];
-          dd[16 + i] = dh[i];
-        }
-      }
-      float off[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) off[e2] = pre[e2] - rr2[e2];  // b_chunk - r = b_loc + off
-#pragma unroll
-      for (int i = 0; i < 32; ++i) dd[i] += row_bcast(off[i & 1], i >> 1);
-    }
+    };
 
-    bf16x8 xr[4];  // key wave: k~; query wave: q~ (MFMA operands, token rows)
-    bf16x8 xs[4];  // key wave: k-hat; query wave: q-bar
-    {
-      // key: k~ = phi_k 2^{-(b - r)}, k-hat = k~ 2^{B - r}
-      // query: q~ = phi_q 2^{b - r}, q-bar = q~ 2^{r}
+    for (int c = c_begin; c < c_end; ++c) {
+      const int slot = SWA ? (c & 1) : 0;
+      const int tq = c * kC + 16 * tile + n;
+      const bool tok_ok = tq < p.L;
+      const unsigned ro1 = ro + chunk_off(c + 1);
+      // ---- phase A: previous chunk's column phase, then this tile's keys
+      column(c - 1);
+      f32x4 u[4];
+      project(smem + LD::WK + lane * 16, xk, u);
+      load_rows(hb.k, ro1, xk);  // next chunk's keys
+      float dd[32];
+      tile_cumsum(xg, gate_is_log, tok_ok, dd);
+      load_gates(hb.g, ro1, xg);
+      float e[32], izp, izn;
+      hedgehog_exp(u, e, izp, izn);
+      const FoldRef r = fold_ref((const float *)(smem + LD::T) + (c & 1) * 4 * kF, tile);
+      bf16x8 xr[4], xs[4];  // k~ (intra scores), k-hat (state update)
       float fs[2];
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) fs[e2] = exp2_fast(kw ? btot[e2] - rr2[e2] : rr2[e2]);
-      const float sgn = kw ? -1.0f : 1.0f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float a8[8], b8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * s + j;
-          a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(sgn * dd[i]);
-          b8[j] = a8[j] * row_bcast(fs[j & 1], i >> 1);
-        }
-        xr[s] = pack8(a8);
-        xs[s] = pack8(b8);
+      for (int e2 = 0; e2 < 2; ++e2) {
+        fs[e2] = r.btot[e2] - r.rr2[e2];
+        fdec[e2] = exp2_fast(r.btot[e2]);
       }
-    }
-    if (kw) {
-      if (!full && !tok_ok) {  // keys past the end contribute nothing
+      fold(e, izp, izn, dd, r, -1.0f, fs, xr, xs);
+      if (!tok_ok) {  // keys past the end contribute nothing
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           xr[s] = zero8();
@@ -530,112 +459,243 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (tile * 4 + s) * kFrag + lane * 16, xr[s]);
-    }
+      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase done
 
-    // window: remaining band scores, masks, one-shot softmax with the sinks
-    f32x4 Wt[5];  // weights^T for key tiles tile-4+i (i = 4: the diagonal tile)
+      // ---- phase C: V^T and k-hat^T fragments of this tile
+      stage_vt(xv, slot);
+      load_vals(hb.v, ro1, xv);  // next chunk's values
+      {  // state tile mt takes its 16 features from K-step s(mt) = 2(mt/4) + (mt%4)/2
+         // of the token-row operand, transposed on the matrix core
+        const int sp = tile >> 1, hf = tile & 1;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    if (SWA && !kw) {
+        for (int m2 = 0; m2 < 4; ++m2) {
+          f32x4 t2[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tile - 4 + i >= 0) band(i);
-      // key position minus query position: 16(i-4) + 4g + j - n; valid when in
-      // (-window, 0] and the key exists (position >= 0)
-      float mx = -INFINITY;
+          for (int d2 = 0; d2 < 2; ++d2) {
+            const int mt = 2 * m2 + d2;
+            const int s2 = 2 * (mt >> 2) + ((mt & 3) >> 1);
+            t2[d2] = mfma(xs[s2], sel[mt & 1], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+          }
 #pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rel = 16 * (i - 4) + 4 * g + j - n;
-          const bool ok = rel <= 0 && rel > -p.window && tq + rel >= 0;
-          sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
-          mx = fmaxf(mx, sc[i][j]);
+          for (int d2 = 0; d2 < 2; ++d2)
+            *(bf16x4 *)(smem + LD::KH + ((2 * m2 + d2) * 2 + sp) * kFrag + lane * 16 + hf * 8) = pack4(t2[d2]);
         }
-      mx = grp_max(mx);
-      mx = fmaxf(mx, meta_max);
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float ex = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
-          sc[i][j] = ex;
-          sum += ex;
-        }
-      sum = grp_sum(sum);
-      sum += meta_sum * exp2_fast(meta_max - mx);  // sum_m 2^{t_m log2e - mx}
-      const float inv = rcp_fast(sum);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) Wt[i] = sc[i] * inv;
-    }
-    if (more && !kw) load8<SWA, L8_A>(p, bh, c + 1, tile, kw, cur);
-    __syncthreads();  // B1: k~ fragments visible, cumsum exchange consumed
-
-    // ================= phase C =================
-    if (kw) {
-      // k-hat^T fragments: state tile mt takes its 16 features from K-step
-      // s(mt) = 2(mt/4) + (mt%4)/2 of the token-row operand, transposed on the
-      // matrix core
-      const int sp = tile >> 1, hf = tile & 1;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int s2 = 2 * (mt >> 2) + ((mt & 3) >> 1);
-        const f32x4 t = mfma(xs[s2], selk[mt & 1], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
-        *(bf16x4 *)(smem + LD::KH + (mt * 2 + sp) * kFrag + lane * 16 + hf * 8) = pack4(t);
       }
-    } else {
-      // intra-chunk scores A^T for key tiles kt = tile-4+i, i = 1..4, kt >= 0
-      {  // diagonal tile: both sides share the reference
+      __syncthreads();  // B2: q-bar, k-hat^T, V^T, weight fragments visible
+    }
+    column(c_end - 1);
+    if (p.state_out && seg == p.P - 1) {
+      float *dst = p.state_out + bh * kF * kDV;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(tile, dt, n)] = S[mt][dt][j];
+    }
+  } else {
+    // ============================== query waves ==============================
+    // meta-memory sinks of this head, base 2
+    float meta_max = -INFINITY, meta_sum = 0.0f;
+    if (SWA) {
+      const float *meta = p.meta + (size_t)h * p.n_meta;
+      for (int m = 0; m < p.n_meta; ++m) meta_max = fmaxf(meta_max, meta[m] * kLog2e);
+      for (int m = 0; m < p.n_meta; ++m) meta_sum += exp2_fast(meta[m] * kLog2e - meta_max);
+      if (p.n_meta == 0) meta_max = 0.0f;  // meta_sum = 0: no sink mass
+      // wave-uniform: keep them in scalar registers
+      meta_max = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, meta_max)));
+      meta_sum = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, meta_sum)));
+    }
+    auto stage_rk = [&](const bf16x8 *xk, int slot) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sts8(smem + LD::RK + ((slot * 4 + tile) * 4 + s) * kFrag + lane * 16, xk[s]);
+    };
+    // q and raw keys of this chunk, gates of the next
+    bf16x8 xq[4], xb[4], xg[4];
+    const HeadBufs hb = head_bufs(p, bh);
+    const unsigned ro = row_off(tile);
+    if (SWA) {  // keys of the chunk before the segment (window part)
+      load_rows(hb.k, ro + chunk_off(c_begin - 1), xb);
+      stage_rk(xb, (c_begin - 1) & 1);
+    }
+    float dd[32];  // cumsums of the chunk being processed
+    {
+      load_rows(hb.q, ro + chunk_off(c_begin), xq);
+      if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
+      load_gates(hb.g, ro + chunk_off(c_begin), xg);
+      tile_cumsum(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dd);
+      if (n == 15) {  // tile totals of the first chunk
+        float *T = (float *)(smem + LD::T) + ((c_begin & 1) * 4 + tile) * kF;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
+      }
+      load_gates(hb.g, ro + chunk_off(c_begin + 1), xg);
+    }
+    const float sl2 =
+        __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale * kLog2e)));
+    __syncthreads();  // staged fragments and the first chunk's totals
+
+    for (int c = c_begin; c < c_end; ++c) {
+      const int slot = SWA ? (c & 1) : 0;
+      const int pslot = slot ^ 1;
+      const int tq = c * kC + 16 * tile + n;
+      const unsigned ro1 = ro + chunk_off(c + 1);
+      // ---- phase A
+      // band scores sc[i] for key tile tile-4+i: tiles of the previous chunk and
+      // the diagonal at the end of this phase (their keys are in LDS: the own
+      // tile's were staged by this wave), the others after B1
+      f32x4 sc[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) sc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      auto band = [&](int i) {
+        const int kt = tile - 4 + i;
+        bf16x8 a[4];
+        issue_fence();  // keep the loads next to their MFMAs
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (kt >= 0)
+            a[s] = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
+          else
+            a[s] = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
+        }
+        issue_fence();
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma(lds8(smem + LD::KT + (tile * 4 + s) * kFrag + lane * 16), xr[s], acc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
-        Wt[4] += acc;
+        for (int s = 0; s < 4; ++s) acc = mfma(a[s], xq[s], acc);
+        sc[i] = acc;
+      };
+      if (SWA) stage_rk(xb, slot);
+      f32x4 u[4];
+      project(smem + LD::WQ + lane * 16, xq, u);
+      float e[32], izp, izn;
+      hedgehog_exp(u, e, izp, izn);
+      bf16x8 xr[4], xs[4];  // q~ (intra scores), q-bar (readout)
+      bool chunk_mode;
+      {
+        const FoldRef r = fold_ref((const float *)(smem + LD::T) + (c & 1) * 4 * kF, tile);
+        fold(e, izp, izn, dd, r, 1.0f, r.rr2, xr, xs);
+        chunk_mode = r.chunk_mode;
       }
-      // earlier tiles: in chunk mode both sides share the reference; in tile mode
-      // q~ is scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
+      // cumsums and tile totals of the next chunk, published one chunk ahead
+      tile_cumsum(xg, gate_is_log, tq + kC < p.L, dd);
+      load_gates(hb.g, ro + chunk_off(c + 2), xg);
+      if (n == 15) {
+        float *T = (float *)(smem + LD::T) + (((c + 1) & 1) * 4 + tile) * kF;
 #pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        const int kt = tile - 4 + i;
-        if (kt >= 0 && chunk_mode) {
+        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
+      }
+      if (SWA) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+          if (i == 4 || tile - 4 + i < 0) band(i);
+      }
+      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase done
+
+      // ---- phase C
+      f32x4 Wt[5];  // weights^T for key tiles tile-4+i (i = 4: the diagonal tile)
+#pragma unroll
+      for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      if (SWA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tile - 4 + i >= 0) band(i);
+        // key position minus query position: 16(i-4) + 4g + j - n; valid when in
+        // (-window, 0] and the key exists (position >= 0)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int rel = 16 * (i - 4) + 4 * g + j - n;
+            const bool ok = rel <= 0 && rel > -p.window && tq + rel >= 0;
+            sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
+            mx = fmaxf(mx, sc[i][j]);
+          }
+        mx = grp_max(mx);
+        mx = fmaxf(mx, meta_max);
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float ex = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
+            sc[i][j] = ex;
+            sum += ex;
+          }
+        sum = grp_sum(sum);
+        sum += meta_sum * exp2_fast(meta_max - mx);  // sum_m 2^{t_m log2e - mx}
+        const float inv = rcp_fast(sum);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) Wt[i] = sc[i] * inv;
+      }
+      // intra-chunk scores A^T for key tiles kt = tile-4+i, i = 1..4, kt >= 0
+      {
+        auto kt_frags = [&](int kt, bf16x8 *kf) {
+          issue_fence();  // keep the loads next to their MFMAs
+#pragma unroll
+          for (int s = 0; s < 4; ++s) kf[s] = lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16);
+          issue_fence();
+        };
+        {  // diagonal tile: both sides share the reference
+          bf16x8 kf[4];
+          kt_frags(tile, kf);
           f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), xr[s], acc);
-          Wt[i] += acc;
-        } else if (kt >= 0) {
-          float fo[2];
+          for (int s = 0; s < 4; ++s) acc = mfma(kf[s], xr[s], acc);
 #pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            float run = 0.0f, tk = 0.0f;  // log-gate sum of tiles kt .. tile-1
+          for (int j = 0; j < 4; ++j)
+            if (4 * g + j > n) acc[j] = 0.0f;  // causal: key after query
+          Wt[4] += acc;
+        }
+        // earlier tiles: in chunk mode both sides share the reference; in tile
+        // mode q~ is scaled by 2^{r_w - r_kt} <= 1 with r_x = P_x + T_x/2
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-              if (w2 >= kt && w2 < tile) run += tt[w2][e2];
-              if (w2 == kt) tk = tt[w2][e2];
+        for (int i = 1; i < 4; ++i) {
+          const int kt = tile - 4 + i;
+          if (kt >= 0 && chunk_mode) {
+            bf16x8 kf[4];
+            kt_frags(kt, kf);
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma(kf[s], xr[s], acc);
+            Wt[i] += acc;
+          } else if (kt >= 0) {
+            bf16x8 kf[4];
+            kt_frags(kt, kf);
+            // tile totals of this chunk again (the slot is rewritten only in the
+            // next chunk's phase A)
+            const float *T = (const float *)(smem + LD::T) + (c & 1) * 4 * kF + feat(g, 2 * n);
+            float fo[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              float run = 0.0f, tk = 0.0f, tw = 0.0f;  // log-gate sum of tiles kt .. tile-1
+#pragma unroll
+              for (int w2 = 0; w2 < 4; ++w2) {
+                const float tv = T[w2 * kF + e2];
+                if (w2 >= kt && w2 < tile) run += tv;
+                if (w2 == kt) tk = tv;
+                if (w2 == tile) tw = tv;
+              }
+              fo[e2] = exp2_fast(run + 0.5f * (tw - tk));
             }
-            fo[e2] = exp2_fast(run + 0.5f * (tw[e2] - tk));
-          }
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            float tmp[8];
+            for (int s = 0; s < 4; ++s) {
+              float tmp[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) tmp[j] = (float)xr[s][j] * row_bcast(fo[j & 1], (8 * s + j) >> 1);
-            acc = mfma(lds8(smem + LD::KT + (kt * 4 + s) * kFrag + lane * 16), pack8(tmp), acc);
+              for (int j = 0; j < 8; ++j) tmp[j] = (float)xr[s][j] * row_bcast(fo[j & 1], (8 * s + j) >> 1);
+              acc = mfma(kf[s], pack8(tmp), acc);
+            }
+            Wt[i] += acc;
           }
-          Wt[i] += acc;
         }
       }
       // weight fragments for the (weights x V) GEMM
+      char *wq = smem + LD::W + tile * LD::WQT;
       if (SWA) {
-        sts8(smem + LD::W + (tile * NKS + 0) * kFrag + lane * 16, pack44(Wt[0], Wt[1]));
-        sts8(smem + LD::W + (tile * NKS + 1) * kFrag + lane * 16, pack44(Wt[2], Wt[3]));
-        sts8(smem + LD::W + (tile * NKS + 2) * kFrag + lane * 16,
-             pack44(Wt[4], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}));
+        sts8(wq + lane * 16, pack44(Wt[0], Wt[1]));
+        sts8(wq + kFrag + lane * 16, pack44(Wt[2], Wt[3]));
+        *(bf16x4 *)(wq + 2 * kFrag + lane * 8) = pack4(Wt[4]);
       } else {
         // absolute key tiles 0..3 of the chunk: tile kt is Wt[kt - tile + 4]
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -646,23 +706,17 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
           case 2: w0 = Wt[2]; w1 = Wt[3]; w2 = Wt[4]; break;
           default: w0 = Wt[1]; w1 = Wt[2]; w2 = Wt[3]; w3 = Wt[4]; break;
         }
-        sts8(smem + LD::W + (tile * NKS + 0) * kFrag + lane * 16, pack44(w0, w1));
-        sts8(smem + LD::W + (tile * NKS + 1) * kFrag + lane * 16, pack44(w2, w3));
+        sts8(wq + lane * 16, pack44(w0, w1));
+        sts8(wq + kFrag + lane * 16, pack44(w2, w3));
       }
-      // q-bar fragments (inter-chunk readout)
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::QB + (tile * 4 + s) * kFrag + lane * 16, xs[s]);
+      // next chunk's queries and raw keys; their first use waits out the key
+      // waves' longer phase A
+      load_rows(hb.q, ro1, xq);
+      if (SWA) load_rows(hb.k, ro1, xb);
+      __syncthreads();  // B2: q-bar, k-hat^T, V^T, weight fragments visible
     }
-    __syncthreads();  // B2: q-bar, k-hat^T, weight fragments visible
-  }
-
-  // ---- epilogue
-  if (p.state_out && seg == p.P - 1) {
-    float *dst = p.state_out + bh * kF * kDV;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + 16 * wave + n] = S[mt][j];
   }
 }
 

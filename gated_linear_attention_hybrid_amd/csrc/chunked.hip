@@ -63,11 +63,6 @@ struct Lds {
   static constexpr int BYTES = T + (GLA ? 4 * kF * 4 : 0);
 };
 
-// d_v column held by lane n, column-tile dt, of wave w (8 contiguous per lane group)
-__device__ __forceinline__ int dvcol(int w, int dt, int n) {
-  return 32 * w + 8 * (n >> 2) + 4 * dt + (n & 3);
-}
-
 // One chunk's inputs held in registers (prefetched one chunk ahead).
 struct ChunkRegs {
   bf16x8 xq[4];  // q[token 16w+n][32g + 8s + j]
