@@ -153,7 +153,7 @@ __device__ __forceinline__ float log2_sigmoid(float g) {
 template <int SRC>
 __device__ __forceinline__ float row_bcast_c(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               0x150 + SRC, 0xF, 0xF, false));
+                                                               0x150 + SRC, 0xF, 0xF, true));
 }
 // the same for an index that is a constant after unrolling (the switch folds)
 __device__ __forceinline__ float row_bcast(float x, int src) {
