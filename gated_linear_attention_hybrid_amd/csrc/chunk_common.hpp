@@ -89,28 +89,11 @@ __device__ __forceinline__ bf16x8 join44(bf16x4 lo, bf16x4 hi) {
   return r;
 }
 
-// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48) with the
-// gfx950 row swaps: v_permlane16_swap with both operands x yields rows
-// (x0, x0, x2, x2) and (x1, x1, x3, x3), v_permlane32_swap yields (x0, x1, x0, x1)
-// and (x2, x3, x2, x3); combining each pair reduces over the rows without LDS.
-template <class Op>
-__device__ __forceinline__ float grp_reduce(float x, Op op) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = op(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
-  const unsigned w = __builtin_bit_cast(unsigned, x);
-  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return op(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
-}
-__device__ __forceinline__ float grp_max(float x) {
-  return grp_reduce(x, [](float a, float b) { return fmaxf(a, b); });
-}
-__device__ __forceinline__ float grp_min(float x) {
-  return grp_reduce(x, [](float a, float b) { return fminf(a, b); });
-}
-__device__ __forceinline__ float grp_sum(float x) {
-  return grp_reduce(x, [](float a, float b) { return a + b; });
-}
+// reductions over the 4 lane groups (lanes n, n+16, n+32, n+48): the gfx950 row
+// swaps of rows_reduce (device_common.hpp), no LDS
+__device__ __forceinline__ float grp_max(float x) { return rows_reduce(x, OpMax()); }
+__device__ __forceinline__ float grp_min(float x) { return rows_reduce(x, OpMin()); }
+__device__ __forceinline__ float grp_sum(float x) { return rows_reduce(x, OpAdd()); }
 
 // inclusive scan over the 16 lanes of a row (the 16 tokens of a tile)
 template <int N>

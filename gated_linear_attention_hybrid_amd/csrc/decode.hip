@@ -5,13 +5,14 @@
 // 2507.09025, Methodology A.1): per (b, h) the step reads the f x d_v fp32 state
 // once and writes it once; everything else is small.  The step is bound by HBM
 // bandwidth, so the block issues its share of the state loads first (16-byte
-// vector loads, 2 x 32 KiB in flight per block) and does the Hedgehog GEMVs and
+// vector loads, 16 KiB in flight per block) and does the Hedgehog GEMVs and
 // the window scores while they are in flight:
 //   * Hedgehog GEMV: each thread loads 4 rows x 8 columns of each projection
-//     with 16-byte loads, partial sums are reduced across lanes and waves.
+//     with 16-byte loads, partial sums are reduced across lanes (DPP and row
+//     swaps) and waves (LDS).
 //   * window scores: 4 threads per key, 32 dimensions each, 16-byte loads.
 //   * window values and ring slots: loaded up front with the state.
-// Block = (b, h, 64-column slice of d_v); blocks of one head share an XCD.
+// Block = (b, h, 32-column slice of d_v); the 4 blocks of a head share an XCD.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -21,7 +22,7 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kD = 128, kF = 128, kF2 = 64, kDV = 128, kMaxW = 64;
-constexpr int kDVS = 64;                 // state columns per block
+constexpr int kDVS = 32;                 // state columns per block
 constexpr int kC4 = kDVS / 4;            // float4 column groups per block
 constexpr int kNRG = kNT / kC4;          // row groups
 constexpr int kRPT = kF / kNRG;          // state rows per thread
@@ -145,14 +146,12 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
         pk[e] += xk[i] * wk[e];
       }
     }
-    // reduce the 8 row groups of this wave (lane bits 3..5)
+    // reduce the 8 row groups of this wave (lane bits 3..5): row_ror:8 pairs
+    // lanes i and i ^ 8 inside a 16-lane row, then the row swaps
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int o = 8; o < 64; o <<= 1) {
-        pq[e] += __shfl_xor(pq[e], o, 64);
-        pk[e] += __shfl_xor(pk[e], o, 64);
-      }
+      pq[e] = rows_reduce(pq[e] + dpp_f<0x128>(pq[e]), OpAdd());
+      pk[e] = rows_reduce(pk[e] + dpp_f<0x128>(pk[e]), OpAdd());
     }
     if ((lane >> 3) == 0) {
 #pragma unroll
@@ -179,8 +178,8 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
         for (int e = 0; e < 8; ++e) acc += a8[e] * b8[e];
       }
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
+    acc += dpp_f<0xB1>(acc);  // lane ^ 1
+    acc += dpp_f<0x4E>(acc);  // lane ^ 2
     if (qd == 0 && j < kMaxW) s_p[j] = acc * p.scale;
   }
   __syncthreads();

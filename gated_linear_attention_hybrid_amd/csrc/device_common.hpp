@@ -47,20 +47,36 @@ __device__ __forceinline__ float log_gate_from(float g, bool gate_is_log) {
   return fminf(g, 0.0f) - kLn2 * log2_fast(1.0f + e);
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+// Cross-lane all-reductions without LDS: DPP quad permutes and row rotations
+// within each 16-lane row, then the gfx950 row swaps (v_permlane16_swap with
+// both operands x gives rows (x0, x0, x2, x2) and (x1, x1, x3, x3);
+// v_permlane32_swap gives (x0, x1, x0, x1) and (x2, x3, x2, x3)).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+template <class Op>
+__device__ __forceinline__ float rows_reduce(float x, Op op) {  // over the 4 rows
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = op(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, x);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return op(__builtin_bit_cast(float, (unsigned)q[0]), __builtin_bit_cast(float, (unsigned)q[1]));
 }
-__device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
-  return x;
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float x, Op op) {  // within each 16-lane row
+  x = op(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]: lane ^ 1
+  x = op(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]: lane ^ 2
+  x = op(x, dpp_f<0x124>(x));  // row_ror:4
+  return op(x, dpp_f<0x128>(x));  // row_ror:8
 }
+struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpMin { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+
+__device__ __forceinline__ float wave_sum(float x) { return rows_reduce(row16_reduce(x, OpAdd()), OpAdd()); }
+__device__ __forceinline__ float wave_max(float x) { return rows_reduce(row16_reduce(x, OpMax()), OpMax()); }
+__device__ __forceinline__ float wave_min(float x) { return rows_reduce(row16_reduce(x, OpMin()), OpMin()); }
 
 }  // namespace glah
