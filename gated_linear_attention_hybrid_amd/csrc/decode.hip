@@ -5,14 +5,15 @@
 // 2507.09025, Methodology A.1): per (b, h) the step reads the f x d_v fp32 state
 // once and writes it once; everything else is small.  The step is bound by HBM
 // bandwidth, so the block issues its share of the state loads first (16-byte
-// vector loads, 16 KiB in flight per block) and does the Hedgehog GEMVs and
-// the window scores while they are in flight:
-//   * Hedgehog GEMV: each thread loads 4 rows x 8 columns of each projection
+// vector loads, the whole 64 KiB state of a head in flight per block) and does
+// the Hedgehog GEMVs and the window scores while they are in flight:
+//   * Hedgehog GEMV: each thread loads 1 row x 8 columns of each projection
 //     with 16-byte loads, partial sums are reduced across lanes (DPP and row
 //     swaps) and waves (LDS).
 //   * window scores: 4 threads per key, 32 dimensions each, 16-byte loads.
 //   * window values and ring slots: loaded up front with the state.
-// Block = (b, h, 32-column slice of d_v); the 4 blocks of a head share an XCD.
+// Block = (b, h), 1024 threads: the projections, the window keys and the new
+// token are read once per head instead of once per column slice.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -20,9 +21,9 @@ namespace glah {
 
 namespace {
 
-constexpr int kNT = 256;
+constexpr int kNT = 1024;
 constexpr int kD = 128, kF = 128, kF2 = 64, kDV = 128, kMaxW = 64;
-constexpr int kDVS = 32;                 // state columns per block
+constexpr int kDVS = 128;                // state columns per block
 constexpr int kC4 = kDVS / 4;            // float4 column groups per block
 constexpr int kNRG = kNT / kC4;          // row groups
 constexpr int kRPT = kF / kNRG;          // state rows per thread
@@ -76,10 +77,13 @@ template <class T, int PARTS>
 __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   constexpr bool SWA = PARTS & PART_SWA;
   using V = Vec<T>;
-  __shared__ float s_uw[4][2][kF2];  // per-wave Hedgehog partial sums
+  constexpr int kWaves = kNT / 64;
+  constexpr int kGR = kD / (kNT / 8);  // GEMV rows per thread
+  __shared__ float s_uw[kWaves][2][kF2];  // per-wave Hedgehog partial sums
   __shared__ float s_ph[2][kF];      // phi(q), phi(k)
   __shared__ float s_gam[kF];
-  __shared__ float s_p[kMaxW];       // window weights
+  __shared__ float s_p[kMaxW + 1];   // window weights: ring slots, then the new token
+  __shared__ float s_qk[2];          // q . k of the new token, per wave of waves 0-1
   __shared__ f32x4 s_red[kNRG][kC4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -112,21 +116,27 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   const T *vt = (const T *)p.v + (size_t)bh * kDV;
   T *kc = SWA ? (T *)p.kcache + (size_t)bh * w * kD : nullptr;
   T *vc = SWA ? (T *)p.vcache + (size_t)bh * w * kDV : nullptr;
-  const int n = SWA ? min(pos + 1, w) : 0;  // window keys: tokens pos, pos-1, ..., pos-n+1
+  // Window keys: the new token pos and the ring tokens pos-1 .. pos-n+1, n =
+  // min(pos+1, w).  The ring is read by slot (slot s holds token pos - ((pos - s)
+  // mod w)), so no load waits for pos; masks are applied after the scores.
+  const int n = SWA ? min(pos + 1, w) : 0;
+  auto ring_ok = [&](int s) {  // slot s holds a token of the window
+    const int j = (pos - s) % w;  // pos >= 0, s < w
+    return s < w && j >= 1 && j < n;
+  };
 
-  // (2) window values this thread will weight: keys j = rg + kNRG * jj
+  // (2) window values this thread will weight: ring slots s = rg + kNRG * jj
   f32x4 vv[kKPT];
   if (SWA) {
 #pragma unroll
     for (int jj = 0; jj < kKPT; ++jj) {
-      const int j = rg + kNRG * jj;
-      vv[jj] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      if (j < n) vv[jj] = V::ld4(j == 0 ? vt + col : vc + (size_t)((pos - j) % w) * kDV + col);
+      const int s2 = rg + kNRG * jj;
+      vv[jj] = s2 < w ? V::ld4(vc + (size_t)s2 * kDV + col) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
   const f32x4 v4 = V::ld4(vt + col);
 
-  // (3) Hedgehog GEMV partials: rows 4*rgw .. 4*rgw+3, columns 8*cb .. 8*cb+7
+  // (3) Hedgehog GEMV partials: rows kGR*rgw .. kGR*rgw+kGR-1, columns 8*cb .. 8*cb+7
   {
     const int cb = tid & 7, rgw = tid >> 3;
     const T *Wq = (const T *)p.wq + (size_t)h * kD * kF2;
@@ -134,16 +144,17 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     float pq[8], pk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pq[e] = pk[e] = 0.0f;
-    const f32x4 xq = V::ld4(qt + 4 * rgw), xk = V::ld4(kt + 4 * rgw);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kGR; ++i) {
+      const int row = kGR * rgw + i;
+      const float xq = to_f32(qt[row]), xk = to_f32(kt[row]);
       float wq[8], wk[8];
-      V::ld8(Wq + (size_t)(4 * rgw + i) * kF2 + 8 * cb, wq);
-      V::ld8(Wk + (size_t)(4 * rgw + i) * kF2 + 8 * cb, wk);
+      V::ld8(Wq + (size_t)row * kF2 + 8 * cb, wq);
+      V::ld8(Wk + (size_t)row * kF2 + 8 * cb, wk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pq[e] += xq[i] * wq[e];
-        pk[e] += xk[i] * wk[e];
+        pq[e] += xq * wq[e];
+        pk[e] += xk * wk[e];
       }
     }
     // reduce the 8 row groups of this wave (lane bits 3..5): row_ror:8 pairs
@@ -163,12 +174,13 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   }
   // (4) gates
   if (tid < kF) s_gam[tid] = gate_from(to_f32(((const T *)p.gate)[(size_t)bh * kF + tid]), p.gate_is_log);
-  // (5) window scores: 4 threads per key, 32 dimensions each
+  // (5) window scores: 4 threads per ring slot, 32 dimensions each; the new
+  // token's q . k is a reduction over waves 0-1 (one dimension per thread)
   if (SWA) {
-    const int j = tid >> 2, qd = tid & 3;
+    const int s2 = tid >> 2, qd = tid & 3;
     float acc = 0.0f;
-    if (j < n) {
-      const T *kr = j == 0 ? kt : kc + (size_t)((pos - j) % w) * kD;
+    if (s2 < w) {
+      const T *kr = kc + (size_t)s2 * kD;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float a8[8], b8[8];
@@ -180,28 +192,40 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     }
     acc += dpp_f<0xB1>(acc);  // lane ^ 1
     acc += dpp_f<0x4E>(acc);  // lane ^ 2
-    if (qd == 0 && j < kMaxW) s_p[j] = acc * p.scale;
+    if (qd == 0 && s2 < kMaxW) s_p[s2] = acc * p.scale;
+    if (wave < 2) {
+      const float pq = wave_sum(to_f32(qt[tid]) * to_f32(kt[tid]));
+      if (lane == 0) s_qk[wave] = pq;
+    }
   }
   __syncthreads();
 
   // (6) wave 0 / 1: log-softmax of +u and -u for q / k; wave 2: window softmax
   if (wave < 2) {
-    const float u = s_uw[0][wave][lane] + s_uw[1][wave][lane] + s_uw[2][wave][lane] + s_uw[3][wave][lane];
+    float u = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) u += s_uw[w2][wave][lane];
     const float mx = wave_max(u), mn = wave_min(u);
     const float ep = exp_fast(u - mx), en = exp_fast(mn - u);
     const float zp = wave_sum(ep), zn = wave_sum(en);
     s_ph[wave][lane] = ep / zp;
     s_ph[wave][kF2 + lane] = en / zn;
   } else if (SWA && wave == 2) {
-    const float s = lane < n ? s_p[lane] : -INFINITY;
-    float m = wave_max(s);
+    // one-shot softmax over the ring slots in the window, the new token and the
+    // meta-memory sinks
+    const bool ok = ring_ok(lane);
+    const float s = ok ? s_p[lane] : -INFINITY;
+    const float snew = (s_qk[0] + s_qk[1]) * p.scale;
+    float m = fmaxf(wave_max(s), snew);
     const float *meta = p.meta + (size_t)h * p.n_meta;
     float tm = lane < p.n_meta ? meta[lane] : -INFINITY;
     m = fmaxf(m, wave_max(tm));
-    const float e = lane < n ? exp_fast(s - m) : 0.0f;
+    const float e = ok ? exp_fast(s - m) : 0.0f;
     const float es = lane < p.n_meta ? exp_fast(tm - m) : 0.0f;
-    const float den = wave_sum(e) + wave_sum(es);
+    const float enew = exp_fast(snew - m);
+    const float den = wave_sum(e) + wave_sum(es) + enew;
     s_p[lane] = e / den;
+    if (lane == 0) s_p[kMaxW] = enew / den;
   }
   __syncthreads();
 
@@ -217,9 +241,10 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   if (SWA) {
 #pragma unroll
     for (int jj = 0; jj < kKPT; ++jj) {
-      const int j = rg + kNRG * jj;
-      if (j < n) acc += s_p[j] * vv[jj];
+      const int s2 = rg + kNRG * jj;
+      if (s2 < w) acc += s_p[s2] * vv[jj];  // zero weight outside the window
     }
+    if (rg == 0) acc += s_p[kMaxW] * v4;
   }
   s_red[rg][c4] = acc;
   __syncthreads();
