@@ -105,12 +105,6 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   const int c4 = tid % kC4, rg = tid / kC4;
   const int col = slice * kDVS + 4 * c4;
 
-  // (1) state slice, first: rows rg + kNRG * ii, four columns per thread
-  float *Sg = p.state + (size_t)bh * kF * kDV;
-  f32x4 S[kRPT];
-#pragma unroll
-  for (int ii = 0; ii < kRPT; ++ii) S[ii] = *(const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col);
-
   const T *qt = (const T *)p.q + (size_t)bh * kD;
   const T *kt = (const T *)p.k + (size_t)bh * kD;
   const T *vt = (const T *)p.v + (size_t)bh * kDV;
@@ -125,7 +119,43 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     return s < w && j >= 1 && j < n;
   };
 
-  // (2) window values this thread will weight: ring slots s = rg + kNRG * jj
+  // All loads are issued before any arithmetic, the operands of the longest
+  // dependent chain (window scores -> softmax -> weighted values) first.
+  // (1) window score operands: 16 threads per ring slot, 8 dimensions each
+  const int ks_slot = tid >> 4, ks_seg = tid & 15;
+  float ka[8], qa[8];
+  if (SWA) {
+    if (ks_slot < w) {
+      V::ld8(kc + (size_t)ks_slot * kD + 8 * ks_seg, ka);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ka[e] = 0.0f;
+    }
+    V::ld8(qt + 8 * ks_seg, qa);
+  }
+  // (2) Hedgehog GEMV operands: rows kGR*rgw .. kGR*rgw+kGR-1, columns 8*cb .. 8*cb+7
+  const int cb = tid & 7, rgw = tid >> 3;
+  float xq[kGR], xk[kGR], wqv[kGR][8], wkv[kGR][8];
+  {
+    const T *Wq = (const T *)p.wq + (size_t)h * kD * kF2;
+    const T *Wk = (const T *)p.wk + (size_t)h * kD * kF2;
+#pragma unroll
+    for (int i = 0; i < kGR; ++i) {
+      const int row = kGR * rgw + i;
+      xq[i] = to_f32(qt[row]);
+      xk[i] = to_f32(kt[row]);
+      V::ld8(Wq + (size_t)row * kF2 + 8 * cb, wqv[i]);
+      V::ld8(Wk + (size_t)row * kF2 + 8 * cb, wkv[i]);
+    }
+  }
+  // (3) state slice: rows rg + kNRG * ii, four columns per thread (streamed:
+  // read and written once per step, non-temporal)
+  float *Sg = p.state + (size_t)bh * kF * kDV;
+  f32x4 S[kRPT];
+#pragma unroll
+  for (int ii = 0; ii < kRPT; ++ii)
+    S[ii] = __builtin_nontemporal_load((const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col));
+  // (4) window values this thread will weight: ring slots s = rg + kNRG * jj
   f32x4 vv[kKPT];
   if (SWA) {
 #pragma unroll
@@ -135,32 +165,36 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     }
   }
   const f32x4 v4 = V::ld4(vt + col);
+  // (5) gates
+  const float graw = tid < kF ? to_f32(((const T *)p.gate)[(size_t)bh * kF + tid]) : 0.0f;
+  const float qn = tid < kD ? to_f32(qt[tid]) : 0.0f, kn = tid < kD ? to_f32(kt[tid]) : 0.0f;
 
-  // (3) Hedgehog GEMV partials: rows kGR*rgw .. kGR*rgw+kGR-1, columns 8*cb .. 8*cb+7
+  // window scores (ring slots) and q . k of the new token (waves 0-1)
+  if (SWA) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += qa[e] * ka[e];
+    acc = row16_reduce(acc, OpAdd());
+    if (ks_seg == 0 && ks_slot < kMaxW) s_p[ks_slot] = acc * p.scale;
+    if (wave < 2) {
+      const float pq = wave_sum(qn * kn);
+      if (lane == 0) s_qk[wave] = pq;
+    }
+  }
+  // Hedgehog GEMV partials, reduced over the 8 row groups of the wave (lane bits
+  // 3..5: row_ror:8 pairs lanes i and i ^ 8 inside a 16-lane row, then the row
+  // swaps) and written per wave
   {
-    const int cb = tid & 7, rgw = tid >> 3;
-    const T *Wq = (const T *)p.wq + (size_t)h * kD * kF2;
-    const T *Wk = (const T *)p.wk + (size_t)h * kD * kF2;
     float pq[8], pk[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pq[e] = pk[e] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kGR; ++i) {
-      const int row = kGR * rgw + i;
-      const float xq = to_f32(qt[row]), xk = to_f32(kt[row]);
-      float wq[8], wk[8];
-      V::ld8(Wq + (size_t)row * kF2 + 8 * cb, wq);
-      V::ld8(Wk + (size_t)row * kF2 + 8 * cb, wk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pq[e] += xq * wq[e];
-        pk[e] += xk * wk[e];
-      }
-    }
-    // reduce the 8 row groups of this wave (lane bits 3..5): row_ror:8 pairs
-    // lanes i and i ^ 8 inside a 16-lane row, then the row swaps
-#pragma unroll
     for (int e = 0; e < 8; ++e) {
+      pq[e] = 0.0f;
+      pk[e] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kGR; ++i) {
+        pq[e] += xq[i] * wqv[i][e];
+        pk[e] += xk[i] * wkv[i][e];
+      }
       pq[e] = rows_reduce(pq[e] + dpp_f<0x128>(pq[e]), OpAdd());
       pk[e] = rows_reduce(pk[e] + dpp_f<0x128>(pk[e]), OpAdd());
     }
@@ -172,32 +206,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
       }
     }
   }
-  // (4) gates
-  if (tid < kF) s_gam[tid] = gate_from(to_f32(((const T *)p.gate)[(size_t)bh * kF + tid]), p.gate_is_log);
-  // (5) window scores: 4 threads per ring slot, 32 dimensions each; the new
-  // token's q . k is a reduction over waves 0-1 (one dimension per thread)
-  if (SWA) {
-    const int s2 = tid >> 2, qd = tid & 3;
-    float acc = 0.0f;
-    if (s2 < w) {
-      const T *kr = kc + (size_t)s2 * kD;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float a8[8], b8[8];
-        V::ld8(qt + 32 * qd + 8 * s, a8);
-        V::ld8(kr + 32 * qd + 8 * s, b8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += a8[e] * b8[e];
-      }
-    }
-    acc += dpp_f<0xB1>(acc);  // lane ^ 1
-    acc += dpp_f<0x4E>(acc);  // lane ^ 2
-    if (qd == 0 && s2 < kMaxW) s_p[s2] = acc * p.scale;
-    if (wave < 2) {
-      const float pq = wave_sum(to_f32(qt[tid]) * to_f32(kt[tid]));
-      if (lane == 0) s_qk[wave] = pq;
-    }
-  }
+  if (tid < kF) s_gam[tid] = gate_from(graw, p.gate_is_log);
   __syncthreads();
 
   // (6) wave 0 / 1: log-softmax of +u and -u for q / k; wave 2: window softmax
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     const int r = rg + kNRG * ii;
     S[ii] = s_gam[r] * S[ii] + s_ph[1][r] * v4;
     acc += s_ph[0][r] * S[ii];
-    *(f32x4 *)(Sg + (size_t)r * kDV + col) = S[ii];
+    __builtin_nontemporal_store(S[ii], (f32x4 *)(Sg + (size_t)r * kDV + col));
   }
   if (SWA) {
 #pragma unroll
