@@ -56,121 +56,6 @@ struct Lds8 {
 };
 static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
 
-// Per-head buffer resources over the [L][128] bf16 rows of q, k, v, gate and o.
-// Loads past the last row return zeros and stores there are dropped by the range
-// check of the buffer instructions (offsets are unsigned, so rows before 0 are
-// past the end too); every consumer masks such tokens anyway.
-struct HeadBufs {
-  __amdgpu_buffer_rsrc_t q, k, v, g, o;
-};
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16 *base, size_t bh, int L) {
-  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + bh * (size_t)L * kD), (short)0, L * kD * 2,
-                                           0x00020000);
-}
-__device__ __forceinline__ HeadBufs head_bufs(const ChunkParams &p, size_t bh) {
-  return {head_rsrc(p.q, bh, p.L), head_rsrc(p.k, bh, p.L), head_rsrc(p.v, bh, p.L),
-          head_rsrc(p.gate, bh, p.L), head_rsrc(p.o, bh, p.L)};
-}
-__device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-// byte offset of chunk c's rows (wraps for c < 0, which reads zeros)
-__device__ __forceinline__ unsigned chunk_off(int c) { return (unsigned)c * (unsigned)(kC * kD * 2); }
-// Per-lane byte offsets within a chunk, lane (n, g) of tile t on token 16t + n:
-// token-row operand x[token][32g + 8s + j], values v[token][32s + 8g + j] and
-// gates gate[token][feat(g, 8s + j)]
-__device__ __forceinline__ unsigned row_off(int tile) { return (unsigned)(16 * tile + (threadIdx.x & 15)) * (kD * 2); }
-__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
-  const unsigned g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 64 * g + 16 * s);
-}
-__device__ __forceinline__ void load_vals(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
-  const unsigned g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 16 * g + 64 * s);
-}
-__device__ __forceinline__ void load_gates(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
-  const unsigned g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 2 * feat(g, 8 * s));
-}
-
-// Unnormalised Hedgehog exponentials of the lane's token: e[4mt + j] =
-// 2^{(u - max u) log2e} (phi+ feature 16g + 4mt + j) and e[16 + 4mt + j] =
-// 2^{(min u - u) log2e} (phi- feature 64 + 16g + 4mt + j), and the reciprocal
-// normalisers of the two halves.
-__device__ __forceinline__ void hedgehog_exp(const f32x4 *u, float *e, float &izp, float &izn) {
-  float mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mx = fmaxf(mx, u[mt][j]);
-      mn = fminf(mn, u[mt][j]);
-    }
-  mx = grp_max(mx) * kLog2e;
-  mn = grp_min(mn) * kLog2e;
-  float zp = 0.0f, zn = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * mt + j;
-      e[i] = exp2_fast(u[mt][j] * kLog2e - mx);
-      e[16 + i] = exp2_fast(mn - u[mt][j] * kLog2e);
-      zp += e[i];
-      zn += e[16 + i];
-    }
-  izp = rcp_fast(grp_sum(zp));
-  izn = rcp_fast(grp_sum(zn));
-}
-
-// u = x Wphi for a 16-token tile (A = Wphi^T fragments in LDS, B = the tile's
-// token rows); the 4 fragments of tile mt+1 are requested before the MFMAs of mt
-__device__ __forceinline__ void project(const char *wb, const bf16x8 *x, f32x4 *u) {
-  bf16x8 wf[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) u[mt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) wf[0][s] = lds8(wb + s * kFrag);
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    if (mt + 1 < 4) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wf[(mt + 1) & 1][s] = lds8(wb + ((mt + 1) * 4 + s) * kFrag);
-    }
-    issue_fence();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) u[mt] = mfma(wf[mt & 1][s], x[s], u[mt]);
-  }
-}
-
-// In-tile inclusive cumsums of the base-2 log-gates of the lane's token for all
-// 32 fold slots (feature feat(g, i)), floored at kMinLog2Gate, zero for tokens
-// past the end.
-__device__ __forceinline__ void tile_cumsum(const bf16x8 *xg, bool gate_is_log, bool tok_ok, float *dd) {
-  if (gate_is_log) {  // one uniform branch around the whole loop
-#pragma unroll
-    for (int i = 0; i < 32; ++i) dd[i] = (float)xg[i >> 3][i & 7] * kLog2e;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) dd[i] = log2_sigmoid((float)xg[i >> 3][i & 7]);
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] = tok_ok ? fmaxf(dd[i], kMinLog2Gate) : 0.0f;
-  // one scan step across all 32 slots at a time, so consecutive DPP reads
-  // never wait on each other
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<1>(dd[i]);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<2>(dd[i]);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<4>(dd[i]);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<8>(dd[i]);
-}
-
 // Per-feature chunk quantities for features 2n, 2n+1 of the lane's group from
 // the tile totals of the chunk (base 2): fold reference rr2, offset off = P_w - r
 // of this wave's tile, total B, and the per-tile totals tt (tile mode).

@@ -673,6 +673,193 @@ void chunk_kernel(ChunkParams p) {
   }
 }
 
+// ---------------------------------------------------------------- state pass
+// End state, from a zero state, of one slice of a segment and the slice's total
+// base-2 log-decay: S <- diag(2^{B}) S + k-hat^T V per chunk with
+// k-hat = phi_k 2^{B - b} (exponent <= 0, so no fold reference is needed).
+// Block = 4 waves, two blocks per CU.  Wave w: token tile w for the row work
+// (u_k, the log-gate cumsums, phi(k), k-hat^T fragments transposed on the matrix
+// core, V^T fragments) and d_v columns [32w, 32w + 32) of the state.  Two
+// barriers per chunk: B1a (tile totals visible, previous update done) and B1
+// (k-hat^T and V^T fragments visible).
+struct LdsState {
+  static constexpr int WK = 0;                   // Wphi_k^T frags [4 mt][4 s]
+  static constexpr int VT = WK + 16 * kFrag;     // V^T half frags [4 tile][8 dv tile]
+  static constexpr int KH = VT + 32 * kHalf;     // k-hat^T frags [8 mt][2 sp]
+  static constexpr int T = KH + 16 * kFrag;      // tile log-gate totals [4 tile][128]
+  static constexpr int BYTES = T + 4 * kF * 4;
+};
+
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void state_kernel(ChunkParams p) {
+  using LD = LdsState;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int NS = (p.P - 1) * p.R;
+  const size_t bh = blockIdx.x / NS;
+  const int seg = blockIdx.x % NS;  // state slice
+  const int h = (int)(bh % p.H);
+  const int ps = seg / p.R, r = seg % p.R;
+  const int seg_end = min((ps + 1) * p.seg_chunks, p.nchunks);
+  const int c_begin = min(ps * p.seg_chunks + r * p.sub_chunks, seg_end);
+  const int c_end = min(c_begin + p.sub_chunks, seg_end);  // may be empty: zero state, zero decay
+  const bool gate_is_log = p.gate_is_log != 0;
+
+  // Wphi_k^T fragments (see the output pass for the layout)
+  for (int idx = tid; idx < 16 * 64; idx += kNT) {
+    const int fi = idx >> 6, l = idx & 63, rr = l & 15, gg = l >> 4;
+    const int mt = fi >> 2, s = fi & 3;
+    const int m = 16 * (rr >> 2) + 4 * mt + (rr & 3);
+    const bf16 *w = p.wk + (size_t)h * kD * kF2;
+    bf16x8 f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = w[(32 * gg + 8 * s + j) * kF2 + m];
+    sts8(smem + LD::WK + fi * kFrag + l * 16, f);
+  }
+  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
+  const HeadBufs hb = head_bufs(p, bh);
+  const unsigned ro = row_off(wave);
+  // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvcol(wave, dt, n)]
+  f32x4 S[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) S[mt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float dsum2[2] = {0.0f, 0.0f};  // total base-2 log-decay (features 2n, 2n+1 of the group)
+  bf16x8 xk[4], xv[4], xg[4];
+  load_rows(hb.k, ro + chunk_off(c_begin), xk);
+  load_vals(hb.v, ro + chunk_off(c_begin), xv);
+  load_gates(hb.g, ro + chunk_off(c_begin), xg);
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const unsigned ro1 = ro + chunk_off(c + 1);
+    const bool tok_ok = c * kC + 16 * wave + n < p.L;
+    // ---- row work of tile `wave` up to the tile totals
+    f32x4 u[4];
+    project(smem + LD::WK + lane * 16, xk, u);
+    load_rows(hb.k, ro1, xk);  // next chunk's keys
+    float dd[32];
+    tile_cumsum(xg, gate_is_log, tok_ok, dd);
+    load_gates(hb.g, ro1, xg);
+    if (n == 15) {
+      float *T = (float *)(smem + LD::T) + wave * kF;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
+    }
+    float e[32], izp, izn;
+    hedgehog_exp(u, e, izp, izn);
+    __syncthreads();  // B1a: tile totals visible; the previous chunk's update done
+
+    // ---- V^T fragments of this tile
+    {
+      char *base = smem + LD::VT + wave * 8 * kHalf + lane * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f32x4 t2[2];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) t2[dt] = mfma(xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t2[dt]);
+      }
+    }
+    load_vals(hb.v, ro1, xv);  // next chunk's values
+    // ---- k-hat = phi_k 2^{B - b} with B - b = (B - P_w) - b_loc <= 0
+    float fdec[2], rest[2];  // 2^{B}; B - P_w
+    {
+      const float *T = (const float *)(smem + LD::T);
+      const int f0 = feat(g, 2 * n);
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        float btot = 0.0f, pre = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float tv = T[w2 * kF + f0 + e2];
+          btot += tv;
+          if (w2 < wave) pre += tv;
+        }
+        fdec[e2] = exp2_fast(btot);
+        dsum2[e2] += btot;
+        rest[e2] = btot - pre;
+      }
+    }
+    bf16x8 kh[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float a8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * s + j;
+        a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(row_bcast(rest[i & 1], i >> 1) - dd[i]);
+      }
+      kh[s] = tok_ok ? pack8(a8) : zero8();  // keys past the end contribute nothing
+    }
+    {  // k-hat^T fragments: state tile mt takes its 16 features from K-step
+       // s(mt) = 2(mt/4) + (mt%4)/2 of the token-row operand
+      const int sp = wave >> 1, hf = wave & 1;
+#pragma unroll
+      for (int m2 = 0; m2 < 4; ++m2) {
+        f32x4 t2[2];
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+          const int mt = 2 * m2 + d2;
+          const int s2 = 2 * (mt >> 2) + ((mt & 3) >> 1);
+          t2[d2] = mfma(kh[s2], sel[mt & 1], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+        }
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+          *(bf16x4 *)(smem + LD::KH + ((2 * m2 + d2) * 2 + sp) * kFrag + lane * 16 + hf * 8) = pack4(t2[d2]);
+      }
+    }
+    __syncthreads();  // B1: k-hat^T and V^T fragments visible
+
+    // ---- S <- diag(2^{B}) S + k-hat^T V (columns of this wave), fragments of a
+    // group of 4 state tiles requested together
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float eb = row_bcast(fdec[j & 1], (4 * mt + j) >> 1);
+        S[mt][0][j] *= eb;
+        S[mt][1][j] *= eb;
+      }
+    bf16x8 bv[2][2];
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const char *vb = smem + LD::VT + ((2 * sp) * 8 + 2 * wave + dt) * kHalf + lane * 8;
+        bv[sp][dt] = join44(*(const bf16x4 *)vb, *(const bf16x4 *)(vb + 8 * kHalf));
+      }
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {  // grp = 2 sp + (mt / 4)
+      const int sp = grp >> 1, mb = 4 * (grp & 1);
+      bf16x8 kf[4];
+      issue_fence();
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) kf[m4] = lds8(smem + LD::KH + ((mb + m4) * 2 + sp) * kFrag + lane * 16);
+      issue_fence();
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) S[mb + m4][dt] = mfma(kf[m4], bv[sp][dt], S[mb + m4][dt]);
+    }
+  }
+
+  float *dst = p.seg_state + (bh * NS + seg) * (size_t)(kF * kDV);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
+  if (wave == 0) {
+    float *dd = p.seg_decay + (bh * NS + seg) * (size_t)kF;
+    *(float2 *)(dd + feat(g, 2 * n)) = make_float2(dsum2[0], dsum2[1]);
+  }
+}
+
 // State after every state slice: S_(0) = e^{D_0} S_in + dS_0,
 // S_(q) = e^{D_q} S_(q-1) + dS_q.  Thread = one state element of one head; the
 // slots are overwritten in place (slot q receives S_(q)).
@@ -778,7 +965,11 @@ hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
     const int NS = s.slices();
     p.seg_state = (float *)a.ws;
     p.seg_decay = p.seg_state + (size_t)bh * NS * kF * kDV;
-    hipError_t e = launch_mode<MODE_STATE>(p, bh * NS, a.stream);
+    hipError_t e = hipFuncSetAttribute((const void *)state_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       LdsState::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(bh * NS)), dim3(kNT), LdsState::BYTES, a.stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t elems = (size_t)bh * kF * kDV;
     hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((elems + kNT - 1) / kNT)), dim3(kNT), 0,
