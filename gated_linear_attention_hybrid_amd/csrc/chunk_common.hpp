@@ -40,7 +40,6 @@ constexpr int kDV = 128;    // value dim
 constexpr int kFrag = 1024; // bytes of one MFMA operand fragment
 constexpr int kHalf = 512;  // bytes of a half fragment (4 bf16 per lane)
 
-enum { MODE_STATE = 0, MODE_GLA = 1, MODE_HYBRID = 2, MODE_SWA = 3 };
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
