@@ -114,22 +114,16 @@ __device__ __forceinline__ float row_bcast15(float x) {
                                                                0xF, 0xF, false));
 }
 
-// Smallest per-token log-gate used by the chunkwise path.  A 16-token tile then
-// spans at most 160 in log space, so with the mid-tile reference every fold
-// factor stays within e^{+-80}.  Gates below e^{-10} (~4.5e-5) act as 4.5e-5:
-// any term they touch is already below 4.5e-5 of its undecayed size, so the
-// change is bounded by that factor.
-constexpr float kMinLog2Gate = -10.0f * kLog2e;
+// Largest per-token base-2 decay exponent (-log2 of the gate) used by the
+// chunkwise path.  A 16-token tile then spans at most 2^{+-231}, so with the
+// mid-tile reference every fold factor stays within 2^{+-116}.  Gates below e^{-10}
+// (~4.5e-5) act as 4.5e-5: any term they touch is already below 4.5e-5 of its
+// undecayed size, so the change is bounded by that factor.
+constexpr float kMaxLog2Decay = 10.0f * kLog2e;
 
 // Largest |chunk log2-decay| for which one chunk-wide fold reference is used:
 // the fold exponents then stay within 2^{+-100}.
 constexpr float kChunkRefLimit = 200.0f;
-
-// log2 sigmoid(g) = -log2(1 + 2^{-g log2e}).  For g below about -88 the power
-// overflows and the result is -inf, which the log-gate floor below replaces.
-__device__ __forceinline__ float log2_sigmoid(float g) {
-  return -log2_fast(1.0f + exp2_fast(-g * kLog2e));
-}
 
 // value of x in lane SRC (0..15) of this lane's 16-lane row (DPP row_newbcast)
 template <int SRC>
@@ -277,29 +271,35 @@ __device__ __forceinline__ void project(const char *wb, const bf16x8 *x, f32x4 *
   }
 }
 
-// In-tile inclusive cumsums of the base-2 log-gates of the lane's token for all
-// 32 fold slots (feature feat(g, i)), floored at kMinLog2Gate, zero for tokens
-// past the end.
-__device__ __forceinline__ void tile_cumsum(const bf16x8 *xg, bool gate_is_log, bool tok_ok, float *dd) {
+// Running decay exponents of the lane's token in a 16-token tile: dn[i] is the
+// sum over tokens s <= n of -log2 Gamma_s for fold slot i (feature feat(g, i)),
+// so the in-tile inclusive cumsum of the base-2 log-gates is b = -dn.  The gate
+// input is the logit g (Gamma = sigmoid(g), -log2 Gamma = log2(1 + 2^{-g log2e}))
+// or, with gate_is_log, log Gamma itself.  The power's exponent is capped at
+// kMaxLog2Decay, which caps each term at kMaxLog2Decay + 2^{-kMaxLog2Decay}/ln 2.
+// Tokens past the end (!tok_ok) contribute 0: their gates read as 0 (range
+// check), which gives 0 in the log form, and a cap of -inf gives log2(1 + 0) = 0
+// in the logit form.
+__device__ __forceinline__ void tile_decay(const bf16x8 *xg, bool gate_is_log, bool tok_ok, float *dn) {
   if (gate_is_log) {  // one uniform branch around the whole loop
 #pragma unroll
-    for (int i = 0; i < 32; ++i) dd[i] = (float)xg[i >> 3][i & 7] * kLog2e;
+    for (int i = 0; i < 32; ++i) dn[i] = fminf((float)xg[i >> 3][i & 7] * -kLog2e, kMaxLog2Decay);
   } else {
+    const float cap = tok_ok ? kMaxLog2Decay : -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) dd[i] = log2_sigmoid((float)xg[i >> 3][i & 7]);
+    for (int i = 0; i < 32; ++i)
+      dn[i] = log2_fast(1.0f + exp2_fast(fminf((float)xg[i >> 3][i & 7] * -kLog2e, cap)));
   }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] = tok_ok ? fmaxf(dd[i], kMinLog2Gate) : 0.0f;
   // one scan step across all 32 slots at a time, so consecutive DPP reads
   // never wait on each other
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<1>(dd[i]);
+  for (int i = 0; i < 32; ++i) dn[i] += row_shr<1>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<2>(dd[i]);
+  for (int i = 0; i < 32; ++i) dn[i] += row_shr<2>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<4>(dd[i]);
+  for (int i = 0; i < 32; ++i) dn[i] += row_shr<4>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dd[i] += row_shr<8>(dd[i]);
+  for (int i = 0; i < 32; ++i) dn[i] += row_shr<8>(dn[i]);
 }
 
 }  // namespace

@@ -51,7 +51,7 @@ struct Lds8 {
   // per query tile: window part 2 full fragments + the diagonal tile as a half
   // fragment (its upper K half is zero); no window: 2 full fragments
   static constexpr int WQT = SWA ? 2 * kFrag + kHalf : 2 * kFrag;
-  static constexpr int T = W + 4 * WQT;                   // tile log-gate totals [2 slot][4 tile][128]
+  static constexpr int T = W + 4 * WQT;                   // tile decay totals (-log2-gate sums) [2 slot][4 tile][128]
   static constexpr int BYTES = T + 2 * 4 * kF * 4;
 };
 static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
@@ -69,9 +69,9 @@ __device__ __forceinline__ FoldRef fold_ref(const float *T, int tile) {
   const int f0 = feat(g, 2 * n);
 #pragma unroll
   for (int w2 = 0; w2 < 4; ++w2) {
-    const float2 v2 = *(const float2 *)(T + w2 * kF + f0);
-    r.tt[w2][0] = v2.x;
-    r.tt[w2][1] = v2.y;
+    const float2 v2 = *(const float2 *)(T + w2 * kF + f0);  // decay exponents: totals are -T
+    r.tt[w2][0] = -v2.x;
+    r.tt[w2][1] = -v2.y;
   }
   float pre[2];
 #pragma unroll
@@ -102,7 +102,7 @@ __device__ __forceinline__ FoldRef fold_ref(const float *T, int tile) {
 // Folded feature operands: xr = phi 2^{sgn (b - r)} (k~ with sgn = -1, q~ with
 // sgn = +1) and xs = xr 2^{fs} (per feature: k-hat with fs = B - r, q-bar with
 // fs = r), as MFMA token-row operands (slot i = 8s + j).
-__device__ __forceinline__ void fold(const float *e, float izp, float izn, const float *dd, const FoldRef &r,
+__device__ __forceinline__ void fold(const float *e, float izp, float izn, const float *dn, const FoldRef &r,
                                      float sgn, const float *fs, bf16x8 *xr, bf16x8 *xs) {
   float fsx[2];
 #pragma unroll
@@ -113,7 +113,7 @@ __device__ __forceinline__ void fold(const float *e, float izp, float izn, const
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = 8 * s + j;
-      const float d = dd[i] + row_bcast(r.off[i & 1], i >> 1);
+      const float d = row_bcast(r.off[i & 1], i >> 1) - dn[i];  // b - r
       a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(sgn * d);
       b8[j] = a8[j] * row_bcast(fsx[i & 1], i >> 1);
     }
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       project(smem + LD::WK + lane * 16, xk, u);
       load_rows(hb.k, ro1, xk);  // next chunk's keys
       float dd[32];
-      tile_cumsum(xg, gate_is_log, tok_ok, dd);
+      tile_decay(xg, gate_is_log, tok_ok, dd);
       load_gates(hb.g, ro1, xg);
       float e[32], izp, izn;
       hedgehog_exp(u, e, izp, izn);
@@ -334,14 +334,10 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         fs[e2] = r.btot[e2] - r.rr2[e2];
         fdec[e2] = exp2_fast(r.btot[e2]);
       }
+      // Keys past the end need no masking: their k~ meets only queries past the
+      // end (causal mask), whose outputs are not stored, and their k-hat meets
+      // value rows that read as zero (range check).
       fold(e, izp, izn, dd, r, -1.0f, fs, xr, xs);
-      if (!tok_ok) {  // keys past the end contribute nothing
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          xr[s] = zero8();
-          xs[s] = zero8();
-        }
-      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (tile * 4 + s) * kFrag + lane * 16, xr[s]);
       __syncthreads();  // B1: raw-k and k~ fragments visible; column phase done
@@ -403,12 +399,12 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       load_rows(hb.k, ro + chunk_off(c_begin - 1), xb);
       stage_rk(xb, (c_begin - 1) & 1);
     }
-    float dd[32];  // cumsums of the chunk being processed
+    float dd[32];  // decay exponents (-cumsums, tile_decay) of the chunk being processed
     {
       load_rows(hb.q, ro + chunk_off(c_begin), xq);
       if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
       load_gates(hb.g, ro + chunk_off(c_begin), xg);
-      tile_cumsum(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dd);
+      tile_decay(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dd);
       if (n == 15) {  // tile totals of the first chunk
         float *T = (float *)(smem + LD::T) + ((c_begin & 1) * 4 + tile) * kF;
 #pragma unroll
@@ -462,7 +458,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         chunk_mode = r.chunk_mode;
       }
       // cumsums and tile totals of the next chunk, published one chunk ahead
-      tile_cumsum(xg, gate_is_log, tq + kC < p.L, dd);
+      tile_decay(xg, gate_is_log, tq + kC < p.L, dd);
       load_gates(hb.g, ro + chunk_off(c + 2), xg);
       if (n == 15) {
         float *T = (float *)(smem + LD::T) + (((c + 1) & 1) * 4 + tile) * kF;
@@ -556,7 +552,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
               float run = 0.0f, tk = 0.0f, tw = 0.0f;  // log-gate sum of tiles kt .. tile-1
 #pragma unroll
               for (int w2 = 0; w2 < 4; ++w2) {
-                const float tv = T[w2 * kF + e2];
+                const float tv = -T[w2 * kF + e2];
                 if (w2 >= kt && w2 < tile) run += tv;
                 if (w2 == kt) tk = tv;
                 if (w2 == tile) tw = tv;

@@ -156,18 +156,21 @@ __global__ __launch_bounds__(kNT) void swa_kernel(ChunkParams p) {
 
 // ---------------------------------------------------------------- state pass
 // End state, from a zero state, of one slice of a segment and the slice's total
-// base-2 log-decay: S <- diag(2^{B}) S + k-hat^T V per chunk with
-// k-hat = phi_k 2^{B - b} (exponent <= 0, so no fold reference is needed).
+// base-2 log-decay.  Unrolled over the slice's chunks the recurrence
+// S <- diag(2^{B_c}) S + k-hat_c^T V_c gives S = sum_c (k-hat_c 2^{R_c})^T V_c with
+// k-hat_c = phi_k 2^{B_c - b} and R_c the log-decay of the chunks after c; taking
+// the chunks last to first builds R_c as a running sum, so every exponent is
+// <= 0 (no fold reference) and the state is never rescaled.
 // Block = 4 waves, two blocks per CU.  Wave w: token tile w for the row work
-// (u_k, the log-gate cumsums, phi(k), k-hat^T fragments transposed on the matrix
-// core, V^T fragments) and d_v columns [32w, 32w + 32) of the state.  Two
+// (u_k, the gate decay exponents, phi(k), k-hat^T fragments transposed on the
+// matrix core, V^T fragments) and d_v columns [32w, 32w + 32) of the state.  Two
 // barriers per chunk: B1a (tile totals visible, previous update done) and B1
 // (k-hat^T and V^T fragments visible).
 struct LdsState {
   static constexpr int WK = 0;                   // Wphi_k^T frags [4 mt][4 s]
   static constexpr int VT = WK + 16 * kFrag;     // V^T half frags [4 tile][8 dv tile]
   static constexpr int KH = VT + 32 * kHalf;     // k-hat^T frags [8 mt][2 sp]
-  static constexpr int T = KH + 16 * kFrag;      // tile log-gate totals [4 tile][128]
+  static constexpr int T = KH + 16 * kFrag;      // tile decay totals (-log2-gate sums) [4 tile][128]
   static constexpr int BYTES = T + 4 * kF * 4;
 };
 
@@ -207,31 +210,36 @@ void state_kernel(ChunkParams p) {
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) S[mt][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  float dsum2[2] = {0.0f, 0.0f};  // total base-2 log-decay (features 2n, 2n+1 of the group)
+  // base-2 log-decay of the chunks after the current one (features 2n, 2n+1 of
+  // the group); the slice total at the end
+  float rsum2[2] = {0.0f, 0.0f};
   bf16x8 xk[4], xv[4], xg[4];
-  load_rows(hb.k, ro + chunk_off(c_begin), xk);
-  load_vals(hb.v, ro + chunk_off(c_begin), xv);
-  load_gates(hb.g, ro + chunk_off(c_begin), xg);
+  load_rows(hb.k, ro + chunk_off(c_end - 1), xk);
+  load_vals(hb.v, ro + chunk_off(c_end - 1), xv);
+  load_gates(hb.g, ro + chunk_off(c_end - 1), xg);
   __syncthreads();
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const unsigned ro1 = ro + chunk_off(c + 1);
-    const bool tok_ok = c * kC + 16 * wave + n < p.L;
+  // The chunks are taken last to first, so the state is never decayed: chunk c
+  // adds (phi_k 2^{B_c - b + R_c})^T V with R_c the log-decay of the later chunks
+  // of the slice, an exponent <= 0.  Rows past the end have V = 0 (range check)
+  // and add nothing.
+  for (int c = c_end - 1; c >= c_begin; --c) {
+    const unsigned ro1 = ro + chunk_off(c - 1);  // c - 1 < 0 wraps past the range: reads 0
     // ---- row work of tile `wave` up to the tile totals
     f32x4 u[4];
     project(smem + LD::WK + lane * 16, xk, u);
-    load_rows(hb.k, ro1, xk);  // next chunk's keys
-    float dd[32];
-    tile_cumsum(xg, gate_is_log, tok_ok, dd);
+    load_rows(hb.k, ro1, xk);  // preceding chunk's keys
+    float dn[32];
+    tile_decay(xg, gate_is_log, c * kC + 16 * wave + n < p.L, dn);
     load_gates(hb.g, ro1, xg);
     if (n == 15) {
       float *T = (float *)(smem + LD::T) + wave * kF;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
+      for (int i = 0; i < 32; ++i) T[feat(g, i)] = dn[i];
     }
     float e[32], izp, izn;
     hedgehog_exp(u, e, izp, izn);
-    __syncthreads();  // B1a: tile totals visible; the previous chunk's update done
+    __syncthreads();  // B1a: tile totals visible; the previous update done
 
     // ---- V^T fragments of this tile
     {
@@ -245,24 +253,23 @@ void state_kernel(ChunkParams p) {
         for (int dt = 0; dt < 2; ++dt) *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t2[dt]);
       }
     }
-    load_vals(hb.v, ro1, xv);  // next chunk's values
-    // ---- k-hat = phi_k 2^{B - b} with B - b = (B - P_w) - b_loc <= 0
-    float fdec[2], rest[2];  // 2^{B}; B - P_w
+    load_vals(hb.v, ro1, xv);  // preceding chunk's values
+    // ---- k-hat = phi_k 2^{B - b + R} with B - b = (B - P_w) - b_loc <= 0
+    float base[2];  // B - P_w + R, then R += B
     {
       const float *T = (const float *)(smem + LD::T);
       const int f0 = feat(g, 2 * n);
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
-        float btot = 0.0f, pre = 0.0f;
+        float btot = 0.0f, rest = 0.0f;  // decay exponents of the chunk and of tiles >= wave
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
           const float tv = T[w2 * kF + f0 + e2];
           btot += tv;
-          if (w2 < wave) pre += tv;
+          if (w2 >= wave) rest += tv;
         }
-        fdec[e2] = exp2_fast(btot);
-        dsum2[e2] += btot;
-        rest[e2] = btot - pre;
+        base[e2] = rsum2[e2] - rest;
+        rsum2[e2] -= btot;
       }
     }
     bf16x8 kh[4];
@@ -272,9 +279,9 @@ void state_kernel(ChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * s + j;
-        a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(row_bcast(rest[i & 1], i >> 1) - dd[i]);
+        a8[j] = e[i] * (i < 16 ? izp : izn) * exp2_fast(row_bcast(base[i & 1], i >> 1) + dn[i]);
       }
-      kh[s] = tok_ok ? pack8(a8) : zero8();  // keys past the end contribute nothing
+      kh[s] = pack8(a8);
     }
     {  // k-hat^T fragments: state tile mt takes its 16 features from K-step
        // s(mt) = 2(mt/4) + (mt%4)/2 of the token-row operand
@@ -295,16 +302,8 @@ void state_kernel(ChunkParams p) {
     }
     __syncthreads();  // B1: k-hat^T and V^T fragments visible
 
-    // ---- S <- diag(2^{B}) S + k-hat^T V (columns of this wave), fragments of a
-    // group of 4 state tiles requested together
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float eb = row_bcast(fdec[j & 1], (4 * mt + j) >> 1);
-        S[mt][0][j] *= eb;
-        S[mt][1][j] *= eb;
-      }
+    // ---- S += k-hat^T V (columns of this wave), fragments of a group of 4 state
+    // tiles requested together
     bf16x8 bv[2][2];
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp)
@@ -337,7 +336,7 @@ void state_kernel(ChunkParams p) {
       for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
   if (wave == 0) {
     float *dd = p.seg_decay + (bh * NS + seg) * (size_t)kF;
-    *(float2 *)(dd + feat(g, 2 * n)) = make_float2(dsum2[0], dsum2[1]);
+    *(float2 *)(dd + feat(g, 2 * n)) = make_float2(rsum2[0], rsum2[1]);
   }
 }
 
