@@ -161,6 +161,11 @@ __device__ __forceinline__ int dvcol(int w, int dt, int n) {
   return 32 * w + 8 * (n >> 2) + 4 * dt + (n & 3);
 }
 
+// d_v column held by lane n, column-tile dt, of wave w in the output pass: the
+// two column tiles of a lane are adjacent columns, so one dword of a value row
+// feeds both
+__device__ __forceinline__ int dvpair(int w, int dt, int n) { return 32 * w + 2 * n + dt; }
+
 // 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
 // picks K-slot (group n/4, element 4*dt + n%4).  A x sel(dt) re-lays a
 // row-per-lane operand (lane = row, 8 K-values) into accumulator form

@@ -12,23 +12,25 @@
 //   state  S  <- diag(2^{B}) S + k-hat^T V,  k-hat = phi_k 2^{B-b}
 // and the window probabilities are added to A^T so one GEMM with V gives both.
 //
-// A block of 512 threads runs 8 waves, two per SIMD, so that the stalls of one
-// wave are filled by the other's work (a lone wave issues vector instructions at
-// about half the rate of two).  Tile t = w & 3:
-//   key wave   (w = 0..3): holds d_v columns [32t, 32t + 32) of the fp32 state in
-//                          MFMA accumulators and runs the column phase (readout,
-//                          weights x V, state update) of the previous chunk; then
-//                          u_k = k Wphi_k, the log-gates of its tile, phi(k), k~,
-//                          k-hat^T and V^T fragments
+// A block of 512 threads runs 8 waves, two per SIMD (waves w and w + 4 share
+// one), so that the stalls of one wave are filled by the other's work (a lone
+// wave issues vector instructions at about half the rate of two).  Tile t = w & 3:
+//   key wave   (w = 0..3): holds d_v columns dvpair(t, 0..1, 0..15) of the fp32
+//                          state in MFMA accumulators and runs the column phase
+//                          (readout, weights x V, state update) of the previous
+//                          chunk, with the value operands read straight from
+//                          memory; then u_k = k Wphi_k, phi(k), k~ and the
+//                          k-hat^T fragments; and, in the second phase, the gate
+//                          decay exponents of its tile of the NEXT chunk, shared
+//                          through LDS, so every wave knows the chunk-wide fold
+//                          reference when a chunk starts and the query waves
+//                          compute no gates
 //   query wave (w = 4..7): raw-k fragments, window scores and softmax, u_q,
 //                          phi(q), q~, q-bar, intra-chunk scores, weight
-//                          fragments; and the log-gates of the NEXT chunk, whose
-//                          tile totals it publishes one chunk ahead, so every
-//                          wave knows the chunk-wide fold reference when a chunk
-//                          starts
+//                          fragments
 // Per chunk there are two barriers: B1 (raw-k and k~ fragments visible, column
-// phase of the previous chunk done) and B2 (q-bar, k-hat^T, V^T and weights
-// visible).
+// phase of the previous chunk and every read of the decay exponents done) and
+// B2 (q-bar, k-hat^T, weights and the next chunk's decay exponents visible).
 #include "chunk_common.hpp"
 
 namespace glah {
@@ -43,34 +45,52 @@ struct Lds8 {
   static constexpr int WQ = 0;                            // Wphi_q^T frags [4 mt][4 s]
   static constexpr int WK = WQ + 16 * kFrag;              // Wphi_k^T frags [4 mt][4 s]
   static constexpr int RK = WK + 16 * kFrag;              // raw k frags [2 slot][4 tile][4 s]
-  static constexpr int VT = RK + (SWA ? 32 * kFrag : 0);  // V^T half frags [slot][4 tile][8 dv tile]
-  static constexpr int KT = VT + (SWA ? 2 : 1) * 32 * kHalf;  // k~ frags [4 tile][4 s]
+  static constexpr int DD = RK + (SWA ? 32 * kFrag : 0);  // decay exponents (fp32) [4 tile][8 q][64 lane][4]
+  static constexpr int KT = DD + 32 * kFrag;              // k~ frags [4 tile][4 s]
   static constexpr int QB = KT + 16 * kFrag;              // q-bar frags [4 tile][4 s]
   static constexpr int KH = QB + 16 * kFrag;              // k-hat^T frags [8 mt][2 sp]
   static constexpr int W = KH + 16 * kFrag;               // weight frags [4 qt][NKS]
   // per query tile: window part 2 full fragments + the diagonal tile as a half
   // fragment (its upper K half is zero); no window: 2 full fragments
   static constexpr int WQT = SWA ? 2 * kFrag + kHalf : 2 * kFrag;
-  static constexpr int T = W + 4 * WQT;                   // tile decay totals (-log2-gate sums) [2 slot][4 tile][128]
-  static constexpr int BYTES = T + 2 * 4 * kF * 4;
+  static constexpr int BYTES = W + 4 * WQT;
 };
 static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
 
+// Decay exponents (tile_decay) of the chunk, exchanged through LDS: tile t,
+// lane l, fold slots 4q .. 4q+3 at ((t * 8 + q) * 64 + l) * 16 bytes.
+__device__ __forceinline__ void store_dd(char *dd, int tile, const float *dn) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    *(f32x4 *)(dd + ((tile * 8 + q) * 64 + lane) * 16) = (f32x4){dn[4 * q], dn[4 * q + 1], dn[4 * q + 2], dn[4 * q + 3]};
+}
+__device__ __forceinline__ void load_dd(const char *dd, int tile, float *dn) {
+  const int lane = threadIdx.x & 63;
+  f32x4 v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = *(const f32x4 *)(dd + ((tile * 8 + q) * 64 + lane) * 16);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dn[4 * q + j] = v[q][j];
+}
+
 // Per-feature chunk quantities for features 2n, 2n+1 of the lane's group from
 // the tile totals of the chunk (base 2): fold reference rr2, offset off = P_w - r
-// of this wave's tile, total B, and the per-tile totals tt (tile mode).
+// of this wave's tile, total B, and the per-tile totals tt (tile mode).  A
+// tile's totals are the decay exponents of its last token (lane 16g + 15).
 struct FoldRef {
   float tt[4][2], tw[2], btot[2], rr2[2], off[2];
   bool chunk_mode;
 };
-__device__ __forceinline__ FoldRef fold_ref(const float *T, int tile) {
+__device__ __forceinline__ FoldRef fold_ref(const char *dd, int tile) {
   FoldRef r;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int f0 = feat(g, 2 * n);
 #pragma unroll
   for (int w2 = 0; w2 < 4; ++w2) {
-    const float2 v2 = *(const float2 *)(T + w2 * kF + f0);  // decay exponents: totals are -T
-    r.tt[w2][0] = -v2.x;
+    const float2 v2 = *(const float2 *)(dd + ((w2 * 8 + (n >> 1)) * 64 + 16 * g + 15) * 16 + (n & 1) * 8);
+    r.tt[w2][0] = -v2.x;  // log2-gate totals are minus the decay totals
     r.tt[w2][1] = -v2.y;
   }
   float pre[2];
@@ -156,14 +176,13 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
   // The column phase of the chunk before the segment runs on zero operands (its
   // outputs are not stored), so the loop needs no first-iteration branch.  The
   // window part's V^T slot of that chunk is staged below.
-  for (int off = LD::KT + tid * 16; off < LD::T; off += kNT8 * 16) sts8(smem + off, zero8());
-  for (int off = LD::VT + tid * 16; off < LD::KT; off += kNT8 * 16) sts8(smem + off, zero8());
+  for (int off = LD::KT + tid * 16; off < LD::BYTES; off += kNT8 * 16) sts8(smem + off, zero8());
   __syncthreads();  // zero fill before the staged fragments below
 
   if (kw) {
     // =============================== key waves ===============================
     const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
-    // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvcol(tile, dt, n)]
+    // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvpair(tile, dt, n)]
     f32x4 S[8][2];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -181,40 +200,71 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvcol(tile, dt, n)];
+            for (int j = 0; j < 4; ++j) S[mt][dt][j] = src[feat(g, 4 * mt + j) * kDV + dvpair(tile, dt, n)];
       }
     }
-    // V^T half fragments of token tile `tile` into ring slot `slot`: for d_v tile
-    // (2w' + dt), lane 16g + r holds v[16 tile + 4g + j][dvcol(w', dt, r)]
-    auto stage_vt = [&](const bf16x8 *xv, int slot) {
-      char *base = smem + LD::VT + (slot * 4 + tile) * 8 * kHalf + lane * 8;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        f32x4 t2[2];
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) t2[dt] = mfma(xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t2[dt]);
-      }
-    };
     const HeadBufs hb = head_bufs(p, bh);
     const unsigned ro = row_off(tile);
-    bf16x8 xk[4], xv[4], xg[4];  // this chunk's keys, values, gates
-    if (SWA) {  // values of the chunk before the segment (window part)
-      load_vals(hb.v, ro + chunk_off(c_begin - 1), xv);
-      stage_vt(xv, (c_begin - 1) & 1);
-    }
+    // Values as MFMA operands, read straight from memory: for the 16 d_v columns
+    // of column tile dt (dvpair(tile, dt, n)) and K-steps over two token tiles
+    // (a, b), lane (n, g) needs v[16a + 4g + j][.] and v[16b + 4g + j][.],
+    // j = 0..3.  One dword per token row holds both column tiles (adjacent
+    // columns 32 tile + 2n, + 1); vt[T][2 dt + h] packs tokens 4g + 2h, 4g + 2h + 1
+    // of tile T for column tile dt.
+    uint32_t vraw[4][4];                 // dwords of the chunk being loaded
+    uint32_t vcur[4][4], vprev[4][4];    // packed: the column phase's chunk and the one before
+    auto load_v = [&](int cc) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vraw[T][j] = __builtin_amdgcn_raw_buffer_load_b32(
+              hb.v, (int)(chunk_off(cc) + (unsigned)(16 * T + 4 * g + j) * (kDV * 2) + 64 * tile + 4 * n), 0, 0);
+    };
+    auto pack_v = [&]() {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          vcur[T][h] = __builtin_amdgcn_perm(vraw[T][2 * h + 1], vraw[T][2 * h], 0x05040100u);      // low halves
+          vcur[T][2 + h] = __builtin_amdgcn_perm(vraw[T][2 * h + 1], vraw[T][2 * h], 0x07060302u);  // high halves
+        }
+    };
+    // operand of column tile dt over token tiles (a, b) of the current (a, b >= 0)
+    // or previous (a, b < 0) chunk; b > 3 gives zeros
+    auto vop = [&](int a, int b, int dt) -> bf16x8 {
+      const uint32_t *ta = a >= 0 ? vcur[a] : vprev[a + 4];
+      u32x4 r;
+      r[0] = ta[2 * dt];
+      r[1] = ta[2 * dt + 1];
+      if (b > 3) {
+        r[2] = 0u;
+        r[3] = 0u;
+      } else {
+        const uint32_t *tb = b >= 0 ? vcur[b] : vprev[b + 4];
+        r[2] = tb[2 * dt];
+        r[3] = tb[2 * dt + 1];
+      }
+      return __builtin_bit_cast(bf16x8, r);
+    };
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vcur[T][j] = 0u;
+    load_v(c_begin - 1);  // the chunk before the segment (window part); zeros before token 0
+    bf16x8 xk[4], xg[4];  // this chunk's keys, the next chunk's gates
     load_rows(hb.k, ro + chunk_off(c_begin), xk);
-    load_vals(hb.v, ro + chunk_off(c_begin), xv);
     load_gates(hb.g, ro + chunk_off(c_begin), xg);
+    {  // decay exponents of the first chunk (later ones: in the previous chunk's phase C)
+      float dn[32];
+      tile_decay(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
+      store_dd(smem + LD::DD, tile, dn);
+    }
     float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
-    __syncthreads();               // staged fragments and the first chunk's totals
+    __syncthreads();               // staged fragments and the first chunk's decay exponents
 
     // column phase of chunk cc: outputs and state
     auto column = [&](int cc) {
-      const int c0 = cc * kC;
-      const int slot = SWA ? (cc & 1) : 0;
-      const int pslot = slot ^ 1;
       f32x4 O[4][2];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt)
@@ -242,61 +292,47 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         }
       }
       // weights x V over the key tiles of each query tile
-      auto vt_half = [&](int kt, int dt) -> bf16x4 {
-        const int sl = kt >= 0 ? slot : pslot;
-        const int tl = kt >= 0 ? kt : kt + 4;
-        return *(const bf16x4 *)(smem + LD::VT + ((sl * 4 + tl) * 8 + 2 * tile + dt) * kHalf + lane * 8);
-      };
-      const bf16x4 z4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        bf16x8 wf[NKS], vf[NKS][2];
+        bf16x8 wf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const char *wb = smem + LD::W + qt * LD::WQT + ks * kFrag;
           if (SWA && ks == 2)
-            wf[ks] = join44(*(const bf16x4 *)(wb + lane * 8), z4);
+            wf[ks] = join44(*(const bf16x4 *)(wb + lane * 8), (bf16x4){(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f});
           else
             wf[ks] = lds8(wb + lane * 16);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            bf16x4 lo, hi;
-            if (SWA) {
-              const int ka = qt - 4 + 2 * ks;
-              lo = vt_half(ka, dt);
-              hi = ks < 2 ? vt_half(ka + 1, dt) : z4;
-            } else {
-              lo = vt_half(2 * ks, dt);
-              hi = vt_half(2 * ks + 1, dt);
-            }
-            vf[ks][dt] = join44(lo, hi);
-          }
         }
         issue_fence();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) O[qt][dt] = mfma(vf[ks][dt], wf[ks], O[qt][dt]);
+          for (int dt = 0; dt < 2; ++dt) {
+            // key tiles (qt - 4 + 2ks, qt - 3 + 2ks) with the window, (2ks, 2ks + 1)
+            // without; the diagonal tile's step has no second tile
+            const int a = SWA ? qt - 4 + 2 * ks : 2 * ks;
+            const int b = SWA && ks == 2 ? 4 : a + 1;
+            O[qt][dt] = mfma(vop(a, b, dt), wf[ks], O[qt][dt]);
+          }
       }
-      // store o: lane (n, g) of query tile qt holds d_v 32 tile + 8g + (4dt + j);
+      // store o: lane (n, g) of query tile qt holds d_v 32 tile + 8g + 2j + dt;
       // rows past the end are dropped by the range check
       if (cc >= c_begin) {
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
+        for (int qt = 0; qt < 4; ++qt) {
+          bf16x8 ov;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ov[2 * j] = (bf16)O[qt][0][j];
+            ov[2 * j + 1] = (bf16)O[qt][1][j];
+          }
           __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(u32x4, pack44(O[qt][0], O[qt][1])), hb.o,
+              __builtin_bit_cast(u32x4, ov), hb.o,
               (int)(chunk_off(cc) + (unsigned)(16 * qt + n) * (kDV * 2) + 64 * tile + 16 * g), 0, 0);
+        }
       }
       // S += k-hat^T V in groups of 4 state tiles (fragments of a group requested
       // together)
-      bf16x8 bv[2][2];
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const char *vb = smem + LD::VT + ((slot * 4 + 2 * sp) * 8 + 2 * tile + dt) * kHalf + lane * 8;
-          bv[sp][dt] = join44(*(const bf16x4 *)vb, *(const bf16x4 *)(vb + 8 * kHalf));
-        }
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {  // grp = 2 sp + (mt / 4)
         const int sp = grp >> 1, mb = 4 * (grp & 1);
@@ -307,26 +343,27 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4)
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt) S[mb + m4][dt] = mfma(kf[m4], bv[sp][dt], S[mb + m4][dt]);
+          for (int dt = 0; dt < 2; ++dt) S[mb + m4][dt] = mfma(kf[m4], vop(2 * sp, 2 * sp + 1, dt), S[mb + m4][dt]);
       }
     };
 
     for (int c = c_begin; c < c_end; ++c) {
-      const int slot = SWA ? (c & 1) : 0;
       const int tq = c * kC + 16 * tile + n;
-      const bool tok_ok = tq < p.L;
       const unsigned ro1 = ro + chunk_off(c + 1);
       // ---- phase A: previous chunk's column phase, then this tile's keys
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vprev[T][j] = vcur[T][j];
+      pack_v();  // values of chunk c - 1
       column(c - 1);
+      load_gates(hb.g, ro1, xg);  // next chunk's gates (decay exponents in phase C)
       f32x4 u[4];
       project(smem + LD::WK + lane * 16, xk, u);
       load_rows(hb.k, ro1, xk);  // next chunk's keys
-      float dd[32];
-      tile_decay(xg, gate_is_log, tok_ok, dd);
-      load_gates(hb.g, ro1, xg);
       float e[32], izp, izn;
       hedgehog_exp(u, e, izp, izn);
-      const FoldRef r = fold_ref((const float *)(smem + LD::T) + (c & 1) * 4 * kF, tile);
+      const FoldRef r = fold_ref(smem + LD::DD, tile);
       bf16x8 xr[4], xs[4];  // k~ (intra scores), k-hat (state update)
       float fs[2];
 #pragma unroll
@@ -334,17 +371,21 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         fs[e2] = r.btot[e2] - r.rr2[e2];
         fdec[e2] = exp2_fast(r.btot[e2]);
       }
-      // Keys past the end need no masking: their k~ meets only queries past the
-      // end (causal mask), whose outputs are not stored, and their k-hat meets
-      // value rows that read as zero (range check).
-      fold(e, izp, izn, dd, r, -1.0f, fs, xr, xs);
+      {
+        float dn[32];
+        load_dd(smem + LD::DD, tile, dn);
+        // Keys past the end need no masking: their k~ meets only queries past the
+        // end (causal mask), whose outputs are not stored, and their k-hat meets
+        // value rows that read as zero (range check).
+        fold(e, izp, izn, dn, r, -1.0f, fs, xr, xs);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (tile * 4 + s) * kFrag + lane * 16, xr[s]);
-      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase done
+      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
 
-      // ---- phase C: V^T and k-hat^T fragments of this tile
-      stage_vt(xv, slot);
-      load_vals(hb.v, ro1, xv);  // next chunk's values
+      // ---- phase C: k-hat^T fragments of this tile, values of this chunk for
+      // the next column phase, decay exponents of the next chunk
+      load_v(c);
       {  // state tile mt takes its 16 features from K-step s(mt) = 2(mt/4) + (mt%4)/2
          // of the token-row operand, transposed on the matrix core
         const int sp = tile >> 1, hf = tile & 1;
@@ -362,8 +403,18 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
             *(bf16x4 *)(smem + LD::KH + ((2 * m2 + d2) * 2 + sp) * kFrag + lane * 16 + hf * 8) = pack4(t2[d2]);
         }
       }
-      __syncthreads();  // B2: q-bar, k-hat^T, V^T, weight fragments visible
+      {
+        float dn[32];
+        tile_decay(xg, gate_is_log, tq + kC < p.L, dn);
+        store_dd(smem + LD::DD, tile, dn);
+      }
+      __syncthreads();  // B2: q-bar, k-hat^T, weight fragments and decay exponents visible
     }
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vprev[T][j] = vcur[T][j];
+    pack_v();
     column(c_end - 1);
     if (p.state_out && seg == p.P - 1) {
       float *dst = p.state_out + bh * kF * kDV;
@@ -372,7 +423,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(tile, dt, n)] = S[mt][dt][j];
+          for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvpair(tile, dt, n)] = S[mt][dt][j];
     }
   } else {
     // ============================== query waves ==============================
@@ -391,35 +442,24 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::RK + ((slot * 4 + tile) * 4 + s) * kFrag + lane * 16, xk[s]);
     };
-    // q and raw keys of this chunk, gates of the next
-    bf16x8 xq[4], xb[4], xg[4];
+    // q and raw keys of this chunk (the key waves compute the gate decay
+    // exponents, one chunk ahead)
+    bf16x8 xq[4], xb[4];
     const HeadBufs hb = head_bufs(p, bh);
     const unsigned ro = row_off(tile);
     if (SWA) {  // keys of the chunk before the segment (window part)
       load_rows(hb.k, ro + chunk_off(c_begin - 1), xb);
       stage_rk(xb, (c_begin - 1) & 1);
     }
-    float dd[32];  // decay exponents (-cumsums, tile_decay) of the chunk being processed
-    {
-      load_rows(hb.q, ro + chunk_off(c_begin), xq);
-      if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
-      load_gates(hb.g, ro + chunk_off(c_begin), xg);
-      tile_decay(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dd);
-      if (n == 15) {  // tile totals of the first chunk
-        float *T = (float *)(smem + LD::T) + ((c_begin & 1) * 4 + tile) * kF;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
-      }
-      load_gates(hb.g, ro + chunk_off(c_begin + 1), xg);
-    }
+    load_rows(hb.q, ro + chunk_off(c_begin), xq);
+    if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
     const float sl2 =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale * kLog2e)));
-    __syncthreads();  // staged fragments and the first chunk's totals
+    __syncthreads();  // staged fragments and the first chunk's decay exponents
 
     for (int c = c_begin; c < c_end; ++c) {
       const int slot = SWA ? (c & 1) : 0;
       const int pslot = slot ^ 1;
-      const int tq = c * kC + 16 * tile + n;
       const unsigned ro1 = ro + chunk_off(c + 1);
       // ---- phase A
       // band scores sc[i] for key tile tile-4+i: tiles of the previous chunk and
@@ -451,20 +491,13 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       float e[32], izp, izn;
       hedgehog_exp(u, e, izp, izn);
       bf16x8 xr[4], xs[4];  // q~ (intra scores), q-bar (readout)
-      bool chunk_mode;
+      const FoldRef r = fold_ref(smem + LD::DD, tile);
       {
-        const FoldRef r = fold_ref((const float *)(smem + LD::T) + (c & 1) * 4 * kF, tile);
-        fold(e, izp, izn, dd, r, 1.0f, r.rr2, xr, xs);
-        chunk_mode = r.chunk_mode;
+        float dn[32];
+        load_dd(smem + LD::DD, tile, dn);
+        fold(e, izp, izn, dn, r, 1.0f, r.rr2, xr, xs);
       }
-      // cumsums and tile totals of the next chunk, published one chunk ahead
-      tile_decay(xg, gate_is_log, tq + kC < p.L, dd);
-      load_gates(hb.g, ro + chunk_off(c + 2), xg);
-      if (n == 15) {
-        float *T = (float *)(smem + LD::T) + (((c + 1) & 1) * 4 + tile) * kF;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) T[feat(g, i)] = dd[i];
-      }
+      const bool chunk_mode = r.chunk_mode;
       if (SWA) {
 #pragma unroll
         for (int i = 0; i < 5; ++i)
@@ -480,26 +513,34 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (tile - 4 + i >= 0) band(i);
-        // key position minus query position: 16(i-4) + 4g + j - n; valid when in
-        // (-window, 0] and the key exists (position >= 0)
+        // query position minus key position: 16(4-i) - j - (4g - n); valid when in
+        // [0, window) (one unsigned compare) and the key exists: its position
+        // 64c + 16(tile + i - 4) + 4g + j is >= 0 exactly when c > 0 or
+        // tile + i >= 4 (uniform per key tile)
+        const unsigned uw = (unsigned)p.window;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          const bool exists = c > 0 || tile + i >= 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const unsigned back = (unsigned)(16 * (4 - i) - j - (4 * g - n));
+            sc[i][j] = (back < uw && exists) ? sc[i][j] : -INFINITY;
+          }
+        }
+        // softmax with the sinks, base 2: the scale is positive, so the row
+        // maximum is taken on the raw scores and scaled once
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 5; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int rel = 16 * (i - 4) + 4 * g + j - n;
-            const bool ok = rel <= 0 && rel > -p.window && tq + rel >= 0;
-            sc[i][j] = ok ? sc[i][j] * sl2 : -INFINITY;
-            mx = fmaxf(mx, sc[i][j]);
-          }
-        mx = grp_max(mx);
-        mx = fmaxf(mx, meta_max);
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[i][j]);
+        mx = fmaxf(grp_max(mx) * sl2, meta_max);
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 5; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float ex = exp2_fast(sc[i][j] - mx);  // 2^{-inf} = 0
+            const float ex = exp2_fast(fmaf(sc[i][j], sl2, -mx));  // 2^{-inf} = 0
             sc[i][j] = ex;
             sum += ex;
           }
@@ -543,16 +584,13 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
           } else if (kt >= 0) {
             bf16x8 kf[4];
             kt_frags(kt, kf);
-            // tile totals of this chunk again (the slot is rewritten only in the
-            // next chunk's phase A)
-            const float *T = (const float *)(smem + LD::T) + (c & 1) * 4 * kF + feat(g, 2 * n);
             float fo[2];
 #pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
-              float run = 0.0f, tk = 0.0f, tw = 0.0f;  // log-gate sum of tiles kt .. tile-1
+              float run = 0.0f, tk = 0.0f, tw = 0.0f;  // log2-gate sum of tiles kt .. tile-1
 #pragma unroll
-              for (int w2 = 0; w2 < 4; ++w2) {
-                const float tv = -T[w2 * kF + e2];
+              for (int w2 = 0; w2 < 4; ++w2) {  // unrolled: no dynamic register indexing
+                const float tv = r.tt[w2][e2];
                 if (w2 >= kt && w2 < tile) run += tv;
                 if (w2 == kt) tk = tv;
                 if (w2 == tile) tw = tv;
