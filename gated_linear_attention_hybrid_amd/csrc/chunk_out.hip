@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         for (int i = 0; i < 5; ++i)
           if (i == 4 || tile - 4 + i < 0) band(i);
       }
-      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase done
+      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
 
       // ---- phase C
       f32x4 Wt[5];  // weights^T for key tiles tile-4+i (i = 4: the diagonal tile)
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       // waves' longer phase A
       load_rows(hb.q, ro1, xq);
       if (SWA) load_rows(hb.k, ro1, xb);
-      __syncthreads();  // B2: q-bar, k-hat^T, V^T, weight fragments visible
+      __syncthreads();  // B2: q-bar, k-hat^T, weight fragments and decay exponents visible
     }
   }
 }
