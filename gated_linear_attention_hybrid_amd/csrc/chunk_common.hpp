@@ -290,7 +290,8 @@ __device__ __forceinline__ void tile_decay(const bf16x8 *xg, bool gate_is_log, b
 #pragma unroll
     for (int i = 0; i < 32; ++i) dn[i] = fminf((float)xg[i >> 3][i & 7] * -kLog2e, kMaxLog2Decay);
   } else {
-    const float cap = tok_ok ? kMaxLog2Decay : -INFINITY;
+    float cap = tok_ok ? kMaxLog2Decay : -INFINITY;
+    asm volatile("" : "+v"(cap));  // opaque: one min per value, no select after it
 #pragma unroll
     for (int i = 0; i < 32; ++i)
       dn[i] = log2_fast(1.0f + exp2_fast(fminf((float)xg[i >> 3][i & 7] * -kLog2e, cap)));
