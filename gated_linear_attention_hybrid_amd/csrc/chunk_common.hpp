@@ -225,6 +225,12 @@ __device__ __forceinline__ void load_gates(__amdgpu_buffer_rsrc_t r, unsigned ba
 #pragma unroll
   for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 2 * feat(g, 8 * s));
 }
+// the gates of fold slots 16h .. 16h + 15 only (fragments 2h, 2h + 1 of load_gates)
+__device__ __forceinline__ void load_gates_half(__amdgpu_buffer_rsrc_t r, unsigned base, int h, bf16x8 *x) {
+  const unsigned g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) x[s] = bload(r, base + 2 * feat(g, 16 * h + 8 * s));
+}
 
 // Unnormalised Hedgehog exponentials of the lane's token: e[4mt + j] =
 // 2^{(u - max u) log2e} (phi+ feature 16g + 4mt + j) and e[16 + 4mt + j] =
@@ -284,28 +290,29 @@ __device__ __forceinline__ void project(const char *wb, const bf16x8 *x, f32x4 *
 // kMaxLog2Decay, which caps each term at kMaxLog2Decay + 2^{-kMaxLog2Decay}/ln 2.
 // Tokens past the end (!tok_ok) contribute 0: their gates read as 0 (range
 // check), which gives 0 in the log form, and a cap of -inf gives log2(1 + 0) = 0
-// in the logit form.
+// in the logit form.  NV slots starting at the first of xg (NV/8 fragments).
+template <int NV = 32>
 __device__ __forceinline__ void tile_decay(const bf16x8 *xg, bool gate_is_log, bool tok_ok, float *dn) {
   if (gate_is_log) {  // one uniform branch around the whole loop
 #pragma unroll
-    for (int i = 0; i < 32; ++i) dn[i] = fminf((float)xg[i >> 3][i & 7] * -kLog2e, kMaxLog2Decay);
+    for (int i = 0; i < NV; ++i) dn[i] = fminf((float)xg[i >> 3][i & 7] * -kLog2e, kMaxLog2Decay);
   } else {
     float cap = tok_ok ? kMaxLog2Decay : -INFINITY;
     asm volatile("" : "+v"(cap));  // opaque: one min per value, no select after it
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < NV; ++i)
       dn[i] = log2_fast(1.0f + exp2_fast(fminf((float)xg[i >> 3][i & 7] * -kLog2e, cap)));
   }
-  // one scan step across all 32 slots at a time, so consecutive DPP reads
-  // never wait on each other
+  // one scan step across all slots at a time, so consecutive DPP reads never
+  // wait on each other
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dn[i] += row_shr<1>(dn[i]);
+  for (int i = 0; i < NV; ++i) dn[i] += row_shr<1>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dn[i] += row_shr<2>(dn[i]);
+  for (int i = 0; i < NV; ++i) dn[i] += row_shr<2>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dn[i] += row_shr<4>(dn[i]);
+  for (int i = 0; i < NV; ++i) dn[i] += row_shr<4>(dn[i]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dn[i] += row_shr<8>(dn[i]);
+  for (int i = 0; i < NV; ++i) dn[i] += row_shr<8>(dn[i]);
 }
 
 }  // namespace

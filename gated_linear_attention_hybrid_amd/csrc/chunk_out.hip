@@ -21,13 +21,14 @@
 //                          chunk, with the value operands read straight from
 //                          memory; then u_k = k Wphi_k, phi(k), k~ and the
 //                          k-hat^T fragments; and, in the second phase, the gate
-//                          decay exponents of its tile of the NEXT chunk, shared
-//                          through LDS, so every wave knows the chunk-wide fold
-//                          reference when a chunk starts and the query waves
-//                          compute no gates
+//                          decay exponents of the phi- features of its tile of
+//                          the NEXT chunk
 //   query wave (w = 4..7): raw-k fragments, window scores and softmax, u_q,
 //                          phi(q), q~, q-bar, intra-chunk scores, weight
-//                          fragments
+//                          fragments; and, in the first phase, the decay
+//                          exponents of the phi+ features of the NEXT chunk
+// The decay exponents are shared through LDS, so each is computed once and
+// every wave knows the chunk-wide fold reference when a chunk starts.
 // Per chunk there are two barriers: B1 (raw-k and k~ fragments visible, column
 // phase of the previous chunk and every read of the decay exponents done) and
 // B2 (q-bar, k-hat^T, weights and the next chunk's decay exponents visible).
@@ -59,11 +60,13 @@ static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
 
 // Decay exponents (tile_decay) of the chunk, exchanged through LDS: tile t,
 // lane l, fold slots 4q .. 4q+3 at ((t * 8 + q) * 64 + l) * 16 bytes.
-__device__ __forceinline__ void store_dd(char *dd, int tile, const float *dn) {
+// the half h of the slots (16h .. 16h + 15) from dn[0 .. 15]
+__device__ __forceinline__ void store_dd_half(char *dd, int tile, int h, const float *dn) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    *(f32x4 *)(dd + ((tile * 8 + q) * 64 + lane) * 16) = (f32x4){dn[4 * q], dn[4 * q + 1], dn[4 * q + 2], dn[4 * q + 3]};
+  for (int q = 0; q < 4; ++q)
+    *(f32x4 *)(dd + ((tile * 8 + 4 * h + q) * 64 + lane) * 16) =
+        (f32x4){dn[4 * q], dn[4 * q + 1], dn[4 * q + 2], dn[4 * q + 3]};
 }
 __device__ __forceinline__ void load_dd(const char *dd, int tile, float *dn) {
   const int lane = threadIdx.x & 63;
@@ -252,13 +255,15 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) vcur[T][j] = 0u;
     load_v(c_begin - 1);  // the chunk before the segment (window part); zeros before token 0
-    bf16x8 xk[4], xg[4];  // this chunk's keys, the next chunk's gates
+    // The decay exponents of a chunk are computed one chunk ahead: slots 16..31
+    // (the phi- features) here in phase C, slots 0..15 by the query waves
+    bf16x8 xk[4], xg[2];  // this chunk's keys, the next chunk's gates (slots 16..31)
     load_rows(hb.k, ro + chunk_off(c_begin), xk);
-    load_gates(hb.g, ro + chunk_off(c_begin), xg);
-    {  // decay exponents of the first chunk (later ones: in the previous chunk's phase C)
-      float dn[32];
-      tile_decay(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
-      store_dd(smem + LD::DD, tile, dn);
+    load_gates_half(hb.g, ro + chunk_off(c_begin), 1, xg);
+    {
+      float dn[16];
+      tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
+      store_dd_half(smem + LD::DD, tile, 1, dn);
     }
     float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
     __syncthreads();               // staged fragments and the first chunk's decay exponents
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         for (int j = 0; j < 4; ++j) vprev[T][j] = vcur[T][j];
       pack_v();  // values of chunk c - 1
       column(c - 1);
-      load_gates(hb.g, ro1, xg);  // next chunk's gates (decay exponents in phase C)
+      load_gates_half(hb.g, ro1, 1, xg);  // next chunk's gates (decay exponents in phase C)
       f32x4 u[4];
       project(smem + LD::WK + lane * 16, xk, u);
       load_rows(hb.k, ro1, xk);  // next chunk's keys
@@ -404,9 +409,9 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         }
       }
       {
-        float dn[32];
-        tile_decay(xg, gate_is_log, tq + kC < p.L, dn);
-        store_dd(smem + LD::DD, tile, dn);
+        float dn[16];
+        tile_decay<16>(xg, gate_is_log, tq + kC < p.L, dn);
+        store_dd_half(smem + LD::DD, tile, 1, dn);
       }
       __syncthreads();  // B2: q-bar, k-hat^T, weight fragments and decay exponents visible
     }
@@ -453,6 +458,16 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
     }
     load_rows(hb.q, ro + chunk_off(c_begin), xq);
     if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
+    // decay exponents of slots 0..15 (the phi+ features), one chunk ahead: the
+    // first chunk's here, the next chunk's in phase A, stored after B1
+    bf16x8 xg[2];
+    load_gates_half(hb.g, ro + chunk_off(c_begin), 0, xg);
+    {
+      float dn[16];
+      tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
+      store_dd_half(smem + LD::DD, tile, 0, dn);
+    }
+    load_gates_half(hb.g, ro + chunk_off(c_begin + 1), 0, xg);
     const float sl2 =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale * kLog2e)));
     __syncthreads();  // staged fragments and the first chunk's decay exponents
@@ -503,7 +518,11 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         for (int i = 0; i < 5; ++i)
           if (i == 4 || tile - 4 + i < 0) band(i);
       }
+      float dnx[16];  // next chunk's, stored once every wave has read this chunk's
+      tile_decay<16>(xg, gate_is_log, (c + 1) * kC + 16 * tile + n < p.L, dnx);
+      load_gates_half(hb.g, ro + chunk_off(c + 2), 0, xg);
       __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
+      store_dd_half(smem + LD::DD, tile, 0, dnx);
 
       // ---- phase C
       f32x4 Wt[5];  // weights^T for key tiles tile-4+i (i = 4: the diagonal tile)
