@@ -109,6 +109,7 @@ glah_status gla_prefill(const glah_desc *desc, const void *q, const void *k, con
     a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k;
     a.state_in = state_in; a.state_out = state_out; a.o = o;
     a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
+    if (a.L == 0) return finish(launch_state_passthrough(a));
     if (chunked_supported(a, PART_GLA)) {
       if (ws_bytes < chunked_workspace_bytes(a, PART_GLA) || (!ws && chunked_workspace_bytes(a, PART_GLA)))
         return GLAH_EWORKSPACE;
@@ -161,6 +162,11 @@ glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k
     a.kcache = kcache_out; a.vcache = vcache_out;
     a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
     hipError_t e;
+    if (a.L == 0) {  // no tokens: the state passes through, the ring is all zeros
+      e = launch_state_passthrough(a);
+      if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
+      return finish(e);
+    }
     if (chunked_supported(a, PART_BOTH)) {
       if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
         return GLAH_EWORKSPACE;

@@ -40,6 +40,8 @@ bool recurrent_supported(const LayerArgs &a, int parts);
 hipError_t launch_recurrent_prefill(const LayerArgs &a, int parts);
 hipError_t launch_decode_step(const LayerArgs &a, int parts);
 hipError_t launch_window_cache(const LayerArgs &a);
+// state_out of an empty sequence (L = 0): the state before it, state_in or zeros
+hipError_t launch_state_passthrough(const LayerArgs &a);
 
 // Bandwidth-oriented decode step at d = f = d_v = 128, window <= 64.
 bool decode128_supported(const LayerArgs &a, int parts);

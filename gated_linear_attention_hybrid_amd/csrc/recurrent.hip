@@ -407,6 +407,13 @@ hipError_t decode_dispatch(const LayerArgs &a, int parts) {
   return hipGetLastError();
 }
 
+// state_out of an empty sequence: a plain copy of state_in, or zeros (a kernel,
+// not a memset, so the call may be captured in a graph)
+__global__ __launch_bounds__(kThreads) void state_passthrough_kernel(const float *in, float *out, size_t n) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) out[i] = in ? in[i] : 0.0f;
+}
+
 }  // namespace
 
 bool recurrent_supported(const LayerArgs &a, int parts) {
@@ -427,6 +434,15 @@ hipError_t launch_decode_step(const LayerArgs &a, int parts) {
   // 32 state columns per block: 4 blocks per head at d_v = 128, so a batch of
   // 8 x 32 heads spreads over 1024 blocks.
   return a.bf16 ? decode_dispatch<bf16, 32>(a, parts) : decode_dispatch<float, 32>(a, parts);
+}
+
+hipError_t launch_state_passthrough(const LayerArgs &a) {
+  if (!a.state_out || a.state_out == a.state_in) return hipSuccess;
+  const size_t n = (size_t)a.B * a.H * a.f * a.dv;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_passthrough_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     a.stream, a.state_in, a.state_out, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_window_cache(const LayerArgs &a) {

@@ -91,7 +91,8 @@ size_t glah_workspace_bytes(const glah_desc *desc);
  * C): chunkwise-parallel form with the cumulative log-gates folded into phi(q)
  * and phi(k), an fp32 inter-chunk state pass, o = o_gla.
  *   state_in   nullable; [B][H][f][d_v] fp32 state before token 0 (0 if NULL)
- *   state_out  nullable; receives S_{L-1}; may equal state_in
+ *   state_out  nullable; receives S_{L-1} (L = 0: the state before the sequence,
+ *              state_in or zeros); may equal state_in
  *   ws         device workspace of ws_bytes >= glah_workspace_bytes(desc)
  */
 glah_status gla_prefill(const glah_desc *desc, const void *q, const void *k,

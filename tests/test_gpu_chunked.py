@@ -191,6 +191,31 @@ def test_state_in_out_continuation():
     assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), sfull.reshape(-1, wl.dv)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_sequence_passes_the_state(dtype):
+    """L = 0: state_out is the state before the sequence (state_in, or zeros
+    without one) and the returned ring is all zeros, on both entry points."""
+    wl = base(H=3, L=0)
+    say("empty sequence, %s" % dtype)
+    x = make_prefill(wl.with_(L=64), DEV)
+    x = {k: (v[:, :, :0].to(dtype).contiguous() if v.dim() == 4 else v.to(dtype) if k in ("wq", "wk") else v)
+         for k, v in x.items()}
+    sin = torch.randn((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    for with_in in (True, False):
+        sout = torch.full_like(sin, 7.0)
+        G.gla_prefill(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"],
+                      state_in=sin if with_in else None, state_out=sout)
+        torch.cuda.synchronize()
+        assert torch.equal(sout, sin if with_in else torch.zeros_like(sin))
+        sout = torch.full_like(sin, 7.0)
+        kc = torch.full((wl.B, wl.H, wl.window, wl.d), 3.0, device=DEV, dtype=dtype)
+        vc = torch.full((wl.B, wl.H, wl.window, wl.dv), 3.0, device=DEV, dtype=dtype)
+        run_hybrid(x, wl, state_in=sin if with_in else None, state_out=sout, kcache_out=kc, vcache_out=vc)
+        torch.cuda.synchronize()
+        assert torch.equal(sout, sin if with_in else torch.zeros_like(sin))
+        assert not kc.any() and not vc.any()
+
+
 def test_window_cache_out_mfma():
     wl = base(H=2, L=200)
     say("window cache out (MFMA path)")
