@@ -30,6 +30,15 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 #          + state 128*128 + window 64*(128+128)
 PREFILL_BYTES_PER_TOKEN_HEAD = 1280
 PREFILL_FLOPS_PER_TOKEN_HEAD = 2 * (2 * 128 * 64 + 65 * 128 + 128 * 128 + 128 * 128 + 64 * 256)
+# MFMA work the kernels execute per token-head at the 32K workload (16x16x32 bf16
+# MFMAs of 16384 flops).  Output pass, per 64-token chunk of a head: readout 128,
+# weights x V 96, state update 128, the two projections 128, window bands 80,
+# intra tiles 40 = 600 MFMAs; state pass (7/8 of the tokens): projection 64 +
+# update 128 = 192 per chunk.  Transposes on the matrix core (0/1 selection
+# operands, no arithmetic work) are counted apart: 32 per output-pass chunk, 64
+# per state-pass chunk.
+PREFILL_EXECUTED_FLOPS_PER_TOKEN_HEAD = (600 * 16384 + 192 * 16384 * 7 // 8) // 64
+PREFILL_TRANSPOSE_FLOPS_PER_TOKEN_HEAD = (32 * 16384 + 64 * 16384 * 7 // 8) // 64
 
 
 def decode_bytes_per_step(B, H, d, f, dv, w, bpe=2):
@@ -168,9 +177,48 @@ def bench_decode(G, torch, steps=256, sets=12, prefix=32768):
     }
 
 
+def measured_ceilings(torch):
+    """What this GPU reaches on plain library work: a 1 GiB device copy (HBM) and
+    a large bf16 GEMM (hipBLASLt through torch), best of 3 each."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_copy = best_gemm = float("inf")
+    for _ in range(4):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best_copy = min(best_copy, e0.elapsed_time(e1))
+        e0.record()
+        torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        best_gemm = min(best_gemm, e0.elapsed_time(e1))
+    del src, dst, a, b
+    return {"copy_GBps": round(2 * 4 * n / (best_copy * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / (best_gemm * 1e-3) / 1e12, 1),
+            "note": "1 GiB device copy (read + write bytes) and an 8192^3 bf16 torch.matmul, best of 4"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, torch, target_s=12.0):
     """fp64 oracle on the host cores: all heads, the first L_s tokens, with L_s
-    sized from a short calibration run so the sample takes roughly target_s."""
+    sized from a short calibration run so the sample takes roughly target_s; then
+    a short sample on one core."""
     import oracle
     from gated_linear_attention_hybrid_amd.inputs import make_prefill, to_f64
     dev = torch.device("cuda")
@@ -189,10 +237,21 @@ def cpu_baseline(wl, torch, target_s=12.0):
     Ls = max(64, (Ls // 64) * 64)
     t = sample(Ls)
     threads = min(oracle.num_threads(), wl.B * wl.H)
+    all_threads = oracle.num_threads()
+    oracle.set_num_threads(1)  # one core: a sample of about a second
+    try:
+        t1c = sample(calib)
+        L1 = max(64, min(wl.L, int(calib * 1.0 / max(t1c, 1e-3))) // 64 * 64)
+        t1 = sample(L1)
+    finally:
+        oracle.set_num_threads(all_threads)
     return {"value": round(wl.B * Ls / t, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "all %d heads of the first %d of %d tokens (fp64 oracle, OpenMP over heads), %.1f s"
-                      % (wl.B * wl.H, Ls, wl.L, t)}
+                      % (wl.B * wl.H, Ls, wl.L, t),
+            "one_core": {"value": round(wl.B * L1 / t1, 1), "unit": "tokens/s",
+                         "sample": "all heads, first %d tokens, %.1f s" % (L1, t1)},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
@@ -251,7 +310,10 @@ def main():
                      "kernel": "hybrid_layer_fwd call (state pass + segment scan + fused output pass)",
                      "us_per_launch": round(per_call_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "mfma_frac": round(nflops / (per_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                     "mfma_frac": round(nflops / (per_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_token_head": PREFILL_FLOPS_PER_TOKEN_HEAD,
+                     "executed_flops_per_token_head": PREFILL_EXECUTED_FLOPS_PER_TOKEN_HEAD,
+                     "transpose_flops_per_token_head": PREFILL_TRANSPOSE_FLOPS_PER_TOKEN_HEAD},
         "nonfinite_outputs": bad,
     }
     if args.copy_calibration_mib > 0:
@@ -263,8 +325,13 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = {"read": nel * 4, "written": nel * 4}
         del src, dst
+    out["measured_ceilings"] = measured_ceilings(torch)
     if not args.no_decode:
         out["decode"] = bench_decode(G, torch)
+        # the step does not depend on the prefix length (constant-size state)
+        short = bench_decode(G, torch, prefix=4096)
+        out["decode"]["flatness"] = {"prefix_4096_us_per_step": short["us_per_step"],
+                                     "prefix_32768_us_per_step": out["decode"]["us_per_step"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)
