@@ -21,6 +21,7 @@ LIBRARY = os.path.join(_PKG, "libglahybrid.so")
 GLAH_OK, GLAH_EINVAL, GLAH_ENOTSUP, GLAH_EWORKSPACE, GLAH_EHIP = range(5)
 GLAH_BF16, GLAH_F32 = 0, 1
 GLAH_GATE_LOGITS, GLAH_GATE_LOG = 0, 1
+GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per token, [H] per head
 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
            "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step")
@@ -94,9 +95,10 @@ def _dtype_code(t):
 
 
 def make_desc(B, H, L, d, dv, f, *, window=0, n_meta=0, chunk=0, scale=0.0, dtype=GLAH_BF16,
-              gate_is_log=False) -> GlahDesc:
+              gate_is_log=False, gate_kind=None) -> GlahDesc:
     return GlahDesc(B, H, L, d, dv, f, chunk, window, n_meta, float(scale or 0.0), dtype,
-                    GLAH_GATE_LOG if gate_is_log else GLAH_GATE_LOGITS)
+                    gate_kind if gate_kind is not None else
+                    (GLAH_GATE_LOG if gate_is_log else GLAH_GATE_LOGITS))
 
 
 def workspace_bytes(desc: GlahDesc) -> int:
@@ -113,12 +115,13 @@ def _workspace(desc, ws, device):
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
-def gla_prefill(q, k, v, gate, wq, wk, *, chunk=0, gate_is_log=False, state_in=None,
+def gla_prefill(q, k, v, gate, wq, wk, *, chunk=0, gate_is_log=False, gate_kind=None, state_in=None,
                 state_out=None, o=None, ws=None, stream=None):
     """Gated linear attention prefill; returns o [B,H,L,dv]."""
     B, H, L, d = q.shape
-    dv, f = v.shape[-1], gate.shape[-1]
-    desc = make_desc(B, H, L, d, dv, f, chunk=chunk, dtype=_dtype_code(q), gate_is_log=gate_is_log)
+    dv, f = v.shape[-1], 2 * wq.shape[-1]
+    desc = make_desc(B, H, L, d, dv, f, chunk=chunk, dtype=_dtype_code(q), gate_is_log=gate_is_log,
+                     gate_kind=gate_kind)
     if o is None:
         o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
     ws, nbytes = _workspace(desc, ws, q.device)
@@ -144,14 +147,14 @@ def swa_meta_attn(q, k, v, meta, *, window, scale=0.0, o=None, stream=None):
 
 
 def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
-                     gate_is_log=False, state_in=None, state_out=None, kcache_out=None,
+                     gate_is_log=False, gate_kind=None, state_in=None, state_out=None, kcache_out=None,
                      vcache_out=None, o=None, ws=None, stream=None):
     """Whole hybrid layer (gated linear + window attention); returns o [B,H,L,dv]."""
     B, H, L, d = q.shape
-    dv, f = v.shape[-1], gate.shape[-1]
+    dv, f = v.shape[-1], 2 * wq.shape[-1]
     n_meta = 0 if meta is None else meta.shape[-1]
     desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log)
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
     if o is None:
         o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
     ws, nbytes = _workspace(desc, ws, q.device)
@@ -163,14 +166,14 @@ def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
 
 
 def gla_decode_step(q, k, v, gate, wq, wk, meta, state, kcache, vcache, pos, *, window,
-                    scale=0.0, gate_is_log=False, o=None, stream=None):
+                    scale=0.0, gate_is_log=False, gate_kind=None, o=None, stream=None):
     """One decode step (state and ring updated in place); returns o [B,H,dv].
     ``pos`` is a device int32 tensor [B] of tokens already consumed."""
     B, H, d = q.shape
-    dv, f = v.shape[-1], gate.shape[-1]
+    dv, f = v.shape[-1], 2 * wq.shape[-1]
     n_meta = 0 if meta is None else meta.shape[-1]
     desc = make_desc(B, H, 1, d, dv, f, window=window, n_meta=n_meta, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log)
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     st = load().gla_decode_step(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),

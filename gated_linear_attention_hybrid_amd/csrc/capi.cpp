@@ -37,7 +37,9 @@ glah_status check_desc(const glah_desc *d, Op op, LayerArgs &a) {
   if ((parts & PART_SWA) && d->window < 1) return GLAH_EINVAL;
   if (op == Op::kDecode && d->window < 0) return GLAH_EINVAL;
   if (d->dtype != GLAH_BF16 && d->dtype != GLAH_F32) return GLAH_EINVAL;
-  if (d->gate_kind != GLAH_GATE_LOGITS && d->gate_kind != GLAH_GATE_LOG) return GLAH_EINVAL;
+  if (d->gate_kind != GLAH_GATE_LOGITS && d->gate_kind != GLAH_GATE_LOG && d->gate_kind != GLAH_GATE_LOG_TOKEN &&
+      d->gate_kind != GLAH_GATE_LOG_HEAD)
+    return GLAH_EINVAL;
   if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
     return GLAH_EINVAL;
   // element counts must stay far from overflow of 64-bit offsets and of the
@@ -55,7 +57,8 @@ glah_status check_desc(const glah_desc *d, Op op, LayerArgs &a) {
   a.chunk = d->chunk == 0 ? 64 : d->chunk;
   a.scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)d->d_qk);
   a.bf16 = d->dtype == GLAH_BF16;
-  a.gate_is_log = d->gate_kind == GLAH_GATE_LOG;
+  a.gate_is_log = d->gate_kind != GLAH_GATE_LOGITS;
+  a.gate_mode = d->gate_kind == GLAH_GATE_LOG_TOKEN ? 1 : d->gate_kind == GLAH_GATE_LOG_HEAD ? 2 : 0;
   return GLAH_OK;
 }
 

@@ -24,6 +24,7 @@ struct ChunkParams {
   int R, sub_chunks;
   float scale;
   int gate_is_log;
+  int gate_mode;  // 0: one gate per feature [BH][L][f]; 1: per token [BH][L]; 2: per head [H]
 };
 
 // Output pass with two waves per 16-token tile (chunk_out.hip); `swa` adds the
@@ -192,14 +193,24 @@ __device__ __forceinline__ bf16x4 pack4(f32x4 x) {
 // past the end too); every consumer masks such tokens anyway.
 struct HeadBufs {
   __amdgpu_buffer_rsrc_t q, k, v, g, o;
+  int gmode;   // gate layout (ChunkParams::gate_mode)
+  unsigned L;  // tokens
 };
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16 *base, size_t bh, int L) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)(base + bh * (size_t)L * kD), (short)0, L * kD * 2,
                                            0x00020000);
 }
 __device__ __forceinline__ HeadBufs head_bufs(const ChunkParams &p, size_t bh) {
-  return {head_rsrc(p.q, bh, p.L), head_rsrc(p.k, bh, p.L), head_rsrc(p.v, bh, p.L),
-          head_rsrc(p.gate, bh, p.L), head_rsrc(p.o, bh, p.L)};
+  // the gates: [L][128] rows (per feature), [L] (per token) or the head's one value
+  __amdgpu_buffer_rsrc_t g;
+  if (p.gate_mode == 1)
+    g = __builtin_amdgcn_make_buffer_rsrc((void *)(p.gate + bh * (size_t)p.L), (short)0, p.L * 2, 0x00020000);
+  else if (p.gate_mode == 2)
+    g = __builtin_amdgcn_make_buffer_rsrc((void *)(p.gate + bh % (size_t)p.H), (short)0, 2, 0x00020000);
+  else
+    g = head_rsrc(p.gate, bh, p.L);
+  return {head_rsrc(p.q, bh, p.L), head_rsrc(p.k, bh, p.L), head_rsrc(p.v, bh, p.L), g,
+          head_rsrc(p.o, bh, p.L), p.gate_mode, (unsigned)p.L};
 }
 __device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -220,16 +231,42 @@ __device__ __forceinline__ void load_vals(__amdgpu_buffer_rsrc_t r, unsigned bas
 #pragma unroll
   for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 16 * g + 64 * s);
 }
-__device__ __forceinline__ void load_gates(__amdgpu_buffer_rsrc_t r, unsigned base, bf16x8 *x) {
+// A scalar log-gate of the lane's token (base = byte offset of its [128] row, as
+// for the per-feature layout) for every fold slot: per-token gates read element
+// base / 256, the per-head gate its one value (0 for tokens past the end, so
+// they add no decay; past-end per-token gates read 0 through the range check).
+__device__ __forceinline__ bf16x8 scalar_gate(const HeadBufs &hb, unsigned base) {
+  const unsigned tok = base >> 8;
+  unsigned raw;
+  if (hb.gmode == 1)
+    raw = __builtin_amdgcn_raw_buffer_load_b16(hb.g, (int)(2 * tok), 0, 0);
+  else
+    raw = tok < hb.L ? __builtin_amdgcn_raw_buffer_load_b16(hb.g, 0, 0, 0) : 0u;
+  const unsigned w = (raw & 0xFFFFu) * 0x10001u;
+  return __builtin_bit_cast(bf16x8, (u32x4){w, w, w, w});
+}
+__device__ __forceinline__ void load_gates(const HeadBufs &hb, unsigned base, bf16x8 *x) {
   const unsigned g = (threadIdx.x & 63) >> 4;
+  if (hb.gmode != 0) {  // uniform
+    const bf16x8 s1 = scalar_gate(hb, base);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) x[s] = bload(r, base + 2 * feat(g, 8 * s));
+    for (int s = 0; s < 4; ++s) x[s] = s1;
+    return;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) x[s] = bload(hb.g, base + 2 * feat(g, 8 * s));
 }
 // the gates of fold slots 16h .. 16h + 15 only (fragments 2h, 2h + 1 of load_gates)
-__device__ __forceinline__ void load_gates_half(__amdgpu_buffer_rsrc_t r, unsigned base, int h, bf16x8 *x) {
+__device__ __forceinline__ void load_gates_half(const HeadBufs &hb, unsigned base, int h, bf16x8 *x) {
   const unsigned g = (threadIdx.x & 63) >> 4;
+  if (hb.gmode != 0) {  // uniform
+    const bf16x8 s1 = scalar_gate(hb, base);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) x[s] = bload(r, base + 2 * feat(g, 16 * h + 8 * s));
+    for (int s = 0; s < 2; ++s) x[s] = s1;
+    return;
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) x[s] = bload(hb.g, base + 2 * feat(g, 16 * h + 8 * s));
 }
 
 // Unnormalised Hedgehog exponentials of the lane's token: e[4mt + j] =

@@ -216,7 +216,7 @@ void state_kernel(ChunkParams p) {
   bf16x8 xk[4], xv[4], xg[4];
   load_rows(hb.k, ro + chunk_off(c_end - 1), xk);
   load_vals(hb.v, ro + chunk_off(c_end - 1), xv);
-  load_gates(hb.g, ro + chunk_off(c_end - 1), xg);
+  load_gates(hb, ro + chunk_off(c_end - 1), xg);
   __syncthreads();
 
   // The chunks are taken last to first, so the state is never decayed: chunk c
@@ -231,7 +231,7 @@ void state_kernel(ChunkParams p) {
     load_rows(hb.k, ro1, xk);  // preceding chunk's keys
     float dn[32];
     tile_decay(xg, gate_is_log, c * kC + 16 * wave + n < p.L, dn);
-    load_gates(hb.g, ro1, xg);
+    load_gates(hb, ro1, xg);
     if (n == 15) {
       float *T = (float *)(smem + LD::T) + wave * kF;
 #pragma unroll
@@ -396,7 +396,7 @@ ChunkParams make_params(const LayerArgs &a, int P, int seg_chunks, int nchunks) 
   p.B = a.B; p.H = a.H; p.L = a.L; p.window = a.window; p.n_meta = a.n_meta;
   p.nchunks = nchunks; p.P = P; p.seg_chunks = seg_chunks;
   p.R = 1; p.sub_chunks = seg_chunks;
-  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0;
+  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
   return p;
 }
 

@@ -39,7 +39,7 @@ struct DecParams {
   void *o;
   int B, H, window, n_meta;
   float scale;
-  int gate_is_log;
+  int gate_is_log, gate_mode;
 };
 
 template <class T> struct Vec;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   }
   const f32x4 v4 = V::ld4(vt + col);
   // (5) gates
-  const float graw = tid < kF ? to_f32(((const T *)p.gate)[(size_t)bh * kF + tid]) : 0.0f;
+  const float graw = tid < kF ? to_f32(((const T *)p.gate)[gate_index(p.gate_mode, bh, p.H, 1, kF, 0, tid)]) : 0.0f;
   const float qn = tid < kD ? to_f32(qt[tid]) : 0.0f, kn = tid < kD ? to_f32(kt[tid]) : 0.0f;
 
   // window scores (ring slots) and q . k of the new token (waves 0-1)
@@ -278,6 +278,7 @@ hipError_t dispatch(const LayerArgs &a, int parts) {
   p.state = a.state; p.kcache = a.kcache; p.vcache = a.vcache; p.pos = a.pos; p.o = a.o;
   p.B = a.B; p.H = a.H; p.window = a.window; p.n_meta = a.n_meta; p.scale = a.scale;
   p.gate_is_log = a.gate_is_log ? 1 : 0;
+  p.gate_mode = a.gate_mode;
   const dim3 grid((unsigned)(a.B * a.H * kNSL)), block(kNT);
   if (parts & PART_SWA)
     hipLaunchKernelGGL((decode128_kernel<T, PART_BOTH>), grid, block, 0, a.stream, p);

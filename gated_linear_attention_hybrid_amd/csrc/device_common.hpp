@@ -33,6 +33,15 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 
 template <class T> __device__ __forceinline__ float ld(const T *p) { return to_f32(*p); }
 
+// Element offset of the gate of head bh (of H), token t (of L), feature r (of f)
+// for gate layout `mode`: 0 = one per feature [BH][L][f], 1 = one per token
+// [BH][L], 2 = one per head [H].  The decode step uses L = 1, t = 0.
+__device__ __forceinline__ size_t gate_index(int mode, size_t bh, int H, int L, int f, int t, int r) {
+  if (mode == 1) return bh * (size_t)L + t;
+  if (mode == 2) return bh % (size_t)H;
+  return (bh * (size_t)L + t) * f + r;
+}
+
 // Gate value Gamma in [0,1] from a logit (sigmoid) or from a log-gate (exp).
 __device__ __forceinline__ float gate_from(float g, bool gate_is_log) {
   if (gate_is_log) return exp_fast(g);

@@ -16,6 +16,9 @@ struct LayerArgs {
   float scale = 1.0f;
   bool bf16 = true;
   bool gate_is_log = false;
+  // gate layout: 0 = one per feature [BH][L][f], 1 = one per token [BH][L],
+  // 2 = one per head [H] (1 and 2 are log-gates)
+  int gate_mode = 0;
   const void *q = nullptr, *k = nullptr, *v = nullptr, *gate = nullptr;
   const void *wq = nullptr, *wk = nullptr;
   const float *meta = nullptr;

@@ -32,7 +32,7 @@ struct RecParams {
   const int32_t *pos;
   int B, H, L, d, dv, f, window, n_meta, nslices;
   float scale;
-  int gate_is_log;
+  int gate_is_log, gate_mode;
 };
 
 struct RecShared {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_prefill_kernel(RecParams p
   const T *q = (const T *)p.q + (size_t)bh * L * d;
   const T *k = (const T *)p.k + (size_t)bh * L * d;
   const T *v = (const T *)p.v + (size_t)bh * L * dv;
-  const T *g = GLA ? (const T *)p.gate + (size_t)bh * L * f : nullptr;
+  const T *g = (const T *)p.gate;
   const T *Wq = GLA ? (const T *)p.wq + (size_t)h * d * f2 : nullptr;
   const T *Wk = GLA ? (const T *)p.wk + (size_t)h * d * f2 : nullptr;
   const float *meta = p.n_meta ? p.meta + (size_t)h * p.n_meta : nullptr;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_prefill_kernel(RecParams p
     }
     if (GLA)
       for (int r = tid; r < f; r += kThreads)
-        sh.gam[r] = gate_from(ld(g + (size_t)t * f + r), p.gate_is_log);
+        sh.gam[r] = gate_from(ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t, r)), p.gate_is_log);
     if (tid < DVS) vt[tid] = (dv0 + tid < dv) ? ld(v + (size_t)t * dv + dv0 + tid) : 0.0f;
     __syncthreads();
     if (GLA) hedgehog_block<T>(sh, Wq, Wk, d, f2);
@@ -294,8 +294,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(RecParams p) {
     sh.xk[i] = ld(kt + i);
   }
   if (GLA) {
-    const T *gt = (const T *)p.gate + (size_t)bh * f;
-    for (int r = tid; r < f; r += kThreads) sh.gam[r] = gate_from(ld(gt + r), p.gate_is_log);
+    const T *gt = (const T *)p.gate;
+    for (int r = tid; r < f; r += kThreads)
+      sh.gam[r] = gate_from(ld(gt + gate_index(p.gate_mode, bh, p.H, 1, f, 0, r)), p.gate_is_log);
   }
   if (tid < DVS) vt[tid] = (dv0 + tid < dv) ? ld(vtg + dv0 + tid) : 0.0f;
   __syncthreads();
@@ -377,7 +378,7 @@ RecParams make_params(const LayerArgs &a) {
   p.o = a.o; p.kcache = a.kcache; p.vcache = a.vcache; p.pos = a.pos;
   p.B = a.B; p.H = a.H; p.L = a.L; p.d = a.d; p.dv = a.dv; p.f = a.f;
   p.window = a.window; p.n_meta = a.n_meta; p.nslices = 1;
-  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0;
+  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
   return p;
 }
 

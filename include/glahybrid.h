@@ -58,9 +58,18 @@ typedef enum {
 
 typedef enum { GLAH_BF16 = 0, GLAH_F32 = 1 } glah_dtype;
 
+/* Gate layouts.  The first two give one gate per feature channel; the last two
+ * are the scalar-decay variants (a per-token scalar as in Mamba-2, a fixed
+ * per-head decay as in RetNet: "LT2" technical summary, 2.1 architecture
+ * variants; "systematic analysis of hybrid linear attention", evaluated models),
+ * run through the same kernels as a log-gate broadcast over the features. */
 typedef enum {
-  GLAH_GATE_LOGITS = 0, /* gate holds g = W_gamma x; the layer applies sigmoid  */
-  GLAH_GATE_LOG = 1     /* gate holds log Gamma <= 0 directly (-inf allowed)    */
+  GLAH_GATE_LOGITS = 0,    /* gate [B][H][L][f] holds g = W_gamma x; Gamma = sigmoid(g) */
+  GLAH_GATE_LOG = 1,       /* gate [B][H][L][f] holds log Gamma <= 0 (-inf allowed)     */
+  GLAH_GATE_LOG_TOKEN = 2, /* gate [B][H][L] holds one log Gamma <= 0 per token, the
+                              same for every feature (decode: [B][H])                 */
+  GLAH_GATE_LOG_HEAD = 3   /* gate [H] holds one fixed log Gamma <= 0 per head, the same
+                              for every token and feature (decode: [H])               */
 } glah_gate_kind;
 
 typedef struct glah_desc {

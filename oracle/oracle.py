@@ -25,6 +25,32 @@ PART_GLA = 1
 PART_SWA = 2
 PART_BOTH = 3
 
+# Gate layouts (the same codes as the library's glah_gate_kind).  The scalar
+# ones are the fixed/scalar-decay variants the pages list beside GLA (a per-token
+# scalar as in Mamba-2, a fixed per-head decay as in RetNet: "LT2" technical
+# summary, 2.1 architecture variants; "systematic analysis of hybrid linear
+# attention", evaluated models): a log-gate equal for every feature.
+GATE_LOGITS = 0     # [B,H,L,f] logits
+GATE_LOG = 1        # [B,H,L,f] log Gamma
+GATE_LOG_TOKEN = 2  # [B,H,L] log Gamma of each token, every feature
+GATE_LOG_HEAD = 3   # [H] fixed log Gamma of each head, every token and feature
+
+
+def _gate_per_feature(g, kind, B, H, L, f):
+    """Per-feature gates [B,H,L,f] (L = None: decode [B,H,f]) and whether they
+    are log-gates, for gate layout ``kind``: scalar gates are broadcast."""
+    g = np.asarray(g, dtype=np.float64)
+    if kind in (GATE_LOGITS, GATE_LOG):
+        return g, kind == GATE_LOG
+    if kind == GATE_LOG_TOKEN:
+        shape = (B, H, f) if L is None else (B, H, L, f)
+        return np.ascontiguousarray(np.broadcast_to(g[..., None], shape)), True
+    if kind == GATE_LOG_HEAD:
+        shape = (B, H, f) if L is None else (B, H, L, f)
+        h = g.reshape(1, H, 1) if L is None else g.reshape(1, H, 1, 1)
+        return np.ascontiguousarray(np.broadcast_to(h, shape)), True
+    raise ValueError("unknown gate kind %r" % (kind,))
+
 _lock = threading.Lock()
 _default = None
 
@@ -81,20 +107,23 @@ class Oracle:
         self.lib.oracle_set_num_threads(int(n))
 
     def layer_fwd(self, q, k, v, g, wq, wk, meta, *, window, scale=None, gate_is_log=False,
-                  parts=PART_BOTH, state_in=None, return_state=False):
+                  parts=PART_BOTH, state_in=None, return_state=False, gate_kind=None):
         """Hybrid layer forward over whole sequences.
 
         q, k: [B,H,L,d]; v: [B,H,L,dv]; g: [B,H,L,f] gate logits (log-gates when
-        ``gate_is_log``); wq, wk: [H,d,f/2]; meta: [H,M] or None; state_in:
-        [B,H,f,dv] or None.  Returns o [B,H,L,dv] (and the final state when
-        ``return_state``).
+        ``gate_is_log``; other layouts with ``gate_kind``); wq, wk: [H,d,f/2];
+        meta: [H,M] or None; state_in: [B,H,f,dv] or None.  Returns o [B,H,L,dv]
+        (and the final state when ``return_state``).
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, H, L, d = q.shape
         dv = v.shape[-1]
         if parts & PART_GLA:
-            g, wq, wk = _f64(g), _f64(wq), _f64(wk)
-            f = g.shape[-1]
+            wq, wk = _f64(wq), _f64(wk)
+            f = 2 * wq.shape[-1]
+            kind = gate_kind if gate_kind is not None else (GATE_LOG if gate_is_log else GATE_LOGITS)
+            g, gate_is_log = _gate_per_feature(g, kind, B, H, L, f)
+            g = _f64(g)
         else:
             g = wq = wk = None
             f = state_in.shape[-2] if state_in is not None else 2
@@ -114,7 +143,7 @@ class Oracle:
         return (o, st) if return_state else o
 
     def decode_step(self, q, k, v, g, wq, wk, meta, state, kcache, vcache, pos, *, window,
-                    scale=None, gate_is_log=False, parts=PART_BOTH):
+                    scale=None, gate_is_log=False, parts=PART_BOTH, gate_kind=None):
         """One decode step; ``state``, ``kcache`` and ``vcache`` (float64,
         C-contiguous) are updated in place.  q,k: [B,H,d]; v: [B,H,dv]; g: [B,H,f];
         pos: [B] ints (tokens already consumed).  Returns o [B,H,dv]."""
@@ -125,6 +154,8 @@ class Oracle:
         B, H, d = q.shape
         dv = v.shape[-1]
         f = state.shape[-2]
+        kind = gate_kind if gate_kind is not None else (GATE_LOG if gate_is_log else GATE_LOGITS)
+        g, gate_is_log = _gate_per_feature(g, kind, B, H, None, f)
         g, wq, wk = _f64(g), _f64(wq), _f64(wk)
         meta = _f64(meta) if meta is not None else None
         n_meta = 0 if meta is None else meta.shape[-1]

@@ -87,9 +87,17 @@ def test_bad_descriptor_is_einval(lib, bad):
 
 
 def test_bad_gate_kind_is_einval(lib):
-    d = _desc()
-    d.gate_kind = 5
-    assert _hybrid(lib, d) == binding.GLAH_EINVAL
+    for kind in (4, 5, -1):
+        d = _desc()
+        d.gate_kind = kind
+        assert _hybrid(lib, d) == binding.GLAH_EINVAL
+
+
+def test_scalar_gate_kinds_are_valid_descriptors(lib):
+    for kind in (binding.GLAH_GATE_LOG_TOKEN, binding.GLAH_GATE_LOG_HEAD):
+        d = _desc()
+        d.gate_kind = kind
+        assert lib.glah_workspace_bytes(ctypes.byref(d)) != ctypes.c_size_t(-1).value
 
 
 def test_null_descriptor_is_einval(lib):
