@@ -24,7 +24,8 @@ GLAH_GATE_LOGITS, GLAH_GATE_LOG = 0, 1
 GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per token, [H] per head
 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
-           "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step")
+           "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step", "glah_bwd_workspace_bytes",
+           "hybrid_layer_bwd")
 
 
 class GlahError(RuntimeError):
@@ -68,6 +69,10 @@ def load(path: str = LIBRARY):
             lib.hybrid_layer_fwd.restype = i32
             lib.gla_decode_step.argtypes = [dp] + [vp] * 12 + [vp]
             lib.gla_decode_step.restype = i32
+            lib.glah_bwd_workspace_bytes.argtypes = [dp]
+            lib.glah_bwd_workspace_bytes.restype = sz
+            lib.hybrid_layer_bwd.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
+            lib.hybrid_layer_bwd.restype = i32
             _lib = lib
     return _lib
 
@@ -181,3 +186,45 @@ def gla_decode_step(q, k, v, gate, wq, wk, meta, state, kcache, vcache, pos, *, 
                                 _stream(stream))
     _check("gla_decode_step", st)
     return o
+
+
+def bwd_workspace_bytes(desc: GlahDesc) -> int:
+    n = load().glah_bwd_workspace_bytes(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlahError("glah_bwd_workspace_bytes", GLAH_EINVAL, "invalid argument")
+    return n
+
+
+def hybrid_layer_bwd(q, k, v, gate, wq, wk, meta, d_o, *, window, scale=0.0, gate_is_log=False,
+                     gate_kind=None, state_in=None, dstate_out=None, need_dstate_in=False, ws=None,
+                     stream=None):
+    """Gradient of hybrid_layer_fwd for the loss sum(o * d_o) + sum(S_final * dstate_out).
+
+    Returns a dict with the gradients named as the forward's inputs: q, k, v,
+    gate (the gate's layout and dtype), wq, wk ([H,d,f/2] fp32), meta ([H,M]
+    fp32, None without sinks) and state_in ([B,H,f,dv] fp32, when
+    ``need_dstate_in``)."""
+    B, H, L, d = q.shape
+    dv, f = v.shape[-1], 2 * wq.shape[-1]
+    n_meta = 0 if meta is None else meta.shape[-1]
+    desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, scale=scale,
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
+    dev = q.device
+    out = dict(q=torch.empty_like(q), k=torch.empty_like(k), v=torch.empty_like(v),
+               gate=torch.empty_like(gate),
+               wq=torch.empty(wq.shape, dtype=torch.float32, device=dev),
+               wk=torch.empty(wk.shape, dtype=torch.float32, device=dev),
+               meta=None if meta is None else torch.empty(meta.shape, dtype=torch.float32, device=dev),
+               state_in=(torch.empty((B, H, f, dv), dtype=torch.float32, device=dev)
+                         if need_dstate_in else None))
+    n = bwd_workspace_bytes(desc)
+    if ws is None and n:
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load().hybrid_layer_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
+                                 _p(meta), _p(state_in), _p(d_o), _p(dstate_out), _p(out["q"]),
+                                 _p(out["k"]), _p(out["v"]), _p(out["gate"]), _p(out["wq"]),
+                                 _p(out["wk"]), _p(out["meta"]), _p(out["state_in"]), _p(ws), nbytes,
+                                 _stream(stream))
+    _check("hybrid_layer_bwd", st)
+    return out

@@ -1,0 +1,714 @@
+// backward.hip -- gradient of the hybrid layer in its token-recurrent form.
+//
+// Gradients of L = <o, dO> + <S_final, dS_final> with respect to q, k, v, the
+// gate input (every layout), both Hedgehog projections, the meta-memory
+// scalars and the initial state: the parameters the two-stage training of
+// Lizard fits ("Lizard" technical summary, gist.science 2507.09025,
+// Methodology B; the layer itself is Methodology A.1 / A.2 / C).
+//
+// Gated part.  With b_t = sum_{r<=t} log Gamma_r (per feature), the output
+// o_t = sum_{s<=t} (phiq_t e^{b_t}) . (phik_s e^{-b_s}) v_s + phiq_t e^{b_t} S_0,
+// so with dS_t = phiq_t dO_t^T + diag(Gamma_{t+1}) dS_{t+1} (dS_{L-1} starting
+// from dS_final):
+//   dphiq_t = S_t dO_t,  dphik_t = dS_t v_t,  dv_t += dS_t^T phik_t,
+//   d b_t   = phiq_t . dphiq_t - phik_t . dphik_t  (+ S_{L-1} . dS_final at t = L-1),
+//   d log Gamma_t = sum_{s>=t} d b_s,  dS_0 = Gamma_0 dS_0^(t=0).
+// Kernels: a prologue (phi and Gamma of every token), a forward state sweep
+// (dphiq), a reverse sweep (dphik, dv), a reverse scan of d b, and a per-token
+// kernel that takes phi's softmax Jacobian back to dq, dk, accumulates the
+// projection gradients and writes the gate gradient in its layout.
+//
+// Window part.  P_tj = e^{s_tj - lse_t}, with the sinks' e^{t_m} inside the
+// normaliser; D_t = dO_t . o_swa,t; ds_tj = P_tj (dO_t . v_j - D_t); a query
+// kernel gives dq, lse, D and the sink gradient -sum_t P_tm D_t; a key kernel
+// gives dk_j = scale sum_t ds_tj q_t and dv_j = sum_t P_tj dO_t.
+//
+// Every reduction is done in a fixed order into per-block partials (no atomics),
+// so the gradients are bitwise repeatable.  All arithmetic is fp32.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace glah {
+
+namespace {
+
+constexpr int kBT = 256;         // threads of every backward block
+constexpr int kSliceCols = 32;   // d_v columns of one sweep block
+constexpr int kPrepTok = 16;     // tokens of one prologue block
+constexpr int kFeatTok = 64;     // tokens of one feature-gradient block
+constexpr int kSwaTok = 16;      // query (key) tokens of one window block
+constexpr int kMaxF2 = kBwdMaxF / 2;
+
+template <class T> __device__ __forceinline__ f32x4 ld4(const T *p);
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) { return *(const f32x4 *)p; }
+template <> __device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
+  const bf16x4 x = *(const bf16x4 *)p;
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+// sum over lanes l ^ 1, l ^ 2, l ^ 4 (the 8 column groups of one row group)
+__device__ __forceinline__ float sum8(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x + __shfl_xor(x, 4);
+}
+// sum over lanes l ^ 8, l ^ 16, l ^ 32 (the 8 row groups of one wave)
+__device__ __forceinline__ float sum_rows8(float x) {
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+struct BwdParams {
+  const void *q, *k, *v, *gate, *wq, *wk, *dout;
+  const float *meta, *state_in, *dstate_out;
+  void *gq, *gk, *gv, *gg;  // dq, dk, dv, dgate
+  float *dwq, *dwk, *dmeta, *dstate_in;
+  // workspace (fp32)
+  float *pq, *pk, *gam, *da;  // [N][f]
+  float *dpq, *dpk;           // [nsl][N][f]
+  float *dvg;                 // [nw][N][dv]
+  float *xs;                  // [2][BH][nsl][f]: S_{L-1}.dS_final, d log Gamma_0
+  float *lse, *del;           // [N]
+  float *dqs, *dks;           // [N][d]
+  float *dvs;                 // [N][dv]
+  float *wqp, *wkp;           // [BH][nft][d][f2]
+  float *gp;                  // [BH][nft]
+  float *mp;                  // [BH][nsb][n_meta]
+  int B, H, L, d, dv, f, f2, lf2, window, n_meta;
+  int nsl, nw, nft, nsb, npt;
+  float scale;
+  int gate_is_log, gate_mode, gla, swa;
+};
+
+// ---------------------------------------------------------------------------
+// Prologue: phi(q_t), phi(k_t) and Gamma_t of every token.  Block = (b, h,
+// kPrepTok tokens); the two projections are staged in LDS as fp32.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdParams p) {
+  __shared__ float W[2][kBwdMaxD * kMaxF2];
+  __shared__ float X[2][kPrepTok][kBwdMaxD];
+  __shared__ float U[2][kPrepTok][kMaxF2];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / p.npt, tile = blockIdx.x % p.npt;
+  const int h = bh % p.H, d = p.d, f = p.f, f2 = p.f2, L = p.L;
+  const int t0 = tile * kPrepTok, nt = min(kPrepTok, L - t0);
+  const size_t row0 = (size_t)bh * L + t0;
+  const T *wq = (const T *)p.wq + (size_t)h * d * f2;
+  const T *wk = (const T *)p.wk + (size_t)h * d * f2;
+  for (int i = tid; i < d * f2; i += kBT) {
+    W[0][i] = ld(wq + i);
+    W[1][i] = ld(wk + i);
+  }
+  for (int i = tid; i < nt * d; i += kBT) {
+    const int tt = i / d, e = i - tt * d;
+    X[0][tt][e] = ld((const T *)p.q + (row0 + tt) * d + e);
+    X[1][tt][e] = ld((const T *)p.k + (row0 + tt) * d + e);
+  }
+  __syncthreads();
+  for (int o = tid; o < 2 * nt * f2; o += kBT) {
+    const int m = o / (nt * f2), r = o - m * nt * f2;
+    const int tt = r / f2, j = r - tt * f2;
+    float acc = 0.0f;
+    for (int e = 0; e < d; ++e) acc += X[m][tt][e] * W[m][e * f2 + j];
+    U[m][tt][j] = acc;
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int row = wave; row < 2 * nt; row += kBT / 64) {
+    const int m = row / nt, tt = row - m * nt;
+    const bool ok = lane < f2;
+    const float u = ok ? U[m][tt][lane] : 0.0f;
+    const float mx = wave_max(ok ? u : -INFINITY), mn = wave_min(ok ? u : INFINITY);
+    const float ep = ok ? exp_fast(u - mx) : 0.0f, en = ok ? exp_fast(mn - u) : 0.0f;
+    const float zp = wave_sum(ep), zn = wave_sum(en);
+    float *dst = (m ? p.pk : p.pq) + (row0 + tt) * f;
+    if (ok) {
+      dst[lane] = ep / zp;
+      dst[f2 + lane] = en / zn;
+    }
+  }
+  const T *g = (const T *)p.gate;
+  for (int i = tid; i < nt * f; i += kBT) {
+    const int tt = i / f, r = i - tt * f;
+    p.gam[(row0 + tt) * f + r] =
+        gate_from(ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t0 + tt, r)), p.gate_is_log);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State sweeps.  Block = (b, h, 32-column slice of d_v); lane l of wave w owns
+// rows 4 (8 w + l / 8) .. +3 and columns 4 (l % 8) .. +3 of the slice, so a
+// row sum over the slice is a sum over 8 adjacent lanes and a column sum over
+// the wave's 32 rows is a sum over lanes l ^ 8, l ^ 16, l ^ 32.  No barriers:
+// every wave is independent; waves whose rows lie beyond f leave at once.
+struct SweepLane {
+  int r0, c0;
+  bool rok, cok;
+};
+
+__device__ __forceinline__ SweepLane sweep_lane(const BwdParams &p, int slice) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  SweepLane s;
+  s.r0 = 4 * (8 * w + (l >> 3));
+  s.c0 = slice * kSliceCols + 4 * (l & 7);
+  s.rok = s.r0 < p.f;
+  s.cok = s.c0 < p.dv;
+  return s;
+}
+
+// Forward sweep: S_t = diag(Gamma_t) S_{t-1} + phik_t v_t^T, then the slice's
+// part of dphiq_t = S_t dO_t; at the end the slice's part of S_{L-1} . dS_final.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
+  const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
+  if (32 * (int)(threadIdx.x >> 6) >= p.f) return;
+  const SweepLane s = sweep_lane(p, slice);
+  const int L = p.L, f = p.f, dv = p.dv;
+  const size_t N = (size_t)p.B * p.H * L;
+  const size_t rowf = (size_t)bh * L * f + s.r0;
+  const size_t rowv = (size_t)bh * L * dv + s.c0;
+  const T *v = (const T *)p.v + rowv;
+  const T *dO = (const T *)p.dout + rowv;
+  float *dpq = p.dpq + (size_t)slice * N * f + rowf;
+  const bool lead = (threadIdx.x & 7) == 0;
+
+  f32x4 S[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    S[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.state_in && s.rok && s.cok) S[i] = *(const f32x4 *)(p.state_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0);
+  }
+  const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < L; ++t) {
+    const f32x4 g4 = s.rok ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
+    const f32x4 k4 = s.rok ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
+    const f32x4 v4 = s.cok ? ld4(v + (size_t)t * dv) : z4;
+    const f32x4 o4 = s.cok ? ld4(dO + (size_t)t * dv) : z4;
+    f32x4 part;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = g4[i] * S[i][j] + k4[i] * v4[j];
+      part[i] = sum8(dot4(S[i], o4));
+    }
+    if (lead && s.rok) *(f32x4 *)(dpq + (size_t)t * f) = part;
+  }
+  if (p.dstate_out) {
+    f32x4 part;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 d4 = (s.rok && s.cok) ? *(const f32x4 *)(p.dstate_out + ((size_t)bh * f + s.r0 + i) * dv + s.c0) : z4;
+      part[i] = sum8(dot4(S[i], d4));
+    }
+    if (lead && s.rok) *(f32x4 *)(p.xs + ((size_t)bh * p.nsl + slice) * f + s.r0) = part;
+  }
+}
+
+// Reverse sweep: dS_t = phiq_t dO_t^T + diag(Gamma_{t+1}) dS_{t+1} from dS_final;
+// the slice's part of dphik_t = dS_t v_t, the wave's part of dS_t^T phik_t, and
+// at the end dS_0-gradient = diag(Gamma_0) dS_0.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
+  const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
+  const int wave = threadIdx.x >> 6;
+  if (32 * wave >= p.f) return;
+  const SweepLane s = sweep_lane(p, slice);
+  const int L = p.L, f = p.f, dv = p.dv;
+  const size_t N = (size_t)p.B * p.H * L;
+  const size_t rowf = (size_t)bh * L * f + s.r0;
+  const size_t rowv = (size_t)bh * L * dv + s.c0;
+  const T *v = (const T *)p.v + rowv;
+  const T *dO = (const T *)p.dout + rowv;
+  float *dpk = p.dpk + (size_t)slice * N * f + rowf;
+  float *dvg = p.dvg + (size_t)wave * N * dv + rowv;
+  const int l = threadIdx.x & 63;
+
+  const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 dS[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dS[i] = z4;
+    if (p.dstate_out && s.rok && s.cok)
+      dS[i] = *(const f32x4 *)(p.dstate_out + ((size_t)bh * f + s.r0 + i) * dv + s.c0);
+  }
+  f32x4 gn = {1.0f, 1.0f, 1.0f, 1.0f};
+  for (int t = L - 1; t >= 0; --t) {
+    const f32x4 q4 = s.rok ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
+    const f32x4 k4 = s.rok ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
+    const f32x4 g4 = s.rok ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
+    const f32x4 v4 = s.cok ? ld4(v + (size_t)t * dv) : z4;
+    const f32x4 o4 = s.cok ? ld4(dO + (size_t)t * dv) : z4;
+    f32x4 a, c = z4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dS[i][j] = gn[i] * dS[i][j] + q4[i] * o4[j];
+      a[i] = sum8(dot4(dS[i], v4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] += dS[i][j] * k4[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = sum_rows8(c[j]);
+    if ((l & 7) == 0 && s.rok) *(f32x4 *)(dpk + (size_t)t * f) = a;
+    if (l < 8 && s.cok) *(f32x4 *)(dvg + (size_t)t * dv) = c;
+    gn = g4;
+  }
+  if (p.dstate_in && s.rok && s.cok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = gn[i] * dS[i][j];
+      *(f32x4 *)(p.dstate_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0) = r;
+    }
+  }
+  // the slice's part of d log Gamma_0 = Gamma_0 (S_in . dS_0), taken directly:
+  // without an initial state it is exactly zero, which a sum of the d b_t
+  // reaches only up to rounding
+  f32x4 x0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 s4 = (p.state_in && s.rok && s.cok)
+                         ? *(const f32x4 *)(p.state_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0) : z4;
+    x0[i] = gn[i] * sum8(dot4(s4, dS[i]));
+  }
+  if ((l & 7) == 0 && s.rok) *(f32x4 *)(p.xs + ((size_t)(p.B * p.H + bh) * p.nsl + slice) * f + s.r0) = x0;
+}
+
+// d log Gamma_t = sum_{s>=t} d b_s with d b_t = phiq_t . dphiq_t - phik_t .
+// dphik_t.  Both ends are known exactly (d log Gamma_{L-1} = d b_{L-1} +
+// S_{L-1} . dS_final, d log Gamma_0 from the reverse sweep), so each half of the
+// sequence is summed from its own end: the rounding of the running sum then
+// spans at most L/2 terms and the exact zeros (no initial state) stay exact.
+// One thread per (b, h, feature); the slice partials of dphiq and dphik are
+// summed here and written back into slice 0.
+__global__ __launch_bounds__(kBT) void bwd_gate_scan_kernel(BwdParams p) {
+  const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
+  const int f = p.f, L = p.L;
+  const size_t BH = (size_t)p.B * p.H;
+  if (idx >= BH * f) return;
+  const size_t bh = idx / f, r = idx - bh * f;
+  const size_t NF = BH * L * f;
+  auto db = [&](int t) {
+    const size_t off = (bh * L + t) * f + r;
+    float dq = 0.0f, dk = 0.0f;
+    for (int sl = 0; sl < p.nsl; ++sl) {
+      dq += p.dpq[sl * NF + off];
+      dk += p.dpk[sl * NF + off];
+    }
+    if (p.nsl > 1) {
+      p.dpq[off] = dq;
+      p.dpk[off] = dk;
+    }
+    return p.pq[off] * dq - p.pk[off] * dk;
+  };
+  const int half = (L + 1) / 2;
+  float acc = 0.0f;
+  if (p.dstate_out)
+    for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[(bh * p.nsl + sl) * f + r];
+  for (int t = L - 1; t >= half; --t) {
+    acc += db(t);
+    p.da[(bh * L + t) * f + r] = acc;
+  }
+  acc = 0.0f;
+  for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[((BH + bh) * p.nsl + sl) * f + r];
+  for (int t = 0; t < half; ++t) {
+    p.da[(bh * L + t) * f + r] = acc;
+    acc -= db(t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token gradients.  Block = (b, h, kFeatTok tokens).  For each token: the
+// softmax Jacobian of both halves of phi, dq and dk (plus the window part),
+// dv (both parts), the gate gradient in its layout, and this block's share of
+// dWphi_q = sum_t q_t^T du_q,t and dWphi_k.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
+  __shared__ float W[2][kBwdMaxD * kMaxF2];
+  __shared__ float X[2][kBwdMaxD];
+  __shared__ float DU[2][kMaxF2];
+  __shared__ float red[kBT / 64];
+  constexpr int NP = kBwdMaxD * kMaxF2 / kBT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x / p.nft, tile = blockIdx.x % p.nft;
+  const int h = bh % p.H, d = p.d, dv = p.dv, f = p.f, f2 = p.f2, L = p.L;
+  const int t0 = tile * kFeatTok, nt = min(kFeatTok, L - t0);
+  const size_t N = (size_t)p.B * p.H * L;
+  const bool gla = p.gla, swa = p.swa;
+  if (gla) {
+    const T *wq = (const T *)p.wq + (size_t)h * d * f2;
+    const T *wk = (const T *)p.wk + (size_t)h * d * f2;
+    for (int i = tid; i < d * f2; i += kBT) {
+      W[0][i] = ld(wq + i);
+      W[1][i] = ld(wk + i);
+    }
+  }
+  const int jj = tid & (f2 - 1);
+  const int i0 = tid >> p.lf2, istep = kBT >> p.lf2;
+  float aq[NP], ak[NP];
+#pragma unroll
+  for (int n = 0; n < NP; ++n) aq[n] = ak[n] = 0.0f;
+  float gsum = 0.0f;
+  const T *g = (const T *)p.gate;
+  T *dg = (T *)p.gg;
+
+  for (int tt = 0; tt < nt; ++tt) {
+    const int t = t0 + tt;
+    const size_t row = (size_t)bh * L + t;
+    __syncthreads();
+    if (gla) {
+      const int m = tid >> 7, i = tid & 127;
+      if (i < d) X[m][i] = ld((const T *)(m ? p.k : p.q) + row * d + i);
+      if (wave < 2) {
+        const float *ph = (wave ? p.pk : p.pq) + row * f;
+        const float *dph = (wave ? p.dpk : p.dpq) + row * f;
+        const bool ok = lane < f2;
+        const float pp = ok ? ph[lane] : 0.0f, dp = ok ? dph[lane] : 0.0f;
+        const float pn = ok ? ph[f2 + lane] : 0.0f, dn = ok ? dph[f2 + lane] : 0.0f;
+        const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
+        if (ok) DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
+      } else {
+        float tsum = 0.0f;
+        for (int r = tid - 128; r < f; r += 128) {
+          const float da = p.da[row * f + r];
+          if (p.gate_mode == 0) {
+            const size_t gi = row * f + r;
+            const float val = p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(ld(g + gi)));
+            dg[gi] = from_f32<T>(val);
+          } else {
+            tsum += da;
+          }
+        }
+        if (p.gate_mode == 1) {
+          tsum = wave_sum(tsum);
+          if (lane == 0) red[wave] = tsum;
+        } else if (p.gate_mode == 2) {
+          gsum += tsum;
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int m = tid >> 7, i = tid & 127;
+      if (i < d) {
+        float acc = 0.0f;
+        if (gla)
+          for (int j = 0; j < f2; ++j) acc += DU[m][j] * W[m][i * f2 + j];
+        if (swa) acc += (m ? p.dks : p.dqs)[row * d + i];
+        ((T *)(m ? p.gk : p.gq))[row * d + i] = from_f32<T>(acc);
+      }
+    }
+    for (int c = tid; c < dv; c += kBT) {
+      float acc = 0.0f;
+      if (gla)
+        for (int w = 0; w < p.nw; ++w) acc += p.dvg[((size_t)w * N + row) * dv + c];
+      if (swa) acc += p.dvs[row * dv + c];
+      ((T *)p.gv)[row * dv + c] = from_f32<T>(acc);
+    }
+    if (gla && p.gate_mode == 1 && tid == 0) dg[row] = from_f32<T>(red[2] + red[3]);
+    if (gla) {
+      const float duq = DU[0][jj], duk = DU[1][jj];
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        const int i = i0 + n * istep;
+        if (i < d) {
+          aq[n] += X[0][i] * duq;
+          ak[n] += X[1][i] * duk;
+        }
+      }
+    }
+  }
+  if (!gla) return;
+  const size_t base = ((size_t)bh * p.nft + tile) * d * f2;
+#pragma unroll
+  for (int n = 0; n < NP; ++n) {
+    const int i = i0 + n * istep;
+    if (i < d) {
+      p.wqp[base + (size_t)i * f2 + jj] = aq[n];
+      p.wkp[base + (size_t)i * f2 + jj] = ak[n];
+    }
+  }
+  if (p.gate_mode == 2) {
+    __syncthreads();
+    const float s = wave_sum(gsum);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    if (tid == 0) p.gp[(size_t)bh * p.nft + tile] = red[2] + red[3];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window part, query side.  One wave per query token, kSwaTok tokens a block.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_swa_q_kernel(BwdParams p) {
+  __shared__ __align__(16) float QS[kBT / 64][kBwdMaxD];
+  __shared__ __align__(16) float DO[kBT / 64][kBwdMaxD];
+  __shared__ float SC[kBT / 64][kBwdMaxWindow];
+  __shared__ float MR[kBT / 64][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x / p.nsb, blk = blockIdx.x % p.nsb;
+  const int h = bh % p.H, d = p.d, dv = p.dv, L = p.L;
+  const T *q = (const T *)p.q, *k = (const T *)p.k, *v = (const T *)p.v, *dO = (const T *)p.dout;
+  const bool sink = lane < p.n_meta;
+  const float mt = sink ? p.meta[(size_t)h * p.n_meta + lane] : -INFINITY;
+  const float mmax = wave_max(mt);
+  float macc = 0.0f;
+  float *sc = SC[wave];
+  for (int tt = wave; tt < kSwaTok; tt += kBT / 64) {
+    const int t = blk * kSwaTok + tt;
+    if (t >= L) break;
+    const size_t row = (size_t)bh * L + t;
+    for (int e = lane; e < d; e += 64) QS[wave][e] = ld(q + row * d + e);
+    for (int c = lane; c < dv; c += 64) DO[wave][c] = ld(dO + row * dv + c);
+    __builtin_amdgcn_wave_barrier();
+    const int n = min(t + 1, p.window);
+    float lmax = -INFINITY;
+    for (int i = lane; i < n; i += 64) {
+      const T *kr = k + (row - i) * d;
+      float acc = 0.0f;
+      for (int e = 0; e < d; e += 4) acc += dot4(ld4(kr + e), *(const f32x4 *)&QS[wave][e]);
+      const float sv = p.scale * acc;
+      sc[i] = sv;
+      lmax = fmaxf(lmax, sv);
+    }
+    const float m = fmaxf(wave_max(lmax), mmax);
+    float z = 0.0f;
+    for (int i = lane; i < n; i += 64) z += exp_fast(sc[i] - m);
+    z = wave_sum(z) + wave_sum(sink ? exp_fast(mt - m) : 0.0f);
+    const float iz = 1.0f / z;
+    for (int i = lane; i < n; i += 64) sc[i] = exp_fast(sc[i] - m) * iz;
+    __builtin_amdgcn_wave_barrier();
+    float dsum = 0.0f;
+    for (int c = lane; c < dv; c += 64) {
+      float o = 0.0f;
+      for (int i = 0; i < n; ++i) o += sc[i] * ld(v + (row - i) * dv + c);
+      dsum += o * DO[wave][c];
+    }
+    const float D = wave_sum(dsum);
+    for (int i = lane; i < n; i += 64) {
+      const T *vr = v + (row - i) * dv;
+      float dp = 0.0f;
+      for (int c = 0; c < dv; c += 4) dp += dot4(ld4(vr + c), *(const f32x4 *)&DO[wave][c]);
+      sc[i] = sc[i] * (dp - D);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < d; e += 64) {
+      float acc = 0.0f;
+      for (int i = 0; i < n; ++i) acc += sc[i] * ld(k + (row - i) * d + e);
+      p.dqs[row * d + e] = p.scale * acc;
+    }
+    if (sink) macc -= exp_fast(mt - m) * iz * D;
+    if (lane == 0) {
+      p.lse[row] = m + logf(z);
+      p.del[row] = D;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (p.n_meta) {
+    MR[wave][lane] = macc;
+    __syncthreads();
+    if (tid < p.n_meta) {
+      float s = 0.0f;
+      for (int w = 0; w < kBT / 64; ++w) s += MR[w][tid];
+      p.mp[((size_t)bh * p.nsb + blk) * p.n_meta + tid] = s;
+    }
+  }
+}
+
+// Window part, key side.  One wave per key token j: the queries t in
+// [j, j + w - 1] that see it.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_swa_kv_kernel(BwdParams p) {
+  __shared__ __align__(16) float KS[kBT / 64][kBwdMaxD];
+  __shared__ __align__(16) float VS[kBT / 64][kBwdMaxD];
+  __shared__ float PS[kBT / 64][kBwdMaxWindow];
+  __shared__ float DS[kBT / 64][kBwdMaxWindow];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x / p.nsb, blk = blockIdx.x % p.nsb;
+  const int d = p.d, dv = p.dv, L = p.L;
+  const T *q = (const T *)p.q, *k = (const T *)p.k, *v = (const T *)p.v, *dO = (const T *)p.dout;
+  for (int jt = wave; jt < kSwaTok; jt += kBT / 64) {
+    const int j = blk * kSwaTok + jt;
+    if (j >= L) break;
+    const size_t row = (size_t)bh * L + j;
+    for (int e = lane; e < d; e += 64) KS[wave][e] = ld(k + row * d + e);
+    for (int c = lane; c < dv; c += 64) VS[wave][c] = ld(v + row * dv + c);
+    __builtin_amdgcn_wave_barrier();
+    const int n = min(p.window, L - j);
+    for (int i = lane; i < n; i += 64) {
+      const size_t tr = row + i;
+      const T *qr = q + tr * d;
+      float s = 0.0f;
+      for (int e = 0; e < d; e += 4) s += dot4(ld4(qr + e), *(const f32x4 *)&KS[wave][e]);
+      const float P = exp_fast(p.scale * s - p.lse[tr]);
+      const T *orow = dO + tr * dv;
+      float dp = 0.0f;
+      for (int c = 0; c < dv; c += 4) dp += dot4(ld4(orow + c), *(const f32x4 *)&VS[wave][c]);
+      PS[wave][i] = P;
+      DS[wave][i] = P * (dp - p.del[tr]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < d; e += 64) {
+      float acc = 0.0f;
+      for (int i = 0; i < n; ++i) acc += DS[wave][i] * ld(q + (row + i) * d + e);
+      p.dks[row * d + e] = p.scale * acc;
+    }
+    for (int c = lane; c < dv; c += 64) {
+      float acc = 0.0f;
+      for (int i = 0; i < n; ++i) acc += PS[wave][i] * ld(dO + (row + i) * dv + c);
+      p.dvs[row * dv + c] = acc;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sums of the per-block partials over batch rows and token blocks: dWphi_q,
+// dWphi_k [H][d][f/2], the sink gradients [H][n_meta] and, for a per-head
+// gate, its gradient [H].  Fixed order, one output per thread.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
+  const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
+  const size_t per = (size_t)p.d * p.f2;
+  const size_t nwt = p.gla ? (size_t)p.H * per : 0;
+  const size_t nm = p.swa ? (size_t)p.H * p.n_meta : 0;
+  const size_t ng = (p.gla && p.gate_mode == 2) ? (size_t)p.H : 0;
+  if (idx < 2 * nwt) {
+    const int m = idx >= nwt;
+    const size_t e = idx - m * nwt, h = e / per, r = e - h * per;
+    const float *src = m ? p.wkp : p.wqp;
+    float acc = 0.0f;
+    for (int b = 0; b < p.B; ++b)
+      for (int tl = 0; tl < p.nft; ++tl) acc += src[(((size_t)b * p.H + h) * p.nft + tl) * per + r];
+    (m ? p.dwk : p.dwq)[e] = acc;
+  } else if (idx < 2 * nwt + nm) {
+    const size_t e = idx - 2 * nwt, h = e / p.n_meta, mm = e - h * p.n_meta;
+    float acc = 0.0f;
+    for (int b = 0; b < p.B; ++b)
+      for (int bl = 0; bl < p.nsb; ++bl) acc += p.mp[(((size_t)b * p.H + h) * p.nsb + bl) * p.n_meta + mm];
+    p.dmeta[e] = acc;
+  } else if (idx < 2 * nwt + nm + ng) {
+    const size_t h = idx - 2 * nwt - nm;
+    float acc = 0.0f;
+    for (int b = 0; b < p.B; ++b)
+      for (int tl = 0; tl < p.nft; ++tl) acc += p.gp[((size_t)b * p.H + h) * p.nft + tl];
+    ((T *)p.gg)[h] = from_f32<T>(acc);
+  }
+}
+
+// Workspace layout, in floats; every region starts on a 256-byte boundary.
+struct BwdLayout {
+  size_t pq, pk, gam, da, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, total;
+};
+
+size_t up64(size_t n) { return (n + 63) & ~(size_t)63; }
+
+BwdLayout bwd_layout(const LayerArgs &a, int parts) {
+  const size_t BH = (size_t)a.B * a.H, N = BH * a.L;
+  const size_t nsl = (a.dv + kSliceCols - 1) / kSliceCols, nw = (a.f + 31) / 32;
+  const size_t nft = (a.L + kFeatTok - 1) / kFeatTok, nsb = (a.L + kSwaTok - 1) / kSwaTok;
+  const bool gla = parts & PART_GLA, swa = parts & PART_SWA;
+  BwdLayout o;
+  size_t at = 0;
+  auto take = [&](size_t n) { const size_t r = at; at += up64(n); return r; };
+  const size_t nf = gla ? N * a.f : 0;
+  o.pq = take(nf); o.pk = take(nf); o.gam = take(nf); o.da = take(nf);
+  o.dpq = take(nsl * nf); o.dpk = take(nsl * nf);
+  o.dvg = take(gla ? nw * N * a.dv : 0);
+  o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
+  o.lse = take(swa ? N : 0); o.del = take(swa ? N : 0);
+  o.dqs = take(swa ? N * a.d : 0); o.dks = take(swa ? N * a.d : 0); o.dvs = take(swa ? N * a.dv : 0);
+  const size_t wp = gla ? BH * nft * a.d * (a.f / 2) : 0;
+  o.wqp = take(wp); o.wkp = take(wp);
+  o.gp = take(gla ? BH * nft : 0);
+  o.mp = take(swa ? BH * nsb * a.n_meta : 0);
+  o.total = at;
+  return o;
+}
+
+template <class T>
+hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
+  BwdParams p = {};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.wq = a.wq; p.wk = a.wk; p.dout = g.dout;
+  p.meta = a.meta; p.state_in = a.state_in; p.dstate_out = g.dstate_out;
+  p.gq = g.dq; p.gk = g.dk; p.gv = g.dv; p.gg = g.dgate;
+  p.dwq = g.dwq; p.dwk = g.dwk; p.dmeta = g.dmeta; p.dstate_in = g.dstate_in;
+  const BwdLayout lay = bwd_layout(a, parts);
+  float *ws = (float *)a.ws;
+  p.pq = ws + lay.pq; p.pk = ws + lay.pk; p.gam = ws + lay.gam; p.da = ws + lay.da;
+  p.dpq = ws + lay.dpq; p.dpk = ws + lay.dpk; p.dvg = ws + lay.dvg; p.xs = ws + lay.xs;
+  p.lse = ws + lay.lse; p.del = ws + lay.del; p.dqs = ws + lay.dqs; p.dks = ws + lay.dks;
+  p.dvs = ws + lay.dvs; p.wqp = ws + lay.wqp; p.wkp = ws + lay.wkp; p.gp = ws + lay.gp; p.mp = ws + lay.mp;
+  p.B = a.B; p.H = a.H; p.L = a.L; p.d = a.d; p.dv = a.dv; p.f = a.f; p.f2 = a.f / 2;
+  p.lf2 = 0;
+  while ((1 << p.lf2) < p.f2) ++p.lf2;
+  p.window = a.window; p.n_meta = a.n_meta;
+  p.nsl = (a.dv + kSliceCols - 1) / kSliceCols; p.nw = (a.f + 31) / 32;
+  p.nft = (a.L + kFeatTok - 1) / kFeatTok; p.nsb = (a.L + kSwaTok - 1) / kSwaTok;
+  p.npt = (a.L + kPrepTok - 1) / kPrepTok;
+  p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
+  p.gla = (parts & PART_GLA) != 0; p.swa = (parts & PART_SWA) != 0;
+  if (!p.gla) p.dstate_out = nullptr;
+
+  const unsigned BH = (unsigned)(a.B * a.H);
+  const dim3 block(kBT);
+  hipError_t e = hipSuccess;
+  auto launched = [&]() { if (e == hipSuccess) e = hipGetLastError(); return e == hipSuccess; };
+  if (p.gla && a.L > 0) {
+    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(BH * p.npt), block, 0, a.stream, p);
+    if (!launched()) return e;
+  }
+  if (p.swa && a.L > 0) {
+    hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+    if (!launched()) return e;
+    hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+    if (!launched()) return e;
+  }
+  if (p.gla && BH > 0) {
+    // with no tokens the sweeps still pass dS_final through to dS_0
+    hipLaunchKernelGGL(bwd_fwd_sweep_kernel<T>, dim3(BH * p.nsl), block, 0, a.stream, p);
+    if (!launched()) return e;
+    hipLaunchKernelGGL(bwd_rev_sweep_kernel<T>, dim3(BH * p.nsl), block, 0, a.stream, p);
+    if (!launched()) return e;
+    if (a.L > 0) {
+      hipLaunchKernelGGL(bwd_gate_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
+                         a.stream, p);
+      if (!launched()) return e;
+    }
+  }
+  if (a.L > 0 && BH > 0) {
+    hipLaunchKernelGGL(bwd_feature_kernel<T>, dim3(BH * p.nft), block, 0, a.stream, p);
+    if (!launched()) return e;
+  }
+  const size_t nred = (p.gla ? 2 * (size_t)a.H * a.d * p.f2 : 0) + (p.swa ? (size_t)a.H * a.n_meta : 0) +
+                      ((p.gla && a.gate_mode == 2) ? (size_t)a.H : 0);
+  if (nred) {
+    hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3((unsigned)((nred + kBT - 1) / kBT)), block, 0, a.stream, p);
+    if (!launched()) return e;
+  }
+  return e;
+}
+
+}  // namespace
+
+bool bwd_supported(const LayerArgs &a, int parts) {
+  if (a.d > kBwdMaxD || a.dv > kBwdMaxD || (a.d & 3) || (a.dv & 3)) return false;
+  if (parts & PART_GLA) {
+    const int f2 = a.f / 2;
+    if (a.f > kBwdMaxF || (a.f & 3) || (f2 & (f2 - 1))) return false;
+  }
+  if ((parts & PART_SWA) && (a.window > kBwdMaxWindow || a.n_meta > 64)) return false;
+  return true;
+}
+
+size_t bwd_workspace_bytes(const LayerArgs &a, int parts) { return bwd_layout(a, parts).total * sizeof(float); }
+
+hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts) {
+  return a.bf16 ? bwd_dispatch<bf16>(a, g, parts) : bwd_dispatch<float>(a, g, parts);
+}
+
+}  // namespace glah

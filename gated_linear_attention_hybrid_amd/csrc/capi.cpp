@@ -212,4 +212,46 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t, const void *
   }
 }
 
+size_t glah_bwd_workspace_bytes(const glah_desc *desc) {
+  LayerArgs a;
+  if (!desc || check_desc(desc, Op::kHybrid, a) != GLAH_OK) return (size_t)-1;
+  if (!bwd_supported(a, PART_BOTH)) return 0;
+  return bwd_workspace_bytes(a, PART_BOTH);
+}
+
+glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k, const void *v,
+                             const void *gate, const void *wphi_q, const void *wphi_k,
+                             const float *meta, const float *state_in, const void *d_o,
+                             const float *dstate_out, void *dq, void *dk, void *dv, void *dgate,
+                             float *dwphi_q, float *dwphi_k, float *dmeta, float *dstate_in, void *ws,
+                             size_t ws_bytes, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kHybrid, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    const bool heads = a.H > 0;
+    const bool head_gate = a.gate_mode == 2 && heads;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work || head_gate) ||
+        !req(d_o, work) || !req(dq, work) || !req(dk, work) || !req(dv, work) ||
+        !req(dgate, work || head_gate) || !req(wphi_q, heads) || !req(wphi_k, heads) ||
+        !req(dwphi_q, heads) || !req(dwphi_k, heads) || !req(meta, a.n_meta > 0 && heads) ||
+        !req(dmeta, a.n_meta > 0 && heads) || !opt(state_in) || !opt(dstate_out) || !opt(dstate_in) ||
+        !opt(ws))
+      return GLAH_EINVAL;
+    if (!bwd_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
+    const size_t need = bwd_workspace_bytes(a, PART_BOTH);
+    if (ws_bytes < need || (!ws && need)) return GLAH_EWORKSPACE;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
+    a.state_in = state_in; a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
+    BwdArgs g;
+    g.dout = d_o; g.dstate_out = dstate_out;
+    g.dq = dq; g.dk = dk; g.dv = dv; g.dgate = dgate;
+    g.dwq = dwphi_q; g.dwk = dwphi_k; g.dmeta = dmeta; g.dstate_in = dstate_in;
+    return finish(launch_layer_bwd(a, g, PART_BOTH));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
 }  // extern "C"

@@ -59,6 +59,21 @@ hipError_t launch_chunked_prefill(const LayerArgs &a, int parts);
 bool swa_mfma_supported(const LayerArgs &a);
 hipError_t launch_swa_mfma(const LayerArgs &a);
 
+// Backward of the layer (token-recurrent VALU kernels, any dtype).
+constexpr int kBwdMaxD = 128;        // d_qk and d_v
+constexpr int kBwdMaxF = 128;        // f (f/2 a power of two)
+constexpr int kBwdMaxWindow = 1024;
+
+struct BwdArgs {
+  const void *dout = nullptr;        // dO, the layout of o
+  const float *dstate_out = nullptr; // gradient of the final state (nullable)
+  void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dgate = nullptr;  // input dtype
+  float *dwq = nullptr, *dwk = nullptr, *dmeta = nullptr, *dstate_in = nullptr;
+};
+bool bwd_supported(const LayerArgs &a, int parts);
+size_t bwd_workspace_bytes(const LayerArgs &a, int parts);
+hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
+
 int device_cu_count();
 
 }  // namespace glah

@@ -154,6 +154,40 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
                             void *vcache, const int32_t *pos, void *o_t,
                             glah_stream_t stream);
 
+/*
+ * hybrid_layer_bwd -- gradient of hybrid_layer_fwd, for training the layer's
+ * parameters (the two-stage training of the Lizard summary, Methodology B, fits
+ * the gate, the Hedgehog feature maps and the meta-memory scalars; the layer is
+ * Methodology A.1, A.2 and C).  For the scalar loss
+ *     L = sum o . d_o + sum S_{L-1} . dstate_out
+ * it writes dL/dx for every input x of the forward:
+ *   dq, dk      [B][H][L][d_qk]   desc->dtype
+ *   dv          [B][H][L][d_v]    desc->dtype
+ *   dgate       the layout and dtype of `gate` (logits, log-gates, per token or
+ *               per head: [H], summed over the batch and every token)
+ *   dwphi_q, dwphi_k  [H][d_qk][f/2] fp32, summed over the batch
+ *   dmeta       [H][n_meta] fp32 (may be NULL only when n_meta == 0)
+ *   dstate_in   nullable, [B][H][f][d_v] fp32: gradient of state_in
+ * Inputs are those of the forward call (same descriptor, same tensors), plus
+ *   d_o         [B][H][L][d_v] desc->dtype, the gradient of o
+ *   dstate_out  nullable, [B][H][f][d_v] fp32, the gradient of the final state
+ *               (NULL = zero)
+ *   ws          device workspace of ws_bytes >= glah_bwd_workspace_bytes(desc)
+ * Supported: d_qk, d_v <= 128 and multiples of 4; f <= 128, a multiple of 4 with
+ * f/2 a power of two; window <= 1024; n_meta <= 64 (otherwise GLAH_ENOTSUP).
+ * All arithmetic is fp32 (token-recurrent form, no chunking); reductions over
+ * tokens and batch rows run in a fixed order, so results are bitwise repeatable.
+ */
+size_t glah_bwd_workspace_bytes(const glah_desc *desc);
+glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k,
+                             const void *v, const void *gate, const void *wphi_q,
+                             const void *wphi_k, const float *meta,
+                             const float *state_in, const void *d_o,
+                             const float *dstate_out, void *dq, void *dk, void *dv,
+                             void *dgate, float *dwphi_q, float *dwphi_k,
+                             float *dmeta, float *dstate_in, void *ws,
+                             size_t ws_bytes, glah_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

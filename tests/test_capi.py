@@ -155,3 +155,28 @@ def test_swa_and_gla_prefill_argument_checks(lib):
                            None) == binding.GLAH_EINVAL
     assert lib.gla_prefill(ctypes.byref(d), f, f, f, None, f, f, None, None, f, None, 0,
                            None) == binding.GLAH_EINVAL
+
+
+def _bwd(lib, desc, ws_bytes=0, **ptrs):
+    names = ["q", "k", "v", "gate", "wq", "wk", "meta", "state_in", "do", "dstate_out", "dq", "dk", "dv",
+             "dgate", "dwq", "dwk", "dmeta", "dstate_in", "ws"]
+    p = {n: FAKE for n in ("q", "k", "v", "gate", "wq", "wk", "meta", "do", "dq", "dk", "dv", "dgate",
+                           "dwq", "dwk", "dmeta", "ws")}
+    p.update(ptrs)
+    args = [ctypes.c_void_p(p.get(n)) if p.get(n) else None for n in names]
+    return lib.hybrid_layer_bwd(ctypes.byref(desc), *args, ws_bytes, None)
+
+
+def test_backward_argument_checks(lib):
+    d = _desc()
+    need = lib.glah_bwd_workspace_bytes(ctypes.byref(d))
+    assert 0 < need < ctypes.c_size_t(-1).value
+    for missing in ("q", "do", "dq", "dgate", "dwq", "dmeta"):
+        assert _bwd(lib, d, need, **{missing: 0}) == binding.GLAH_EINVAL, missing
+    assert _bwd(lib, d, need, dq=FAKE + 8) == binding.GLAH_EINVAL
+    assert _bwd(lib, d, need - 1) == binding.GLAH_EWORKSPACE
+    assert _bwd(lib, d, need, ws=0) == binding.GLAH_EWORKSPACE
+    # sizes beyond the backward kernels: valid but unsupported
+    for bad in (dict(d=256), dict(dv=66), dict(f=96), dict(f=256), dict(window=2048)):
+        assert _bwd(lib, _desc(**bad), 1 << 40) == binding.GLAH_ENOTSUP, bad
+    assert lib.glah_bwd_workspace_bytes(ctypes.byref(_desc(f=7))) == ctypes.c_size_t(-1).value
