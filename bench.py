@@ -41,6 +41,11 @@ PREFILL_EXECUTED_FLOPS_PER_TOKEN_HEAD = (600 * 16384 + 192 * 16384 * 7 // 8) // 
 PREFILL_TRANSPOSE_FLOPS_PER_TOKEN_HEAD = (32 * 16384 + 64 * 16384 * 7 // 8) // 64
 
 
+# backward at d = f = d_v = 128 (bf16): q, k, v, gate and dO read once, dq, dk,
+# dv and dgate written once (9 x 256 B); the projections and sinks are per head
+BACKWARD_BYTES_PER_TOKEN_HEAD = 9 * 256
+
+
 def decode_bytes_per_step(B, H, d, f, dv, w, bpe=2):
     state = B * H * f * dv * 4 * 2          # fp32 state read + written
     ring = B * H * w * (d + dv) * bpe       # window keys and values read
@@ -177,6 +182,48 @@ def bench_decode(G, torch, steps=256, sets=12, prefix=32768):
     }
 
 
+def bench_backward(G, torch, wl, reps=5, warmup=2):
+    """hybrid_layer_bwd over one prefill workload: gradients of every input for a
+    seeded upstream gradient dO, timed with HIP events on the launch stream."""
+    from gated_linear_attention_hybrid_amd.inputs import make_prefill
+    dev = torch.device("cuda")
+    x = make_prefill(wl, dev)
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 77)
+    dO = torch.randn((wl.B, wl.H, wl.L, wl.dv), generator=gen, device=dev).to(wl.torch_dtype)
+    desc = G.make_desc(wl.B, wl.H, wl.L, wl.d, wl.dv, wl.f, window=wl.window, n_meta=wl.n_meta,
+                       dtype=G.GLAH_BF16)
+    ws = torch.empty(max(1, G.bwd_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        return G.hybrid_layer_bwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], dO,
+                                  window=wl.window, ws=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        g = call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    bad = sum(int((~torch.isfinite(t.float())).sum().item()) for t in g.values() if t is not None)
+    nbytes = BACKWARD_BYTES_PER_TOKEN_HEAD * wl.B * wl.H * wl.L
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    ws_bytes = ws.numel()
+    del x, dO, ws, g
+    return {"workload": "%s: B=%d H=%d L=%d d=f=d_v=%d window %d, %d sinks, bf16"
+                        % (wl.name, wl.B, wl.H, wl.L, wl.d, wl.window, wl.n_meta),
+            "ms_per_call": round(ms, 3), "tokens_per_s": round(wl.B * wl.L / (ms * 1e-3), 1),
+            "workspace_bytes": ws_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": nbytes},
+            "nonfinite_outputs": bad}
+
+
 def measured_ceilings(torch):
     """What this GPU reaches on plain library work: a 1 GiB device copy (HBM) and
     a large bf16 GEMM (hipBLASLt through torch), best of 3 each."""
@@ -261,6 +308,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only the backward leg (for profiling) and print its JSON")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -282,6 +332,10 @@ def main():
 
     wl = WORKLOADS["prefill_32k"]
     torch.cuda.set_device(0)
+    if args.backward_only:
+        print(json.dumps({"backward": [bench_backward(G, torch, WORKLOADS["prefill_2k"]),
+                                       bench_backward(G, torch, wl)]}), flush=True)
+        return
     ms_step, per_call_ms, bad = bench_prefill(G, wl, args.steps, args.warmup, torch)
     token_heads = wl.B * wl.H * wl.L
     nbytes = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads
@@ -332,6 +386,8 @@ def main():
         short = bench_decode(G, torch, prefix=4096)
         out["decode"]["flatness"] = {"prefix_4096_us_per_step": short["us_per_step"],
                                      "prefix_32768_us_per_step": out["decode"]["us_per_step"]}
+    if not args.no_backward:
+        out["backward"] = [bench_backward(G, torch, WORKLOADS["prefill_2k"]), bench_backward(G, torch, wl)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)

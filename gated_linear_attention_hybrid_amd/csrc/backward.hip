@@ -14,9 +14,12 @@
 //   d b_t   = phiq_t . dphiq_t - phik_t . dphik_t  (+ S_{L-1} . dS_final at t = L-1),
 //   d log Gamma_t = sum_{s>=t} d b_s,  dS_0 = Gamma_0 dS_0^(t=0).
 // Kernels: a prologue (phi and Gamma of every token), a forward state sweep
-// (dphiq), a reverse sweep (dphik, dv), a reverse scan of d b, and a per-token
-// kernel that takes phi's softmax Jacobian back to dq, dk, accumulates the
-// projection gradients and writes the gate gradient in its layout.
+// (dphiq, per-tile sums of phiq . dphiq), a reverse sweep (dphik, dv, per-tile
+// sums of phik . dphik, d log Gamma_0), a scan over 64-token tiles giving
+// d log Gamma at each tile's first token, and a per-token kernel that finishes
+// d log Gamma inside the tile, takes phi's softmax Jacobian back to dq and dk,
+// accumulates the projection gradients and writes the gate gradient in its
+// layout.
 //
 // Window part.  P_tj = e^{s_tj - lse_t}, with the sinks' e^{t_m} inside the
 // normaliser; D_t = dO_t . o_swa,t; ds_tj = P_tj (dO_t . v_j - D_t); a query
@@ -67,10 +70,12 @@ struct BwdParams {
   void *gq, *gk, *gv, *gg;  // dq, dk, dv, dgate
   float *dwq, *dwk, *dmeta, *dstate_in;
   // workspace (fp32)
-  float *pq, *pk, *gam, *da;  // [N][f]
+  float *pq, *pk, *gam;       // [N][f]
   float *dpq, *dpk;           // [nsl][N][f]
   float *dvg;                 // [nw][N][dv]
   float *xs;                  // [2][BH][nsl][f]: S_{L-1}.dS_final, d log Gamma_0
+  float *tq, *tk;             // [nsl][BH][nft][f]: tile sums of phiq.dphiq, phik.dphik
+  float *ta;                  // [BH][nft][f]: d log Gamma at each tile's first token
   float *lse, *del;           // [N]
   float *dqs, *dks;           // [N][d]
   float *dvs;                 // [N][dv]
@@ -159,42 +164,85 @@ __device__ __forceinline__ SweepLane sweep_lane(const BwdParams &p, int slice) {
   return s;
 }
 
+// Raw quads of the I/O dtype, widened when used: a prefetched bf16 quad costs
+// two registers.
+template <class T> struct Quad;
+template <> struct Quad<float> { typedef f32x4 type; };
+template <> struct Quad<bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 widen(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+template <class Q> __device__ __forceinline__ Q zero_quad() {
+  Q z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+  return z;
+}
+
+constexpr int kPF = 8;  // tokens a sweep loads ahead of the one it computes
+
 // Forward sweep: S_t = diag(Gamma_t) S_{t-1} + phik_t v_t^T, then the slice's
-// part of dphiq_t = S_t dO_t; at the end the slice's part of S_{L-1} . dS_final.
+// part of dphiq_t = S_t dO_t, and per 64-token tile the slice's part of
+// sum_t phiq_t . dphiq_t; at the end the slice's part of S_{L-1} . dS_final.
+// Each step's operands are loaded kPF tokens ahead (the step is a chain of
+// dependent arithmetic on the state; its loads must not wait on it).
 template <class T>
 __global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
+  typedef typename Quad<T>::type Q;
   const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
   if (32 * (int)(threadIdx.x >> 6) >= p.f) return;
   const SweepLane s = sweep_lane(p, slice);
   const int L = p.L, f = p.f, dv = p.dv;
-  const size_t N = (size_t)p.B * p.H * L;
+  const size_t BH = (size_t)p.B * p.H, N = BH * L;
   const size_t rowf = (size_t)bh * L * f + s.r0;
   const size_t rowv = (size_t)bh * L * dv + s.c0;
   const T *v = (const T *)p.v + rowv;
   const T *dO = (const T *)p.dout + rowv;
   float *dpq = p.dpq + (size_t)slice * N * f + rowf;
+  float *tq = p.tq + ((size_t)slice * BH + bh) * p.nft * f + s.r0;
   const bool lead = (threadIdx.x & 7) == 0;
+  const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   f32x4 S[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    S[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    S[i] = z4;
     if (p.state_in && s.rok && s.cok) S[i] = *(const f32x4 *)(p.state_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0);
   }
-  const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = 0; t < L; ++t) {
-    const f32x4 g4 = s.rok ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
-    const f32x4 k4 = s.rok ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
-    const f32x4 v4 = s.cok ? ld4(v + (size_t)t * dv) : z4;
-    const f32x4 o4 = s.cok ? ld4(dO + (size_t)t * dv) : z4;
-    f32x4 part;
+  f32x4 bg[kPF], bk[kPF], bq[kPF];
+  Q bv[kPF], bo[kPF];
+  auto fetch = [&](int u, int t) {
+    const bool r = s.rok && t < L, c = s.cok && t < L;
+    bg[u] = r ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
+    bk[u] = r ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
+    bq[u] = r ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
+    bv[u] = c ? *(const Q *)(v + (size_t)t * dv) : zero_quad<Q>();
+    bo[u] = c ? *(const Q *)(dO + (size_t)t * dv) : zero_quad<Q>();
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int u = 0; u < kPF; ++u) fetch(u, u);
+  f32x4 tile = z4;
+  for (int t0 = 0; t0 < L; t0 += kPF) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = g4[i] * S[i][j] + k4[i] * v4[j];
-      part[i] = sum8(dot4(S[i], o4));
+    for (int u = 0; u < kPF; ++u) {
+      const int t = t0 + u;
+      if (t < L) {
+        const f32x4 g4 = bg[u], k4 = bk[u], q4 = bq[u], v4 = widen(bv[u]), o4 = widen(bo[u]);
+        fetch(u, t + kPF);
+        f32x4 part;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) S[i][j] = g4[i] * S[i][j] + k4[i] * v4[j];
+          part[i] = sum8(dot4(S[i], o4));
+          tile[i] += q4[i] * part[i];
+        }
+        if (lead && s.rok) *(f32x4 *)(dpq + (size_t)t * f) = part;
+        if ((t & (kFeatTok - 1)) == kFeatTok - 1 || t == L - 1) {
+          if (lead && s.rok) *(f32x4 *)(tq + (size_t)(t / kFeatTok) * f) = tile;
+          tile = z4;
+        }
+      }
     }
-    if (lead && s.rok) *(f32x4 *)(dpq + (size_t)t * f) = part;
   }
   if (p.dstate_out) {
     f32x4 part;
@@ -208,23 +256,27 @@ __global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
 }
 
 // Reverse sweep: dS_t = phiq_t dO_t^T + diag(Gamma_{t+1}) dS_{t+1} from dS_final;
-// the slice's part of dphik_t = dS_t v_t, the wave's part of dS_t^T phik_t, and
-// at the end dS_0-gradient = diag(Gamma_0) dS_0.
+// the slice's part of dphik_t = dS_t v_t (and per tile of sum_t phik_t .
+// dphik_t), the wave's part of dS_t^T phik_t, dS_0-gradient = diag(Gamma_0)
+// dS_0, and the slice's part of d log Gamma_0 = Gamma_0 (S_in . dS_0).
 template <class T>
 __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
+  typedef typename Quad<T>::type Q;
   const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
   const int wave = threadIdx.x >> 6;
   if (32 * wave >= p.f) return;
   const SweepLane s = sweep_lane(p, slice);
   const int L = p.L, f = p.f, dv = p.dv;
-  const size_t N = (size_t)p.B * p.H * L;
+  const size_t BH = (size_t)p.B * p.H, N = BH * L;
   const size_t rowf = (size_t)bh * L * f + s.r0;
   const size_t rowv = (size_t)bh * L * dv + s.c0;
   const T *v = (const T *)p.v + rowv;
   const T *dO = (const T *)p.dout + rowv;
   float *dpk = p.dpk + (size_t)slice * N * f + rowf;
   float *dvg = p.dvg + (size_t)wave * N * dv + rowv;
+  float *tk = p.tk + ((size_t)slice * BH + bh) * p.nft * f + s.r0;
   const int l = threadIdx.x & 63;
+  const bool lead = (l & 7) == 0;
 
   const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
   f32x4 dS[4];
@@ -234,27 +286,48 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
     if (p.dstate_out && s.rok && s.cok)
       dS[i] = *(const f32x4 *)(p.dstate_out + ((size_t)bh * f + s.r0 + i) * dv + s.c0);
   }
+  f32x4 bq[kPF], bk[kPF], bg[kPF];
+  Q bv[kPF], bo[kPF];
+  auto fetch = [&](int u, int t) {
+    const bool r = s.rok && t >= 0, c = s.cok && t >= 0;
+    bq[u] = r ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
+    bk[u] = r ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
+    bg[u] = r ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
+    bv[u] = c ? *(const Q *)(v + (size_t)t * dv) : zero_quad<Q>();
+    bo[u] = c ? *(const Q *)(dO + (size_t)t * dv) : zero_quad<Q>();
+  };
+#pragma unroll
+  for (int u = 0; u < kPF; ++u) fetch(u, L - 1 - u);
   f32x4 gn = {1.0f, 1.0f, 1.0f, 1.0f};
-  for (int t = L - 1; t >= 0; --t) {
-    const f32x4 q4 = s.rok ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
-    const f32x4 k4 = s.rok ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
-    const f32x4 g4 = s.rok ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
-    const f32x4 v4 = s.cok ? ld4(v + (size_t)t * dv) : z4;
-    const f32x4 o4 = s.cok ? ld4(dO + (size_t)t * dv) : z4;
-    f32x4 a, c = z4;
+  f32x4 tile = z4;
+  for (int t0 = L - 1; t0 >= 0; t0 -= kPF) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int u = 0; u < kPF; ++u) {
+      const int t = t0 - u;
+      if (t >= 0) {
+        const f32x4 q4 = bq[u], k4 = bk[u], g4 = bg[u], v4 = widen(bv[u]), o4 = widen(bo[u]);
+        fetch(u, t - kPF);
+        f32x4 a, c = z4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dS[i][j] = gn[i] * dS[i][j] + q4[i] * o4[j];
-      a[i] = sum8(dot4(dS[i], v4));
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] += dS[i][j] * k4[i];
+          for (int j = 0; j < 4; ++j) dS[i][j] = gn[i] * dS[i][j] + q4[i] * o4[j];
+          a[i] = sum8(dot4(dS[i], v4));
+          tile[i] += k4[i] * a[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c[j] += dS[i][j] * k4[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = sum_rows8(c[j]);
+        if (lead && s.rok) *(f32x4 *)(dpk + (size_t)t * f) = a;
+        if (l < 8 && s.cok) *(f32x4 *)(dvg + (size_t)t * dv) = c;
+        if ((t & (kFeatTok - 1)) == 0) {
+          if (lead && s.rok) *(f32x4 *)(tk + (size_t)(t / kFeatTok) * f) = tile;
+          tile = z4;
+        }
+        gn = g4;
+      }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = sum_rows8(c[j]);
-    if ((l & 7) == 0 && s.rok) *(f32x4 *)(dpk + (size_t)t * f) = a;
-    if (l < 8 && s.cok) *(f32x4 *)(dvg + (size_t)t * dv) = c;
-    gn = g4;
   }
   if (p.dstate_in && s.rok && s.cok) {
 #pragma unroll
@@ -265,9 +338,8 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
       *(f32x4 *)(p.dstate_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0) = r;
     }
   }
-  // the slice's part of d log Gamma_0 = Gamma_0 (S_in . dS_0), taken directly:
-  // without an initial state it is exactly zero, which a sum of the d b_t
-  // reaches only up to rounding
+  // taken directly: without an initial state it is exactly zero, which a sum
+  // of the d b_t reaches only up to rounding
   f32x4 x0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -275,76 +347,75 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
                          ? *(const f32x4 *)(p.state_in + ((size_t)bh * f + s.r0 + i) * dv + s.c0) : z4;
     x0[i] = gn[i] * sum8(dot4(s4, dS[i]));
   }
-  if ((l & 7) == 0 && s.rok) *(f32x4 *)(p.xs + ((size_t)(p.B * p.H + bh) * p.nsl + slice) * f + s.r0) = x0;
+  if (lead && s.rok) *(f32x4 *)(p.xs + ((BH + bh) * p.nsl + slice) * f + s.r0) = x0;
 }
 
-// d log Gamma_t = sum_{s>=t} d b_s with d b_t = phiq_t . dphiq_t - phik_t .
-// dphik_t.  Both ends are known exactly (d log Gamma_{L-1} = d b_{L-1} +
-// S_{L-1} . dS_final, d log Gamma_0 from the reverse sweep), so each half of the
-// sequence is summed from its own end: the rounding of the running sum then
-// spans at most L/2 terms and the exact zeros (no initial state) stay exact.
-// One thread per (b, h, feature); the slice partials of dphiq and dphik are
-// summed here and written back into slice 0.
-__global__ __launch_bounds__(kBT) void bwd_gate_scan_kernel(BwdParams p) {
+// d log Gamma at the first token of every 64-token tile.  With d b_t =
+// phiq_t . dphiq_t - phik_t . dphik_t and tile totals T_i (from the sweeps),
+// d log Gamma_t = sum_{s>=t} d b_s is known exactly at both ends (d log Gamma_0
+// from the reverse sweep, the sum past the end = S_{L-1} . dS_final), so the
+// first half of the tiles is summed forward from the start and the second half
+// backward from the end: the exact zero of Gamma_0 without an initial state
+// stays exact, and no running sum spans more than half the sequence.  One
+// thread per (b, h, feature).
+__global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
   const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
-  const int f = p.f, L = p.L;
+  const int f = p.f, nft = p.nft;
   const size_t BH = (size_t)p.B * p.H;
   if (idx >= BH * f) return;
   const size_t bh = idx / f, r = idx - bh * f;
-  const size_t NF = BH * L * f;
-  auto db = [&](int t) {
-    const size_t off = (bh * L + t) * f + r;
-    float dq = 0.0f, dk = 0.0f;
+  auto total = [&](int i) {
+    float s = 0.0f;
     for (int sl = 0; sl < p.nsl; ++sl) {
-      dq += p.dpq[sl * NF + off];
-      dk += p.dpk[sl * NF + off];
+      const size_t o = (((size_t)sl * BH + bh) * nft + i) * f + r;
+      s += p.tq[o] - p.tk[o];
     }
-    if (p.nsl > 1) {
-      p.dpq[off] = dq;
-      p.dpk[off] = dk;
-    }
-    return p.pq[off] * dq - p.pk[off] * dk;
+    return s;
   };
-  const int half = (L + 1) / 2;
+  const int half = (nft + 1) / 2;
   float acc = 0.0f;
-  if (p.dstate_out)
-    for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[(bh * p.nsl + sl) * f + r];
-  for (int t = L - 1; t >= half; --t) {
-    acc += db(t);
-    p.da[(bh * L + t) * f + r] = acc;
+  for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[((BH + bh) * p.nsl + sl) * f + r];
+  for (int i = 0; i < half; ++i) {
+    p.ta[(bh * nft + i) * f + r] = acc;
+    acc -= total(i);
   }
   acc = 0.0f;
-  for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[((BH + bh) * p.nsl + sl) * f + r];
-  for (int t = 0; t < half; ++t) {
-    p.da[(bh * L + t) * f + r] = acc;
-    acc -= db(t);
+  if (p.dstate_out)
+    for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[(bh * p.nsl + sl) * f + r];
+  for (int i = nft - 1; i >= half; --i) {
+    acc += total(i);
+    p.ta[(bh * nft + i) * f + r] = acc;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Per-token gradients.  Block = (b, h, kFeatTok tokens).  For each token: the
-// softmax Jacobian of both halves of phi, dq and dk (plus the window part),
-// dv (both parts), the gate gradient in its layout, and this block's share of
-// dWphi_q = sum_t q_t^T du_q,t and dWphi_k.
+// slice sums of dphiq and dphik, the softmax Jacobian of both halves of phi,
+// dq and dk (plus the window part), dv (both parts), d log Gamma_t (the tile's
+// start value minus the d b of the tile's earlier tokens) turned into the gate
+// gradient of its layout, and this block's share of dWphi_q = sum_t q_t^T
+// du_q,t and of dWphi_k.  The projections sit in LDS transposed ([f/2][d]) so
+// that the lanes of dq = du Wphi^T read consecutive words.
 template <class T>
 __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
-  __shared__ float W[2][kBwdMaxD * kMaxF2];
+  __shared__ float WT[2][kMaxF2 * kBwdMaxD];
   __shared__ float X[2][kBwdMaxD];
   __shared__ float DU[2][kMaxF2];
-  __shared__ float red[kBT / 64];
+  __shared__ float E[2][kBwdMaxF];
   constexpr int NP = kBwdMaxD * kMaxF2 / kBT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int bh = blockIdx.x / p.nft, tile = blockIdx.x % p.nft;
   const int h = bh % p.H, d = p.d, dv = p.dv, f = p.f, f2 = p.f2, L = p.L;
   const int t0 = tile * kFeatTok, nt = min(kFeatTok, L - t0);
-  const size_t N = (size_t)p.B * p.H * L;
+  const size_t N = (size_t)p.B * p.H * L, NF = N * f;
   const bool gla = p.gla, swa = p.swa;
   if (gla) {
     const T *wq = (const T *)p.wq + (size_t)h * d * f2;
     const T *wk = (const T *)p.wk + (size_t)h * d * f2;
     for (int i = tid; i < d * f2; i += kBT) {
-      W[0][i] = ld(wq + i);
-      W[1][i] = ld(wk + i);
+      const int e = i >> p.lf2, j = i & (f2 - 1);
+      WT[0][j * d + e] = ld(wq + i);
+      WT[1][j * d + e] = ld(wk + i);
     }
   }
   const int jj = tid & (f2 - 1);
@@ -352,6 +423,14 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
   float aq[NP], ak[NP];
 #pragma unroll
   for (int n = 0; n < NP; ++n) aq[n] = ak[n] = 0.0f;
+  // wave 2 carries d log Gamma of features lane and lane + 64 through the tile
+  float run[2] = {0.0f, 0.0f};
+  if (gla && wave == 2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = lane + 64 * u;
+      if (r < f) run[u] = p.ta[((size_t)bh * p.nft + tile) * f + r];
+    }
   float gsum = 0.0f;
   const T *g = (const T *)p.gate;
   T *dg = (T *)p.gg;
@@ -367,37 +446,51 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         const float *ph = (wave ? p.pk : p.pq) + row * f;
         const float *dph = (wave ? p.dpk : p.dpq) + row * f;
         const bool ok = lane < f2;
-        const float pp = ok ? ph[lane] : 0.0f, dp = ok ? dph[lane] : 0.0f;
-        const float pn = ok ? ph[f2 + lane] : 0.0f, dn = ok ? dph[f2 + lane] : 0.0f;
-        const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
-        if (ok) DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
-      } else {
-        float tsum = 0.0f;
-        for (int r = tid - 128; r < f; r += 128) {
-          const float da = p.da[row * f + r];
-          if (p.gate_mode == 0) {
-            const size_t gi = row * f + r;
-            const float val = p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(ld(g + gi)));
-            dg[gi] = from_f32<T>(val);
-          } else {
-            tsum += da;
+        float dp = 0.0f, dn = 0.0f;
+        if (ok)
+          for (int sl = 0; sl < p.nsl; ++sl) {
+            dp += dph[sl * NF + lane];
+            dn += dph[sl * NF + f2 + lane];
           }
-        }
-        if (p.gate_mode == 1) {
-          tsum = wave_sum(tsum);
-          if (lane == 0) red[wave] = tsum;
-        } else if (p.gate_mode == 2) {
-          gsum += tsum;
+        const float pp = ok ? ph[lane] : 0.0f, pn = ok ? ph[f2 + lane] : 0.0f;
+        const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
+        if (ok) {
+          DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
+          E[wave][lane] = pp * dp;
+          E[wave][f2 + lane] = pn * dn;
         }
       }
     }
     __syncthreads();
+    if (gla && wave == 2) {
+      float tsum = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = lane + 64 * u;
+        if (r < f) {
+          const float da = run[u];
+          run[u] = da - (E[0][r] - E[1][r]);
+          if (p.gate_mode == 0) {
+            const size_t gi = row * f + r;
+            dg[gi] = from_f32<T>(p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(ld(g + gi))));
+          } else {
+            tsum += da;
+          }
+        }
+      }
+      if (p.gate_mode == 1) {
+        tsum = wave_sum(tsum);
+        if (lane == 0) dg[row] = from_f32<T>(tsum);
+      } else if (p.gate_mode == 2) {
+        gsum += tsum;
+      }
+    }
     {
       const int m = tid >> 7, i = tid & 127;
       if (i < d) {
         float acc = 0.0f;
         if (gla)
-          for (int j = 0; j < f2; ++j) acc += DU[m][j] * W[m][i * f2 + j];
+          for (int j = 0; j < f2; ++j) acc += DU[m][j] * WT[m][j * d + i];
         if (swa) acc += (m ? p.dks : p.dqs)[row * d + i];
         ((T *)(m ? p.gk : p.gq))[row * d + i] = from_f32<T>(acc);
       }
@@ -409,7 +502,6 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
       if (swa) acc += p.dvs[row * dv + c];
       ((T *)p.gv)[row * dv + c] = from_f32<T>(acc);
     }
-    if (gla && p.gate_mode == 1 && tid == 0) dg[row] = from_f32<T>(red[2] + red[3]);
     if (gla) {
       const float duq = DU[0][jj], duk = DU[1][jj];
 #pragma unroll
@@ -432,12 +524,9 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
       p.wkp[base + (size_t)i * f2 + jj] = ak[n];
     }
   }
-  if (p.gate_mode == 2) {
-    __syncthreads();
-    const float s = wave_sum(gsum);
-    if (lane == 0) red[wave] = s;
-    __syncthreads();
-    if (tid == 0) p.gp[(size_t)bh * p.nft + tile] = red[2] + red[3];
+  if (p.gate_mode == 2 && wave == 2) {
+    const float s2 = wave_sum(gsum);
+    if (lane == 0) p.gp[(size_t)bh * p.nft + tile] = s2;
   }
 }
 
@@ -602,7 +691,7 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
 
 // Workspace layout, in floats; every region starts on a 256-byte boundary.
 struct BwdLayout {
-  size_t pq, pk, gam, da, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, total;
+  size_t pq, pk, gam, tq, tk, ta, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, total;
 };
 
 size_t up64(size_t n) { return (n + 63) & ~(size_t)63; }
@@ -616,7 +705,9 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   size_t at = 0;
   auto take = [&](size_t n) { const size_t r = at; at += up64(n); return r; };
   const size_t nf = gla ? N * a.f : 0;
-  o.pq = take(nf); o.pk = take(nf); o.gam = take(nf); o.da = take(nf);
+  o.pq = take(nf); o.pk = take(nf); o.gam = take(nf);
+  const size_t nt = gla ? BH * nft * a.f : 0;
+  o.tq = take(nsl * nt); o.tk = take(nsl * nt); o.ta = take(nt);
   o.dpq = take(nsl * nf); o.dpk = take(nsl * nf);
   o.dvg = take(gla ? nw * N * a.dv : 0);
   o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
@@ -639,7 +730,8 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.dwq = g.dwq; p.dwk = g.dwk; p.dmeta = g.dmeta; p.dstate_in = g.dstate_in;
   const BwdLayout lay = bwd_layout(a, parts);
   float *ws = (float *)a.ws;
-  p.pq = ws + lay.pq; p.pk = ws + lay.pk; p.gam = ws + lay.gam; p.da = ws + lay.da;
+  p.pq = ws + lay.pq; p.pk = ws + lay.pk; p.gam = ws + lay.gam;
+  p.tq = ws + lay.tq; p.tk = ws + lay.tk; p.ta = ws + lay.ta;
   p.dpq = ws + lay.dpq; p.dpk = ws + lay.dpk; p.dvg = ws + lay.dvg; p.xs = ws + lay.xs;
   p.lse = ws + lay.lse; p.del = ws + lay.del; p.dqs = ws + lay.dqs; p.dks = ws + lay.dks;
   p.dvs = ws + lay.dvs; p.wqp = ws + lay.wqp; p.wkp = ws + lay.wkp; p.gp = ws + lay.gp; p.mp = ws + lay.mp;
@@ -675,7 +767,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     hipLaunchKernelGGL(bwd_rev_sweep_kernel<T>, dim3(BH * p.nsl), block, 0, a.stream, p);
     if (!launched()) return e;
     if (a.L > 0) {
-      hipLaunchKernelGGL(bwd_gate_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
+      hipLaunchKernelGGL(bwd_tile_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
                          a.stream, p);
       if (!launched()) return e;
     }
