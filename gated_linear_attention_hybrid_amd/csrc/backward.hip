@@ -41,6 +41,8 @@ constexpr int kPrepTok = 16;     // tokens of one prologue block
 constexpr int kFeatTok = 64;     // tokens of one feature-gradient block
 constexpr int kSwaTok = 16;      // query (key) tokens of one window block
 constexpr int kMaxF2 = kBwdMaxF / 2;
+constexpr int kMaxSlices = kBwdMaxD / kSliceCols;  // d_v slices of the sweeps
+constexpr int kMaxRowWaves = kBwdMaxF / 32;       // row waves of the reverse sweep
 
 template <class T> __device__ __forceinline__ f32x4 ld4(const T *p);
 template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) { return *(const f32x4 *)p; }
@@ -51,17 +53,19 @@ template <> __device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
-// sum over lanes l ^ 1, l ^ 2, l ^ 4 (the 8 column groups of one row group)
+// Sum over the 8 lanes of an aligned group (the column groups of one row
+// group): quad permutes l ^ 1, l ^ 2, then the half-row mirror 7 - l, which
+// pairs each quad with the other quad of its group.  DPP only, no LDS trip.
 __device__ __forceinline__ float sum8(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  return x + __shfl_xor(x, 4);
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  return x + dpp_f<0x141>(x);
 }
-// sum over lanes l ^ 8, l ^ 16, l ^ 32 (the 8 row groups of one wave)
+// Sum over lanes l, l ^ 8, ..., l ^ 56 (the 8 row groups of one wave): a row
+// rotate by 8 pairs the halves of each 16-lane row, then the row swaps.
 __device__ __forceinline__ float sum_rows8(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  x += dpp_f<0x128>(x);
+  return rows_reduce(x, OpAdd());
 }
 
 struct BwdParams {
@@ -435,24 +439,61 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
   const T *g = (const T *)p.gate;
   T *dg = (T *)p.gg;
 
-  for (int tt = 0; tt < nt; ++tt) {
-    const int t = t0 + tt;
-    const size_t row = (size_t)bh * L + t;
-    __syncthreads();
+  // every global operand of one token, loaded one token ahead
+  struct Pre {
+    float x, pp, pn, dp[kMaxSlices], dn[kMaxSlices], gr[2], ds, dvw[kMaxRowWaves], dvs;
+  };
+  const int m = tid >> 7, mi = tid & 127;
+  auto fetch = [&](int tt) {
+    Pre r = {};
+    if (tt >= nt) return r;
+    const size_t row = (size_t)bh * L + t0 + tt;
     if (gla) {
-      const int m = tid >> 7, i = tid & 127;
-      if (i < d) X[m][i] = ld((const T *)(m ? p.k : p.q) + row * d + i);
-      if (wave < 2) {
+      if (mi < d) r.x = ld((const T *)(m ? p.k : p.q) + row * d + mi);
+      if (wave < 2 && lane < f2) {
         const float *ph = (wave ? p.pk : p.pq) + row * f;
         const float *dph = (wave ? p.dpk : p.dpq) + row * f;
+        r.pp = ph[lane];
+        r.pn = ph[f2 + lane];
+#pragma unroll
+        for (int sl = 0; sl < kMaxSlices; ++sl)
+          if (sl < p.nsl) {
+            r.dp[sl] = dph[sl * NF + lane];
+            r.dn[sl] = dph[sl * NF + f2 + lane];
+          }
+      }
+      if (wave == 2 && p.gate_mode == 0 && !p.gate_is_log)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (lane + 64 * u < f) r.gr[u] = ld(g + row * f + lane + 64 * u);
+      if (tid < dv)
+#pragma unroll
+        for (int w = 0; w < kMaxRowWaves; ++w)
+          if (w < p.nw) r.dvw[w] = p.dvg[((size_t)w * N + row) * dv + tid];
+    }
+    if (swa) {
+      if (mi < d) r.ds = (m ? p.dks : p.dqs)[row * d + mi];
+      if (tid < dv) r.dvs = p.dvs[row * dv + tid];
+    }
+    return r;
+  };
+
+  Pre cur = fetch(0);
+  for (int tt = 0; tt < nt; ++tt) {
+    const size_t row = (size_t)bh * L + t0 + tt;
+    const Pre nxt = fetch(tt + 1);
+    __syncthreads();
+    if (gla) {
+      if (mi < d) X[m][mi] = cur.x;
+      if (wave < 2) {
         const bool ok = lane < f2;
         float dp = 0.0f, dn = 0.0f;
-        if (ok)
-          for (int sl = 0; sl < p.nsl; ++sl) {
-            dp += dph[sl * NF + lane];
-            dn += dph[sl * NF + f2 + lane];
-          }
-        const float pp = ok ? ph[lane] : 0.0f, pn = ok ? ph[f2 + lane] : 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < kMaxSlices; ++sl) {
+          dp += cur.dp[sl];
+          dn += cur.dn[sl];
+        }
+        const float pp = cur.pp, pn = cur.pn;
         const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
         if (ok) {
           DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
@@ -470,12 +511,10 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         if (r < f) {
           const float da = run[u];
           run[u] = da - (E[0][r] - E[1][r]);
-          if (p.gate_mode == 0) {
-            const size_t gi = row * f + r;
-            dg[gi] = from_f32<T>(p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(ld(g + gi))));
-          } else {
+          if (p.gate_mode == 0)
+            dg[row * f + r] = from_f32<T>(p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(cur.gr[u])));
+          else
             tsum += da;
-          }
         }
       }
       if (p.gate_mode == 1) {
@@ -485,22 +524,17 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         gsum += tsum;
       }
     }
-    {
-      const int m = tid >> 7, i = tid & 127;
-      if (i < d) {
-        float acc = 0.0f;
-        if (gla)
-          for (int j = 0; j < f2; ++j) acc += DU[m][j] * WT[m][j * d + i];
-        if (swa) acc += (m ? p.dks : p.dqs)[row * d + i];
-        ((T *)(m ? p.gk : p.gq))[row * d + i] = from_f32<T>(acc);
-      }
-    }
-    for (int c = tid; c < dv; c += kBT) {
-      float acc = 0.0f;
+    if (mi < d) {
+      float acc = cur.ds;
       if (gla)
-        for (int w = 0; w < p.nw; ++w) acc += p.dvg[((size_t)w * N + row) * dv + c];
-      if (swa) acc += p.dvs[row * dv + c];
-      ((T *)p.gv)[row * dv + c] = from_f32<T>(acc);
+        for (int j = 0; j < f2; ++j) acc += DU[m][j] * WT[m][j * d + mi];
+      ((T *)(m ? p.gk : p.gq))[row * d + mi] = from_f32<T>(acc);
+    }
+    if (tid < dv) {
+      float acc = cur.dvs;
+#pragma unroll
+      for (int w = 0; w < kMaxRowWaves; ++w) acc += cur.dvw[w];
+      ((T *)p.gv)[row * dv + tid] = from_f32<T>(acc);
     }
     if (gla) {
       const float duq = DU[0][jj], duk = DU[1][jj];
@@ -513,6 +547,7 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         }
       }
     }
+    cur = nxt;
   }
   if (!gla) return;
   const size_t base = ((size_t)bh * p.nft + tile) * d * f2;
