@@ -245,9 +245,12 @@ __device__ __forceinline__ bf16x8 scalar_gate(const HeadBufs &hb, unsigned base)
   const unsigned w = (raw & 0xFFFFu) * 0x10001u;
   return __builtin_bit_cast(bf16x8, (u32x4){w, w, w, w});
 }
+// SG: the scalar layouts (per token or per head), a compile-time choice so the
+// per-feature kernels carry no branch for them
+template <bool SG>
 __device__ __forceinline__ void load_gates(const HeadBufs &hb, unsigned base, bf16x8 *x) {
   const unsigned g = (threadIdx.x & 63) >> 4;
-  if (hb.gmode != 0) {  // uniform
+  if constexpr (SG) {
     const bf16x8 s1 = scalar_gate(hb, base);
 #pragma unroll
     for (int s = 0; s < 4; ++s) x[s] = s1;
@@ -257,9 +260,10 @@ __device__ __forceinline__ void load_gates(const HeadBufs &hb, unsigned base, bf
   for (int s = 0; s < 4; ++s) x[s] = bload(hb.g, base + 2 * feat(g, 8 * s));
 }
 // the gates of fold slots 16h .. 16h + 15 only (fragments 2h, 2h + 1 of load_gates)
+template <bool SG>
 __device__ __forceinline__ void load_gates_half(const HeadBufs &hb, unsigned base, int h, bf16x8 *x) {
   const unsigned g = (threadIdx.x & 63) >> 4;
-  if (hb.gmode != 0) {  // uniform
+  if constexpr (SG) {
     const bf16x8 s1 = scalar_gate(hb, base);
 #pragma unroll
     for (int s = 0; s < 2; ++s) x[s] = s1;

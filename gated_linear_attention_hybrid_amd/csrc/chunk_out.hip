@@ -146,7 +146,7 @@ __device__ __forceinline__ void fold(const float *e, float izp, float izn, const
 }
 
 // ---------------------------------------------------------------- the kernel
-template <bool SWA>
+template <bool SWA, bool SG>
 __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
   using LD = Lds8<SWA>;
   constexpr int NKS = LD::NKS;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
     // (the phi- features) here in phase C, slots 0..15 by the query waves
     bf16x8 xk[4], xg[2];  // this chunk's keys, the next chunk's gates (slots 16..31)
     load_rows(hb.k, ro + chunk_off(c_begin), xk);
-    load_gates_half(hb, ro + chunk_off(c_begin), 1, xg);
+    load_gates_half<SG>(hb, ro + chunk_off(c_begin), 1, xg);
     {
       float dn[16];
       tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         for (int j = 0; j < 4; ++j) vprev[T][j] = vcur[T][j];
       pack_v();  // values of chunk c - 1
       column(c - 1);
-      load_gates_half(hb, ro1, 1, xg);  // next chunk's gates (decay exponents in phase C)
+      load_gates_half<SG>(hb, ro1, 1, xg);  // next chunk's gates (decay exponents in phase C)
       f32x4 u[4];
       project(smem + LD::WK + lane * 16, xk, u);
       load_rows(hb.k, ro1, xk);  // next chunk's keys
@@ -461,13 +461,13 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
     // decay exponents of slots 0..15 (the phi+ features), one chunk ahead: the
     // first chunk's here, the next chunk's in phase A, stored after B1
     bf16x8 xg[2];
-    load_gates_half(hb, ro + chunk_off(c_begin), 0, xg);
+    load_gates_half<SG>(hb, ro + chunk_off(c_begin), 0, xg);
     {
       float dn[16];
       tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
       store_dd_half(smem + LD::DD, tile, 0, dn);
     }
-    load_gates_half(hb, ro + chunk_off(c_begin + 1), 0, xg);
+    load_gates_half<SG>(hb, ro + chunk_off(c_begin + 1), 0, xg);
     const float sl2 =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale * kLog2e)));
     __syncthreads();  // staged fragments and the first chunk's decay exponents
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       }
       float dnx[16];  // next chunk's, stored once every wave has read this chunk's
       tile_decay<16>(xg, gate_is_log, (c + 1) * kC + 16 * tile + n < p.L, dnx);
-      load_gates_half(hb, ro + chunk_off(c + 2), 0, xg);
+      load_gates_half<SG>(hb, ro + chunk_off(c + 2), 0, xg);
       __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
       store_dd_half(smem + LD::DD, tile, 0, dnx);
 
@@ -658,20 +658,22 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
   }
 }
 
-template <bool SWA>
+template <bool SWA, bool SG>
 hipError_t launch8(const ChunkParams &p, int blocks, hipStream_t stream) {
   const int bytes = Lds8<SWA>::BYTES;
-  hipError_t e = hipFuncSetAttribute((const void *)chunk_out_kernel<SWA>,
+  hipError_t e = hipFuncSetAttribute((const void *)chunk_out_kernel<SWA, SG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_out_kernel<SWA>, dim3((unsigned)blocks), dim3(kNT8), bytes, stream, p);
+  hipLaunchKernelGGL((chunk_out_kernel<SWA, SG>), dim3((unsigned)blocks), dim3(kNT8), bytes, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunk_out(const ChunkParams &p, bool swa, int blocks, hipStream_t stream) {
-  return swa ? launch8<true>(p, blocks, stream) : launch8<false>(p, blocks, stream);
+  if (p.gate_mode != 0)
+    return swa ? launch8<true, true>(p, blocks, stream) : launch8<false, true>(p, blocks, stream);
+  return swa ? launch8<true, false>(p, blocks, stream) : launch8<false, false>(p, blocks, stream);
 }
 
 }  // namespace glah

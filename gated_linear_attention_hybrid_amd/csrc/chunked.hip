@@ -174,6 +174,7 @@ struct LdsState {
   static constexpr int BYTES = T + 4 * kF * 4;
 };
 
+template <bool SG>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void state_kernel(ChunkParams p) {
   using LD = LdsState;
@@ -216,7 +217,7 @@ void state_kernel(ChunkParams p) {
   bf16x8 xk[4], xv[4], xg[4];
   load_rows(hb.k, ro + chunk_off(c_end - 1), xk);
   load_vals(hb.v, ro + chunk_off(c_end - 1), xv);
-  load_gates(hb, ro + chunk_off(c_end - 1), xg);
+  load_gates<SG>(hb, ro + chunk_off(c_end - 1), xg);
   __syncthreads();
 
   // The chunks are taken last to first, so the state is never decayed: chunk c
@@ -231,7 +232,7 @@ void state_kernel(ChunkParams p) {
     load_rows(hb.k, ro1, xk);  // preceding chunk's keys
     float dn[32];
     tile_decay(xg, gate_is_log, c * kC + 16 * wave + n < p.L, dn);
-    load_gates(hb, ro1, xg);
+    load_gates<SG>(hb, ro1, xg);
     if (n == 15) {
       float *T = (float *)(smem + LD::T) + wave * kF;
 #pragma unroll
@@ -435,10 +436,13 @@ hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
     const int NS = s.slices();
     p.seg_state = (float *)a.ws;
     p.seg_decay = p.seg_state + (size_t)bh * NS * kF * kDV;
-    hipError_t e = hipFuncSetAttribute((const void *)state_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LdsState::BYTES);
+    const void *fn = p.gate_mode != 0 ? (const void *)state_kernel<true> : (const void *)state_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LdsState::BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(bh * NS)), dim3(kNT), LdsState::BYTES, a.stream, p);
+    if (p.gate_mode != 0)
+      hipLaunchKernelGGL(state_kernel<true>, dim3((unsigned)(bh * NS)), dim3(kNT), LdsState::BYTES, a.stream, p);
+    else
+      hipLaunchKernelGGL(state_kernel<false>, dim3((unsigned)(bh * NS)), dim3(kNT), LdsState::BYTES, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t elems = (size_t)bh * kF * kDV;
