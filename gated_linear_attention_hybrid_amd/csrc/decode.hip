@@ -11,7 +11,10 @@
 //     with 16-byte loads, partial sums are reduced across lanes (DPP and row
 //     swaps) and waves (LDS).
 //   * window scores: 4 threads per key, 32 dimensions each, 16-byte loads.
-//   * window values and ring slots: loaded up front with the state.
+//   * window values: loaded up front with the state, 16 bytes per lane (two
+//     lanes share eight columns of two ring slots and swap halves by DPP).
+//   * the sinks and the new key for the ring append are loaded up front too,
+//     so no load sits in the softmax chain or in the kernel's tail.
 // Block = (b, h), 1024 threads: the projections, the window keys and the new
 // token are read once per head instead of once per column slice.
 #include "device_common.hpp"
@@ -28,7 +31,7 @@ constexpr int kC4 = kDVS / 4;            // float4 column groups per block
 constexpr int kNRG = kNT / kC4;          // row groups
 constexpr int kRPT = kF / kNRG;          // state rows per thread
 constexpr int kNSL = kDV / kDVS;         // blocks per head
-constexpr int kKPT = kMaxW / kNRG;       // window keys per thread (values)
+static_assert(2 * kNRG == kMaxW, "two ring slots per row group (the value loads)");
 
 struct DecParams {
   const void *q, *k, *v, *gate, *wq, *wk;
@@ -155,19 +158,27 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
 #pragma unroll
   for (int ii = 0; ii < kRPT; ++ii)
     S[ii] = __builtin_nontemporal_load((const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col));
-  // (4) window values this thread will weight: ring slots s = rg + kNRG * jj
-  f32x4 vv[kKPT];
+  // (4) window values, 16 bytes per lane: ring slot rg + kNRG (c4 & 1), columns
+  // 8 (c4 >> 1) .. +7, i.e. this thread's four columns and those of lane ^ 1;
+  // after weighting, the two lanes swap the halves they do not own
+  float vw[8];
+  const int vslot = rg + kNRG * (c4 & 1);
   if (SWA) {
+    if (vslot < w) {
+      V::ld8(vc + (size_t)vslot * kDV + slice * kDVS + 8 * (c4 >> 1), vw);
+    } else {
 #pragma unroll
-    for (int jj = 0; jj < kKPT; ++jj) {
-      const int s2 = rg + kNRG * jj;
-      vv[jj] = s2 < w ? V::ld4(vc + (size_t)s2 * kDV + col) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int e = 0; e < 8; ++e) vw[e] = 0.0f;
     }
   }
   const f32x4 v4 = V::ld4(vt + col);
   // (5) gates
   const float graw = tid < kF ? to_f32(((const T *)p.gate)[gate_index(p.gate_mode, bh, p.H, 1, kF, 0, tid)]) : 0.0f;
   const float qn = tid < kD ? to_f32(qt[tid]) : 0.0f, kn = tid < kD ? to_f32(kt[tid]) : 0.0f;
+  // (5b) operands of the ring append and of the sink softmax, so that no load
+  // sits in the dependent chain after the first barrier or in the kernel's tail
+  const f32x4 kt4 = (SWA && slice == 0 && tid < kD / 4) ? V::ld4(kt + 4 * tid) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  const float tmeta = (SWA && wave == 2 && lane < p.n_meta) ? p.meta[(size_t)h * p.n_meta + lane] : -INFINITY;
 
   // window scores (ring slots) and q . k of the new token (waves 0-1)
   if (SWA) {
@@ -226,8 +237,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     const float s = ok ? s_p[lane] : -INFINITY;
     const float snew = (s_qk[0] + s_qk[1]) * p.scale;
     float m = fmaxf(wave_max(s), snew);
-    const float *meta = p.meta + (size_t)h * p.n_meta;
-    float tm = lane < p.n_meta ? meta[lane] : -INFINITY;
+    const float tm = tmeta;
     m = fmaxf(m, wave_max(tm));
     const float e = ok ? exp_fast(s - m) : 0.0f;
     const float es = lane < p.n_meta ? exp_fast(tm - m) : 0.0f;
@@ -248,10 +258,16 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     __builtin_nontemporal_store(S[ii], (f32x4 *)(Sg + (size_t)r * kDV + col));
   }
   if (SWA) {
+    {
+      // weight 0 outside the window; even c4 owns columns 0..3 of the eight
+      // loaded, odd c4 columns 4..7 (lane ^ 1 is quad_perm [1,0,3,2])
+      const float pw = s_p[vslot];
 #pragma unroll
-    for (int jj = 0; jj < kKPT; ++jj) {
-      const int s2 = rg + kNRG * jj;
-      if (s2 < w) acc += s_p[s2] * vv[jj];  // zero weight outside the window
+      for (int e = 0; e < 4; ++e) {
+        const float lo = pw * vw[e], hi = pw * vw[4 + e];
+        const float own = (c4 & 1) ? hi : lo, other = (c4 & 1) ? lo : hi;
+        acc[e] += own + dpp_f<0xB1>(other);
+      }
     }
     if (rg == 0) acc += s_p[kMaxW] * v4;
   }
@@ -266,8 +282,8 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   // (8) ring append: slot pos % w holds token pos - w, which no block reads now
   if (SWA) {
     const int slot = pos % w;
-    if (slice == 0 && tid < kD / 4) V::st4(kc + (size_t)slot * kD + 4 * tid, V::ld4(kt + 4 * tid));
-    if (tid < kC4) V::st4(vc + (size_t)slot * kDV + slice * kDVS + 4 * tid, V::ld4(vt + slice * kDVS + 4 * tid));
+    if (slice == 0 && tid < kD / 4) V::st4(kc + (size_t)slot * kD + 4 * tid, kt4);
+    if (tid < kC4) V::st4(vc + (size_t)slot * kDV + col, v4);  // rg == 0: col = slice * kDVS + 4 tid
   }
 }
 
