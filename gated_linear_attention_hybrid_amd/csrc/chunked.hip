@@ -413,7 +413,9 @@ int device_cu_count() {
 
 bool chunked_supported(const LayerArgs &a, int parts) {
   if (!a.bf16 || a.d != kD || a.dv != kDV) return false;
-  if ((parts & PART_GLA) && (a.f != kF || a.chunk != kC)) return false;
+  // every accepted chunk request (16, 32, 64, 128) is served with 64-token
+  // chunks: the blocking changes only the rounding, not the result
+  if ((parts & PART_GLA) && a.f != kF) return false;
   if ((parts & PART_SWA) && (a.window < 1 || a.window > kC)) return false;
   return true;
 }

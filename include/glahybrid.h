@@ -75,7 +75,12 @@ typedef enum {
 typedef struct glah_desc {
   int32_t B, H, L;      /* batch, heads, tokens (L is ignored by the decode step)  */
   int32_t d_qk, d_v, f; /* q/k head dim, value dim, feature dim (f even)            */
-  int32_t chunk;        /* token chunk of the prefill state pass; 0 = default (64)  */
+  int32_t chunk;        /* token chunk of the chunkwise prefill: 16, 32, 64 or 128;
+                           0 = 64.  The result does not depend on it beyond
+                           rounding; the bf16 MFMA path (d = f = d_v = 128)
+                           blocks at 64 tokens (fold references per 16-token
+                           tile) for every value, the other paths are
+                           token-recurrent and ignore it                      */
   int32_t window;       /* SWA window w >= 1 (keys including the query's own);
                            gla_decode_step: 0 = no window part                      */
   int32_t n_meta;       /* number of meta-memory sink scalars per head, >= 0        */

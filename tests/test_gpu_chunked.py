@@ -256,8 +256,13 @@ def test_strong_decay_8k_sampled_heads():
     wl = WORKLOADS["strong_decay_8k"]
     say("strong decay B=8 L=8192, oracle on 4 sampled heads")
     x = make_prefill(wl, DEV)
+    # the workload names 128-token chunks; the MFMA path serves that request with
+    # its 64-token blocking, so it must give exactly what a 64-token request gives
     o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
-                           window=wl.window, chunk=64)
+                           window=wl.window, chunk=wl.chunk)
+    o64 = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                             window=wl.window, chunk=64)
+    assert wl.chunk == 128 and torch.equal(o, o64)
     assert_finite(o, "o")
     heads = [(0, 0), (3, 9), (5, 20), (7, 31)]
     got = gpu_f64(o)
