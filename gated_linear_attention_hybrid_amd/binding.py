@@ -25,7 +25,7 @@ GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per 
 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
            "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step", "glah_bwd_workspace_bytes",
-           "hybrid_layer_bwd")
+           "hybrid_layer_bwd", "gdn_prefill", "gdn_decode_step")
 
 
 class GlahError(RuntimeError):
@@ -73,6 +73,10 @@ def load(path: str = LIBRARY):
             lib.glah_bwd_workspace_bytes.restype = sz
             lib.hybrid_layer_bwd.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
             lib.hybrid_layer_bwd.restype = i32
+            lib.gdn_prefill.argtypes = [dp] + [vp] * 8 + [vp]
+            lib.gdn_prefill.restype = i32
+            lib.gdn_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
+            lib.gdn_decode_step.restype = i32
             _lib = lib
     return _lib
 
@@ -228,3 +232,32 @@ def hybrid_layer_bwd(q, k, v, gate, wq, wk, meta, d_o, *, window, scale=0.0, gat
                                  _stream(stream))
     _check("hybrid_layer_bwd", st)
     return out
+
+
+def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=None, stream=None):
+    """Gated delta rule over whole sequences; returns o [B,H,L,dv].  q, k
+    [B,H,L,d], v [B,H,L,dv], log_alpha and beta [B,H,L] (the dtype of q); states
+    [B,H,dv,d] fp32."""
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, L, d, dv, d, dtype=_dtype_code(q))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    st = load().gdn_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(log_alpha), _p(beta),
+                            _p(state_in), _p(state_out), _p(o), _stream(stream))
+    _check("gdn_prefill", st)
+    return o
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None):
+    """One gated delta rule token (state [B,H,dv,d] fp32 updated in place);
+    returns o [B,H,dv]."""
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, 1, d, dv, d, dtype=_dtype_code(q))
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    st = load().gdn_decode_step(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(log_alpha), _p(beta),
+                                _p(state), _p(o), _stream(stream))
+    _check("gdn_decode_step", st)
+    return o

@@ -69,6 +69,21 @@ bool opt(const void *p) { return aligned16(p); }
 
 glah_status finish(hipError_t e) { return e == hipSuccess ? GLAH_OK : GLAH_EHIP; }
 
+// Descriptor of the gated delta rule: B, H, L (prefill), d_qk, d_v, dtype.
+glah_status check_delta_desc(const glah_desc *d, bool decode, LayerArgs &a) {
+  if (!d) return GLAH_EINVAL;
+  if (d->B < 0 || d->H < 0 || d->d_qk <= 0 || d->d_v <= 0 || (!decode && d->L < 0)) return GLAH_EINVAL;
+  if (d->dtype != GLAH_BF16 && d->dtype != GLAH_F32) return GLAH_EINVAL;
+  const double L = decode ? 1.0 : (double)d->L;
+  if ((double)d->B * d->H * L * fmax((double)d->d_qk, (double)d->d_v) > 9.0e15 ||
+      (double)d->B * d->H * ((double)d->d_v + 15.0) / 16.0 > 2.0e9)
+    return GLAH_EINVAL;
+  a.B = d->B; a.H = d->H; a.L = decode ? 1 : d->L;
+  a.d = d->d_qk; a.dv = d->d_v; a.f = d->d_qk;  // the state is d_v x d_qk
+  a.bf16 = d->dtype == GLAH_BF16;
+  return delta_supported(a) ? GLAH_OK : GLAH_ENOTSUP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +264,45 @@ glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k
     g.dq = dq; g.dk = dk; g.dv = dv; g.dgate = dgate;
     g.dwq = dwphi_q; g.dwk = dwphi_k; g.dmeta = dmeta; g.dstate_in = dstate_in;
     return finish(launch_layer_bwd(a, g, PART_BOTH));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k, const void *v,
+                        const void *log_alpha, const void *beta, const float *state_in,
+                        float *state_out, void *o, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_delta_desc(desc, false, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(log_alpha, work) || !req(beta, work) ||
+        !req(o, work) || !opt(state_in) || !opt(state_out))
+      return GLAH_EINVAL;
+    a.q = q; a.k = k; a.v = v; a.gate = log_alpha; a.beta = beta;
+    a.state_in = state_in; a.state_out = state_out; a.o = o; a.stream = (hipStream_t)stream;
+    if (a.L == 0) return finish(launch_state_passthrough(a));  // f = d_qk: d_v x d_qk floats
+    return finish(launch_delta(a, false));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status gdn_decode_step(const glah_desc *desc, const void *q_t, const void *k_t, const void *v_t,
+                            const void *log_alpha_t, const void *beta_t, float *state, void *o_t,
+                            glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_delta_desc(desc, true, a);
+    if (st != GLAH_OK) return st;
+    const bool work = (size_t)a.B * a.H > 0;
+    if (!req(q_t, work) || !req(k_t, work) || !req(v_t, work) || !req(log_alpha_t, work) ||
+        !req(beta_t, work) || !req(state, work) || !req(o_t, work))
+      return GLAH_EINVAL;
+    a.q = q_t; a.k = k_t; a.v = v_t; a.gate = log_alpha_t; a.beta = beta_t;
+    a.state = state; a.o = o_t; a.stream = (hipStream_t)stream;
+    return finish(launch_delta(a, true));
   } catch (...) {
     return GLAH_EHIP;
   }

@@ -21,6 +21,7 @@ struct LayerArgs {
   int gate_mode = 0;
   const void *q = nullptr, *k = nullptr, *v = nullptr, *gate = nullptr;
   const void *wq = nullptr, *wk = nullptr;
+  const void *beta = nullptr;        // gated delta rule: write strength per token
   const float *meta = nullptr;
   const float *state_in = nullptr;
   float *state_out = nullptr;
@@ -73,6 +74,12 @@ struct BwdArgs {
 bool bwd_supported(const LayerArgs &a, int parts);
 size_t bwd_workspace_bytes(const LayerArgs &a, int parts);
 hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
+
+// Gated delta rule (token-recurrent prefill, bandwidth-bound decode step):
+// q, k [B][H][L][d], v and o [B][H][L][dv], log-decay (gate) and beta [B][H][L],
+// state [B][H][dv][d] fp32.
+bool delta_supported(const LayerArgs &a);
+hipError_t launch_delta(const LayerArgs &a, bool decode);
 
 int device_cu_count();
 

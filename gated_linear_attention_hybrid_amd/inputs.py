@@ -125,6 +125,38 @@ def make_decode_token(wl: Workload, step: int, device="cpu") -> dict:
     }
 
 
+def _delta_draws(wl: Workload, shape_tok, gen, dev, decay_mean=None):
+    dt = wl.torch_dtype
+    out = {
+        "q": _randn(shape_tok + (wl.d,), wl.x_std, 0.0, gen, dev, dt),
+        "k": _randn(shape_tok + (wl.d,), wl.x_std, 0.0, gen, dev, dt),
+        "v": _randn(shape_tok + (wl.dv,), wl.x_std, 0.0, gen, dev, dt),
+    }
+    mean = wl.gate_mean if decay_mean is None else decay_mean
+    # log-decays and write strengths as a Gated DeltaNet layer forms them from
+    # its projections: log sigmoid and sigmoid of normal logits
+    la = torch.randn(shape_tok, generator=gen, device=dev) * wl.gate_std + mean
+    out["log_alpha"] = torch.nn.functional.logsigmoid(la).to(dt)
+    bl = torch.randn(shape_tok, generator=gen, device=dev)
+    out["beta"] = torch.sigmoid(bl).to(dt)
+    return out
+
+
+def make_delta(wl: Workload, device="cpu", decay_mean=None) -> dict:
+    """Inputs of one gated delta rule prefill: q, k [B,H,L,d], v [B,H,L,dv],
+    log_alpha and beta [B,H,L].  Draw order q, k, v, decay logits, write-strength
+    logits; decay logits ~ N(gate_mean or decay_mean, gate_std), write-strength
+    logits ~ N(0, 1); its own seed stream (seed + 500)."""
+    dev = torch.device(device)
+    return _delta_draws(wl, (wl.B, wl.H, wl.L), _gen(wl.seed + 500, dev), dev, decay_mean)
+
+
+def make_delta_token(wl: Workload, step: int, device="cpu") -> dict:
+    """Per-step inputs of gated delta rule decode step ``step`` ([B,H,*])."""
+    dev = torch.device(device)
+    return _delta_draws(wl, (wl.B, wl.H), _gen((wl.seed + 500) * 1000003 + 7919 * (step + 1), dev), dev)
+
+
 def to_f64(t: torch.Tensor):
     """Exact widening of a (bf16 or fp32) tensor to a float64 numpy array."""
     return t.detach().to("cpu", torch.float64).numpy()

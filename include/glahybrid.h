@@ -193,6 +193,44 @@ glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k
                              float *dmeta, float *dstate_in, void *ws,
                              size_t ws_bytes, glah_stream_t stream);
 
+/*
+ * gdn_prefill -- the gated delta rule (Gated DeltaNet), the token mixer that
+ * "systematic analysis of hybrid linear attention" (2507.06457, findings and
+ * recommendations) and the "LT2" summary (2605.20670, hybrid designs) pair
+ * with attention: an error-correcting write into the state with gated
+ * forgetting.  The pages give it in words only; this is the published
+ * recurrence, per (b, h), with the state M kept as d_v rows of d_qk:
+ *     k^ = k_t / sqrt(|k_t|^2 + 1e-6),  q^ = q_t / sqrt(|q_t|^2 + 1e-6)
+ *     M_t = alpha_t M_{t-1} (I - beta_t k^ k^T) + beta_t v_t k^T,  alpha_t = e^{a_t}
+ *     o_t = M_t q^
+ *   q, k        [B][H][L][d_qk]  desc->dtype
+ *   v, o        [B][H][L][d_v]   desc->dtype
+ *   log_alpha   [B][H][L]        desc->dtype, a_t <= 0 (-inf allowed: alpha = 0)
+ *   beta        [B][H][L]        desc->dtype, write strength in [0, 1]
+ *   state_in    nullable; [B][H][d_v][d_qk] fp32 state before token 0 (0 if NULL)
+ *   state_out   nullable; [B][H][d_v][d_qk] fp32, receives M_{L-1} (L = 0: the
+ *               state before the sequence); may equal state_in
+ * Reads B, H, L, d_qk, d_v and dtype of the descriptor; the other fields are
+ * ignored.  Supported: d_qk in {32, 64, 128}, any d_v >= 1 (else
+ * GLAH_ENOTSUP).  fp32 arithmetic, token-recurrent (each value row of the
+ * state is an independent recurrence), bitwise repeatable; no workspace.
+ */
+glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k,
+                        const void *v, const void *log_alpha, const void *beta,
+                        const float *state_in, float *state_out, void *o,
+                        glah_stream_t stream);
+
+/*
+ * gdn_decode_step -- one token of the gated delta rule for every (b, h): the
+ * same update as gdn_prefill with L = 1, the state updated in place.
+ *   q_t, k_t    [B][H][d_qk]; v_t, o_t [B][H][d_v]; log_alpha_t, beta_t [B][H]
+ *   state       [B][H][d_v][d_qk] fp32, in/out
+ */
+glah_status gdn_decode_step(const glah_desc *desc, const void *q_t,
+                            const void *k_t, const void *v_t,
+                            const void *log_alpha_t, const void *beta_t,
+                            float *state, void *o_t, glah_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

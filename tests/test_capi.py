@@ -180,3 +180,48 @@ def test_backward_argument_checks(lib):
     for bad in (dict(d=256), dict(dv=66), dict(f=96), dict(f=256), dict(window=2048)):
         assert _bwd(lib, _desc(**bad), 1 << 40) == binding.GLAH_ENOTSUP, bad
     assert lib.glah_bwd_workspace_bytes(ctypes.byref(_desc(f=7))) == ctypes.c_size_t(-1).value
+
+
+def _gdn_desc(**kw):
+    base = dict(B=1, H=2, L=16, d=64, dv=64)
+    base.update(kw)
+    return binding.make_desc(base["B"], base["H"], base["L"], base["d"], base["dv"], base["d"],
+                             dtype=kw.get("dtype", binding.GLAH_F32))
+
+
+def _gdn_prefill(lib, desc, ptrs=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs  # q k v a beta state_in state_out o
+    return lib.gdn_prefill(ctypes.byref(desc), *[ctypes.c_void_p(x) for x in p[:8]], None)
+
+
+@pytest.mark.parametrize("bad", [dict(d=0), dict(dv=0), dict(B=-1), dict(H=-1), dict(L=-1), dict(dtype=9)])
+def test_gdn_bad_descriptor_is_einval(lib, bad):
+    assert _gdn_prefill(lib, _gdn_desc(**bad)) == binding.GLAH_EINVAL
+
+
+@pytest.mark.parametrize("d", [16, 48, 256])
+def test_gdn_unsupported_key_dim_is_enotsup(lib, d):
+    assert _gdn_prefill(lib, _gdn_desc(d=d)) == binding.GLAH_ENOTSUP
+
+
+@pytest.mark.parametrize("missing", range(5))
+def test_gdn_missing_input_is_einval(lib, missing):
+    p = [FAKE] * 8
+    p[missing] = 0
+    assert _gdn_prefill(lib, _gdn_desc(), p) == binding.GLAH_EINVAL
+
+
+def test_gdn_misaligned_and_null_checks(lib):
+    p = [FAKE] * 8
+    p[4] = FAKE + 2
+    assert _gdn_prefill(lib, _gdn_desc(), p) == binding.GLAH_EINVAL
+    p = [FAKE] * 8
+    p[7] = 0  # o
+    assert _gdn_prefill(lib, _gdn_desc(), p) == binding.GLAH_EINVAL
+    assert lib.gdn_prefill(None, *[ctypes.c_void_p(FAKE)] * 8, None) == binding.GLAH_EINVAL
+    d = _gdn_desc()
+    args = [ctypes.c_void_p(FAKE)] * 7
+    args[5] = ctypes.c_void_p(0)  # state
+    assert lib.gdn_decode_step(ctypes.byref(d), *args, None) == binding.GLAH_EINVAL
+    assert lib.gdn_decode_step(ctypes.byref(_gdn_desc(d=96)), *[ctypes.c_void_p(FAKE)] * 7,
+                               None) == binding.GLAH_ENOTSUP
