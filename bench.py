@@ -224,6 +224,88 @@ def bench_backward(G, torch, wl, reps=5, warmup=2):
             "nonfinite_outputs": bad}
 
 
+# gated delta rule at d = d_v = 128, bf16: q, k, v read and o written once
+# (4 x 256 B) plus the log-decay and write strength (2 x 2 B) per token-head
+DELTA_BYTES_PER_TOKEN_HEAD = 4 * 256 + 2 * 2
+
+
+def bench_delta(G, torch, reps=5, warmup=2, steps=256, sets=12):
+    """gdn_prefill over the 32K-token shape (32 heads of 128) and the gdn_decode_step
+    at batch 8 (256 graph-captured steps rotating over 12 state sets), each against
+    the HBM roofline of its algorithmic bytes."""
+    from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_delta, make_delta_token
+    dev = torch.device("cuda")
+    wl = WORKLOADS["prefill_32k"]
+    x = make_delta(wl, dev)
+    st = torch.empty((wl.B, wl.H, wl.dv, wl.d), device=dev)
+    o = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=wl.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        G.gdn_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state_out=st, o=o, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    nbytes = DELTA_BYTES_PER_TOKEN_HEAD * wl.B * wl.H * wl.L
+    pre = {"workload": "gdn prefill: B=%d H=%d L=%d d=d_v=%d bf16, fp32 state" % (wl.B, wl.H, wl.L, wl.d),
+           "ms_per_call": round(ms, 3), "tokens_per_s": round(wl.B * wl.L / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": nbytes},
+           "nonfinite_outputs": int((~torch.isfinite(o.float())).sum().item())}
+    del x, o
+    wd = WORKLOADS["decode_b8"]
+    B, H = wd.B, wd.H
+    x = make_delta(wd.with_(L=64), dev)
+    st0 = torch.empty((B, H, wd.dv, wd.d), device=dev)
+    G.gdn_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state_out=st0)
+    states = [st0.clone() for _ in range(sets)]
+    toks = [make_delta_token(wd, s, dev) for s in range(steps)]
+    outs = [torch.empty((B, H, wd.dv), dtype=wd.torch_dtype, device=dev) for _ in range(steps)]
+
+    def run_all(strm):
+        for s in range(steps):
+            t = toks[s]
+            G.gdn_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], states[s % sets],
+                              o=outs[s], stream=strm)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all(torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (5 * steps)
+    dbytes = B * H * wd.dv * wd.d * 4 * 2 + B * H * (3 * wd.d + wd.dv + 2) * 2
+    dec = {"workload": "gdn decode: B=%d H=%d state %dx%d fp32, bf16 I/O" % (B, H, wd.dv, wd.d),
+           "steps_per_graph": steps, "state_sets": sets, "us_per_step": round(us, 3),
+           "tokens_per_s": round(B / (us * 1e-6), 1),
+           "roofline": {"bound": "hbm", "achieved": round(dbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_step": dbytes},
+           "nonfinite_outputs": int((~torch.isfinite(outs[-1].float())).sum().item())}
+    return {"prefill": pre, "decode": dec}
+
+
 def measured_ceilings(torch):
     """What this GPU reaches on plain library work: a 1 GiB device copy (HBM) and
     a large bf16 GEMM (hipBLASLt through torch), best of 3 each."""
@@ -309,6 +391,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-delta", action="store_true")
+    ap.add_argument("--delta-only", action="store_true",
+                    help="run only the gated delta rule leg (for profiling) and print its JSON")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the backward leg (for profiling) and print its JSON")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -335,6 +420,9 @@ def main():
     if args.backward_only:
         print(json.dumps({"backward": [bench_backward(G, torch, WORKLOADS["prefill_2k"]),
                                        bench_backward(G, torch, wl)]}), flush=True)
+        return
+    if args.delta_only:
+        print(json.dumps({"gated_delta": bench_delta(G, torch)}), flush=True)
         return
     ms_step, per_call_ms, bad = bench_prefill(G, wl, args.steps, args.warmup, torch)
     token_heads = wl.B * wl.H * wl.L
@@ -388,6 +476,8 @@ def main():
                                      "prefix_32768_us_per_step": out["decode"]["us_per_step"]}
     if not args.no_backward:
         out["backward"] = [bench_backward(G, torch, WORKLOADS["prefill_2k"]), bench_backward(G, torch, wl)]
+    if not args.no_delta:
+        out["gated_delta"] = bench_delta(G, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)

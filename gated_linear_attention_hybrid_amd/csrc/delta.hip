@@ -27,7 +27,6 @@ constexpr int kLPR = 16;                 // lanes per state row
 constexpr int kThreads = 256;            // 4 waves x 4 rows = 16 rows per block
 constexpr int kRowsPerBlock = kThreads / kLPR;
 constexpr float kNormEps = 1e-6f;        // added to |x|^2 under the root
-constexpr int kAhead = 8;                // prefill: tokens of operands in flight
 
 struct DeltaParams {
   const void *q, *k, *v, *a, *beta;
@@ -42,8 +41,7 @@ struct VecOf {
   typedef T type __attribute__((ext_vector_type(N)));
 };
 
-// Operands of one token for one lane, as loaded (widened to fp32 only where
-// they are used, so a load in flight never stalls the lane).
+// Operands of one decode token for one lane, as loaded.
 template <class T, int EPL>
 struct TokenOps {
   typename VecOf<T, EPL>::type k, q;  // this lane's d_k / 16 elements of k_t and q_t
@@ -63,52 +61,164 @@ __device__ __forceinline__ void load_token(const DeltaParams &p, size_t bh, int 
   x.beta = ((const T *)p.beta)[tok];
 }
 
-// One token of one row: updates m in place and returns o_t[row] (every lane
-// of the row holds it).
-template <class T, int EPL>
-__device__ __forceinline__ float delta_token(float (&m)[EPL], const TokenOps<T, EPL> &x) {
-  float k[EPL], q[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    k[e] = to_f32(x.k[e]);
-    q[e] = to_f32(x.q[e]);
+// Sum over groups of G consecutive lanes (G in {4, 8, 16, 32}), every lane
+// of a group receiving its group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f<0xB1>(x);  // lane ^ 1
+  x += dpp_f<0x4E>(x);  // lane ^ 2
+  if constexpr (G >= 8) x += dpp_f<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if constexpr (G >= 16) x += dpp_f<0x140>(x);  // row_mirror: the other 8 of the 16
+  if constexpr (G >= 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0<->1, 2<->3
+    x = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
   }
-  float kk = 0.0f, qq = 0.0f;
+  return x;
+}
+
+// Dot product of a lane's EPL elements with two partial sums (a shorter
+// dependent chain than one running sum).
+template <int EPL>
+__device__ __forceinline__ float dot2(const float (&x)[EPL], const float (&y)[EPL]) {
+  float s0 = x[0] * y[0], s1 = EPL > 1 ? x[1] * y[1] : 0.0f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    kk += k[e] * k[e];
-    qq += q[e] * q[e];
+  for (int e = 2; e < EPL; e += 2) {
+    s0 += x[e] * y[e];
+    if (e + 1 < EPL) s1 += x[e + 1] * y[e + 1];
   }
-  kk = row16_reduce(kk, OpAdd());
-  qq = row16_reduce(qq, OpAdd());
-  const float rk = __builtin_amdgcn_rsqf(kk + kNormEps);
-  const float rq = __builtin_amdgcn_rsqf(qq + kNormEps);
-  // recall of the normalised key: (m . k) / |k|
-  float mk = 0.0f;
+  return s0 + s1;
+}
+
+// One token of one row from the normalised key and query slices: updates m in
+// place and returns o_t[row] (every lane of the 16-lane row holds it).
+//   m <- alpha m + beta (v - alpha (m . k^)) k^,   o = m . q^
+template <int EPL>
+__device__ __forceinline__ float delta_row(float (&m)[EPL], const float (&kh)[EPL], const float (&qh)[EPL],
+                                           float v, float alpha, float beta) {
+  const float mk = row16_reduce(dot2<EPL>(m, kh), OpAdd());
+  const float c = beta * (v - alpha * mk);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) mk += m[e] * k[e];
-  mk = row16_reduce(mk, OpAdd()) * rk;
-  const float alpha = exp2_fast(to_f32(x.a) * kLog2e);  // a = -inf gives 0
-  const float c = to_f32(x.beta) * (to_f32(x.v) - alpha * mk) * rk;  // coefficient of the raw key
-  float mq = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    m[e] = alpha * m[e] + c * k[e];
-    mq += m[e] * q[e];
-  }
-  return row16_reduce(mq, OpAdd()) * rq;
+  for (int e = 0; e < EPL; ++e) m[e] = alpha * m[e] + c * kh[e];
+  return row16_reduce(dot2<EPL>(m, qh), OpAdd());
+}
+
+// 1 / sqrt(|x|^2 + eps) of the row a 16-lane group holds (EPL elements per lane)
+template <int EPL>
+__device__ __forceinline__ float row_rnorm(const float (&x)[EPL]) {
+  return __builtin_amdgcn_rsqf(row16_reduce(dot2<EPL>(x, x), OpAdd()) + kNormEps);
 }
 
 // Prefill: one 16-lane row per state row, the whole sequence in registers.
-// Operands are loaded kAhead tokens ahead into a register ring so the serial
-// chain of each row never waits on memory.
+// The block's 16 rows belong to one head and share every token's k, q, a and
+// beta, so the block stages tiles of kTile tokens in LDS, already prepared:
+// k^ and q^ normalised in fp32, alpha = e^a and beta widened.  While the waves
+// run the recurrence of one tile from LDS, the next tile's global loads are in
+// flight in registers (issued at the start of the tile, prepared and written to
+// the other LDS buffer at its end, one barrier per tile), so the serial chain
+// of a row waits only on LDS and holds only the state-dependent work.  Outputs
+// go to LDS and leave once per tile.
+constexpr int kTile = 32;
+
+template <class T, int EPL>
+struct DeltaTile {
+  static constexpr int DK = EPL * kLPR;
+  static constexpr int kCE = 16 / (int)sizeof(T);                    // elements per 16-byte chunk
+  static constexpr int kCPT = DK / kCE;                               // chunks per token row
+  static constexpr int kChunks = kTile * kCPT;                        // chunks of k (or q) per tile
+  static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;   // per thread
+  static constexpr int kVPer = kTile * kRowsPerBlock / kThreads;     // v (and o) elements per thread
+  alignas(16) float kh[2][kTile][DK];
+  alignas(16) float qh[2][kTile][DK];
+  float alpha[2][kTile], beta[2][kTile];
+  T v[2][kTile][kRowsPerBlock], o[2][kTile][kRowsPerBlock];
+};
+
+template <class T, int EPL>
+struct TileRegs {
+  u32x4 k[DeltaTile<T, EPL>::kPer], q[DeltaTile<T, EPL>::kPer];
+  T v[DeltaTile<T, EPL>::kVPer];
+  T ab;  // a (threads 0 .. kTile-1) or beta (kTile .. 2 kTile-1)
+};
+
+template <class T, int EPL>
+__device__ __forceinline__ void tile_load(const DeltaParams &p, size_t bh, int rb, int t0, TileRegs<T, EPL> &r) {
+  using Tl = DeltaTile<T, EPL>;
+  const int tid = threadIdx.x;
+  // k and q rows of tokens t0 .. t0 + kTile - 1 are contiguous; past the end
+  // the chunk index is clamped to the last token's chunks (never used)
+  const size_t base = bh * (size_t)p.L * Tl::kCPT;
+  const size_t last = (size_t)p.L * Tl::kCPT - 1;
+#pragma unroll
+  for (int c = 0; c < Tl::kPer; ++c) {
+    const int ch = tid + c * kThreads;
+    if (ch < Tl::kChunks) {
+      const size_t g = base + min((size_t)t0 * Tl::kCPT + ch, last);
+      r.k[c] = ((const u32x4 *)p.k)[g];
+      r.q[c] = ((const u32x4 *)p.q)[g];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < Tl::kVPer; ++e) {
+    const int idx = tid + e * kThreads, tt = idx / kRowsPerBlock, rr = rb * kRowsPerBlock + idx % kRowsPerBlock;
+    const size_t tok = bh * (size_t)p.L + min(t0 + tt, p.L - 1);
+    r.v[e] = ((const T *)p.v)[tok * p.dv + min(rr, p.dv - 1)];
+  }
+  if (tid < 2 * kTile) {
+    const size_t tok = bh * (size_t)p.L + min(t0 + (tid % kTile), p.L - 1);
+    r.ab = tid < kTile ? ((const T *)p.a)[tok] : ((const T *)p.beta)[tok];
+  }
+}
+
+// Normalises the tile's keys and queries (the kCPT chunks of a token row sit in
+// kCPT consecutive lanes, so |k|^2 is a group sum) and writes the prepared tile.
+template <class T, int EPL>
+__device__ __forceinline__ void tile_store(DeltaTile<T, EPL> &lds, int buf, const TileRegs<T, EPL> &r) {
+  using Tl = DeltaTile<T, EPL>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < Tl::kPer; ++c) {
+    const int ch = tid + c * kThreads;
+    if (Tl::kChunks % kThreads == 0 || ch < Tl::kChunks) {  // whole lane groups either way
+      float kx[Tl::kCE], qx[Tl::kCE];
+      const T *ke = (const T *)&r.k[c], *qe = (const T *)&r.q[c];
+#pragma unroll
+      for (int j = 0; j < Tl::kCE; ++j) {
+        kx[j] = to_f32(ke[j]);
+        qx[j] = to_f32(qe[j]);
+      }
+      const float rk = __builtin_amdgcn_rsqf(group_sum<Tl::kCPT>(dot2<Tl::kCE>(kx, kx)) + kNormEps);
+      const float rq = __builtin_amdgcn_rsqf(group_sum<Tl::kCPT>(dot2<Tl::kCE>(qx, qx)) + kNormEps);
+      float *kd = &lds.kh[buf][0][0] + ch * Tl::kCE, *qd = &lds.qh[buf][0][0] + ch * Tl::kCE;
+#pragma unroll
+      for (int j = 0; j < Tl::kCE; j += 4) {
+        *(f32x4 *)(kd + j) = (f32x4){kx[j] * rk, kx[j + 1] * rk, kx[j + 2] * rk, kx[j + 3] * rk};
+        *(f32x4 *)(qd + j) = (f32x4){qx[j] * rq, qx[j + 1] * rq, qx[j + 2] * rq, qx[j + 3] * rq};
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < Tl::kVPer; ++e) {
+    const int idx = tid + e * kThreads;
+    lds.v[buf][idx / kRowsPerBlock][idx % kRowsPerBlock] = r.v[e];
+  }
+  if (tid < kTile)
+    lds.alpha[buf][tid] = exp2_fast(to_f32(r.ab) * kLog2e);  // a = -inf gives 0
+  else if (tid < 2 * kTile)
+    lds.beta[buf][tid - kTile] = to_f32(r.ab);
+}
+
 template <class T, int EPL>
 __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(DeltaParams p) {
+  using Tl = DeltaTile<T, EPL>;
   constexpr int DK = EPL * kLPR;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
+  __shared__ Tl lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
   const int nrb = (p.dv + kRowsPerBlock - 1) / kRowsPerBlock;
   const size_t bh = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x % nrb) * kRowsPerBlock + wave * 4 + (lane >> 4);
+  const int rb = blockIdx.x % nrb;
+  const int rloc = wave * 4 + (lane >> 4);  // row within the block
+  const int row0 = rb * kRowsPerBlock + rloc;
   const bool live = row0 < p.dv;
   const int row = live ? row0 : p.dv - 1;  // rows past d_v compute a copy, store nothing
 
@@ -121,22 +231,63 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(DeltaParams p) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) m[e] = 0.0f;
   }
-  T *o = (T *)p.o + bh * (size_t)p.L * p.dv + row;
 
-  TokenOps<T, EPL> ring[kAhead];
+  TileRegs<T, EPL> regs;
+  tile_load<T, EPL>(p, bh, rb, 0, regs);
+  tile_store<T, EPL>(lds, 0, regs);
+  __syncthreads();
+  const int ntiles = (p.L + kTile - 1) / kTile;
+  for (int i = 0; i < ntiles; ++i) {
+    const int buf = i & 1, t0 = i * kTile;
+    const bool more = i + 1 < ntiles;
+    if (more) tile_load<T, EPL>(p, bh, rb, t0 + kTile, regs);
+    const int n = min(kTile, p.L - t0);
+    // o_t of the row for token j is kept by lane j % 16 of the row (ob[j / 16]),
+    // so the token loop has no branch and no LDS write: the next token's LDS
+    // reads can be issued while this token's chain runs
+    float ob0 = 0.0f, ob1 = 0.0f;
+    auto token = [&](int j) {
+      float kh[EPL], qh[EPL];
+      if constexpr (EPL % 4 == 0) {
 #pragma unroll
-  for (int j = 0; j < kAhead; ++j) load_token<T, EPL>(p, bh, row, l16, min(j, p.L - 1), ring[j]);
-  for (int t0 = 0; t0 < p.L; t0 += kAhead) {
+        for (int e = 0; e < EPL; e += 4) {
+          const f32x4 a = *(const f32x4 *)__builtin_assume_aligned(&lds.kh[buf][j][l16 * EPL + e], 16);
+          const f32x4 b = *(const f32x4 *)__builtin_assume_aligned(&lds.qh[buf][j][l16 * EPL + e], 16);
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) {
-      const int t = t0 + j;
-      if (t < p.L) {
-        const float ot = delta_token<T, EPL>(m, ring[j]);
-        if (live && l16 == 0) o[(size_t)t * p.dv] = from_f32<T>(ot);
-        // refill the slot with token t + kAhead (clamped: the last token is
-        // re-read past the end and never used)
-        load_token<T, EPL>(p, bh, row, l16, min(t + kAhead, p.L - 1), ring[j]);
+          for (int u = 0; u < 4; ++u) {
+            kh[e + u] = a[u];
+            qh[e + u] = b[u];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          kh[e] = lds.kh[buf][j][l16 * EPL + e];
+          qh[e] = lds.qh[buf][j][l16 * EPL + e];
+        }
       }
+      const float ot = delta_row<EPL>(m, kh, qh, to_f32(lds.v[buf][j][rloc]), lds.alpha[buf][j], lds.beta[buf][j]);
+      ob0 = (j == l16) ? ot : ob0;
+      ob1 = (j == l16 + 16) ? ot : ob1;
+    };
+    if (n == kTile) {
+#pragma unroll 4
+      for (int j = 0; j < kTile; ++j) token(j);
+    } else {
+      for (int j = 0; j < n; ++j) token(j);
+    }
+    lds.o[buf][l16][rloc] = from_f32<T>(ob0);
+    lds.o[buf][l16 + 16][rloc] = from_f32<T>(ob1);
+    if (more) tile_store<T, EPL>(lds, buf ^ 1, regs);
+    __syncthreads();
+    // the tile's outputs: kRowsPerBlock consecutive values of each token row
+    // (double-buffered: the next tile writes the other half while slower waves
+    // may still read this one)
+#pragma unroll
+    for (int e = 0; e < Tl::kVPer; ++e) {
+      const int idx = tid + e * kThreads, tt = idx / kRowsPerBlock, rr = rb * kRowsPerBlock + idx % kRowsPerBlock;
+      if (tt < n && rr < p.dv)
+        ((T *)p.o)[(bh * (size_t)p.L + t0 + tt) * p.dv + rr] = lds.o[buf][tt][idx % kRowsPerBlock];
     }
   }
   if (p.state_out && live) {
@@ -177,7 +328,19 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(DeltaParams p) {
     one.L = 1;
     load_token<T, EPL>(one, bh, row, l16, 0, x);
   }
-  const float ot = delta_token<T, EPL>(m, x);
+  float kh[EPL], qh[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    kh[e] = to_f32(x.k[e]);
+    qh[e] = to_f32(x.q[e]);
+  }
+  const float rk = row_rnorm<EPL>(kh), rq = row_rnorm<EPL>(qh);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    kh[e] *= rk;
+    qh[e] *= rq;
+  }
+  const float ot = delta_row<EPL>(m, kh, qh, to_f32(x.v), exp2_fast(to_f32(x.a) * kLog2e), to_f32(x.beta));
   if (live) {
     if constexpr (EPL % 4 == 0) {
 #pragma unroll
