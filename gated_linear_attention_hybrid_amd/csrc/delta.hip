@@ -92,12 +92,12 @@ __device__ __forceinline__ float dot2(const float (&x)[EPL], const float (&y)[EP
 
 // One token of one row from the normalised key and query slices: updates m in
 // place and returns o_t[row] (every lane of the 16-lane row holds it).
-//   m <- alpha m + beta (v - alpha (m . k^)) k^,   o = m . q^
+//   m <- alpha m + (beta v - alpha beta (m . k^)) k^,   o = m . q^
 template <int EPL>
 __device__ __forceinline__ float delta_row(float (&m)[EPL], const float (&kh)[EPL], const float (&qh)[EPL],
-                                           float v, float alpha, float beta) {
+                                           float alpha, float alpha_beta, float beta_v) {
   const float mk = row16_reduce(dot2<EPL>(m, kh), OpAdd());
-  const float c = beta * (v - alpha * mk);
+  const float c = beta_v - alpha_beta * mk;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) m[e] = alpha * m[e] + c * kh[e];
   return row16_reduce(dot2<EPL>(m, qh), OpAdd());
@@ -130,8 +130,10 @@ struct DeltaTile {
   static constexpr int kVPer = kTile * kRowsPerBlock / kThreads;     // v (and o) elements per thread
   alignas(16) float kh[2][kTile][DK];
   alignas(16) float qh[2][kTile][DK];
-  float alpha[2][kTile], beta[2][kTile];
-  T v[2][kTile][kRowsPerBlock], o[2][kTile][kRowsPerBlock];
+  // per token and row: alpha, alpha beta, beta v_t[row] (one 16-byte read)
+  alignas(16) f32x4 rec[2][kTile][kRowsPerBlock];
+  float alpha[kTile], beta[kTile];  // of the tile being prepared
+  T o[2][kTile][kRowsPerBlock];
 };
 
 template <class T, int EPL>
@@ -197,15 +199,17 @@ __device__ __forceinline__ void tile_store(DeltaTile<T, EPL> &lds, int buf, cons
       }
     }
   }
+  if (tid < kTile)
+    lds.alpha[tid] = exp2_fast(to_f32(r.ab) * kLog2e);  // a = -inf gives 0
+  else if (tid < 2 * kTile)
+    lds.beta[tid - kTile] = to_f32(r.ab);
+  __syncthreads();  // alpha, beta of the tile visible to the record writers
 #pragma unroll
   for (int e = 0; e < Tl::kVPer; ++e) {
-    const int idx = tid + e * kThreads;
-    lds.v[buf][idx / kRowsPerBlock][idx % kRowsPerBlock] = r.v[e];
+    const int idx = tid + e * kThreads, tt = idx / kRowsPerBlock;
+    const float al = lds.alpha[tt], be = lds.beta[tt];
+    lds.rec[buf][tt][idx % kRowsPerBlock] = (f32x4){al, al * be, be * to_f32(r.v[e]), 0.0f};
   }
-  if (tid < kTile)
-    lds.alpha[buf][tid] = exp2_fast(to_f32(r.ab) * kLog2e);  // a = -inf gives 0
-  else if (tid < 2 * kTile)
-    lds.beta[buf][tid - kTile] = to_f32(r.ab);
 }
 
 template <class T, int EPL>
@@ -266,7 +270,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(DeltaParams p) {
           qh[e] = lds.qh[buf][j][l16 * EPL + e];
         }
       }
-      const float ot = delta_row<EPL>(m, kh, qh, to_f32(lds.v[buf][j][rloc]), lds.alpha[buf][j], lds.beta[buf][j]);
+      const f32x4 rc = lds.rec[buf][j][rloc];
+      const float ot = delta_row<EPL>(m, kh, qh, rc[0], rc[1], rc[2]);
       ob0 = (j == l16) ? ot : ob0;
       ob1 = (j == l16 + 16) ? ot : ob1;
     };
@@ -340,7 +345,8 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(DeltaParams p) {
     kh[e] *= rk;
     qh[e] *= rq;
   }
-  const float ot = delta_row<EPL>(m, kh, qh, to_f32(x.v), exp2_fast(to_f32(x.a) * kLog2e), to_f32(x.beta));
+  const float alpha = exp2_fast(to_f32(x.a) * kLog2e), beta = to_f32(x.beta);
+  const float ot = delta_row<EPL>(m, kh, qh, alpha, alpha * beta, beta * to_f32(x.v));
   if (live) {
     if constexpr (EPL % 4 == 0) {
 #pragma unroll
