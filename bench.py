@@ -306,6 +306,66 @@ def bench_delta(G, torch, reps=5, warmup=2, steps=256, sets=12):
     return {"prefill": pre, "decode": dec}
 
 
+def bench_serving(G, torch, reps=20):
+    """Serving pieces at the 32K layer shape: the output-gate epilogue over the
+    whole output (HBM roofline: o read and written, g read, 3 x 256 B per
+    token-head) and a 2048-token continuation prefill at position 30720 (state
+    and window ring of the previous 30720 tokens in and out)."""
+    from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_prefill
+    dev = torch.device("cuda")
+    wl = WORKLOADS["prefill_32k"]
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 91)
+    o = torch.randn((wl.B, wl.H, wl.L, wl.dv), generator=gen, device=dev).to(wl.torch_dtype)
+    g = torch.randn((wl.B, wl.H, wl.L, wl.dv), generator=gen, device=dev).to(wl.torch_dtype)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+
+    ms = timed(lambda: G.output_gate(o, g, stream=stream))
+    nbytes = 3 * o.numel() * o.element_size()
+    gate = {"workload": "output gate o * sigmoid(g), [1,32,32768,128] bf16", "us_per_call": round(ms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": nbytes}}
+    del o, g
+    pw = wl.with_(L=2048)
+    x = make_prefill(pw, dev)
+    start = 30720
+    st = torch.randn((pw.B, pw.H, pw.f, pw.dv), generator=gen, device=dev) * 0.01
+    kc = torch.randn((pw.B, pw.H, pw.window, pw.d), generator=gen, device=dev).to(pw.torch_dtype)
+    vc = torch.randn((pw.B, pw.H, pw.window, pw.dv), generator=gen, device=dev).to(pw.torch_dtype)
+    st_out, kco, vco = torch.empty_like(st), torch.empty_like(kc), torch.empty_like(vc)
+    oo = torch.empty((pw.B, pw.H, pw.L, pw.dv), dtype=pw.torch_dtype, device=dev)
+    desc = G.make_desc(pw.B, pw.H, pw.L, pw.d, pw.dv, pw.f, window=pw.window, n_meta=pw.n_meta, dtype=G.GLAH_BF16)
+    ws = torch.empty(max(1, G.workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+
+    def cont():
+        G.hybrid_layer_fwd_cont(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], window=pw.window,
+                                start=start, state_in=st, kcache_in=kc, vcache_in=vc, state_out=st_out,
+                                kcache_out=kco, vcache_out=vco, o=oo, ws=ws, stream=stream)
+
+    def whole():
+        G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], window=pw.window,
+                           state_in=st, state_out=st_out, kcache_out=kco, vcache_out=vco, o=oo, ws=ws,
+                           stream=stream)
+
+    ms_c, ms_w = timed(cont), timed(whole)
+    contd = {"workload": "continuation prefill: 2048 tokens at position 30720, B=1 H=32 d=f=d_v=128, window 64",
+             "us_per_call": round(ms_c * 1e3, 2), "tokens_per_s": round(pw.L / (ms_c * 1e-3), 1),
+             "same_call_from_position_0_us": round(ms_w * 1e3, 2)}
+    return {"output_gate": gate, "continuation": contd}
+
+
 def measured_ceilings(torch):
     """What this GPU reaches on plain library work: a 1 GiB device copy (HBM) and
     a large bf16 GEMM (hipBLASLt through torch), best of 3 each."""
@@ -392,6 +452,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-delta", action="store_true")
+    ap.add_argument("--no-serving", action="store_true")
     ap.add_argument("--delta-only", action="store_true",
                     help="run only the gated delta rule leg (for profiling) and print its JSON")
     ap.add_argument("--backward-only", action="store_true",
@@ -422,7 +483,7 @@ def main():
                                        bench_backward(G, torch, wl)]}), flush=True)
         return
     if args.delta_only:
-        print(json.dumps({"gated_delta": bench_delta(G, torch)}), flush=True)
+        print(json.dumps({"gated_delta": bench_delta(G, torch), "serving": bench_serving(G, torch)}), flush=True)
         return
     ms_step, per_call_ms, bad = bench_prefill(G, wl, args.steps, args.warmup, torch)
     token_heads = wl.B * wl.H * wl.L
@@ -478,6 +539,8 @@ def main():
         out["backward"] = [bench_backward(G, torch, WORKLOADS["prefill_2k"]), bench_backward(G, torch, wl)]
     if not args.no_delta:
         out["gated_delta"] = bench_delta(G, torch)
+    if not args.no_serving:
+        out["serving"] = bench_serving(G, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)

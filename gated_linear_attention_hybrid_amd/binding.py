@@ -25,7 +25,8 @@ GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per 
 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
            "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step", "glah_bwd_workspace_bytes",
-           "hybrid_layer_bwd", "gdn_prefill", "gdn_decode_step")
+           "hybrid_layer_bwd", "gdn_prefill", "gdn_decode_step", "hybrid_layer_fwd_cont",
+           "glah_output_gate")
 
 
 class GlahError(RuntimeError):
@@ -73,6 +74,10 @@ def load(path: str = LIBRARY):
             lib.glah_bwd_workspace_bytes.restype = sz
             lib.hybrid_layer_bwd.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
             lib.hybrid_layer_bwd.restype = i32
+            lib.hybrid_layer_fwd_cont.argtypes = [dp, ctypes.c_int32] + [vp] * 15 + [sz, vp]
+            lib.hybrid_layer_fwd_cont.restype = i32
+            lib.glah_output_gate.argtypes = [dp, vp, vp, vp]
+            lib.glah_output_gate.restype = i32
             lib.gdn_prefill.argtypes = [dp] + [vp] * 8 + [vp]
             lib.gdn_prefill.restype = i32
             lib.gdn_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
@@ -171,6 +176,37 @@ def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
                                  _p(wk), _p(meta), _p(state_in), _p(state_out), _p(kcache_out),
                                  _p(vcache_out), _p(o), _p(ws), nbytes, _stream(stream))
     _check("hybrid_layer_fwd", st)
+    return o
+
+
+def hybrid_layer_fwd_cont(q, k, v, gate, wq, wk, meta, *, window, start, state_in=None, kcache_in=None,
+                          vcache_in=None, state_out=None, kcache_out=None, vcache_out=None, chunk=0, scale=0.0,
+                          gate_is_log=False, gate_kind=None, o=None, ws=None, stream=None):
+    """Hybrid layer over tokens start .. start+L-1 of sequences that already
+    consumed ``start`` tokens (state and window ring of the previous call in,
+    optionally the new ones out); returns o [B,H,L,dv]."""
+    B, H, L, d = q.shape
+    dv, f = v.shape[-1], 2 * wq.shape[-1]
+    n_meta = 0 if meta is None else meta.shape[-1]
+    desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
+                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    ws, nbytes = _workspace(desc, ws, q.device)
+    st = load().hybrid_layer_fwd_cont(ctypes.byref(desc), int(start), _p(q), _p(k), _p(v), _p(gate), _p(wq),
+                                      _p(wk), _p(meta), _p(state_in), _p(kcache_in), _p(vcache_in),
+                                      _p(state_out), _p(kcache_out), _p(vcache_out), _p(o), _p(ws), nbytes,
+                                      _stream(stream))
+    _check("hybrid_layer_fwd_cont", st)
+    return o
+
+
+def output_gate(o, g, *, stream=None):
+    """o <- o * sigmoid(g) in place (o, g [B,H,L,dv], the same dtype); returns o."""
+    B, H, L, dv = o.shape
+    desc = make_desc(B, H, L, 1, dv, 2, dtype=_dtype_code(o))
+    st = load().glah_output_gate(ctypes.byref(desc), _p(o), _p(g), _stream(stream))
+    _check("glah_output_gate", st)
     return o
 
 

@@ -269,6 +269,66 @@ glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k
   }
 }
 
+glah_status hybrid_layer_fwd_cont(const glah_desc *desc, int32_t start, const void *q, const void *k,
+                                  const void *v, const void *gate, const void *wphi_q, const void *wphi_k,
+                                  const float *meta, const float *state_in, const void *kcache_in,
+                                  const void *vcache_in, float *state_out, void *kcache_out, void *vcache_out,
+                                  void *o, void *ws, size_t ws_bytes, glah_stream_t stream) {
+  try {
+    LayerArgs a;
+    glah_status st = check_desc(desc, Op::kHybrid, a);
+    if (st != GLAH_OK) return st;
+    if (start < 0) return GLAH_EINVAL;
+    const bool work = (size_t)a.B * a.H * a.L > 0;
+    const bool heads = (size_t)a.B * a.H > 0;
+    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work) || !req(o, work) ||
+        !req(wphi_q, heads) || !req(wphi_k, heads) || !req(meta, a.n_meta > 0 && a.H > 0) ||
+        !req(kcache_in, start > 0 && heads) || !req(vcache_in, start > 0 && heads) || !opt(state_in) ||
+        !opt(state_out) || !opt(ws) || !opt(kcache_out) || !opt(vcache_out))
+      return GLAH_EINVAL;
+    if ((kcache_out == nullptr) != (vcache_out == nullptr) || (kcache_in == nullptr) != (vcache_in == nullptr))
+      return GLAH_EINVAL;
+    if (!halo_supported(a)) return GLAH_ENOTSUP;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
+    a.state_in = state_in; a.state_out = state_out; a.o = o;
+    a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (a.L == 0) {
+      e = launch_state_passthrough(a);
+    } else if (chunked_supported(a, PART_BOTH)) {
+      if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
+        return GLAH_EWORKSPACE;
+      e = launch_chunked_prefill(a, PART_BOTH);
+    } else {
+      if (!recurrent_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
+      e = launch_recurrent_prefill(a, PART_BOTH);
+    }
+    // the first window - 1 queries also see the ring's keys (read before the
+    // ring is rewritten, which may be in place)
+    if (e == hipSuccess && a.L > 0) e = launch_halo_fix(a, start, kcache_in, vcache_in);
+    if (e == hipSuccess && kcache_out) {
+      a.kcache = kcache_out; a.vcache = vcache_out;
+      e = launch_ring_cont(a, start, kcache_in, vcache_in);
+    }
+    return finish(e);
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status glah_output_gate(const glah_desc *desc, void *o, const void *g, glah_stream_t stream) {
+  try {
+    if (!desc || desc->B < 0 || desc->H < 0 || desc->L < 0 || desc->d_v <= 0) return GLAH_EINVAL;
+    if (desc->dtype != GLAH_BF16 && desc->dtype != GLAH_F32) return GLAH_EINVAL;
+    const double n = (double)desc->B * desc->H * desc->L * desc->d_v;
+    if (n > 9.0e15) return GLAH_EINVAL;
+    if (!req(o, n > 0) || !req(g, n > 0)) return GLAH_EINVAL;
+    return finish(launch_output_gate(o, g, (size_t)n, desc->dtype == GLAH_BF16, (hipStream_t)stream));
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
 glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k, const void *v,
                         const void *log_alpha, const void *beta, const float *state_in,
                         float *state_out, void *o, glah_stream_t stream) {

@@ -81,6 +81,14 @@ hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 bool delta_supported(const LayerArgs &a);
 hipError_t launch_delta(const LayerArgs &a, bool decode);
 
+// Continuation prefill (serving.hip): window part of the first w - 1 queries
+// reaching into the input ring, and the ring after the call (global positions).
+bool halo_supported(const LayerArgs &a);
+hipError_t launch_halo_fix(const LayerArgs &a, long start, const void *kcache_in, const void *vcache_in);
+hipError_t launch_ring_cont(const LayerArgs &a, long start, const void *kcache_in, const void *vcache_in);
+// o <- o * sigmoid(g) over n elements
+hipError_t launch_output_gate(void *o, const void *g, size_t n, bool is_bf16, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace glah

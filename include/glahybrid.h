@@ -194,6 +194,48 @@ glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k
                              size_t ws_bytes, glah_stream_t stream);
 
 /*
+ * hybrid_layer_fwd_cont -- hybrid_layer_fwd for sequences that continue: this
+ * call's L tokens sit at positions start .. start+L-1 of sequences that have
+ * already consumed `start` tokens (the same count for every batch row), as in
+ * a prefill cut into pieces or a prompt appended after decoding.  The gated
+ * part continues from state_in; the window of the query at position P covers
+ * keys [P-window+1, P] (Methodology A.2), those before `start` read from the
+ * input ring.  The result equals the matching rows of one hybrid_layer_fwd
+ * over the whole sequence.
+ *   start       host int32 >= 0
+ *   state_in    nullable; [B][H][f][d_v] fp32 state after token start-1
+ *   kcache_in, vcache_in  [B][H][window][d] ring after token start-1 (slot p %
+ *               window holds token p, as hybrid_layer_fwd and gla_decode_step
+ *               leave it); may be NULL only when start == 0
+ *   kcache_out, vcache_out  nullable; the ring after this call (same layout,
+ *               global positions); may be the same buffers as the input ring
+ *   other arguments as hybrid_layer_fwd
+ * Supported: window <= 64 and n_meta <= 64 (else GLAH_ENOTSUP).  The first
+ * window-1 queries get their window term corrected in fp32 after the layer
+ * kernels (the difference between the softmax over ring and call keys and the
+ * one over call keys alone), so for bf16 output they are rounded twice.
+ */
+glah_status hybrid_layer_fwd_cont(const glah_desc *desc, int32_t start,
+                                  const void *q, const void *k, const void *v,
+                                  const void *gate, const void *wphi_q,
+                                  const void *wphi_k, const float *meta,
+                                  const float *state_in, const void *kcache_in,
+                                  const void *vcache_in, float *state_out,
+                                  void *kcache_out, void *vcache_out, void *o,
+                                  void *ws, size_t ws_bytes,
+                                  glah_stream_t stream);
+
+/*
+ * glah_output_gate -- output-gate epilogue o <- o * sigmoid(g), elementwise, in
+ * place (the attention-output gate of the "LT2" technical summary, 2605.20670,
+ * contributions: it keeps activations from growing across loop iterations).
+ *   o, g        [B][H][L][d_v], desc->dtype; g holds the gate logits (W_o x)
+ * Reads B, H, L, d_v and dtype of the descriptor.
+ */
+glah_status glah_output_gate(const glah_desc *desc, void *o, const void *g,
+                             glah_stream_t stream);
+
+/*
  * gdn_prefill -- the gated delta rule (Gated DeltaNet), the token mixer that
  * "systematic analysis of hybrid linear attention" (2507.06457, findings and
  * recommendations) and the "LT2" summary (2605.20670, hybrid designs) pair

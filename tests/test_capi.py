@@ -225,3 +225,31 @@ def test_gdn_misaligned_and_null_checks(lib):
     assert lib.gdn_decode_step(ctypes.byref(d), *args, None) == binding.GLAH_EINVAL
     assert lib.gdn_decode_step(ctypes.byref(_gdn_desc(d=96)), *[ctypes.c_void_p(FAKE)] * 7,
                                None) == binding.GLAH_ENOTSUP
+
+
+def _cont(lib, desc, start, ptrs=None):
+    p = [FAKE] * 15 if ptrs is None else ptrs  # q k v gate wq wk meta s_in kc_in vc_in s_out kc_out vc_out o ws
+    return lib.hybrid_layer_fwd_cont(ctypes.byref(desc), start, *[ctypes.c_void_p(x) for x in p], 1 << 40, None)
+
+
+def test_continuation_argument_checks(lib):
+    assert _cont(lib, _desc(), -1) == binding.GLAH_EINVAL
+    p = [FAKE] * 15
+    p[8] = 0  # kcache_in missing with start > 0
+    assert _cont(lib, _desc(), 3, p) == binding.GLAH_EINVAL
+    p = [FAKE] * 15
+    p[12] = 0  # one-sided output ring
+    assert _cont(lib, _desc(), 3, p) == binding.GLAH_EINVAL
+    assert _cont(lib, _desc(window=65), 3) == binding.GLAH_ENOTSUP
+    assert lib.hybrid_layer_fwd_cont(None, 0, *[ctypes.c_void_p(FAKE)] * 15, 0, None) == binding.GLAH_EINVAL
+
+
+def test_output_gate_argument_checks(lib):
+    d = _desc()
+    assert lib.glah_output_gate(ctypes.byref(d), None, ctypes.c_void_p(FAKE), None) == binding.GLAH_EINVAL
+    assert lib.glah_output_gate(ctypes.byref(d), ctypes.c_void_p(FAKE + 4), ctypes.c_void_p(FAKE),
+                                None) == binding.GLAH_EINVAL
+    assert lib.glah_output_gate(None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == binding.GLAH_EINVAL
+    bad = _desc(dtype=5)
+    assert lib.glah_output_gate(ctypes.byref(bad), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                None) == binding.GLAH_EINVAL

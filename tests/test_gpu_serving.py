@@ -1,0 +1,164 @@
+"""GPU checks of the serving entry points, through the C ABI:
+
+* hybrid_layer_fwd_cont (a prefill continuing a sequence: state and window ring
+  of the previous call in) against the fp64 oracle run over the WHOLE sequence:
+  a continuation must give the matching rows of one long prefill;
+* glah_output_gate against the fp64 oracle of the epilogue.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import epilogue
+from gated_linear_attention_hybrid_amd import binding as G
+from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_decode_token, make_prefill, to_f64
+from parity import TOL_BF16, TOL_F32, assert_finite, gpu_f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def say(msg):
+    print("[serving]", msg, flush=True)
+    sys.stdout.flush()
+
+
+def piece(x, a, b):
+    return {n: (t[:, :, a:b].contiguous() if n in ("q", "k", "v", "gate") else t) for n, t in x.items()}
+
+
+def ring_of(x, end, w):
+    """Expected ring after token end-1: slot p % w holds token p (zeros before 0)."""
+    k, v = x["k"], x["v"]
+    kc = torch.zeros(k.shape[:2] + (w, k.shape[-1]), dtype=k.dtype, device=k.device)
+    vc = torch.zeros(v.shape[:2] + (w, v.shape[-1]), dtype=v.dtype, device=v.device)
+    for p in range(max(0, end - w), end):
+        kc[:, :, p % w] = k[:, :, p]
+        vc[:, :, p % w] = v[:, :, p]
+    return kc, vc
+
+
+def run_pieces(x, wl, cuts, in_place=False):
+    """Prefill the sequence in pieces [cuts[i], cuts[i+1]); returns the pieces'
+    outputs concatenated, the final state and the final ring."""
+    B, H = wl.B, wl.H
+    st = None
+    kc = vc = None
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        y = piece(x, a, b)
+        st_out = torch.empty((B, H, wl.f, wl.dv), device=DEV)
+        if in_place and kc is not None:
+            kco, vco = kc, vc
+        else:
+            kco = torch.full((B, H, wl.window, wl.d), 9.0, dtype=wl.torch_dtype, device=DEV)
+            vco = torch.full((B, H, wl.window, wl.dv), 9.0, dtype=wl.torch_dtype, device=DEV)
+        o = G.hybrid_layer_fwd_cont(y["q"], y["k"], y["v"], y["gate"], y["wq"], y["wk"], y["meta"],
+                                    window=wl.window, start=a, state_in=st, kcache_in=kc, vcache_in=vc,
+                                    state_out=st_out, kcache_out=kco, vcache_out=vco)
+        outs.append(o)
+        st, kc, vc = st_out, kco, vco
+    return torch.cat(outs, dim=2), st, kc, vc
+
+
+def whole_oracle(x, wl):
+    f = {n: to_f64(t) for n, t in x.items()}
+    return oracle.layer_fwd(f["q"], f["k"], f["v"], f["gate"], f["wq"], f["wk"], f["meta"], window=wl.window,
+                            return_state=True)
+
+
+@pytest.mark.parametrize("cuts", [(0, 1, 300), (0, 37, 300), (0, 64, 300), (0, 200, 203, 300),
+                                  (0, 100, 130, 131, 300)])
+def test_continuation_bf16_equals_whole_sequence(cuts):
+    wl = WORKLOADS["prefill_2k"].with_(H=4, L=300)
+    say("bf16 continuation, cuts %s" % (cuts,))
+    x = make_prefill(wl, DEV)
+    o, st, kc, vc = run_pieces(x, wl, list(cuts))
+    assert_finite(o, "o")
+    ref, ref_st = whole_oracle(x, wl)
+    assert row_rel_err(gpu_f64(o), ref) <= TOL_BF16
+    assert row_rel_err(gpu_f64(st), ref_st) <= TOL_BF16
+    ekc, evc = ring_of(x, wl.L, wl.window)
+    assert torch.equal(kc, ekc) and torch.equal(vc, evc)
+
+
+def test_continuation_in_place_ring_and_peaked_window():
+    # peaked scores (q, k ~ N(0, 1)) so the ring keys carry real weight
+    wl = WORKLOADS["prefill_2k"].with_(H=4, L=400, x_std=1.0, seed=1201)
+    say("bf16 continuation, peaked window, ring updated in place")
+    x = make_prefill(wl, DEV)
+    o, st, kc, vc = run_pieces(x, wl, [0, 150, 170, 400], in_place=True)
+    ref, ref_st = whole_oracle(x, wl)
+    assert row_rel_err(gpu_f64(o), ref) <= TOL_BF16
+    assert row_rel_err(gpu_f64(st), ref_st) <= TOL_BF16
+    ekc, evc = ring_of(x, wl.L, wl.window)
+    assert torch.equal(kc, ekc) and torch.equal(vc, evc)
+
+
+@pytest.mark.parametrize("cuts", [(0, 100, 256), (0, 7, 9, 256)])
+def test_continuation_fp32(cuts):
+    wl = WORKLOADS["tiny_fp32"]
+    say("fp32 continuation, cuts %s" % (cuts,))
+    x = make_prefill(wl, DEV)
+    o, st, kc, vc = run_pieces(x, wl, list(cuts))
+    ref, ref_st = whole_oracle(x, wl)
+    assert row_rel_err(gpu_f64(o), ref) <= TOL_F32
+    assert row_rel_err(gpu_f64(st), ref_st) <= TOL_F32
+
+
+def test_start_zero_is_hybrid_layer_fwd():
+    wl = WORKLOADS["prefill_2k"].with_(H=4, L=200)
+    x = make_prefill(wl, DEV)
+    a = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], window=wl.window)
+    b = G.hybrid_layer_fwd_cont(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                                window=wl.window, start=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_after_continuation():
+    wl = WORKLOADS["prefill_2k"].with_(B=2, H=4, L=160)
+    say("decode step after a continued prefill")
+    x = make_prefill(wl, DEV)
+    _, st, kc, vc = run_pieces(x, wl, [0, 90, 160])
+    t = make_decode_token(wl, 0, DEV)
+    pos = torch.full((wl.B,), wl.L, dtype=torch.int32, device=DEV)
+    od = G.gla_decode_step(t["q"], t["k"], t["v"], t["gate"], x["wq"], x["wk"], x["meta"], st, kc, vc, pos,
+                           window=wl.window)
+    f = {n: to_f64(v) for n, v in x.items()}
+    _, ref_st = whole_oracle(x, wl)
+    ekc, evc = ring_of(x, wl.L, wl.window)
+    ft = {n: to_f64(v) for n, v in t.items()}
+    ref = oracle.decode_step(ft["q"], ft["k"], ft["v"], ft["gate"], f["wq"], f["wk"], f["meta"],
+                             np.ascontiguousarray(ref_st), to_f64(ekc), to_f64(evc), np.full(wl.B, wl.L),
+                             window=wl.window)
+    assert row_rel_err(gpu_f64(od), ref) <= TOL_BF16
+
+
+def test_continuation_argument_errors():
+    wl = WORKLOADS["prefill_2k"].with_(H=2, L=16)
+    x = make_prefill(wl, DEV)
+    with pytest.raises(G.GlahError) as e:  # start > 0 needs the ring
+        G.hybrid_layer_fwd_cont(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                                window=wl.window, start=5)
+    assert e.value.status == G.GLAH_EINVAL
+    with pytest.raises(G.GlahError) as e:  # negative start
+        G.hybrid_layer_fwd_cont(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
+                                window=wl.window, start=-1)
+    assert e.value.status == G.GLAH_EINVAL
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 32, 2048, 128), torch.bfloat16), ((2, 3, 5, 3), torch.bfloat16),
+                                         ((2, 3, 7, 5), torch.float32), ((1, 4, 64, 64), torch.float32)])
+def test_output_gate(shape, dtype):
+    say("output gate %s %s" % (shape, dtype))
+    g0 = torch.Generator(device="cpu").manual_seed(sum(shape))
+    o = torch.randn(shape, generator=g0).to(dtype).to(DEV)
+    g = (torch.randn(shape, generator=g0) * 3).to(dtype).to(DEV)
+    ref = epilogue.output_gate(to_f64(o), to_f64(g))
+    out = G.output_gate(o.clone(), g)
+    tol = TOL_BF16 if dtype == torch.bfloat16 else 1e-5
+    assert row_rel_err(gpu_f64(out), ref) <= tol
