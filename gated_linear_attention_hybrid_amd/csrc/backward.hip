@@ -28,6 +28,8 @@
 //
 // Every reduction is done in a fixed order into per-block partials (no atomics),
 // so the gradients are bitwise repeatable.  All arithmetic is fp32.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -691,6 +693,244 @@ __global__ __launch_bounds__(kBT) void bwd_swa_kv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Window part in 64-token tiles (bf16, d = d_v = 128, window <= 64, n_meta <=
+// 16): the same quantities as the two per-token kernels above, computed as
+// LDS-tiled fp32 products.  A query tile (64 queries of chunk c) meets the 128
+// keys of chunks c-1 and c; a key tile (64 keys of chunk c) meets the 128
+// queries of chunks c and c+1.  512 threads: thread (rg, cg) = (tid / 16,
+// tid % 16) holds score rows 2rg, 2rg+1 and columns cg + 16j (j < 8), so each
+// row's 16 threads are one 16-lane DPP row; the products with the scores hold
+// rows 2rg, 2rg+1 and output columns 8cg .. 8cg+7.
+constexpr int kWT = 512;          // threads of a window tile block
+constexpr int kWC = 64;           // tokens of a tile
+constexpr int kWD = 128;          // d = d_v of the tiled path
+constexpr int kWS = kWD + 8;      // LDS row stride (bf16): consecutive rows 4 banks apart
+constexpr int kWP = 2 * kWC + 1;  // score row stride (fp32)
+
+struct WinTileLds {
+  bf16 a[kWC][kWS];          // query tile: Q; key tile: K
+  bf16 b[kWC][kWS];          // query tile: dO; key tile: V
+  bf16 c[2 * kWC][kWS];      // query tile: K; key tile: Q
+  bf16 e[2 * kWC][kWS];      // query tile: V; key tile: dO
+  float sc[kWC][kWP];        // scores / weights of the tile
+  float lse[2 * kWC], del[2 * kWC];
+  float mp[kWT / 16][16];
+};
+
+// Rows [r0, r0 + n) of a [L][128] bf16 matrix of head bh into LDS rows
+// (zeros outside [0, L)).
+__device__ __forceinline__ void win_stage(bf16 (*dst)[kWS], const bf16 *src, size_t bh, int L, int r0, int n) {
+  for (int idx = threadIdx.x; idx < n * (kWD / 8); idx += kWT) {
+    const int r = idx / (kWD / 8), c8 = (idx % (kWD / 8)) * 8, pos = r0 + r;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (pos >= 0 && pos < L) x = *(const u32x4 *)(src + ((size_t)bh * L + pos) * kWD + c8);
+    *(u32x4 *)&dst[r][c8] = x;
+  }
+}
+
+__device__ __forceinline__ void bf8(const bf16 *p, float (&x)[8]) {
+  const u32x4 w = *(const u32x4 *)p;
+  const bf16 *e = (const bf16 *)&w;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)e[j];
+}
+
+// acc[i][j] = sum_e A[2rg+i][e] B[cg+16j][e] over e < 128 (A rows broadcast
+// in the 16-lane row, B rows 16 apart)
+__device__ __forceinline__ void win_scores(const bf16 (*A)[kWS], const bf16 (*Bm)[kWS], int rg, int cg,
+                                           float (&acc)[2][8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+  for (int e = 0; e < kWD; e += 8) {
+    float a0[8], a1[8];
+    bf8(&A[2 * rg][e], a0);
+    bf8(&A[2 * rg + 1][e], a1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float b[8];
+      bf8(&Bm[cg + 16 * j][e], b);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc[0][j] += a0[u] * b[u];
+        acc[1][j] += a1[u] * b[u];
+      }
+    }
+  }
+}
+
+// out[i][u] = sum_x W[2rg+i][x] M[x][8cg+u] over x < 2 kWC (W the fp32 score
+// tile, M a bf16 LDS matrix)
+__device__ __forceinline__ void win_apply(const float (*W)[kWP], const bf16 (*M)[kWS], int rg, int cg,
+                                          float (&out)[2][8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) out[i][u] = 0.0f;
+  for (int x = 0; x < 2 * kWC; ++x) {
+    float m[8];
+    bf8(&M[x][8 * cg], m);
+    const float w0 = W[2 * rg][x], w1 = W[2 * rg + 1][x];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      out[0][u] += w0 * m[u];
+      out[1][u] += w1 * m[u];
+    }
+  }
+}
+
+// Query tile: dq (window part), lse, D and the sinks' gradient partial.
+__global__ __launch_bounds__(kWT) void bwd_swa_tile_q_kernel(BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  WinTileLds &S = *(WinTileLds *)smem;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int nch = (p.L + kWC - 1) / kWC;
+  const size_t bh = blockIdx.x / nch;
+  const int c = blockIdx.x % nch, t0 = c * kWC, h = (int)(bh % p.H);
+  const bf16 *q = (const bf16 *)p.q, *k = (const bf16 *)p.k, *v = (const bf16 *)p.v, *dO = (const bf16 *)p.dout;
+  win_stage(S.a, q, bh, p.L, t0, kWC);
+  win_stage(S.b, dO, bh, p.L, t0, kWC);
+  win_stage(S.c, k, bh, p.L, t0 - kWC, 2 * kWC);
+  win_stage(S.e, v, bh, p.L, t0 - kWC, 2 * kWC);
+  __syncthreads();
+
+  float sc[2][8], dp[2][8];
+  win_scores(S.a, S.c, rg, cg, sc);
+  win_scores(S.b, S.e, rg, cg, dp);
+  const float tm = cg < p.n_meta ? p.meta[(size_t)h * p.n_meta + cg] : -INFINITY;
+  float mm = tm;  // max of the sinks over the 16 lanes
+  mm = fmaxf(mm, dpp_f<0xB1>(mm));
+  mm = fmaxf(mm, dpp_f<0x4E>(mm));
+  mm = fmaxf(mm, dpp_f<0x141>(mm));
+  mm = fmaxf(mm, dpp_f<0x140>(mm));
+  float mpart = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 2 * rg + i;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kp = t0 - kWC + cg + 16 * j;  // key position
+      const bool ok = t < p.L && kp >= 0 && kp <= t && t - kp < p.window;
+      sc[i][j] = ok ? sc[i][j] * p.scale : -INFINITY;
+      mx = fmaxf(mx, sc[i][j]);
+    }
+    const float m = fmaxf(row16_reduce(mx, OpMax()), mm);
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sc[i][j] = exp_fast(sc[i][j] - m);  // 0 outside the window
+      z += sc[i][j];
+    }
+    const float es = cg < p.n_meta ? exp_fast(tm - m) : 0.0f;
+    z = row16_reduce(z + es, OpAdd());
+    const float iz = 1.0f / z;
+    float dsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sc[i][j] *= iz;
+      dsum += sc[i][j] * dp[i][j];
+    }
+    const float D = row16_reduce(dsum, OpAdd());
+#pragma unroll
+    for (int j = 0; j < 8; ++j) S.sc[2 * rg + i][cg + 16 * j] = sc[i][j] * (dp[i][j] - D);
+    if (t < p.L) {
+      mpart -= es * iz * D;
+      if (cg == 0) {
+        p.lse[bh * p.L + t] = m + logf(z);
+        p.del[bh * p.L + t] = D;
+      }
+    }
+  }
+  S.mp[rg][cg] = mpart;
+  __syncthreads();
+  float dq[2][8];
+  win_apply(S.sc, S.c, rg, cg, dq);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 2 * rg + i;
+    if (t < p.L) {
+      float *dst = p.dqs + (bh * p.L + t) * kWD + 8 * cg;
+      *(f32x4 *)dst = (f32x4){dq[i][0], dq[i][1], dq[i][2], dq[i][3]} * p.scale;
+      *(f32x4 *)(dst + 4) = (f32x4){dq[i][4], dq[i][5], dq[i][6], dq[i][7]} * p.scale;
+    }
+  }
+  // the sinks' gradient of this tile goes to its first 16-token block, zeros
+  // to the others (the reduction sums all blocks in a fixed order)
+  if (tid < p.n_meta * (kWC / kSwaTok)) {
+    const int m = tid % p.n_meta, sub = tid / p.n_meta, blk = c * (kWC / kSwaTok) + sub;
+    float acc = 0.0f;
+    if (sub == 0)
+      for (int r = 0; r < kWT / 16; ++r) acc += S.mp[r][m];
+    if (blk < p.nsb) p.mp[(bh * p.nsb + blk) * p.n_meta + m] = acc;
+  }
+}
+
+// Key tile: dk and dv (window parts) of the 64 keys of chunk c from the 128
+// queries of chunks c and c+1, with the query kernel's lse and D.
+__global__ __launch_bounds__(kWT) void bwd_swa_tile_kv_kernel(BwdParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  WinTileLds &S = *(WinTileLds *)smem;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int nch = (p.L + kWC - 1) / kWC;
+  const size_t bh = blockIdx.x / nch;
+  const int c = blockIdx.x % nch, j0 = c * kWC;
+  const bf16 *q = (const bf16 *)p.q, *k = (const bf16 *)p.k, *v = (const bf16 *)p.v, *dO = (const bf16 *)p.dout;
+  win_stage(S.a, k, bh, p.L, j0, kWC);
+  win_stage(S.b, v, bh, p.L, j0, kWC);
+  win_stage(S.c, q, bh, p.L, j0, 2 * kWC);
+  win_stage(S.e, dO, bh, p.L, j0, 2 * kWC);
+  if (tid < 2 * kWC) {
+    const int t = j0 + tid;
+    S.lse[tid] = t < p.L ? p.lse[bh * p.L + t] : 0.0f;
+    S.del[tid] = t < p.L ? p.del[bh * p.L + t] : 0.0f;
+  }
+  __syncthreads();
+
+  float sc[2][8], dp[2][8];
+  win_scores(S.a, S.c, rg, cg, sc);
+  win_scores(S.b, S.e, rg, cg, dp);
+  float pw[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kp = j0 + 2 * rg + i;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int x = cg + 16 * j, t = j0 + x;  // query position
+      const bool ok = kp < p.L && t < p.L && t >= kp && t - kp < p.window;
+      pw[i][j] = ok ? exp_fast(sc[i][j] * p.scale - S.lse[x]) : 0.0f;
+      S.sc[2 * rg + i][x] = pw[i][j];
+    }
+  }
+  __syncthreads();
+  float dvv[2][8];
+  win_apply(S.sc, S.e, rg, cg, dvv);  // dv_j = sum_t P_tj dO_t
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int x = cg + 16 * j;
+      S.sc[2 * rg + i][x] = pw[i][j] * (dp[i][j] - S.del[x]);
+    }
+  __syncthreads();
+  float dkk[2][8];
+  win_apply(S.sc, S.c, rg, cg, dkk);  // dk_j = scale sum_t ds_tj q_t
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kp = j0 + 2 * rg + i;
+    if (kp < p.L) {
+      float *dk = p.dks + (bh * p.L + kp) * kWD + 8 * cg, *dvp = p.dvs + (bh * p.L + kp) * kWD + 8 * cg;
+      *(f32x4 *)dk = (f32x4){dkk[i][0], dkk[i][1], dkk[i][2], dkk[i][3]} * p.scale;
+      *(f32x4 *)(dk + 4) = (f32x4){dkk[i][4], dkk[i][5], dkk[i][6], dkk[i][7]} * p.scale;
+      *(f32x4 *)dvp = (f32x4){dvv[i][0], dvv[i][1], dvv[i][2], dvv[i][3]};
+      *(f32x4 *)(dvp + 4) = (f32x4){dvv[i][4], dvv[i][5], dvv[i][6], dvv[i][7]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Sums of the per-block partials over batch rows and token blocks: dWphi_q,
 // dWphi_k [H][d][f/2], the sink gradients [H][n_meta] and, for a per-head
 // gate, its gradient [H].  Fixed order, one output per thread.
@@ -790,10 +1030,26 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     if (!launched()) return e;
   }
   if (p.swa && a.L > 0) {
-    hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
-    if (!launched()) return e;
-    hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
-    if (!launched()) return e;
+    if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
+      const unsigned nch = (unsigned)((a.L + kWC - 1) / kWC);
+      const size_t lds = sizeof(WinTileLds);
+      // dynamic LDS above 64 KiB has to be allowed for each kernel
+      e = hipFuncSetAttribute((const void *)bwd_swa_tile_q_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)bwd_swa_tile_kv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_swa_tile_q_kernel, dim3(BH * nch), dim3(kWT), lds, a.stream, p);
+      if (!launched()) return e;
+      hipLaunchKernelGGL(bwd_swa_tile_kv_kernel, dim3(BH * nch), dim3(kWT), lds, a.stream, p);
+      if (!launched()) return e;
+    } else {
+      hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+      if (!launched()) return e;
+      hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+      if (!launched()) return e;
+    }
   }
   if (p.gla && BH > 0) {
     // with no tokens the sweeps still pass dS_final through to dS_0

@@ -102,6 +102,16 @@ def test_backward_bf16_d128(L):
     compare(got, ref, TOL_BF16)
 
 
+@pytest.mark.parametrize("window,n_meta,x_std", [(17, 4, 0.0884), (64, 0, 1.0), (64, 4, 1.0), (2, 3, 1.0)])
+def test_backward_bf16_window_tiles(window, n_meta, x_std):
+    """The 64-token window tiles: short windows, no sinks, and peaked scores
+    (q, k ~ N(0, 1)) so the window softmax is far from uniform; B = 2, ragged L."""
+    wl = WORKLOADS["prefill_2k"].with_(B=2, H=2, L=150, window=window, n_meta=n_meta, x_std=x_std, seed=1301)
+    say("backward bf16 window tiles w=%d M=%d x_std=%g" % (window, n_meta, x_std))
+    got, ref = run_case(wl)
+    compare(got, ref, TOL_BF16)
+
+
 def test_backward_bf16_slow_decay():
     """Gate logits ~ N(6, 1): the state carries across hundreds of tokens."""
     wl = WORKLOADS["prefill_2k"].with_(H=2, L=400, gate_mean=6.0)
