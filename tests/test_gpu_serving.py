@@ -162,3 +162,19 @@ def test_output_gate(shape, dtype):
     out = G.output_gate(o.clone(), g)
     tol = TOL_BF16 if dtype == torch.bfloat16 else 1e-5
     assert row_rel_err(gpu_f64(out), ref) <= tol
+
+
+def test_continuation_empty_piece():
+    """L = 0 at start > 0: the state passes through and the ring is copied."""
+    wl = WORKLOADS["prefill_2k"].with_(H=2, L=100)
+    x = make_prefill(wl, DEV)
+    _, st, kc, vc = run_pieces(x, wl, [0, 100])
+    e = piece(x, 100, 100)
+    st2 = torch.full_like(st, 5.0)
+    kc2, vc2 = torch.full_like(kc, 3.0), torch.full_like(vc, 3.0)
+    o = G.hybrid_layer_fwd_cont(e["q"], e["k"], e["v"], e["gate"], e["wq"], e["wk"], e["meta"], window=wl.window,
+                                start=100, state_in=st, kcache_in=kc, vcache_in=vc, state_out=st2,
+                                kcache_out=kc2, vcache_out=vc2)
+    torch.cuda.synchronize()
+    assert o.shape[2] == 0
+    assert torch.equal(st2, st) and torch.equal(kc2, kc) and torch.equal(vc2, vc)
