@@ -200,9 +200,6 @@ __global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
   const int L = p.L, f = p.f, dv = p.dv;
   const size_t BH = (size_t)p.B * p.H, N = BH * L;
   const size_t rowf = (size_t)bh * L * f + s.r0;
-  const size_t rowv = (size_t)bh * L * dv + s.c0;
-  const T *v = (const T *)p.v + rowv;
-  const T *dO = (const T *)p.dout + rowv;
   float *dpq = p.dpq + (size_t)slice * N * f + rowf;
   float *tq = p.tq + ((size_t)slice * BH + bh) * p.nft * f + s.r0;
   const bool lead = (threadIdx.x & 7) == 0;
@@ -216,40 +213,55 @@ __global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
   }
   f32x4 bg[kPF], bk[kPF], bq[kPF];
   Q bv[kPF], bo[kPF];
+  // Loads are unconditional, from clamped rows, columns and tokens (lanes past f
+  // or d_v are masked where the values are used): a predicated load made the
+  // compiler wait for every load in flight before each token.
+  const size_t rowf_ld = (size_t)bh * L * f + min(s.r0, f - 4);
+  const size_t rowv_ld = (size_t)bh * L * dv + min(s.c0, dv - 4);
   auto fetch = [&](int u, int t) {
-    const bool r = s.rok && t < L, c = s.cok && t < L;
-    bg[u] = r ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
-    bk[u] = r ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
-    bq[u] = r ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
-    bv[u] = c ? *(const Q *)(v + (size_t)t * dv) : zero_quad<Q>();
-    bo[u] = c ? *(const Q *)(dO + (size_t)t * dv) : zero_quad<Q>();
+    const size_t tc = (size_t)min(t, L - 1);
+    bg[u] = *(const f32x4 *)(p.gam + rowf_ld + tc * f);
+    bk[u] = *(const f32x4 *)(p.pk + rowf_ld + tc * f);
+    bq[u] = *(const f32x4 *)(p.pq + rowf_ld + tc * f);
+    bv[u] = *(const Q *)((const T *)p.v + rowv_ld + tc * dv);
+    bo[u] = *(const Q *)((const T *)p.dout + rowv_ld + tc * dv);
   };
+  // L = 0 (the sweeps still pass the state gradient through): no token to load
+  if (L > 0) {
 #pragma unroll
-  for (int u = 0; u < kPF; ++u) fetch(u, u);
+    for (int u = 0; u < kPF; ++u) fetch(u, u);
+  }
   f32x4 tile = z4;
-  for (int t0 = 0; t0 < L; t0 += kPF) {
+  auto step = [&](int u, int t) {
+    const f32x4 g4 = s.rok ? bg[u] : z4, k4 = s.rok ? bk[u] : z4, q4 = s.rok ? bq[u] : z4;
+    const f32x4 v4 = s.cok ? widen(bv[u]) : z4, o4 = s.cok ? widen(bo[u]) : z4;
+    fetch(u, t + kPF);
+    f32x4 part;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = g4[i] * S[i][j] + k4[i] * v4[j];
+      part[i] = sum8(dot4(S[i], o4));
+      tile[i] += q4[i] * part[i];
+    }
+    if (lead && s.rok) *(f32x4 *)(dpq + (size_t)t * f) = part;
+    if ((t & (kFeatTok - 1)) == kFeatTok - 1 || t == L - 1) {
+      if (lead && s.rok) *(f32x4 *)(tq + (size_t)(t / kFeatTok) * f) = tile;
+      tile = z4;
+    }
+  };
+  // whole groups without a per-token branch, then the last L % kPF tokens
+  int t0 = 0;
+  for (; t0 + kPF <= L; t0 += kPF) {
 #pragma unroll
     for (int u = 0; u < kPF; ++u) {
-      const int t = t0 + u;
-      if (t < L) {
-        const f32x4 g4 = bg[u], k4 = bk[u], q4 = bq[u], v4 = widen(bv[u]), o4 = widen(bo[u]);
-        fetch(u, t + kPF);
-        f32x4 part;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) S[i][j] = g4[i] * S[i][j] + k4[i] * v4[j];
-          part[i] = sum8(dot4(S[i], o4));
-          tile[i] += q4[i] * part[i];
-        }
-        if (lead && s.rok) *(f32x4 *)(dpq + (size_t)t * f) = part;
-        if ((t & (kFeatTok - 1)) == kFeatTok - 1 || t == L - 1) {
-          if (lead && s.rok) *(f32x4 *)(tq + (size_t)(t / kFeatTok) * f) = tile;
-          tile = z4;
-        }
-      }
+      step(u, t0 + u);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int u = 0; u < kPF - 1; ++u)
+    if (t0 + u < L) step(u, t0 + u);
   if (p.dstate_out) {
     f32x4 part;
 #pragma unroll
@@ -276,8 +288,6 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
   const size_t BH = (size_t)p.B * p.H, N = BH * L;
   const size_t rowf = (size_t)bh * L * f + s.r0;
   const size_t rowv = (size_t)bh * L * dv + s.c0;
-  const T *v = (const T *)p.v + rowv;
-  const T *dO = (const T *)p.dout + rowv;
   float *dpk = p.dpk + (size_t)slice * N * f + rowf;
   float *dvg = p.dvg + (size_t)wave * N * dv + rowv;
   float *tk = p.tk + ((size_t)slice * BH + bh) * p.nft * f + s.r0;
@@ -294,47 +304,61 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
   }
   f32x4 bq[kPF], bk[kPF], bg[kPF];
   Q bv[kPF], bo[kPF];
+  // unconditional loads from clamped rows, columns and tokens, masked where used
+  // (as in the forward sweep)
+  const size_t rowf_ld = (size_t)bh * L * f + min(s.r0, f - 4);
+  const size_t rowv_ld = (size_t)bh * L * dv + min(s.c0, dv - 4);
   auto fetch = [&](int u, int t) {
-    const bool r = s.rok && t >= 0, c = s.cok && t >= 0;
-    bq[u] = r ? *(const f32x4 *)(p.pq + rowf + (size_t)t * f) : z4;
-    bk[u] = r ? *(const f32x4 *)(p.pk + rowf + (size_t)t * f) : z4;
-    bg[u] = r ? *(const f32x4 *)(p.gam + rowf + (size_t)t * f) : z4;
-    bv[u] = c ? *(const Q *)(v + (size_t)t * dv) : zero_quad<Q>();
-    bo[u] = c ? *(const Q *)(dO + (size_t)t * dv) : zero_quad<Q>();
+    const size_t tc = (size_t)max(t, 0);
+    bq[u] = *(const f32x4 *)(p.pq + rowf_ld + tc * f);
+    bk[u] = *(const f32x4 *)(p.pk + rowf_ld + tc * f);
+    bg[u] = *(const f32x4 *)(p.gam + rowf_ld + tc * f);
+    bv[u] = *(const Q *)((const T *)p.v + rowv_ld + tc * dv);
+    bo[u] = *(const Q *)((const T *)p.dout + rowv_ld + tc * dv);
   };
+  // L = 0 (the sweeps still pass the state gradient through): no token to load
+  if (L > 0) {
 #pragma unroll
-  for (int u = 0; u < kPF; ++u) fetch(u, L - 1 - u);
+    for (int u = 0; u < kPF; ++u) fetch(u, L - 1 - u);
+  }
   f32x4 gn = {1.0f, 1.0f, 1.0f, 1.0f};
   f32x4 tile = z4;
-  for (int t0 = L - 1; t0 >= 0; t0 -= kPF) {
+  auto step = [&](int u, int t) {
+    const f32x4 q4 = s.rok ? bq[u] : z4, k4 = s.rok ? bk[u] : z4, g4 = s.rok ? bg[u] : z4;
+    const f32x4 v4 = s.cok ? widen(bv[u]) : z4, o4 = s.cok ? widen(bo[u]) : z4;
+    fetch(u, t - kPF);
+    f32x4 a, c = z4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dS[i][j] = gn[i] * dS[i][j] + q4[i] * o4[j];
+      a[i] = sum8(dot4(dS[i], v4));
+      tile[i] += k4[i] * a[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] += dS[i][j] * k4[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = sum_rows8(c[j]);
+    if (lead && s.rok) *(f32x4 *)(dpk + (size_t)t * f) = a;
+    if (l < 8 && s.cok) *(f32x4 *)(dvg + (size_t)t * dv) = c;
+    if ((t & (kFeatTok - 1)) == 0) {
+      if (lead && s.rok) *(f32x4 *)(tk + (size_t)(t / kFeatTok) * f) = tile;
+      tile = z4;
+    }
+    gn = g4;
+  };
+  // whole groups without a per-token branch, then the first L % kPF tokens
+  int t0 = L - 1;
+  for (; t0 - kPF + 1 >= 0; t0 -= kPF) {
 #pragma unroll
     for (int u = 0; u < kPF; ++u) {
-      const int t = t0 - u;
-      if (t >= 0) {
-        const f32x4 q4 = bq[u], k4 = bk[u], g4 = bg[u], v4 = widen(bv[u]), o4 = widen(bo[u]);
-        fetch(u, t - kPF);
-        f32x4 a, c = z4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dS[i][j] = gn[i] * dS[i][j] + q4[i] * o4[j];
-          a[i] = sum8(dot4(dS[i], v4));
-          tile[i] += k4[i] * a[i];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) c[j] += dS[i][j] * k4[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c[j] = sum_rows8(c[j]);
-        if (lead && s.rok) *(f32x4 *)(dpk + (size_t)t * f) = a;
-        if (l < 8 && s.cok) *(f32x4 *)(dvg + (size_t)t * dv) = c;
-        if ((t & (kFeatTok - 1)) == 0) {
-          if (lead && s.rok) *(f32x4 *)(tk + (size_t)(t / kFeatTok) * f) = tile;
-          tile = z4;
-        }
-        gn = g4;
-      }
+      step(u, t0 - u);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int u = 0; u < kPF - 1; ++u)
+    if (t0 - u >= 0) step(u, t0 - u);
   if (p.dstate_in && s.rok && s.cok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
