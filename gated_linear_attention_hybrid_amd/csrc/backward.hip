@@ -149,6 +149,77 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Prologue in 64-token tiles (d a multiple of 4 up to 128, f/2 a multiple of 4
+// up to 64): the projections as a register-tiled product, thread (tg, fg) =
+// (tid / 16, tid % 16) computing tokens 4tg .. 4tg+3 by features 4fg .. 4fg+3
+// from the tile's inputs transposed in LDS (16-byte reads of four tokens and
+// of four features per step), the two maps one after the other.  The
+// projection is staged once per 64 tokens instead of once per 16; u reuses the
+// input tile's LDS (65 KiB a block, two blocks per CU).
+constexpr int kPrepTile = 64;
+
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_prep_tile_kernel(BwdParams p) {
+  __shared__ __align__(16) float W[kBwdMaxD * kMaxF2];   // [d][f/2]
+  __shared__ __align__(16) float XT[kBwdMaxD][kPrepTile];  // [d][token]; then u [token][f/2 + 1]
+  float (*U)[kMaxF2 + 1] = (float (*)[kMaxF2 + 1])&XT[0][0];
+  static_assert(kPrepTile * (kMaxF2 + 1) <= kBwdMaxD * kPrepTile, "u fits in the input tile");
+  const int tid = threadIdx.x, tg = tid >> 4, fg = tid & 15;
+  const int ntl = (p.L + kPrepTile - 1) / kPrepTile;
+  const int bh = blockIdx.x / ntl, tile = blockIdx.x % ntl;
+  const int h = bh % p.H, d = p.d, f = p.f, f2 = p.f2, L = p.L;
+  const int t0 = tile * kPrepTile, nt = min(kPrepTile, L - t0);
+  const size_t row0 = (size_t)bh * L + t0;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int m = 0; m < 2; ++m) {
+    const T *w = (const T *)(m ? p.wk : p.wq) + (size_t)h * d * f2;
+    const T *x = (const T *)(m ? p.k : p.q);
+    for (int i = tid; i < d * f2; i += kBT) W[i] = ld(w + i);
+    for (int i = tid; i < kPrepTile * d; i += kBT) {
+      const int tt = i / d, e = i - tt * d;
+      XT[e][tt] = tt < nt ? ld(x + (row0 + tt) * d + e) : 0.0f;
+    }
+    __syncthreads();
+    f32x4 acc[4] = {};
+    if (4 * fg < f2) {
+      for (int e = 0; e < d; ++e) {
+        const f32x4 x4 = *(const f32x4 *)&XT[e][4 * tg];
+        const f32x4 w4 = *(const f32x4 *)&W[e * f2 + 4 * fg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += x4[i] * w4;
+      }
+    }
+    __syncthreads();  // every read of the input tile done: u takes its place
+    if (4 * fg < f2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) U[4 * tg + i][4 * fg + j] = acc[i][j];
+    }
+    __syncthreads();
+    // phi = [softmax(u), softmax(-u)] of each token: one wave per token row
+    for (int tt = wave; tt < nt; tt += kBT / 64) {
+      const bool ok = lane < f2;
+      const float u = ok ? U[tt][lane] : 0.0f;
+      const float mx = wave_max(ok ? u : -INFINITY), mn = wave_min(ok ? u : INFINITY);
+      const float ep = ok ? exp_fast(u - mx) : 0.0f, en = ok ? exp_fast(mn - u) : 0.0f;
+      const float zp = wave_sum(ep), zn = wave_sum(en);
+      float *dst = (m ? p.pk : p.pq) + (row0 + tt) * f;
+      if (ok) {
+        dst[lane] = ep / zp;
+        dst[f2 + lane] = en / zn;
+      }
+    }
+    __syncthreads();  // W, XT and U are reused by the next map
+  }
+  const T *g = (const T *)p.gate;
+  for (int i = tid; i < nt * f; i += kBT) {
+    const int tt = i / f, r = i - tt * f;
+    p.gam[(row0 + tt) * f + r] =
+        gate_from(ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t0 + tt, r)), p.gate_is_log);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // State sweeps.  Block = (b, h, 32-column slice of d_v); lane l of wave w owns
 // rows 4 (8 w + l / 8) .. +3 and columns 4 (l % 8) .. +3 of the slice, so a
@@ -1050,7 +1121,12 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   hipError_t e = hipSuccess;
   auto launched = [&]() { if (e == hipSuccess) e = hipGetLastError(); return e == hipSuccess; };
   if (p.gla && a.L > 0) {
-    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(BH * p.npt), block, 0, a.stream, p);
+    if (a.f / 2 % 4 == 0) {
+      const unsigned ntl = (unsigned)((a.L + kPrepTile - 1) / kPrepTile);
+      hipLaunchKernelGGL(bwd_prep_tile_kernel<T>, dim3(BH * ntl), block, 0, a.stream, p);
+    } else {
+      hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(BH * p.npt), block, 0, a.stream, p);
+    }
     if (!launched()) return e;
   }
   if (p.swa && a.L > 0) {
