@@ -26,6 +26,7 @@ namespace {
 constexpr int kLPR = 16;                 // lanes per state row
 constexpr int kThreads = 256;            // 4 waves x 4 rows = 16 rows per block
 constexpr int kRowsPerBlock = kThreads / kLPR;
+constexpr int kDecRows = 2 * kRowsPerBlock;  // decode: two state rows per 16-lane group
 constexpr float kNormEps = 1e-6f;        // added to |x|^2 under the root
 
 struct DeltaParams {
@@ -308,31 +309,41 @@ template <class T, int EPL>
 __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(DeltaParams p) {
   constexpr int DK = EPL * kLPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15;
-  const int nrb = (p.dv + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int nrb = (p.dv + kDecRows - 1) / kDecRows;
   const size_t bh = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x % nrb) * kRowsPerBlock + wave * 4 + (lane >> 4);
-  const bool live = row0 < p.dv;
-  const int row = live ? row0 : p.dv - 1;
-
-  float *s = p.state_out + (bh * p.dv + row) * DK + l16 * EPL;
-  float m[EPL];
-  if constexpr (EPL % 4 == 0) {
+  // each 16-lane group holds rows g and g + 16 of the block's 32: twice the
+  // state bytes in flight per lane, and the token's k, q, a and beta (with the
+  // key and query norms) are loaded and formed once for both rows
+  const int g = wave * 4 + (lane >> 4);
+  int rows[2];
+  bool live[2];
+  float *sp[2];
+  float m[2][EPL];
 #pragma unroll
-    for (int c = 0; c < EPL / 4; ++c) {
-      const f32x4 w = __builtin_nontemporal_load((const f32x4 *)(s + 4 * c));
+  for (int r = 0; r < 2; ++r) {
+    const int row0 = (blockIdx.x % nrb) * kDecRows + 16 * r + g;
+    live[r] = row0 < p.dv;
+    rows[r] = live[r] ? row0 : p.dv - 1;  // rows past d_v compute a copy, store nothing
+    sp[r] = p.state_out + (bh * p.dv + rows[r]) * DK + l16 * EPL;
+    if constexpr (EPL % 4 == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m[4 * c + j] = w[j];
+      for (int c = 0; c < EPL / 4; ++c) {
+        const f32x4 w = __builtin_nontemporal_load((const f32x4 *)(sp[r] + 4 * c));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[r][4 * c + j] = w[j];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m[r][e] = sp[r][e];
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) m[e] = s[e];
   }
   TokenOps<T, EPL> x;
   {
     DeltaParams one = p;
     one.L = 1;
-    load_token<T, EPL>(one, bh, row, l16, 0, x);
+    load_token<T, EPL>(one, bh, rows[0], l16, 0, x);
   }
+  const float v1 = to_f32(((const T *)p.v)[bh * p.dv + rows[1]]);
   float kh[EPL], qh[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
@@ -346,18 +357,23 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(DeltaParams p) {
     qh[e] *= rq;
   }
   const float alpha = exp2_fast(to_f32(x.a) * kLog2e), beta = to_f32(x.beta);
-  const float ot = delta_row<EPL>(m, kh, qh, alpha, alpha * beta, beta * to_f32(x.v));
-  if (live) {
-    if constexpr (EPL % 4 == 0) {
+  float ot[2];
+  ot[0] = delta_row<EPL>(m[0], kh, qh, alpha, alpha * beta, beta * to_f32(x.v));
+  ot[1] = delta_row<EPL>(m[1], kh, qh, alpha, alpha * beta, beta * v1);
 #pragma unroll
-      for (int c = 0; c < EPL / 4; ++c)
-        __builtin_nontemporal_store((f32x4){m[4 * c], m[4 * c + 1], m[4 * c + 2], m[4 * c + 3]},
-                                    (f32x4 *)(s + 4 * c));
-    } else {
+  for (int r = 0; r < 2; ++r) {
+    if (live[r]) {
+      if constexpr (EPL % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s[e] = m[e];
+        for (int c = 0; c < EPL / 4; ++c)
+          __builtin_nontemporal_store((f32x4){m[r][4 * c], m[r][4 * c + 1], m[r][4 * c + 2], m[r][4 * c + 3]},
+                                      (f32x4 *)(sp[r] + 4 * c));
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sp[r][e] = m[r][e];
+      }
+      if (l16 == 0) ((T *)p.o)[bh * p.dv + rows[r]] = from_f32<T>(ot[r]);
     }
-    if (l16 == 0) ((T *)p.o)[bh * p.dv + row] = from_f32<T>(ot);
   }
 }
 
@@ -369,7 +385,8 @@ hipError_t launch(const LayerArgs &a, bool decode) {
   p.state_out = decode ? a.state : a.state_out;
   p.o = a.o;
   p.L = a.L; p.dv = a.dv;
-  const size_t nrb = (size_t)(a.dv + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int rows = decode ? kDecRows : kRowsPerBlock;
+  const size_t nrb = (size_t)(a.dv + rows - 1) / rows;
   const dim3 grid((unsigned)((size_t)a.B * a.H * nrb)), block(kThreads);
   if (decode)
     hipLaunchKernelGGL((gdn_decode_kernel<T, EPL>), grid, block, 0, a.stream, p);

@@ -171,3 +171,21 @@ def test_decode_equals_prefill_token():
     torch.cuda.synchronize()
     assert torch.allclose(o_pre[:, :, 0].float(), o_dec.float(), rtol=1e-5, atol=1e-6)
     assert torch.allclose(s_pre, s_dec, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("d,dv,dtype", [(32, 40, "bf16"), (64, 5, "f32"), (128, 48, "bf16")])
+def test_decode_ragged_value_rows(d, dv, dtype):
+    """Value-row counts that fill no whole block of the decode step."""
+    wl = WORKLOADS["decode_b8"].with_(B=3, H=5, L=20, d=d, dv=dv, dtype=dtype)
+    say("decode ragged d=%d dv=%d %s" % (d, dv, dtype))
+    x = make_delta(wl, DEV)
+    st = torch.empty((wl.B, wl.H, dv, d), device=DEV)
+    run(x, state_out=st)
+    _, ref_s = oracle_fwd(x)
+    t = make_delta_token(wl, 0, DEV)
+    o = G.gdn_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], st)
+    f = {k: to_f64(v) for k, v in t.items()}
+    ref_o, ref_s = D.gdn_decode_step(f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], ref_s)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert row_rel_err(gpu_f64(o), ref_o) <= tol
+    assert row_rel_err(gpu_f64(st), ref_s) <= tol
