@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
 // gradient of its layout, and this block's share of dWphi_q = sum_t q_t^T
 // du_q,t and of dWphi_k.  The projections sit in LDS transposed ([f/2][d]) so
 // that the lanes of dq = du Wphi^T read consecutive words.
-template <class T>
+template <class T, bool GLA, bool SWA>
 __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
   __shared__ float WT[2][kMaxF2 * kBwdMaxD];
   __shared__ float X[2][kBwdMaxD];
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
   const int h = bh % p.H, d = p.d, dv = p.dv, f = p.f, f2 = p.f2, L = p.L;
   const int t0 = tile * kFeatTok, nt = min(kFeatTok, L - t0);
   const size_t N = (size_t)p.B * p.H * L, NF = N * f;
-  const bool gla = p.gla, swa = p.swa;
+  constexpr bool gla = GLA;
   if (gla) {
     const T *wq = (const T *)p.wq + (size_t)h * d * f2;
     const T *wk = (const T *)p.wk + (size_t)h * d * f2;
@@ -541,36 +541,46 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
     float x, pp, pn, dp[kMaxSlices], dn[kMaxSlices], gr[2], ds, dvw[kMaxRowWaves], dvs;
   };
   const int m = tid >> 7, mi = tid & 127;
+  // Every lane loads every operand from clamped indices (tokens past the tile,
+  // features past f/2, slices past nsl, row waves past nw, columns past d or
+  // d_v read valid memory and are masked where used): loads under a lane or
+  // wave condition made the compiler wait for every load in flight, the next
+  // token's included, before each token.
+  const int mic = min(mi, d - 1), lanec = min(lane, f2 - 1), tidv = min(tid, dv - 1);
   auto fetch = [&](int tt) {
-    Pre r = {};
-    if (tt >= nt) return r;
-    const size_t row = (size_t)bh * L + t0 + tt;
-    if (gla) {
-      if (mi < d) r.x = ld((const T *)(m ? p.k : p.q) + row * d + mi);
-      if (wave < 2 && lane < f2) {
-        const float *ph = (wave ? p.pk : p.pq) + row * f;
-        const float *dph = (wave ? p.dpk : p.dpq) + row * f;
-        r.pp = ph[lane];
-        r.pn = ph[f2 + lane];
+    Pre r;
+    const int tl = t0 + min(tt, nt - 1);
+    const size_t row = (size_t)bh * L + tl;
+    if constexpr (GLA) {
+      r.x = ld((const T *)(m ? p.k : p.q) + row * d + mic);
+      const float *ph = ((wave & 1) ? p.pk : p.pq) + row * f;
+      const float *dph = ((wave & 1) ? p.dpk : p.dpq) + row * f;
+      r.pp = ph[lanec];
+      r.pn = ph[f2 + lanec];
 #pragma unroll
-        for (int sl = 0; sl < kMaxSlices; ++sl)
-          if (sl < p.nsl) {
-            r.dp[sl] = dph[sl * NF + lane];
-            r.dn[sl] = dph[sl * NF + f2 + lane];
-          }
+      for (int sl = 0; sl < kMaxSlices; ++sl) {
+        const size_t slc = (size_t)min(sl, p.nsl - 1);
+        r.dp[sl] = dph[slc * NF + lanec];
+        r.dn[sl] = dph[slc * NF + f2 + lanec];
       }
-      if (wave == 2 && p.gate_mode == 0 && !p.gate_is_log)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (lane + 64 * u < f) r.gr[u] = ld(g + row * f + lane + 64 * u);
-      if (tid < dv)
+      for (int u = 0; u < 2; ++u)
+        r.gr[u] = ld(g + gate_index(p.gate_mode, bh, p.H, L, f, tl, min(lane + 64 * u, f - 1)));
 #pragma unroll
-        for (int w = 0; w < kMaxRowWaves; ++w)
-          if (w < p.nw) r.dvw[w] = p.dvg[((size_t)w * N + row) * dv + tid];
+      for (int w = 0; w < kMaxRowWaves; ++w)
+        r.dvw[w] = p.dvg[((size_t)min(w, p.nw - 1) * N + row) * dv + tidv];
+    } else {
+      r.x = r.pp = r.pn = r.gr[0] = r.gr[1] = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxSlices; ++sl) r.dp[sl] = r.dn[sl] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kMaxRowWaves; ++w) r.dvw[w] = 0.0f;
     }
-    if (swa) {
-      if (mi < d) r.ds = (m ? p.dks : p.dqs)[row * d + mi];
-      if (tid < dv) r.dvs = p.dvs[row * dv + tid];
+    if constexpr (SWA) {
+      r.ds = (m ? p.dks : p.dqs)[row * d + mic];
+      r.dvs = p.dvs[row * dv + tidv];
+    } else {
+      r.ds = r.dvs = 0.0f;
     }
     return r;
   };
@@ -587,10 +597,10 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         float dp = 0.0f, dn = 0.0f;
 #pragma unroll
         for (int sl = 0; sl < kMaxSlices; ++sl) {
-          dp += cur.dp[sl];
-          dn += cur.dn[sl];
+          dp += sl < p.nsl ? cur.dp[sl] : 0.0f;
+          dn += sl < p.nsl ? cur.dn[sl] : 0.0f;
         }
-        const float pp = cur.pp, pn = cur.pn;
+        const float pp = ok ? cur.pp : 0.0f, pn = ok ? cur.pn : 0.0f;
         const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
         if (ok) {
           DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
@@ -630,7 +640,7 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
     if (tid < dv) {
       float acc = cur.dvs;
 #pragma unroll
-      for (int w = 0; w < kMaxRowWaves; ++w) acc += cur.dvw[w];
+      for (int w = 0; w < kMaxRowWaves; ++w) acc += w < p.nw ? cur.dvw[w] : 0.0f;
       ((T *)p.gv)[row * dv + tid] = from_f32<T>(acc);
     }
     if (gla) {
@@ -1164,7 +1174,12 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     }
   }
   if (a.L > 0 && BH > 0) {
-    hipLaunchKernelGGL(bwd_feature_kernel<T>, dim3(BH * p.nft), block, 0, a.stream, p);
+    if (p.gla && p.swa)
+      hipLaunchKernelGGL((bwd_feature_kernel<T, true, true>), dim3(BH * p.nft), block, 0, a.stream, p);
+    else if (p.gla)
+      hipLaunchKernelGGL((bwd_feature_kernel<T, true, false>), dim3(BH * p.nft), block, 0, a.stream, p);
+    else
+      hipLaunchKernelGGL((bwd_feature_kernel<T, false, true>), dim3(BH * p.nft), block, 0, a.stream, p);
     if (!launched()) return e;
   }
   const size_t nred = (p.gla ? 2 * (size_t)a.H * a.d * p.f2 : 0) + (p.swa ? (size_t)a.H * a.n_meta : 0) +
