@@ -123,17 +123,16 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   };
 
   // All loads are issued before any arithmetic, the operands of the longest
-  // dependent chain (window scores -> softmax -> weighted values) first.
+  // dependent chain (window scores -> softmax -> weighted values) first.  Every
+  // load is unconditional, from a clamped index (slots past the window, lanes
+  // past a row), and masked where it is used: a load under a lane condition
+  // made the compiler wait for it, and for everything issued before it, right
+  // where it was issued.
   // (1) window score operands: 16 threads per ring slot, 8 dimensions each
   const int ks_slot = tid >> 4, ks_seg = tid & 15;
   float ka[8], qa[8];
   if (SWA) {
-    if (ks_slot < w) {
-      V::ld8(kc + (size_t)ks_slot * kD + 8 * ks_seg, ka);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ka[e] = 0.0f;
-    }
+    V::ld8(kc + (size_t)min(ks_slot, w - 1) * kD + 8 * ks_seg, ka);  // slots past w: masked by ring_ok
     V::ld8(qt + 8 * ks_seg, qa);
   }
   // (2) Hedgehog GEMV operands: rows kGR*rgw .. kGR*rgw+kGR-1, columns 8*cb .. 8*cb+7
@@ -163,22 +162,18 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   // after weighting, the two lanes swap the halves they do not own
   float vw[8];
   const int vslot = rg + kNRG * (c4 & 1);
-  if (SWA) {
-    if (vslot < w) {
-      V::ld8(vc + (size_t)vslot * kDV + slice * kDVS + 8 * (c4 >> 1), vw);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vw[e] = 0.0f;
-    }
-  }
+  if (SWA) V::ld8(vc + (size_t)min(vslot, w - 1) * kDV + slice * kDVS + 8 * (c4 >> 1), vw);  // weight 0 past w
   const f32x4 v4 = V::ld4(vt + col);
   // (5) gates
-  const float graw = tid < kF ? to_f32(((const T *)p.gate)[gate_index(p.gate_mode, bh, p.H, 1, kF, 0, tid)]) : 0.0f;
-  const float qn = tid < kD ? to_f32(qt[tid]) : 0.0f, kn = tid < kD ? to_f32(kt[tid]) : 0.0f;
+  const float graw = to_f32(((const T *)p.gate)[gate_index(p.gate_mode, bh, p.H, 1, kF, 0, min(tid, kF - 1))]);
+  const float qn = to_f32(qt[min(tid, kD - 1)]), kn = to_f32(kt[min(tid, kD - 1)]);  // used by waves 0-1 only
   // (5b) operands of the ring append and of the sink softmax, so that no load
   // sits in the dependent chain after the first barrier or in the kernel's tail
-  const f32x4 kt4 = (SWA && slice == 0 && tid < kD / 4) ? V::ld4(kt + 4 * tid) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  const float tmeta = (SWA && wave == 2 && lane < p.n_meta) ? p.meta[(size_t)h * p.n_meta + lane] : -INFINITY;
+  const f32x4 kt4 = V::ld4(kt + 4 * min(tid, kD / 4 - 1));  // stored by threads tid < kD / 4
+  // p.meta is a valid address even without sinks (the host passes another
+  // buffer then); lanes past n_meta are masked
+  const float tmraw = p.meta[(size_t)h * max(p.n_meta, 1) * (p.n_meta > 0) + min(lane, max(p.n_meta - 1, 0))];
+  const float tmeta = lane < p.n_meta ? tmraw : -INFINITY;
 
   // window scores (ring slots) and q . k of the new token (waves 0-1)
   if (SWA) {
@@ -290,7 +285,8 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
 template <class T>
 hipError_t dispatch(const LayerArgs &a, int parts) {
   DecParams p;
-  p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.wq = a.wq; p.wk = a.wk; p.meta = a.meta;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.wq = a.wq; p.wk = a.wk;
+  p.meta = a.meta && a.n_meta > 0 ? a.meta : a.state;  // the kernel loads it unconditionally
   p.state = a.state; p.kcache = a.kcache; p.vcache = a.vcache; p.pos = a.pos; p.o = a.o;
   p.B = a.B; p.H = a.H; p.window = a.window; p.n_meta = a.n_meta; p.scale = a.scale;
   p.gate_is_log = a.gate_is_log ? 1 : 0;
