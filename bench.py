@@ -54,10 +54,17 @@ def decode_bytes_per_step(B, H, d, f, dv, w, bpe=2):
     return state + ring + wphi + io
 
 
-def source_hash():
+# Sources of the kernels and host dispatch of one hybrid_layer_fwd prefill call:
+# the stored HBM traffic of that call stays valid while these are unchanged.
+PREFILL_SOURCES = ("capi.cpp", "chunk_common.hpp", "chunk_out.hip", "chunked.hip", "device_common.hpp",
+                   "launch.hpp")
+
+
+def source_hash(names=None):
+    """Hash of the named csrc files (all of them by default)."""
     h = hashlib.sha256()
     cs = os.path.join(ROOT, "gated_linear_attention_hybrid_amd", "csrc")
-    for name in sorted(os.listdir(cs)):
+    for name in sorted(names if names is not None else os.listdir(cs)):
         with open(os.path.join(cs, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -65,7 +72,7 @@ def source_hash():
 
 def load_traffic(key):
     """HBM traffic per launch from the committed rocprofv3 counter summary, only
-    when it was taken on the current kernel sources."""
+    when the sources it was taken on (the entry's file list) are unchanged."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
@@ -73,7 +80,7 @@ def load_traffic(key):
     except (OSError, ValueError):
         return None
     ent = rec.get(key)
-    if not ent or ent.get("source_hash") != source_hash():
+    if not ent or ent.get("source_hash") != source_hash(ent.get("sources")):
         return None
     return ent.get("bytes_per_launch")
 
