@@ -263,9 +263,9 @@ constexpr int kPF = 8;  // tokens a sweep loads ahead of the one it computes
 // Each step's operands are loaded kPF tokens ahead (the step is a chain of
 // dependent arithmetic on the state; its loads must not wait on it).
 template <class T>
-__global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
+__device__ __forceinline__ void fwd_sweep(const BwdParams &p, int blk) {
   typedef typename Quad<T>::type Q;
-  const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
+  const int bh = blk / p.nsl, slice = blk % p.nsl;
   if (32 * (int)(threadIdx.x >> 6) >= p.f) return;
   const SweepLane s = sweep_lane(p, slice);
   const int L = p.L, f = p.f, dv = p.dv;
@@ -349,9 +349,9 @@ __global__ __launch_bounds__(kBT) void bwd_fwd_sweep_kernel(BwdParams p) {
 // dphik_t), the wave's part of dS_t^T phik_t, dS_0-gradient = diag(Gamma_0)
 // dS_0, and the slice's part of d log Gamma_0 = Gamma_0 (S_in . dS_0).
 template <class T>
-__global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
+__device__ __forceinline__ void rev_sweep(const BwdParams &p, int blk) {
   typedef typename Quad<T>::type Q;
-  const int bh = blockIdx.x / p.nsl, slice = blockIdx.x % p.nsl;
+  const int bh = blk / p.nsl, slice = blk % p.nsl;
   const int wave = threadIdx.x >> 6;
   if (32 * wave >= p.f) return;
   const SweepLane s = sweep_lane(p, slice);
@@ -449,6 +449,19 @@ __global__ __launch_bounds__(kBT) void bwd_rev_sweep_kernel(BwdParams p) {
     x0[i] = gn[i] * sum8(dot4(s4, dS[i]));
   }
   if (lead && s.rok) *(f32x4 *)(p.xs + ((BH + bh) * p.nsl + slice) * f + s.r0) = x0;
+}
+
+// Both sweeps in one launch: they share only inputs, and each has B H nsl
+// blocks of one wave per SIMD (128 at 32 heads of 128 columns), so apart they
+// leave half of the compute units idle.  The longer reverse sweep takes the
+// first blocks.
+template <class T>
+__global__ __launch_bounds__(kBT) void bwd_sweeps_kernel(BwdParams p) {
+  const int n = p.B * p.H * p.nsl;
+  if ((int)blockIdx.x < n)
+    rev_sweep<T>(p, (int)blockIdx.x);
+  else
+    fwd_sweep<T>(p, (int)blockIdx.x - n);
 }
 
 // d log Gamma at the first token of every 64-token tile.  With d b_t =
@@ -1163,9 +1176,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   }
   if (p.gla && BH > 0) {
     // with no tokens the sweeps still pass dS_final through to dS_0
-    hipLaunchKernelGGL(bwd_fwd_sweep_kernel<T>, dim3(BH * p.nsl), block, 0, a.stream, p);
-    if (!launched()) return e;
-    hipLaunchKernelGGL(bwd_rev_sweep_kernel<T>, dim3(BH * p.nsl), block, 0, a.stream, p);
+    hipLaunchKernelGGL(bwd_sweeps_kernel<T>, dim3(2 * BH * p.nsl), block, 0, a.stream, p);
     if (!launched()) return e;
     if (a.L > 0) {
       hipLaunchKernelGGL(bwd_tile_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
