@@ -41,6 +41,7 @@ constexpr int kBT = 256;         // threads of every backward block
 constexpr int kSliceCols = 32;   // d_v columns of one sweep block
 constexpr int kPrepTok = 16;     // tokens of one prologue block
 constexpr int kFeatTok = 64;     // tokens of one feature-gradient block
+constexpr int kFeatPF = 2;       // tokens the feature-gradient block loads ahead
 constexpr int kSwaTok = 16;      // query (key) tokens of one window block
 constexpr int kMaxF2 = kBwdMaxF / 2;
 constexpr int kMaxSlices = kBwdMaxD / kSliceCols;  // d_v slices of the sweeps
@@ -511,13 +512,14 @@ __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
 // du_q,t and of dWphi_k.  The projections sit in LDS transposed ([f/2][d]) so
 // that the lanes of dq = du Wphi^T read consecutive words.
 template <class T, bool GLA, bool SWA>
-__global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_feature_kernel(BwdParams p) {
   __shared__ float WT[2][kMaxF2 * kBwdMaxD];
   __shared__ float X[2][kBwdMaxD];
-  __shared__ float DU[2][kMaxF2];
+  __shared__ __align__(16) float DU[2][kMaxF2];
   __shared__ float E[2][kBwdMaxF];
   constexpr int NP = kBwdMaxD * kMaxF2 / kBT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int bh = blockIdx.x / p.nft, tile = blockIdx.x % p.nft;
   const int h = bh % p.H, d = p.d, dv = p.dv, f = p.f, f2 = p.f2, L = p.L;
   const int t0 = tile * kFeatTok, nt = min(kFeatTok, L - t0);
@@ -553,35 +555,59 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
   struct Pre {
     float x, pp, pn, dp[kMaxSlices], dn[kMaxSlices], gr[2], ds, dvw[kMaxRowWaves], dvs;
   };
-  const int m = tid >> 7, mi = tid & 127;
+  const int m = wave >> 1, mi = tid & 127;  // m = tid >> 7
   // Every lane loads every operand from clamped indices (tokens past the tile,
   // features past f/2, slices past nsl, row waves past nw, columns past d or
   // d_v read valid memory and are masked where used): loads under a lane or
   // wave condition made the compiler wait for every load in flight, the next
   // token's included, before each token.
   const int mic = min(mi, d - 1), lanec = min(lane, f2 - 1), tidv = min(tid, dv - 1);
+  // Wave-uniform base pointers at the tile's first token (m and wave & 1 are
+  // wave-uniform), formed once; a token adds a 32-bit offset of a fixed stride,
+  // so the token loop carries no 64-bit index arithmetic.
+  const size_t row0 = (size_t)bh * L + t0;
+  const T *bx = (const T *)(m ? p.k : p.q) + row0 * d;
+  const float *bph = ((wave & 1) ? p.pk : p.pq) + row0 * f;
+  const float *bdp[kMaxSlices];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSlices; ++sl)
+    bdp[sl] = ((wave & 1) ? p.dpk : p.dpq) + (size_t)min(sl, p.nsl - 1) * NF + row0 * f;
+  const float *bdvw[kMaxRowWaves];
+#pragma unroll
+  for (int w = 0; w < kMaxRowWaves; ++w) bdvw[w] = p.dvg + ((size_t)min(w, p.nw - 1) * N + row0) * dv;
+  const float *bds = (m ? p.dks : p.dqs) + row0 * d;
+  const float *bdvs = p.dvs + row0 * dv;
+  // gates: per feature (stride f), per token (stride 1) or one per head
+  const T *bg = g + gate_index(p.gate_mode, bh, p.H, L, f, t0, 0);
+  const unsigned gstep = p.gate_mode == 0 ? (unsigned)f : p.gate_mode == 1 ? 1u : 0u;
+  const unsigned glane0 = p.gate_mode == 0 ? (unsigned)min(lane, f - 1) : 0u;
+  const unsigned glane1 = p.gate_mode == 0 ? (unsigned)min(lane + 64, f - 1) : 0u;
+  // outputs of the tile's first token: dq or dk (per wave), dv, the gate gradient
+  T *bgx = (T *)(m ? p.gk : p.gq) + row0 * d;
+  T *bgv = (T *)p.gv + row0 * dv;
+  T *bdg = dg + row0 * (p.gate_mode == 0 ? (size_t)f : (size_t)1);
+  // a load at a 32-bit byte offset from a wave-uniform base (scalar base plus
+  // vector offset addressing)
+  auto at = [](const auto *base, unsigned elems) {
+    typedef typename std::remove_cv<typename std::remove_reference<decltype(*base)>::type>::type E;
+    return *(const E *)((const char *)base + elems * (unsigned)sizeof(E));
+  };
   auto fetch = [&](int tt) {
     Pre r;
-    const int tl = t0 + min(tt, nt - 1);
-    const size_t row = (size_t)bh * L + tl;
+    const unsigned tl = (unsigned)min(tt, nt - 1);  // token within the tile
     if constexpr (GLA) {
-      r.x = ld((const T *)(m ? p.k : p.q) + row * d + mic);
-      const float *ph = ((wave & 1) ? p.pk : p.pq) + row * f;
-      const float *dph = ((wave & 1) ? p.dpk : p.dpq) + row * f;
-      r.pp = ph[lanec];
-      r.pn = ph[f2 + lanec];
+      r.x = to_f32(at(bx, tl * d + mic));
+      r.pp = at(bph, tl * f + lanec);
+      r.pn = at(bph, tl * f + f2 + lanec);
 #pragma unroll
       for (int sl = 0; sl < kMaxSlices; ++sl) {
-        const size_t slc = (size_t)min(sl, p.nsl - 1);
-        r.dp[sl] = dph[slc * NF + lanec];
-        r.dn[sl] = dph[slc * NF + f2 + lanec];
+        r.dp[sl] = at(bdp[sl], tl * f + lanec);
+        r.dn[sl] = at(bdp[sl], tl * f + f2 + lanec);
       }
+      r.gr[0] = to_f32(at(bg, tl * gstep + glane0));
+      r.gr[1] = to_f32(at(bg, tl * gstep + glane1));
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        r.gr[u] = ld(g + gate_index(p.gate_mode, bh, p.H, L, f, tl, min(lane + 64 * u, f - 1)));
-#pragma unroll
-      for (int w = 0; w < kMaxRowWaves; ++w)
-        r.dvw[w] = p.dvg[((size_t)min(w, p.nw - 1) * N + row) * dv + tidv];
+      for (int w = 0; w < kMaxRowWaves; ++w) r.dvw[w] = at(bdvw[w], tl * dv + tidv);
     } else {
       r.x = r.pp = r.pn = r.gr[0] = r.gr[1] = 0.0f;
 #pragma unroll
@@ -590,18 +616,20 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
       for (int w = 0; w < kMaxRowWaves; ++w) r.dvw[w] = 0.0f;
     }
     if constexpr (SWA) {
-      r.ds = (m ? p.dks : p.dqs)[row * d + mic];
-      r.dvs = p.dvs[row * dv + tidv];
+      r.ds = at(bds, tl * d + mic);
+      r.dvs = at(bdvs, tl * dv + tidv);
     } else {
       r.ds = r.dvs = 0.0f;
     }
     return r;
   };
 
-  Pre cur = fetch(0);
-  for (int tt = 0; tt < nt; ++tt) {
-    const size_t row = (size_t)bh * L + t0 + tt;
-    const Pre nxt = fetch(tt + 1);
+  // One token's work.  Tokens past the tile (the last group of a short tile)
+  // run with zero feature gradients and store nothing, so every group runs whole
+  // with no per-token branch.
+  auto token = [&](const Pre &cur, int tt) {
+    const bool live = tt < nt;
+    const unsigned ut = (unsigned)tt;
     __syncthreads();
     if (gla) {
       if (mi < d) X[m][mi] = cur.x;
@@ -613,7 +641,7 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
           dp += sl < p.nsl ? cur.dp[sl] : 0.0f;
           dn += sl < p.nsl ? cur.dn[sl] : 0.0f;
         }
-        const float pp = ok ? cur.pp : 0.0f, pn = ok ? cur.pn : 0.0f;
+        const float pp = (ok && live) ? cur.pp : 0.0f, pn = (ok && live) ? cur.pn : 0.0f;
         const float sp = wave_sum(pp * dp), sn = wave_sum(pn * dn);
         if (ok) {
           DU[wave][lane] = pp * (dp - sp) - pn * (dn - sn);
@@ -631,43 +659,77 @@ __global__ __launch_bounds__(kBT) void bwd_feature_kernel(BwdParams p) {
         if (r < f) {
           const float da = run[u];
           run[u] = da - (E[0][r] - E[1][r]);
-          if (p.gate_mode == 0)
-            dg[row * f + r] = from_f32<T>(p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(cur.gr[u])));
-          else
+          if (p.gate_mode == 0) {
+            if (live)
+              *(T *)((char *)bdg + (ut * f + r) * (unsigned)sizeof(T)) = from_f32<T>(p.gate_is_log ? da : da * rcp_fast(1.0f + exp_fast(cur.gr[u])));
+          } else {
             tsum += da;
+          }
         }
       }
       if (p.gate_mode == 1) {
         tsum = wave_sum(tsum);
-        if (lane == 0) dg[row] = from_f32<T>(tsum);
+        if (lane == 0 && live) *(T *)((char *)bdg + ut * (unsigned)sizeof(T)) = from_f32<T>(tsum);
       } else if (p.gate_mode == 2) {
-        gsum += tsum;
+        gsum += live ? tsum : 0.0f;
       }
     }
-    if (mi < d) {
+    if (mi < d && live) {
       float acc = cur.ds;
-      if (gla)
-        for (int j = 0; j < f2; ++j) acc += DU[m][j] * WT[m][j * d + mi];
-      ((T *)(m ? p.gk : p.gq))[row * d + mi] = from_f32<T>(acc);
+      if (gla) {
+        // du . Wphi^T column mi: LDS reads requested 8 at a time into separate
+        // sums (one dependent LDS round trip per feature otherwise)
+        const float *du = DU[m], *wt = &WT[m][mi];
+        if (f2 % 8 == 0) {
+          float a8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+          for (int j = 0; j < f2; j += 8) {
+            float x8[8], w8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              x8[e] = du[j + e];
+              w8[e] = wt[(j + e) * d];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a8[e] += x8[e] * w8[e];
+          }
+          acc += ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
+        } else {
+          for (int j = 0; j < f2; ++j) acc += du[j] * wt[j * d];
+        }
+      }
+      *(T *)((char *)bgx + (ut * d + mi) * (unsigned)sizeof(T)) = from_f32<T>(acc);
     }
-    if (tid < dv) {
+    if (tid < dv && live) {
       float acc = cur.dvs;
 #pragma unroll
       for (int w = 0; w < kMaxRowWaves; ++w) acc += w < p.nw ? cur.dvw[w] : 0.0f;
-      ((T *)p.gv)[row * dv + tid] = from_f32<T>(acc);
+      *(T *)((char *)bgv + (ut * dv + tid) * (unsigned)sizeof(T)) = from_f32<T>(acc);
     }
     if (gla) {
+      // rows i >= d accumulate into sums that are never stored (clamped reads,
+      // no per-row branch)
       const float duq = DU[0][jj], duk = DU[1][jj];
 #pragma unroll
       for (int n = 0; n < NP; ++n) {
-        const int i = i0 + n * istep;
-        if (i < d) {
-          aq[n] += X[0][i] * duq;
-          ak[n] += X[1][i] * duk;
-        }
+        const int i = min(i0 + n * istep, kBwdMaxD - 1);
+        aq[n] += X[0][i] * duq;
+        ak[n] += X[1][i] * duk;
       }
     }
-    cur = nxt;
+  };
+  // Operands kFeatPF tokens ahead in a ring whose slots are fixed registers (a
+  // loop-carried copy of the next token's operands made every token wait for
+  // its loads, one memory round trip per token).
+  Pre ring[kFeatPF];
+#pragma unroll
+  for (int u = 0; u < kFeatPF; ++u) ring[u] = fetch(u);
+  for (int g0 = 0; g0 < nt; g0 += kFeatPF) {
+#pragma unroll
+    for (int u = 0; u < kFeatPF; ++u) {
+      const Pre cur = ring[u];
+      ring[u] = fetch(g0 + u + kFeatPF);
+      token(cur, g0 + u);
+    }
   }
   if (!gla) return;
   const size_t base = ((size_t)bh * p.nft + tile) * d * f2;
