@@ -150,6 +150,20 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Raw quads of the I/O dtype, widened when used: a prefetched bf16 quad costs
+// two registers.
+template <class T> struct Quad;
+template <> struct Quad<float> { typedef f32x4 type; };
+template <> struct Quad<bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 widen(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+template <class Q> __device__ __forceinline__ Q zero_quad() {
+  Q z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+  return z;
+}
+
 // Prologue in 64-token tiles (d a multiple of 4 up to 128, f/2 a multiple of 4
 // up to 64): the projections as a register-tiled product, thread (tg, fg) =
 // (tid / 16, tid % 16) computing tokens 4tg .. 4tg+3 by features 4fg .. 4fg+3
@@ -172,13 +186,35 @@ __global__ __launch_bounds__(kBT) void bwd_prep_tile_kernel(BwdParams p) {
   const int t0 = tile * kPrepTile, nt = min(kPrepTile, L - t0);
   const size_t row0 = (size_t)bh * L + t0;
   const int wave = tid >> 6, lane = tid & 63;
+  typedef typename Quad<T>::type Q;
+  // quads (4 elements) each thread stages: of W (d x f/2) and of the input tile
+  // (64 tokens x d); all of a thread's loads are issued before its LDS stores
+  constexpr int kNQ = kBwdMaxD * kMaxF2 / 4 / kBT;
+  constexpr int kXQ = kPrepTile * kBwdMaxD / 4 / kBT;
+  static_assert(kNQ * 4 * kBT == kBwdMaxD * kMaxF2 && kXQ * 4 * kBT == kPrepTile * kBwdMaxD, "whole quads");
+  const int d4 = d >> 2, nwq = d * f2 / 4, nxq = kPrepTile * d4;
   for (int m = 0; m < 2; ++m) {
     const T *w = (const T *)(m ? p.wk : p.wq) + (size_t)h * d * f2;
-    const T *x = (const T *)(m ? p.k : p.q);
-    for (int i = tid; i < d * f2; i += kBT) W[i] = ld(w + i);
-    for (int i = tid; i < kPrepTile * d; i += kBT) {
-      const int tt = i / d, e = i - tt * d;
-      XT[e][tt] = tt < nt ? ld(x + (row0 + tt) * d + e) : 0.0f;
+    const T *x = (const T *)(m ? p.k : p.q) + row0 * d;
+    Q wv[kNQ], xv[kXQ];
+#pragma unroll
+    for (int k = 0; k < kNQ; ++k) wv[k] = *(const Q *)(w + 4 * min(tid + kBT * k, nwq - 1));
+#pragma unroll
+    for (int k = 0; k < kXQ; ++k) {
+      const int q = min(tid + kBT * k, nxq - 1), tt = q / d4;
+      xv[k] = *(const Q *)(x + (size_t)min(tt, nt - 1) * d + 4 * (q - tt * d4));
+    }
+#pragma unroll
+    for (int k = 0; k < kNQ; ++k)
+      if (tid + kBT * k < nwq) *(f32x4 *)&W[4 * (tid + kBT * k)] = widen(wv[k]);
+#pragma unroll
+    for (int k = 0; k < kXQ; ++k) {
+      const int q = tid + kBT * k, tt = q / d4, e = 4 * (q - tt * d4);
+      if (q < nxq) {
+        const f32x4 v4 = widen(xv[k]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) XT[e + j][tt] = tt < nt ? v4[j] : 0.0f;
+      }
     }
     __syncthreads();
     f32x4 acc[4] = {};
@@ -214,10 +250,31 @@ __global__ __launch_bounds__(kBT) void bwd_prep_tile_kernel(BwdParams p) {
     __syncthreads();  // W, XT and U are reused by the next map
   }
   const T *g = (const T *)p.gate;
-  for (int i = tid; i < nt * f; i += kBT) {
-    const int tt = i / f, r = i - tt * f;
-    p.gam[(row0 + tt) * f + r] =
-        gate_from(ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t0 + tt, r)), p.gate_is_log);
+  if (p.gate_mode == 0) {
+    // per-feature gates: quads of the tile's [nt][f] rows, loads first
+    constexpr int kGQ = kPrepTile * kBwdMaxF / 4 / kBT;
+    const int f4 = f >> 2, ngq = nt * f4;
+    const T *gb = g + row0 * f;
+    Q gv[kGQ];
+#pragma unroll
+    for (int k = 0; k < kGQ; ++k) gv[k] = *(const Q *)(gb + 4 * (size_t)min(tid + kBT * k, ngq - 1));
+#pragma unroll
+    for (int k = 0; k < kGQ; ++k) {
+      const int q = tid + kBT * k;
+      if (q < ngq) {
+        const f32x4 v4 = widen(gv[k]);
+        f32x4 r4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r4[j] = gate_from(v4[j], p.gate_is_log);
+        *(f32x4 *)(p.gam + row0 * f + 4 * (size_t)q) = r4;
+      }
+    }
+  } else {
+    for (int i = tid; i < nt * f; i += kBT) {
+      const int tt = i / f, r = i - tt * f;
+      p.gam[(row0 + tt) * f + r] =
+          gate_from(ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t0 + tt, r)), p.gate_is_log);
+    }
   }
 }
 
@@ -240,20 +297,6 @@ __device__ __forceinline__ SweepLane sweep_lane(const BwdParams &p, int slice) {
   s.rok = s.r0 < p.f;
   s.cok = s.c0 < p.dv;
   return s;
-}
-
-// Raw quads of the I/O dtype, widened when used: a prefetched bf16 quad costs
-// two registers.
-template <class T> struct Quad;
-template <> struct Quad<float> { typedef f32x4 type; };
-template <> struct Quad<bf16> { typedef bf16x4 type; };
-__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
-__device__ __forceinline__ f32x4 widen(bf16x4 x) { return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
-template <class Q> __device__ __forceinline__ Q zero_quad() {
-  Q z;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) z[i] = 0.0f;
-  return z;
 }
 
 constexpr int kPF = 8;  // tokens a sweep loads ahead of the one it computes
