@@ -940,14 +940,46 @@ struct WinTileLds {
   float mp[kWT / 16][16];
 };
 
-// Rows [r0, r0 + n) of a [L][128] bf16 matrix of head bh into LDS rows
-// (zeros outside [0, L)).
-__device__ __forceinline__ void win_stage(bf16 (*dst)[kWS], const bf16 *src, size_t bh, int L, int r0, int n) {
-  for (int idx = threadIdx.x; idx < n * (kWD / 8); idx += kWT) {
-    const int r = idx / (kWD / 8), c8 = (idx % (kWD / 8)) * 8, pos = r0 + r;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (pos >= 0 && pos < L) x = *(const u32x4 *)(src + ((size_t)bh * L + pos) * kWD + c8);
-    *(u32x4 *)&dst[r][c8] = x;
+// The four operand matrices of a tile: rows [ra, ra + kWC) of sa and sb, rows
+// [rc, rc + 2 kWC) of sc and se (zeros outside [0, L), L >= 1).  Every load
+// is issued (from clamped rows) before the first LDS store: a load per store
+// made each block wait one memory round trip per step.
+__device__ __forceinline__ void win_stage_all(WinTileLds &S, const bf16 *sa, const bf16 *sb, int ra, const bf16 *sc,
+                                              const bf16 *se, int rc, size_t bh, int L) {
+  constexpr int kQ = kWD / 8;             // 16-byte quads per row
+  constexpr int kA = kWC * kQ / kWT;      // quads per thread of a kWC-row matrix
+  constexpr int kC = 2 * kWC * kQ / kWT;  // of a 2 kWC-row matrix
+  static_assert(kA * kWT == kWC * kQ && kC * kWT == 2 * kWC * kQ, "whole quads per thread");
+  const int tid = threadIdx.x;
+  auto at = [&](const bf16 *src, int r0, int idx) {
+    const int pos = min(max(r0 + idx / kQ, 0), L - 1);
+    return *(const u32x4 *)(src + ((size_t)bh * L + pos) * kWD + (idx % kQ) * 8);
+  };
+  u32x4 xa[kA], xb[kA], xc[kC], xe[kC];
+#pragma unroll
+  for (int k = 0; k < kA; ++k) {
+    xa[k] = at(sa, ra, tid + kWT * k);
+    xb[k] = at(sb, ra, tid + kWT * k);
+  }
+#pragma unroll
+  for (int k = 0; k < kC; ++k) {
+    xc[k] = at(sc, rc, tid + kWT * k);
+    xe[k] = at(se, rc, tid + kWT * k);
+  }
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < kA; ++k) {
+    const int idx = tid + kWT * k, r = idx / kQ, c8 = (idx % kQ) * 8;
+    const bool ok = ra + r >= 0 && ra + r < L;
+    *(u32x4 *)&S.a[r][c8] = ok ? xa[k] : z;
+    *(u32x4 *)&S.b[r][c8] = ok ? xb[k] : z;
+  }
+#pragma unroll
+  for (int k = 0; k < kC; ++k) {
+    const int idx = tid + kWT * k, r = idx / kQ, c8 = (idx % kQ) * 8;
+    const bool ok = rc + r >= 0 && rc + r < L;
+    *(u32x4 *)&S.c[r][c8] = ok ? xc[k] : z;
+    *(u32x4 *)&S.e[r][c8] = ok ? xe[k] : z;
   }
 }
 
@@ -1012,10 +1044,7 @@ __global__ __launch_bounds__(kWT) void bwd_swa_tile_q_kernel(BwdParams p) {
   const size_t bh = blockIdx.x / nch;
   const int c = blockIdx.x % nch, t0 = c * kWC, h = (int)(bh % p.H);
   const bf16 *q = (const bf16 *)p.q, *k = (const bf16 *)p.k, *v = (const bf16 *)p.v, *dO = (const bf16 *)p.dout;
-  win_stage(S.a, q, bh, p.L, t0, kWC);
-  win_stage(S.b, dO, bh, p.L, t0, kWC);
-  win_stage(S.c, k, bh, p.L, t0 - kWC, 2 * kWC);
-  win_stage(S.e, v, bh, p.L, t0 - kWC, 2 * kWC);
+  win_stage_all(S, q, dO, t0, k, v, t0 - kWC, bh, p.L);
   __syncthreads();
 
   float sc[2][8], dp[2][8];
@@ -1100,14 +1129,12 @@ __global__ __launch_bounds__(kWT) void bwd_swa_tile_kv_kernel(BwdParams p) {
   const size_t bh = blockIdx.x / nch;
   const int c = blockIdx.x % nch, j0 = c * kWC;
   const bf16 *q = (const bf16 *)p.q, *k = (const bf16 *)p.k, *v = (const bf16 *)p.v, *dO = (const bf16 *)p.dout;
-  win_stage(S.a, k, bh, p.L, j0, kWC);
-  win_stage(S.b, v, bh, p.L, j0, kWC);
-  win_stage(S.c, q, bh, p.L, j0, 2 * kWC);
-  win_stage(S.e, dO, bh, p.L, j0, 2 * kWC);
+  win_stage_all(S, k, v, j0, q, dO, j0, bh, p.L);
   if (tid < 2 * kWC) {
     const int t = j0 + tid;
-    S.lse[tid] = t < p.L ? p.lse[bh * p.L + t] : 0.0f;
-    S.del[tid] = t < p.L ? p.del[bh * p.L + t] : 0.0f;
+    const float ls = p.lse[bh * p.L + min(t, p.L - 1)], de = p.del[bh * p.L + min(t, p.L - 1)];
+    S.lse[tid] = t < p.L ? ls : 0.0f;
+    S.del[tid] = t < p.L ? de : 0.0f;
   }
   __syncthreads();
 
