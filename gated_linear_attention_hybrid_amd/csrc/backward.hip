@@ -28,6 +28,7 @@
 //
 // Every reduction is done in a fixed order into per-block partials (no atomics),
 // so the gradients are bitwise repeatable.  All arithmetic is fp32.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1246,6 +1247,43 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   return o;
 }
 
+// A side stream and two events per device, created on first use and kept
+// until the process ends: the window part of the backward runs on it beside
+// the prologue and the state sweeps (the two share only inputs, and a window
+// tile block fits on a compute unit next to a sweep block).  The lock is held
+// while a call enqueues, so concurrent calls do not interleave their event
+// records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream, or nullptr: no device id, creation failed,
+// or the caller's stream is being captured into a graph before the side stream
+// exists (creating one then is not allowed); the caller then runs everything
+// on its own stream.  Call with g_side_mu held.
+SideStream *side_stream(hipStream_t main) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream &ss = g_side[dev];
+  if (!ss.tried) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    ss.tried = true;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.s = nullptr;
+      (void)hipGetLastError();
+    }
+  }
+  return ss.s ? &ss : nullptr;
+}
+
 template <class T>
 hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   BwdParams p = {};
@@ -1275,14 +1313,19 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   const dim3 block(kBT);
   hipError_t e = hipSuccess;
   auto launched = [&]() { if (e == hipSuccess) e = hipGetLastError(); return e == hipSuccess; };
-  if (p.gla && a.L > 0) {
-    if (a.f / 2 % 4 == 0) {
-      const unsigned ntl = (unsigned)((a.L + kPrepTile - 1) / kPrepTile);
-      hipLaunchKernelGGL(bwd_prep_tile_kernel<T>, dim3(BH * ntl), block, 0, a.stream, p);
-    } else {
-      hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(BH * p.npt), block, 0, a.stream, p);
-    }
-    if (!launched()) return e;
+  // the window part on the side stream when both parts run (forked from and
+  // joined back to the caller's stream), else on the caller's stream
+  std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+  SideStream *ss = nullptr;
+  if (p.gla && p.swa && a.L > 0 && BH > 0) {
+    lock.lock();
+    ss = side_stream(a.stream);
+    if (!ss) lock.unlock();
+  }
+  const hipStream_t wstream = ss ? ss->s : a.stream;
+  if (ss) {
+    if ((e = hipEventRecord(ss->fork, a.stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   }
   if (p.swa && a.L > 0) {
     if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
@@ -1295,16 +1338,25 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
         e = hipFuncSetAttribute((const void *)bwd_swa_tile_kv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(bwd_swa_tile_q_kernel, dim3(BH * nch), dim3(kWT), lds, a.stream, p);
+      hipLaunchKernelGGL(bwd_swa_tile_q_kernel, dim3(BH * nch), dim3(kWT), lds, wstream, p);
       if (!launched()) return e;
-      hipLaunchKernelGGL(bwd_swa_tile_kv_kernel, dim3(BH * nch), dim3(kWT), lds, a.stream, p);
+      hipLaunchKernelGGL(bwd_swa_tile_kv_kernel, dim3(BH * nch), dim3(kWT), lds, wstream, p);
       if (!launched()) return e;
     } else {
-      hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+      hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
       if (!launched()) return e;
-      hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, a.stream, p);
+      hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
       if (!launched()) return e;
     }
+  }
+  if (p.gla && a.L > 0) {
+    if (a.f / 2 % 4 == 0) {
+      const unsigned ntl = (unsigned)((a.L + kPrepTile - 1) / kPrepTile);
+      hipLaunchKernelGGL(bwd_prep_tile_kernel<T>, dim3(BH * ntl), block, 0, a.stream, p);
+    } else {
+      hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(BH * p.npt), block, 0, a.stream, p);
+    }
+    if (!launched()) return e;
   }
   if (p.gla && BH > 0) {
     // with no tokens the sweeps still pass dS_final through to dS_0
@@ -1315,6 +1367,11 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
                          a.stream, p);
       if (!launched()) return e;
     }
+  }
+  if (ss) {  // the per-token kernel reads the window part's outputs
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a.stream, ss->join, 0)) != hipSuccess) return e;
+    lock.unlock();
   }
   if (a.L > 0 && BH > 0) {
     if (p.gla && p.swa)

@@ -182,6 +182,13 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  * f/2 a power of two; window <= 1024; n_meta <= 64 (otherwise GLAH_ENOTSUP).
  * All arithmetic is fp32 (token-recurrent form, no chunking); reductions over
  * tokens and batch rows run in a fixed order, so results are bitwise repeatable.
+ * Streams: with both parts (f > 0 and window > 0) the window part runs on a
+ * side stream of the library (one per device, with two events, created on the
+ * first such call and kept until the process ends), forked from `stream` at
+ * the call and joined back into it before the call's last kernels, so all of
+ * the call's work is ordered on `stream` as usual.  When `stream` is being
+ * captured into a graph before the side stream exists, the call uses `stream`
+ * alone.
  */
 size_t glah_bwd_workspace_bytes(const glah_desc *desc);
 glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k,
