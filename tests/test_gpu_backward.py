@@ -168,3 +168,40 @@ def test_backward_full_length_sampled_heads():
         sub = {n: (got[n][h:h + 1] if n in ("wq", "wk", "meta") else got[n][:, h:h + 1])
                for n in ("q", "k", "v", "gate", "wq", "wk", "meta")}
         compare(sub, ref, TOL_BF16)
+
+
+def test_backward_graph_replays_match_eager():
+    """The window part runs on the library's side stream (forked from and joined
+    back into the caller's stream): captured into a graph after an eager call
+    has created that stream, every replay, with eager work in between, must give
+    the eager call's gradients bit for bit."""
+    wl = WORKLOADS["prefill_2k"].with_(H=2, L=300)
+    say("backward graph capture and replays")
+    x = make_prefill(wl, DEV)
+    dO = grads_seed((wl.B, wl.H, wl.L, wl.dv), 8, wl.torch_dtype)
+    names = ("q", "k", "v", "gate", "wq", "wk", "meta")
+
+    def call():
+        return G.hybrid_layer_bwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], dO,
+                                  window=wl.window)
+
+    ref = call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    for r in range(3):
+        for n in names:
+            out[n].fill_(-7.0)
+        graph.replay()
+        other = call()  # eager work between replays
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(out[n], ref[n]), (r, n)
+            assert torch.equal(other[n], ref[n]), (r, n)
