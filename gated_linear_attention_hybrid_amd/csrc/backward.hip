@@ -523,27 +523,55 @@ __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
   const size_t BH = (size_t)p.B * p.H;
   if (idx >= BH * f) return;
   const size_t bh = idx / f, r = idx - bh * f;
-  auto total = [&](int i) {
-    float s = 0.0f;
-    for (int sl = 0; sl < p.nsl; ++sl) {
-      const size_t o = (((size_t)sl * BH + bh) * nft + i) * f + r;
-      s += p.tq[o] - p.tk[o];
+  // tile totals kTS at a time, every load of a group issued (clamped tiles and
+  // slices, masked) before the running sum uses them: one memory round trip
+  // per group instead of one per tile
+  constexpr int kTS = 8;
+  auto totals = [&](int i0, int dir, float (&tot)[kTS]) {
+    float a[kTS][kMaxSlices], b[kTS][kMaxSlices];
+#pragma unroll
+    for (int u = 0; u < kTS; ++u)
+#pragma unroll
+      for (int sl = 0; sl < kMaxSlices; ++sl) {
+        const int i = min(max(i0 + dir * u, 0), nft - 1);
+        const size_t o = (((size_t)min(sl, p.nsl - 1) * BH + bh) * nft + i) * f + r;
+        a[u][sl] = p.tq[o];
+        b[u][sl] = p.tk[o];
+      }
+#pragma unroll
+    for (int u = 0; u < kTS; ++u) {
+      float s = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxSlices; ++sl)
+        if (sl < p.nsl) s += a[u][sl] - b[u][sl];
+      tot[u] = s;
     }
-    return s;
   };
   const int half = (nft + 1) / 2;
   float acc = 0.0f;
   for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[((BH + bh) * p.nsl + sl) * f + r];
-  for (int i = 0; i < half; ++i) {
-    p.ta[(bh * nft + i) * f + r] = acc;
-    acc -= total(i);
+  for (int i0 = 0; i0 < half; i0 += kTS) {
+    float tot[kTS];
+    totals(i0, 1, tot);
+#pragma unroll
+    for (int u = 0; u < kTS; ++u)
+      if (i0 + u < half) {
+        p.ta[(bh * nft + i0 + u) * f + r] = acc;
+        acc -= tot[u];
+      }
   }
   acc = 0.0f;
   if (p.dstate_out)
     for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[(bh * p.nsl + sl) * f + r];
-  for (int i = nft - 1; i >= half; --i) {
-    acc += total(i);
-    p.ta[(bh * nft + i) * f + r] = acc;
+  for (int i0 = nft - 1; i0 >= half; i0 -= kTS) {
+    float tot[kTS];
+    totals(i0, -1, tot);
+#pragma unroll
+    for (int u = 0; u < kTS; ++u)
+      if (i0 - u >= half) {
+        acc += tot[u];
+        p.ta[(bh * nft + i0 - u) * f + r] = acc;
+      }
   }
 }
 
