@@ -1224,9 +1224,21 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
     const int m = idx >= nwt;
     const size_t e = idx - m * nwt, h = e / per, r = e - h * per;
     const float *src = m ? p.wkp : p.wqp;
+    // the partials of kRG tiles load (clamped, masked) before they are added, in
+    // the same order as one tile at a time
+    constexpr int kRG = 16;
     float acc = 0.0f;
-    for (int b = 0; b < p.B; ++b)
-      for (int tl = 0; tl < p.nft; ++tl) acc += src[(((size_t)b * p.H + h) * p.nft + tl) * per + r];
+    for (int b = 0; b < p.B; ++b) {
+      const float *row = src + ((size_t)b * p.H + h) * p.nft * per + r;
+      for (int t0 = 0; t0 < p.nft; t0 += kRG) {
+        float x[kRG];
+#pragma unroll
+        for (int u = 0; u < kRG; ++u) x[u] = row[(size_t)min(t0 + u, p.nft - 1) * per];
+#pragma unroll
+        for (int u = 0; u < kRG; ++u)
+          if (t0 + u < p.nft) acc += x[u];
+      }
+    }
     (m ? p.dwk : p.dwq)[e] = acc;
   } else if (idx < 2 * nwt + nm) {
     const size_t e = idx - 2 * nwt, h = e / p.n_meta, mm = e - h * p.n_meta;
