@@ -112,6 +112,19 @@ def test_backward_bf16_window_tiles(window, n_meta, x_std):
     compare(got, ref, TOL_BF16)
 
 
+@pytest.mark.parametrize("dtype,d,f,dv,L", [("f32", 12, 4, 8, 70), ("bf16", 64, 16, 36, 131)])
+def test_backward_small_and_ragged_sizes(dtype, d, f, dv, L):
+    """Sizes off the 128 path: f/2 = 2 (the per-token prologue and the one-feature-
+    at-a-time du . Wphi^T), f/2 = 8 with d_v = 36 (sweep columns past d_v, the
+    per-token window kernels at bf16), tiles of the per-token kernel ending on an
+    odd token count."""
+    wl = WORKLOADS["tiny_fp32"].with_(B=2, H=2, L=L, d=d, f=f, dv=dv, window=5, n_meta=2, dtype=dtype,
+                                      seed=1401)
+    say("backward %s d=%d f=%d dv=%d L=%d" % (dtype, d, f, dv, L))
+    got, ref = run_case(wl, with_state=True)
+    compare(got, ref, TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
 def test_backward_bf16_slow_decay():
     """Gate logits ~ N(6, 1): the state carries across hundreds of tokens."""
     wl = WORKLOADS["prefill_2k"].with_(H=2, L=400, gate_mean=6.0)
