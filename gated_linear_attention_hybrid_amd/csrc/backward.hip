@@ -13,9 +13,10 @@
 //   dphiq_t = S_t dO_t,  dphik_t = dS_t v_t,  dv_t += dS_t^T phik_t,
 //   d b_t   = phiq_t . dphiq_t - phik_t . dphik_t  (+ S_{L-1} . dS_final at t = L-1),
 //   d log Gamma_t = sum_{s>=t} d b_s,  dS_0 = Gamma_0 dS_0^(t=0).
-// Kernels: a prologue (phi and Gamma of every token), a forward state sweep
-// (dphiq, per-tile sums of phiq . dphiq), a reverse sweep (dphik, dv, per-tile
-// sums of phik . dphik, d log Gamma_0), a scan over 64-token tiles giving
+// Kernels: a prologue (phi and Gamma of every token), the forward state sweep
+// (dphiq, per-tile sums of phiq . dphiq) and the reverse sweep (dphik, dv,
+// per-tile sums of phik . dphik, d log Gamma_0) in one launch, a scan over
+// 64-token tiles giving
 // d log Gamma at each tile's first token, and a per-token kernel that finishes
 // d log Gamma inside the tile, takes phi's softmax Jacobian back to dq and dk,
 // accumulates the projection gradients and writes the gate gradient in its
@@ -24,7 +25,9 @@
 // Window part.  P_tj = e^{s_tj - lse_t}, with the sinks' e^{t_m} inside the
 // normaliser; D_t = dO_t . o_swa,t; ds_tj = P_tj (dO_t . v_j - D_t); a query
 // kernel gives dq, lse, D and the sink gradient -sum_t P_tm D_t; a key kernel
-// gives dk_j = scale sum_t ds_tj q_t and dv_j = sum_t P_tj dO_t.
+// gives dk_j = scale sum_t ds_tj q_t and dv_j = sum_t P_tj dO_t.  The two
+// window kernels run on a side stream beside the prologue and the sweeps; the
+// per-token kernel, which adds their dq, dk and dv, waits for them.
 //
 // Every reduction is done in a fixed order into per-block partials (no atomics),
 // so the gradients are bitwise repeatable.  All arithmetic is fp32.
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const T *g = (const T *)p.gate;
   T *dg = (T *)p.gg;
 
-  // every global operand of one token, loaded one token ahead
+  // every global operand of one token (loaded kFeatPF tokens ahead)
   struct Pre {
     float x, pp, pn, dp[kMaxSlices], dn[kMaxSlices], gr[2], ds, dvw[kMaxRowWaves], dvs;
   };
