@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
 template <class T, bool GLA, bool SWA>
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_feature_kernel(BwdParams p) {
   __shared__ float WT[2][kMaxF2 * kBwdMaxD];
-  __shared__ float X[2][kBwdMaxD];
+  __shared__ __align__(16) float X[2][kBwdMaxD];
   __shared__ __align__(16) float DU[2][kMaxF2];
   __shared__ float E[2][kBwdMaxF];
   constexpr int NP = kBwdMaxD * kMaxF2 / kBT;
@@ -610,7 +610,9 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const int jj = tid & (f2 - 1);
-  const int i0 = tid >> p.lf2, istep = kBT >> p.lf2;
+  // thread (i0, jj) accumulates dW rows i0 NP .. i0 NP + NP - 1 of feature jj:
+  // contiguous rows, so the X reads are 16-byte (broadcast) reads
+  const int i0 = tid >> p.lf2, ib = min(i0 * NP, kBwdMaxD - NP);
   float aq[NP], ak[NP];
 #pragma unroll
   for (int n = 0; n < NP; ++n) aq[n] = ak[n] = 0.0f;
@@ -781,14 +783,13 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *(T *)((char *)bgv + (ut * dv + tid) * (unsigned)sizeof(T)) = from_f32<T>(acc);
     }
     if (gla) {
-      // rows i >= d accumulate into sums that are never stored (clamped reads,
-      // no per-row branch)
+      // rows i >= d (and groups past the last row) accumulate into sums that
+      // are never stored (clamped reads, no per-row branch)
       const float duq = DU[0][jj], duk = DU[1][jj];
 #pragma unroll
       for (int n = 0; n < NP; ++n) {
-        const int i = min(i0 + n * istep, kBwdMaxD - 1);
-        aq[n] += X[0][i] * duq;
-        ak[n] += X[1][i] * duk;
+        aq[n] += X[0][ib + n] * duq;
+        ak[n] += X[1][ib + n] * duk;
       }
     }
   };
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t base = ((size_t)bh * p.nft + tile) * d * f2;
 #pragma unroll
   for (int n = 0; n < NP; ++n) {
-    const int i = i0 + n * istep;
+    const int i = i0 * NP + n;
     if (i < d) {
       p.wqp[base + (size_t)i * f2 + jj] = aq[n];
       p.wkp[base + (size_t)i * f2 + jj] = ak[n];
