@@ -584,11 +584,14 @@ __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
 // dq and dk (plus the window part), dv (both parts), d log Gamma_t (the tile's
 // start value minus the d b of the tile's earlier tokens) turned into the gate
 // gradient of its layout, and this block's share of dWphi_q = sum_t q_t^T
-// du_q,t and of dWphi_k.  The projections sit in LDS transposed ([f/2][d]) so
-// that the lanes of dq = du Wphi^T read consecutive words.
+// du_q,t and of dWphi_k.  The projections sit in LDS as padded [d][f/2] rows,
+// so a lane of dq = du Wphi^T reads its row 16 bytes at a time.
 template <class T, bool GLA, bool SWA>
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_feature_kernel(BwdParams p) {
-  __shared__ float WT[2][kMaxF2 * kBwdMaxD];
+  // W_phi rows [d][f/2], padded to kWR floats (16-byte reads of consecutive
+  // rows by consecutive lanes fall on different banks)
+  constexpr int kWR = kMaxF2 + 4;
+  __shared__ __align__(16) float WT[2][kBwdMaxD * kWR];
   __shared__ __align__(16) float X[2][kBwdMaxD];
   __shared__ __align__(16) float DU[2][kMaxF2];
   __shared__ float E[2][kBwdMaxF];
@@ -605,8 +608,8 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const T *wk = (const T *)p.wk + (size_t)h * d * f2;
     for (int i = tid; i < d * f2; i += kBT) {
       const int e = i >> p.lf2, j = i & (f2 - 1);
-      WT[0][j * d + e] = ld(wq + i);
-      WT[1][j * d + e] = ld(wk + i);
+      WT[0][e * kWR + j] = ld(wq + i);
+      WT[1][e * kWR + j] = ld(wk + i);
     }
   }
   const int jj = tid & (f2 - 1);
@@ -756,7 +759,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (gla) {
         // du . Wphi^T column mi: LDS reads requested 8 at a time into separate
         // sums (one dependent LDS round trip per feature otherwise)
-        const float *du = DU[m], *wt = &WT[m][mi];
+        const float *du = DU[m], *wt = &WT[m][mi * kWR];
         if (f2 % 8 == 0) {
           float a8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
           for (int j = 0; j < f2; j += 8) {
@@ -764,14 +767,14 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               x8[e] = du[j + e];
-              w8[e] = wt[(j + e) * d];
+              w8[e] = wt[j + e];
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) a8[e] += x8[e] * w8[e];
           }
           acc += ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
         } else {
-          for (int j = 0; j < f2; ++j) acc += du[j] * wt[j * d];
+          for (int j = 0; j < f2; ++j) acc += du[j] * wt[j];
         }
       }
       *(T *)((char *)bgx + (ut * d + mi) * (unsigned)sizeof(T)) = from_f32<T>(acc);
