@@ -1,8 +1,10 @@
 """Python binding of ``libglahybrid.so`` (C ABI in ``include/glahybrid.h``).
 
-Argument marshalling only: each function reads shapes from torch tensors, fills
-the ``glah_desc`` descriptor, passes raw device pointers and the current HIP
-stream, and raises :class:`GlahError` on a non-zero status.  Every step of the
+Argument marshalling only: each function checks its tensors (shapes, element
+types, dense row-major layout, one device: the C boundary sees only
+addresses and could not), reads the sizes into the ``glah_desc`` descriptor,
+passes raw device pointers and the current HIP stream, and raises
+:class:`GlahError` on a non-zero status.  Every step of the
 layer runs in the library's HIP kernels; torch only provides device memory
 (outputs and workspace are allocated with ``torch.empty`` when not given) and
 the stream.  Loading fails loudly when the library has not been built.
@@ -95,6 +97,119 @@ def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class _Checked:
+    """Checks of the tensor arguments of one call before their pointers cross
+    the C boundary, which sees only addresses: each tensor's shape, element
+    type and dense row-major layout as it is named (``need``), then, once all
+    of those hold, that every tensor is on the same GPU (``on_device``).
+    Raises TypeError / ValueError."""
+
+    def __init__(self):
+        self.seen = []
+
+    def need(self, name, t, shape, dtype, optional=False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError("%s is required" % name)
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if t.dtype != dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (dense row-major)" % name)
+        self.seen.append((name, t))
+        return t
+
+    def on_device(self, device):
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError("%s must be a GPU tensor, got device %s" % (name, t.device))
+            if t.device != device:
+                raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, device))
+
+
+def _gate_shape(kind, B, H, L, f):
+    """Shape of the gate tensor for gate layout ``kind`` (L = None: decode)."""
+    tok = (B, H) if L is None else (B, H, L)
+    if kind in (GLAH_GATE_LOGITS, GLAH_GATE_LOG):
+        return tok + (f,)
+    if kind == GLAH_GATE_LOG_TOKEN:
+        return tok
+    if kind == GLAH_GATE_LOG_HEAD:
+        return (H,)
+    raise ValueError("unknown gate kind %r" % (kind,))
+
+
+def _kind(gate_is_log, gate_kind):
+    return gate_kind if gate_kind is not None else (GLAH_GATE_LOG if gate_is_log else GLAH_GATE_LOGITS)
+
+
+def _layer_args(ck, q, k, v, wq, wk, meta, gate=None, kind=GLAH_GATE_LOGITS, with_gla=True):
+    """Check the inputs shared by the layer entry points (into ``ck``);
+    returns (B, H, L, d, dv, f, n_meta)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, L, d] tensor")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32, got %s" % q.dtype)
+    B, H, L, d = q.shape
+    dt = q.dtype
+    ck.need("q", q, (B, H, L, d), dt)
+    ck.need("k", k, (B, H, L, d), dt)
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a [B, H, L, d_v] tensor")
+    dv = v.shape[-1]
+    ck.need("v", v, (B, H, L, dv), dt)
+    f = 0
+    if with_gla:
+        if not isinstance(wq, torch.Tensor) or wq.dim() != 3:
+            raise ValueError("wq must be a [H, d, f/2] tensor")
+        f = 2 * wq.shape[-1]
+        ck.need("wq", wq, (H, d, f // 2), dt)
+        ck.need("wk", wk, (H, d, f // 2), dt)
+        ck.need("gate", gate, _gate_shape(kind, B, H, L, f), dt)
+    n_meta = _meta(ck, meta, H)
+    return B, H, L, d, dv, f, n_meta
+
+
+def _meta(ck, meta, H):
+    """Check the optional [H, n_meta] fp32 sink logits; returns n_meta."""
+    if meta is None:
+        return 0
+    if not isinstance(meta, torch.Tensor) or meta.dim() != 2:
+        raise ValueError("meta must be a [H, n_meta] tensor")
+    ck.need("meta", meta, (H, meta.shape[-1]), torch.float32)
+    return meta.shape[-1]
+
+
+def _rings(ck, q, B, H, window, d, dv, **named):
+    """Window ring tensors (optional) [B,H,window,d|dv] in q's dtype."""
+    for name, t in named.items():
+        width = d if name.startswith("k") else dv
+        ck.need(name, t, (B, H, max(int(window), 0), width), q.dtype, optional=True)
+
+
+def _states(ck, shape, **named):
+    """fp32 state tensors (optional) of the given shape."""
+    for name, t in named.items():
+        ck.need(name, t, shape, torch.float32, optional=True)
+
+
+def _out(ck, name, t, shape, like, dtype=None):
+    """An output tensor: checked like an input when given (allocated by the
+    caller of this after the device check when None)."""
+    dtype = like.dtype if dtype is None else dtype
+    if t is not None:
+        ck.need(name, t, shape, dtype)
+    return t
+
+
+def _alloc(t, shape, like, dtype=None):
+    return torch.empty(shape, dtype=like.dtype if dtype is None else dtype, device=like.device) if t is None else t
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -122,22 +237,26 @@ def workspace_bytes(desc: GlahDesc) -> int:
     return n
 
 
-def _workspace(desc, ws, device):
-    n = workspace_bytes(desc)
+def _workspace(desc, ws, device, need=None):
+    n = workspace_bytes(desc) if need is None else need
     if ws is None and n:
         ws = torch.empty(n, dtype=torch.uint8, device=device)
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or not ws.is_contiguous() or ws.device != device:
+            raise ValueError("ws must be a contiguous tensor on %s" % device)
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
 def gla_prefill(q, k, v, gate, wq, wk, *, chunk=0, gate_is_log=False, gate_kind=None, state_in=None,
                 state_out=None, o=None, ws=None, stream=None):
     """Gated linear attention prefill; returns o [B,H,L,dv]."""
-    B, H, L, d = q.shape
-    dv, f = v.shape[-1], 2 * wq.shape[-1]
-    desc = make_desc(B, H, L, d, dv, f, chunk=chunk, dtype=_dtype_code(q), gate_is_log=gate_is_log,
-                     gate_kind=gate_kind)
-    if o is None:
-        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, L, d, dv, f, _ = _layer_args(ck, q, k, v, wq, wk, None, gate, kind)
+    _states(ck, (B, H, f, dv), state_in=state_in, state_out=state_out)
+    _out(ck, "o", o, (B, H, L, dv), q)
+    ck.on_device(q.device)
+    desc = make_desc(B, H, L, d, dv, f, chunk=chunk, dtype=_dtype_code(q), gate_kind=kind)
+    o = _alloc(o, (B, H, L, dv), q)
     ws, nbytes = _workspace(desc, ws, q.device)
     st = load().gla_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
                             _p(state_in), _p(state_out), _p(o), _p(ws), nbytes, _stream(stream))
@@ -147,13 +266,13 @@ def gla_prefill(q, k, v, gate, wq, wk, *, chunk=0, gate_is_log=False, gate_kind=
 
 def swa_meta_attn(q, k, v, meta, *, window, scale=0.0, o=None, stream=None):
     """Sliding-window attention with meta-memory sinks; returns o [B,H,L,dv]."""
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
-    n_meta = 0 if meta is None else meta.shape[-1]
+    ck = _Checked()
+    B, H, L, d, dv, _, n_meta = _layer_args(ck, q, k, v, None, None, meta, with_gla=False)
+    _out(ck, "o", o, (B, H, L, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, 2, window=window, n_meta=n_meta, scale=scale,
                      dtype=_dtype_code(q))
-    if o is None:
-        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    o = _alloc(o, (B, H, L, dv), q)
     st = load().swa_meta_attn(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(meta), _p(o),
                               _stream(stream))
     _check("swa_meta_attn", st)
@@ -164,13 +283,15 @@ def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
                      gate_is_log=False, gate_kind=None, state_in=None, state_out=None, kcache_out=None,
                      vcache_out=None, o=None, ws=None, stream=None):
     """Whole hybrid layer (gated linear + window attention); returns o [B,H,L,dv]."""
-    B, H, L, d = q.shape
-    dv, f = v.shape[-1], 2 * wq.shape[-1]
-    n_meta = 0 if meta is None else meta.shape[-1]
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, L, d, dv, f, n_meta = _layer_args(ck, q, k, v, wq, wk, meta, gate, kind)
+    _states(ck, (B, H, f, dv), state_in=state_in, state_out=state_out)
+    _rings(ck, q, B, H, window, d, dv, kcache_out=kcache_out, vcache_out=vcache_out)
+    _out(ck, "o", o, (B, H, L, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
-    if o is None:
-        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+                     dtype=_dtype_code(q), gate_kind=kind)
+    o = _alloc(o, (B, H, L, dv), q)
     ws, nbytes = _workspace(desc, ws, q.device)
     st = load().hybrid_layer_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq),
                                  _p(wk), _p(meta), _p(state_in), _p(state_out), _p(kcache_out),
@@ -185,13 +306,16 @@ def hybrid_layer_fwd_cont(q, k, v, gate, wq, wk, meta, *, window, start, state_i
     """Hybrid layer over tokens start .. start+L-1 of sequences that already
     consumed ``start`` tokens (state and window ring of the previous call in,
     optionally the new ones out); returns o [B,H,L,dv]."""
-    B, H, L, d = q.shape
-    dv, f = v.shape[-1], 2 * wq.shape[-1]
-    n_meta = 0 if meta is None else meta.shape[-1]
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, L, d, dv, f, n_meta = _layer_args(ck, q, k, v, wq, wk, meta, gate, kind)
+    _states(ck, (B, H, f, dv), state_in=state_in, state_out=state_out)
+    _rings(ck, q, B, H, window, d, dv, kcache_in=kcache_in, vcache_in=vcache_in, kcache_out=kcache_out,
+           vcache_out=vcache_out)
+    _out(ck, "o", o, (B, H, L, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
-    if o is None:
-        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+                     dtype=_dtype_code(q), gate_kind=kind)
+    o = _alloc(o, (B, H, L, dv), q)
     ws, nbytes = _workspace(desc, ws, q.device)
     st = load().hybrid_layer_fwd_cont(ctypes.byref(desc), int(start), _p(q), _p(k), _p(v), _p(gate), _p(wq),
                                       _p(wk), _p(meta), _p(state_in), _p(kcache_in), _p(vcache_in),
@@ -203,24 +327,56 @@ def hybrid_layer_fwd_cont(q, k, v, gate, wq, wk, meta, *, window, start, state_i
 
 def output_gate(o, g, *, stream=None):
     """o <- o * sigmoid(g) in place (o, g [B,H,L,dv], the same dtype); returns o."""
+    if not isinstance(o, torch.Tensor) or o.dim() != 4:
+        raise ValueError("o must be a [B, H, L, d_v] tensor")
+    dtype = _dtype_code(o)
     B, H, L, dv = o.shape
-    desc = make_desc(B, H, L, 1, dv, 2, dtype=_dtype_code(o))
+    ck = _Checked()
+    ck.need("o", o, (B, H, L, dv), o.dtype)
+    ck.need("g", g, (B, H, L, dv), o.dtype)
+    ck.on_device(o.device)
+    desc = make_desc(B, H, L, 1, dv, 2, dtype=dtype)
     st = load().glah_output_gate(ctypes.byref(desc), _p(o), _p(g), _stream(stream))
     _check("glah_output_gate", st)
     return o
+
+
+def _token_args(ck, q, k, v):
+    """Check the one-token q, k [B,H,d] and v [B,H,dv]; returns (B, H, d, dv)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, H, d] tensor")
+    if not isinstance(v, torch.Tensor) or v.dim() != 3:
+        raise ValueError("v must be a [B, H, d_v] tensor")
+    _dtype_code(q)
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    ck.need("q", q, (B, H, d), q.dtype)
+    ck.need("k", k, (B, H, d), q.dtype)
+    ck.need("v", v, (B, H, dv), q.dtype)
+    return B, H, d, dv
 
 
 def gla_decode_step(q, k, v, gate, wq, wk, meta, state, kcache, vcache, pos, *, window,
                     scale=0.0, gate_is_log=False, gate_kind=None, o=None, stream=None):
     """One decode step (state and ring updated in place); returns o [B,H,dv].
     ``pos`` is a device int32 tensor [B] of tokens already consumed."""
-    B, H, d = q.shape
-    dv, f = v.shape[-1], 2 * wq.shape[-1]
-    n_meta = 0 if meta is None else meta.shape[-1]
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, d, dv = _token_args(ck, q, k, v)
+    if not isinstance(wq, torch.Tensor) or wq.dim() != 3:
+        raise ValueError("wq must be a [H, d, f/2] tensor")
+    f = 2 * wq.shape[-1]
+    ck.need("gate", gate, _gate_shape(kind, B, H, None, f), q.dtype)
+    ck.need("wq", wq, (H, d, f // 2), q.dtype)
+    ck.need("wk", wk, (H, d, f // 2), q.dtype)
+    n_meta = _meta(ck, meta, H)
+    ck.need("state", state, (B, H, f, dv), torch.float32)
+    _rings(ck, q, B, H, window, d, dv, kcache=kcache, vcache=vcache)
+    ck.need("pos", pos, (B,), torch.int32)
+    _out(ck, "o", o, (B, H, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, 1, d, dv, f, window=window, n_meta=n_meta, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
-    if o is None:
-        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+                     dtype=_dtype_code(q), gate_kind=kind)
+    o = _alloc(o, (B, H, dv), q)
     st = load().gla_decode_step(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
                                 _p(meta), _p(state), _p(kcache), _p(vcache), _p(pos), _p(o),
                                 _stream(stream))
@@ -244,11 +400,13 @@ def hybrid_layer_bwd(q, k, v, gate, wq, wk, meta, d_o, *, window, scale=0.0, gat
     gate (the gate's layout and dtype), wq, wk ([H,d,f/2] fp32), meta ([H,M]
     fp32, None without sinks) and state_in ([B,H,f,dv] fp32, when
     ``need_dstate_in``)."""
-    B, H, L, d = q.shape
-    dv, f = v.shape[-1], 2 * wq.shape[-1]
-    n_meta = 0 if meta is None else meta.shape[-1]
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, L, d, dv, f, n_meta = _layer_args(ck, q, k, v, wq, wk, meta, gate, kind)
+    ck.need("d_o", d_o, (B, H, L, dv), q.dtype)
+    _states(ck, (B, H, f, dv), state_in=state_in, dstate_out=dstate_out)
+    ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, scale=scale,
-                     dtype=_dtype_code(q), gate_is_log=gate_is_log, gate_kind=gate_kind)
+                     dtype=_dtype_code(q), gate_kind=kind)
     dev = q.device
     out = dict(q=torch.empty_like(q), k=torch.empty_like(k), v=torch.empty_like(v),
                gate=torch.empty_like(gate),
@@ -257,10 +415,7 @@ def hybrid_layer_bwd(q, k, v, gate, wq, wk, meta, d_o, *, window, scale=0.0, gat
                meta=None if meta is None else torch.empty(meta.shape, dtype=torch.float32, device=dev),
                state_in=(torch.empty((B, H, f, dv), dtype=torch.float32, device=dev)
                          if need_dstate_in else None))
-    n = bwd_workspace_bytes(desc)
-    if ws is None and n:
-        ws = torch.empty(n, dtype=torch.uint8, device=dev)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, nbytes = _workspace(desc, ws, dev, need=bwd_workspace_bytes(desc))
     st = load().hybrid_layer_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
                                  _p(meta), _p(state_in), _p(d_o), _p(dstate_out), _p(out["q"]),
                                  _p(out["k"]), _p(out["v"]), _p(out["gate"]), _p(out["wq"]),
@@ -274,11 +429,15 @@ def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=No
     """Gated delta rule over whole sequences; returns o [B,H,L,dv].  q, k
     [B,H,L,d], v [B,H,L,dv], log_alpha and beta [B,H,L] (the dtype of q); states
     [B,H,dv,d] fp32."""
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
+    ck = _Checked()
+    B, H, L, d, dv, _, _ = _layer_args(ck, q, k, v, None, None, None, with_gla=False)
+    ck.need("log_alpha", log_alpha, (B, H, L), q.dtype)
+    ck.need("beta", beta, (B, H, L), q.dtype)
+    _states(ck, (B, H, dv, d), state_in=state_in, state_out=state_out)
+    _out(ck, "o", o, (B, H, L, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, d, dtype=_dtype_code(q))
-    if o is None:
-        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    o = _alloc(o, (B, H, L, dv), q)
     st = load().gdn_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(log_alpha), _p(beta),
                             _p(state_in), _p(state_out), _p(o), _stream(stream))
     _check("gdn_prefill", st)
@@ -288,11 +447,15 @@ def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=No
 def gdn_decode_step(q, k, v, log_alpha, beta, state, *, o=None, stream=None):
     """One gated delta rule token (state [B,H,dv,d] fp32 updated in place);
     returns o [B,H,dv]."""
-    B, H, d = q.shape
-    dv = v.shape[-1]
+    ck = _Checked()
+    B, H, d, dv = _token_args(ck, q, k, v)
+    ck.need("log_alpha", log_alpha, (B, H), q.dtype)
+    ck.need("beta", beta, (B, H), q.dtype)
+    ck.need("state", state, (B, H, dv, d), torch.float32)
+    _out(ck, "o", o, (B, H, dv), q)
+    ck.on_device(q.device)
     desc = make_desc(B, H, 1, d, dv, d, dtype=_dtype_code(q))
-    if o is None:
-        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    o = _alloc(o, (B, H, dv), q)
     st = load().gdn_decode_step(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(log_alpha), _p(beta),
                                 _p(state), _p(o), _stream(stream))
     _check("gdn_decode_step", st)

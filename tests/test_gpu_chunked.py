@@ -44,6 +44,16 @@ def ref(x, wl, parts=oracle.PART_BOTH, gate_is_log=False, heads=None, **kw):
     return np.stack(outs)
 
 
+def ref_states(x, wl, heads):
+    """Oracle outputs and final states of the sampled (b, h) heads, run as one
+    batch row of len(heads) heads (OpenMP over heads)."""
+    tok = {k: np.stack([to_f64(x[k][b, h]) for b, h in heads])[None] for k in ("q", "k", "v", "gate")}
+    w = {k: np.stack([to_f64(x[k][h]) for _, h in heads]) for k in ("wq", "wk", "meta")}
+    o, s = oracle.layer_fwd(tok["q"], tok["k"], tok["v"], tok["gate"], w["wq"], w["wk"], w["meta"],
+                            window=wl.window, return_state=True)
+    return o[0], s[0]
+
+
 def base(H=4, **kw):
     return WORKLOADS["prefill_2k"].with_(H=H, **kw)
 
@@ -248,8 +258,13 @@ def test_prefill_32k_sampled_heads():
     assert_finite(o, "o")
     heads = [(0, 0), (0, 17), (0, 31)]
     got = gpu_f64(o)
-    exp = ref(x, wl, heads=heads)
+    exp, sexp = ref_states(x, wl, heads)
     assert row_rel_err(np.stack([got[b, h] for b, h in heads]), exp) <= TOL_BF16
+    # the final state (what a decode continuing this prefill starts from)
+    assert_finite(st, "state_out")
+    sg = gpu_f64(st)
+    assert row_rel_err(np.stack([sg[b, h] for b, h in heads]).reshape(-1, wl.dv),
+                       sexp.reshape(-1, wl.dv)) <= TOL_BF16
 
 
 def test_strong_decay_8k_sampled_heads():
@@ -258,12 +273,18 @@ def test_strong_decay_8k_sampled_heads():
     x = make_prefill(wl, DEV)
     # the workload names 128-token chunks; the MFMA path serves that request with
     # its 64-token blocking, so it must give exactly what a 64-token request gives
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
     o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
-                           window=wl.window, chunk=wl.chunk)
+                           window=wl.window, chunk=wl.chunk, state_out=st)
     o64 = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"],
                              window=wl.window, chunk=64)
     assert wl.chunk == 128 and torch.equal(o, o64)
     assert_finite(o, "o")
+    assert_finite(st, "state_out")
     heads = [(0, 0), (3, 9), (5, 20), (7, 31)]
     got = gpu_f64(o)
-    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), ref(x, wl, heads=heads)) <= TOL_BF16
+    exp, sexp = ref_states(x, wl, heads)
+    assert row_rel_err(np.stack([got[b, h] for b, h in heads]), exp) <= TOL_BF16
+    sg = gpu_f64(st)
+    assert row_rel_err(np.stack([sg[b, h] for b, h in heads]).reshape(-1, wl.dv),
+                       sexp.reshape(-1, wl.dv)) <= TOL_BF16
