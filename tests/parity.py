@@ -40,3 +40,11 @@ def oracle_inputs(x: dict):
 def assert_finite(t: torch.Tensor, what: str):
     bad = (~torch.isfinite(t.float())).sum().item()
     assert bad == 0, "%s has %d non-finite values" % (what, bad)
+
+
+def seeded_randn(shape, seed, device="cuda"):
+    """Standard normal draws from their own seeded CPU generator, on ``device``
+    (test inputs never come from the process-global RNG, whose state depends on
+    which tests ran before)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randn(shape, generator=gen).to(device)

@@ -12,7 +12,7 @@ import torch
 from oracle import delta as D
 from gated_linear_attention_hybrid_amd import binding as G
 from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_delta, make_delta_token, to_f64
-from parity import TOL_BF16, TOL_F32, assert_finite, gpu_f64, row_rel_err
+from parity import TOL_BF16, TOL_F32, assert_finite, gpu_f64, row_rel_err, seeded_randn
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -108,7 +108,7 @@ def test_extreme_decay_and_strength():
 def test_empty_sequence_passes_state_through():
     wl = WORKLOADS["tiny_fp32"].with_(L=0)
     x = make_delta(wl, DEV)
-    s_in = torch.randn((wl.B, wl.H, wl.dv, wl.d), device=DEV)
+    s_in = seeded_randn((wl.B, wl.H, wl.dv, wl.d), 42, DEV)
     s_out = torch.full_like(s_in, 7.0)
     run(x, state_in=s_in, state_out=s_out)
     torch.cuda.synchronize()
@@ -161,7 +161,8 @@ def test_decode_equals_prefill_token():
     """A decode step from state S gives what a one-token prefill from S gives."""
     wl = WORKLOADS["decode_b8"].with_(L=1, B=2, H=8)
     x = make_delta(wl, DEV)
-    s0 = torch.randn((wl.B, wl.H, wl.dv, wl.d), device=DEV) * 0.1
+    gen = torch.Generator(device="cpu").manual_seed(31)
+    s0 = (torch.randn((wl.B, wl.H, wl.dv, wl.d), generator=gen) * 0.1).to(DEV)
     s_pre = torch.empty_like(s0)
     o_pre = run(x, state_in=s0, state_out=s_pre)
     s_dec = s0.clone()
@@ -169,7 +170,10 @@ def test_decode_equals_prefill_token():
                               x["v"][:, :, 0].contiguous(), x["log_alpha"][:, :, 0].contiguous(),
                               x["beta"][:, :, 0].contiguous(), s_dec)
     torch.cuda.synchronize()
-    assert torch.allclose(o_pre[:, :, 0].float(), o_dec.float(), rtol=1e-5, atol=1e-6)
+    # the two kernels reduce the dot products in different orders, so their fp32
+    # results differ by a few fp32 ulps and the bf16 output may round one bf16
+    # ulp (at most 2^-7 relative) apart; the fp32 states agree to 1e-5
+    assert torch.allclose(o_pre[:, :, 0].float(), o_dec.float(), rtol=2.0 ** -7, atol=1e-6)
     assert torch.allclose(s_pre, s_dec, rtol=1e-5, atol=1e-6)
 
 
