@@ -28,7 +28,7 @@ GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
            "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step", "glah_bwd_workspace_bytes",
            "hybrid_layer_bwd", "gdn_prefill", "gdn_decode_step", "hybrid_layer_fwd_cont",
-           "glah_output_gate")
+           "glah_output_gate", "hybrid_layer_fwd_noalloc")
 
 
 class GlahError(RuntimeError):
@@ -70,6 +70,8 @@ def load(path: str = LIBRARY):
             lib.swa_meta_attn.restype = i32
             lib.hybrid_layer_fwd.argtypes = [dp] + [vp] * 12 + [vp, sz, vp]
             lib.hybrid_layer_fwd.restype = i32
+            lib.hybrid_layer_fwd_noalloc.argtypes = [dp] + [vp] * 12 + [vp]
+            lib.hybrid_layer_fwd_noalloc.restype = i32
             lib.gla_decode_step.argtypes = [dp] + [vp] * 12 + [vp]
             lib.gla_decode_step.restype = i32
             lib.glah_bwd_workspace_bytes.argtypes = [dp]
@@ -297,6 +299,28 @@ def hybrid_layer_fwd(q, k, v, gate, wq, wk, meta, *, window, chunk=0, scale=0.0,
                                  _p(wk), _p(meta), _p(state_in), _p(state_out), _p(kcache_out),
                                  _p(vcache_out), _p(o), _p(ws), nbytes, _stream(stream))
     _check("hybrid_layer_fwd", st)
+    return o
+
+
+def hybrid_layer_fwd_noalloc(q, k, v, gate, wq, wk, meta, o, *, window, chunk=0, scale=0.0,
+                             gate_is_log=False, gate_kind=None, state_in=None, state_out=None,
+                             kcache_out=None, vcache_out=None, stream=None):
+    """hybrid_layer_fwd without a workspace (the library's per-device scratch
+    array holds the segment states): the caller passes the output ``o``
+    [B,H,L,dv], so neither this function nor the library allocates.  Calls that
+    overlap on one device race on the scratch array; returns o."""
+    ck, kind = _Checked(), _kind(gate_is_log, gate_kind)
+    B, H, L, d, dv, f, n_meta = _layer_args(ck, q, k, v, wq, wk, meta, gate, kind)
+    _states(ck, (B, H, f, dv), state_in=state_in, state_out=state_out)
+    _rings(ck, q, B, H, window, d, dv, kcache_out=kcache_out, vcache_out=vcache_out)
+    ck.need("o", o, (B, H, L, dv), q.dtype)
+    ck.on_device(q.device)
+    desc = make_desc(B, H, L, d, dv, f, window=window, n_meta=n_meta, chunk=chunk, scale=scale,
+                     dtype=_dtype_code(q), gate_kind=kind)
+    st = load().hybrid_layer_fwd_noalloc(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(gate), _p(wq), _p(wk),
+                                         _p(meta), _p(state_in), _p(state_out), _p(kcache_out),
+                                         _p(vcache_out), _p(o), _stream(stream))
+    _check("hybrid_layer_fwd_noalloc", st)
     return o
 
 

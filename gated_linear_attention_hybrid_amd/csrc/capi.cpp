@@ -84,6 +84,44 @@ glah_status check_delta_desc(const glah_desc *d, bool decode, LayerArgs &a) {
   return delta_supported(a) ? GLAH_OK : GLAH_ENOTSUP;
 }
 
+// hybrid_layer_fwd with the workspace given: checks, then the chunked MFMA path
+// (or the token-recurrent one), then the ring copy.
+glah_status hybrid_fwd(const glah_desc *desc, const void *q, const void *k, const void *v, const void *gate,
+                       const void *wphi_q, const void *wphi_k, const float *meta, const float *state_in,
+                       float *state_out, void *kcache_out, void *vcache_out, void *o, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  LayerArgs a;
+  glah_status st = check_desc(desc, Op::kHybrid, a);
+  if (st != GLAH_OK) return st;
+  const bool work = (size_t)a.B * a.H * a.L > 0;
+  const bool heads = (size_t)a.B * a.H > 0;
+  if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work) || !req(o, work) ||
+      !req(wphi_q, heads) || !req(wphi_k, heads) || !req(meta, a.n_meta > 0 && a.H > 0) ||
+      !opt(state_in) || !opt(state_out) || !opt(ws) || !opt(kcache_out) || !opt(vcache_out))
+    return GLAH_EINVAL;
+  if ((kcache_out == nullptr) != (vcache_out == nullptr)) return GLAH_EINVAL;
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
+  a.state_in = state_in; a.state_out = state_out; a.o = o;
+  a.kcache = kcache_out; a.vcache = vcache_out;
+  a.ws = ws; a.ws_bytes = ws_bytes; a.stream = stream;
+  hipError_t e;
+  if (a.L == 0) {  // no tokens: the state passes through, the ring is all zeros
+    e = launch_state_passthrough(a);
+    if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
+    return finish(e);
+  }
+  if (chunked_supported(a, PART_BOTH)) {
+    if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
+      return GLAH_EWORKSPACE;
+    e = launch_chunked_prefill(a, PART_BOTH);
+  } else {
+    if (!recurrent_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
+    e = launch_recurrent_prefill(a, PART_BOTH);
+  }
+  if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
+  return finish(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,36 +203,24 @@ glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k
                              void *kcache_out, void *vcache_out, void *o, void *ws,
                              size_t ws_bytes, glah_stream_t stream) {
   try {
-    LayerArgs a;
-    glah_status st = check_desc(desc, Op::kHybrid, a);
-    if (st != GLAH_OK) return st;
-    const bool work = (size_t)a.B * a.H * a.L > 0;
-    const bool heads = (size_t)a.B * a.H > 0;
-    if (!req(q, work) || !req(k, work) || !req(v, work) || !req(gate, work) || !req(o, work) ||
-        !req(wphi_q, heads) || !req(wphi_k, heads) || !req(meta, a.n_meta > 0 && a.H > 0) ||
-        !opt(state_in) || !opt(state_out) || !opt(ws) || !opt(kcache_out) || !opt(vcache_out))
-      return GLAH_EINVAL;
-    if ((kcache_out == nullptr) != (vcache_out == nullptr)) return GLAH_EINVAL;
-    a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
-    a.state_in = state_in; a.state_out = state_out; a.o = o;
-    a.kcache = kcache_out; a.vcache = vcache_out;
-    a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;
-    hipError_t e;
-    if (a.L == 0) {  // no tokens: the state passes through, the ring is all zeros
-      e = launch_state_passthrough(a);
-      if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
-      return finish(e);
-    }
-    if (chunked_supported(a, PART_BOTH)) {
-      if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
-        return GLAH_EWORKSPACE;
-      e = launch_chunked_prefill(a, PART_BOTH);
-    } else {
-      if (!recurrent_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
-      e = launch_recurrent_prefill(a, PART_BOTH);
-    }
-    if (e == hipSuccess && kcache_out) e = launch_window_cache(a);
-    return finish(e);
+    return hybrid_fwd(desc, q, k, v, gate, wphi_q, wphi_k, meta, state_in, state_out, kcache_out, vcache_out, o,
+                      ws, ws_bytes, (hipStream_t)stream);
+  } catch (...) {
+    return GLAH_EHIP;
+  }
+}
+
+glah_status hybrid_layer_fwd_noalloc(const glah_desc *desc, const void *q, const void *k, const void *v,
+                                     const void *gate, const void *wphi_q, const void *wphi_k,
+                                     const float *meta, const float *state_in, float *state_out,
+                                     void *kcache_out, void *vcache_out, void *o, glah_stream_t stream) {
+  try {
+    void *scratch = nullptr;
+    if (noalloc_scratch(&scratch) != hipSuccess) return GLAH_EHIP;
+    // a call whose segment states would not fit the scratch array is rejected
+    // with GLAH_EWORKSPACE before anything is launched
+    return hybrid_fwd(desc, q, k, v, gate, wphi_q, wphi_k, meta, state_in, state_out, kcache_out, vcache_out, o,
+                      scratch, kNoAllocScratchBytes, (hipStream_t)stream);
   } catch (...) {
     return GLAH_EHIP;
   }

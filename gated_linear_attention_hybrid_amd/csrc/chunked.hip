@@ -24,8 +24,16 @@
 //
 // Operands are exchanged through LDS as ready-made MFMA fragments (1 KiB: 64
 // lanes x 16 B).
+#include <mutex>
+
 #include "chunk_common.hpp"
 #include "launch.hpp"
+
+// Device scratch of the no-allocation entry point: the segment states of the
+// state pass live here instead of in a caller workspace.  One copy per device,
+// held until the process ends; every call on a device shares it.  Host code
+// uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[glah::kNoAllocScratchBytes];
 
 namespace glah {
 
@@ -425,6 +433,25 @@ size_t chunked_workspace_bytes(const LayerArgs &a, int parts) {
   const SegPlan s = plan_segments(a);
   const size_t bh = (size_t)a.B * a.H;
   return bh * s.slices() * ((size_t)kF * kDV + kF) * sizeof(float);
+}
+
+hipError_t noalloc_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {

@@ -56,6 +56,13 @@ bool chunked_supported(const LayerArgs &a, int parts);
 size_t chunked_workspace_bytes(const LayerArgs &a, int parts);
 hipError_t launch_chunked_prefill(const LayerArgs &a, int parts);
 
+// Device scratch of hybrid_layer_fwd_noalloc (chunked.hip): a static device
+// array of kNoAllocScratchBytes per device; *ptr receives the current device's
+// copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void **ptr);
+
 // Banded MFMA window attention (bf16, d = d_v = 128).
 bool swa_mfma_supported(const LayerArgs &a);
 hipError_t launch_swa_mfma(const LayerArgs &a);

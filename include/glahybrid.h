@@ -142,6 +142,33 @@ glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k
                              void *ws, size_t ws_bytes, glah_stream_t stream);
 
 /*
+ * hybrid_layer_fwd_noalloc -- hybrid_layer_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as hybrid_layer_fwd
+ * without the workspace: the state pass keeps its segment states in a static
+ * device array of the library, GLAH_NOALLOC_SCRATCH_BYTES on every device the
+ * library runs on, held until the process ends.  The call allocates and frees
+ * nothing (the array's address is looked up once per device, on the first call
+ * with that device current).
+ *   - A call whose segment states need more than GLAH_NOALLOC_SCRATCH_BYTES
+ *     returns GLAH_EWORKSPACE before launching anything (the need is
+ *     glah_workspace_bytes(desc); on a 256-CU MI355X it is at most about 34 MB
+ *     for any size, since the plan cuts the sequences into at most two slices
+ *     per compute unit).
+ *   - Every call on one device shares the array and leaves it holding that
+ *     call's segment states; nothing in it has to start at zero.  Calls that
+ *     overlap on one device (concurrent streams, or host threads enqueueing on
+ *     different streams) race on it: order them on one stream or with events.
+ */
+#define GLAH_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+glah_status hybrid_layer_fwd_noalloc(const glah_desc *desc, const void *q, const void *k,
+                                     const void *v, const void *gate, const void *wphi_q,
+                                     const void *wphi_k, const float *meta,
+                                     const float *state_in, float *state_out,
+                                     void *kcache_out, void *vcache_out, void *o,
+                                     glah_stream_t stream);
+
+/*
  * gla_decode_step -- one token of constant-memory recurrent inference
  * (Methodology A.1: the state is updated token by token instead of keeping a KV
  * cache; A.2 for the window part).  For every (b, h):
