@@ -4,15 +4,16 @@
 // Constant-memory inference ("Lizard" technical summary, gist.science
 // 2507.09025, Methodology A.1): per (b, h) the step reads the f x d_v fp32 state
 // once and writes it once; everything else is small.  The step is bound by HBM
-// bandwidth, so the block issues its share of the state loads first (16-byte
-// vector loads, the whole 64 KiB state of a head in flight per block) and does
-// the Hedgehog GEMVs and the window scores while they are in flight:
+// bandwidth, so the block issues every load before any arithmetic (16-byte
+// vector loads, the whole 64 KiB state of a head in flight per block), the
+// state last, and does the Hedgehog GEMVs and the window scores while the
+// state streams in; each state row is written back as soon as it arrives:
 //   * Hedgehog GEMV: each thread loads 1 row x 8 columns of each projection
 //     with 16-byte loads, partial sums are reduced across lanes (DPP and row
 //     swaps) and waves (LDS).
-//   * window scores: 4 threads per key, 32 dimensions each, 16-byte loads.
-//   * window values: loaded up front with the state, 16 bytes per lane (two
-//     lanes share eight columns of two ring slots and swap halves by DPP).
+//   * window scores: 16 threads per ring slot, 8 dimensions each, 16-byte loads.
+//   * window values: loaded up front, 16 bytes per lane (two lanes share
+//     eight columns of two ring slots and swap halves by DPP).
 //   * the sinks and the new key for the ring append are loaded up front too,
 //     so no load sits in the softmax chain or in the kernel's tail.
 // Block = (b, h), 1024 threads: the projections, the window keys and the new
@@ -32,6 +33,7 @@ constexpr int kNRG = kNT / kC4;          // row groups
 constexpr int kRPT = kF / kNRG;          // state rows per thread
 constexpr int kNSL = kDV / kDVS;         // blocks per head
 static_assert(2 * kNRG == kMaxW, "two ring slots per row group (the value loads)");
+static_assert(kNRG == 2 * (kNT / 64), "two row groups per wave, in lanes l and l + 32");
 
 struct DecParams {
   const void *q, *k, *v, *gate, *wq, *wk;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   __shared__ float s_gam[kF];
   __shared__ float s_p[kMaxW + 1];   // window weights: ring slots, then the new token
   __shared__ float s_qk[2];          // q . k of the new token, per wave of waves 0-1
-  __shared__ f32x4 s_red[kNRG][kC4];
+  __shared__ f32x4 s_red[kNT / 64][kC4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int bh, slice;
@@ -150,30 +152,34 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
       V::ld8(Wk + (size_t)row * kF2 + 8 * cb, wkv[i]);
     }
   }
-  // (3) state slice: rows rg + kNRG * ii, four columns per thread (streamed:
-  // read and written once per step, non-temporal)
-  float *Sg = p.state + (size_t)bh * kF * kDV;
-  f32x4 S[kRPT];
-#pragma unroll
-  for (int ii = 0; ii < kRPT; ++ii)
-    S[ii] = __builtin_nontemporal_load((const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col));
-  // (4) window values, 16 bytes per lane: ring slot rg + kNRG (c4 & 1), columns
+  // (3) window values, 16 bytes per lane: ring slot rg + kNRG (c4 & 1), columns
   // 8 (c4 >> 1) .. +7, i.e. this thread's four columns and those of lane ^ 1;
   // after weighting, the two lanes swap the halves they do not own
   float vw[8];
   const int vslot = rg + kNRG * (c4 & 1);
   if (SWA) V::ld8(vc + (size_t)min(vslot, w - 1) * kDV + slice * kDVS + 8 * (c4 >> 1), vw);  // weight 0 past w
   const f32x4 v4 = V::ld4(vt + col);
-  // (5) gates
+  // (4) gates
   const float graw = to_f32(((const T *)p.gate)[gate_index(p.gate_mode, bh, p.H, 1, kF, 0, min(tid, kF - 1))]);
   const float qn = to_f32(qt[min(tid, kD - 1)]), kn = to_f32(kt[min(tid, kD - 1)]);  // used by waves 0-1 only
-  // (5b) operands of the ring append and of the sink softmax, so that no load
+  // (5) operands of the ring append and of the sink softmax, so that no load
   // sits in the dependent chain after the first barrier or in the kernel's tail
   const f32x4 kt4 = V::ld4(kt + 4 * min(tid, kD / 4 - 1));  // stored by threads tid < kD / 4
   // p.meta is a valid address even without sinks (the host passes another
   // buffer then); lanes past n_meta are masked
   const float tmraw = p.meta[(size_t)h * max(p.n_meta, 1) * (p.n_meta > 0) + min(lane, max(p.n_meta - 1, 0))];
   const float tmeta = lane < p.n_meta ? tmraw : -INFINITY;
+  // (6) state slice, LAST: rows rg + kNRG * ii, four columns per thread
+  // (streamed: read and written once per step, non-temporal).  Loads complete
+  // in order for the wait counter, so everything the two barriers wait for
+  // (projections, gates, window operands) was issued before; each state row
+  // is then updated and stored as soon as its own load lands, and the state
+  // writes overlap the state reads still in flight.
+  float *Sg = p.state + (size_t)bh * kF * kDV;
+  f32x4 S[kRPT];
+#pragma unroll
+  for (int ii = 0; ii < kRPT; ++ii)
+    S[ii] = __builtin_nontemporal_load((const f32x4 *)(Sg + (size_t)(rg + kNRG * ii) * kDV + col));
 
   // window scores (ring slots) and q . k of the new token (waves 0-1)
   if (SWA) {
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   if (tid < kF) s_gam[tid] = gate_from(graw, p.gate_is_log);
   __syncthreads();
 
-  // (6) wave 0 / 1: log-softmax of +u and -u for q / k; wave 2: window softmax
+  // (7) wave 0 / 1: log-softmax of +u and -u for q / k; wave 2: window softmax
   if (wave < 2) {
     float u = 0.0f;
 #pragma unroll
@@ -243,7 +249,16 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
   }
   __syncthreads();
 
-  // (7) state update, readout, window weights x values
+  // (8) ring append, before the state update so these stores are not the
+  // kernel's tail: slot pos % w holds token pos - w, outside this step's window
+  // (its score is masked and its weight is 0, so the loads of that slot at
+  // the start may see the old or the new token)
+  if (SWA) {
+    const int slot = pos % w;
+    if (slice == 0 && tid < kD / 4) V::st4(kc + (size_t)slot * kD + 4 * tid, kt4);
+    if (tid < kC4) V::st4(vc + (size_t)slot * kDV + col, v4);  // rg == 0: col = slice * kDVS + 4 tid
+  }
+  // (9) state update, readout, window weights x values
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int ii = 0; ii < kRPT; ++ii) {
@@ -266,19 +281,17 @@ __global__ __launch_bounds__(kNT) void decode128_kernel(DecParams p) {
     }
     if (rg == 0) acc += s_p[kMaxW] * v4;
   }
-  s_red[rg][c4] = acc;
+  // column sums over the row groups: lanes l and l + 32 hold row groups
+  // 2 wave and 2 wave + 1 of the same columns, then one partial per wave
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32);
+  if (lane < 32) s_red[wave][c4] = acc;
   __syncthreads();
   if (tid < kC4) {
     f32x4 s = s_red[0][tid];
 #pragma unroll
-    for (int r2 = 1; r2 < kNRG; ++r2) s += s_red[r2][tid];
+    for (int r2 = 1; r2 < kWaves; ++r2) s += s_red[r2][tid];
     V::st4((T *)p.o + (size_t)bh * kDV + slice * kDVS + 4 * tid, s);
-  }
-  // (8) ring append: slot pos % w holds token pos - w, which no block reads now
-  if (SWA) {
-    const int slot = pos % w;
-    if (slice == 0 && tid < kD / 4) V::st4(kc + (size_t)slot * kD + 4 * tid, kt4);
-    if (tid < kC4) V::st4(vc + (size_t)slot * kDV + col, v4);  // rg == 0: col = slice * kDVS + 4 tid
   }
 }
 
