@@ -442,6 +442,41 @@ def bench_serving(G, torch, reps=20):
     return {"output_gate": gate, "continuation": contd}
 
 
+def bench_wide_window(G, torch, windows=(256, 1024), reps=10):
+    """hybrid_layer_fwd at the 32K layer shape with windows wider than one chunk
+    (the gated part in the chunked kernels, then the window part with an online
+    softmax over 64-key chunks, added to o), median of ``reps`` calls."""
+    from gated_linear_attention_hybrid_amd.inputs import WORKLOADS, make_prefill
+    dev = torch.device("cuda")
+    wl = WORKLOADS["prefill_32k"]
+    x = make_prefill(wl, dev)
+    o = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=wl.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    out = []
+    for w in windows:
+        desc = G.make_desc(wl.B, wl.H, wl.L, wl.d, wl.dv, wl.f, window=w, n_meta=wl.n_meta, dtype=G.GLAH_BF16)
+        ws = torch.empty(max(1, G.workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+
+        def call():
+            G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], window=w, o=o,
+                               ws=ws, stream=stream)
+
+        for _ in range(3):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        out.append({"window": w, "us_per_call": round(ms * 1e3, 1), "tokens_per_s": round(wl.L / (ms * 1e-3), 1),
+                    "nonfinite_outputs": int((~torch.isfinite(o.float())).sum().item())})
+        del ws
+    del x, o
+    return {"workload": "prefill_32k layer with a window wider than one chunk, B=1 H=32 L=32768", "calls": out}
+
+
 def measured_ceilings(torch):
     """What this GPU reaches on plain library work: a 1 GiB device copy (HBM) and
     a large bf16 GEMM (hipBLASLt through torch), best of 3 each."""
@@ -591,6 +626,7 @@ def main():
         legs["gated_delta"] = bench_delta(G, torch)
     if not args.no_serving:
         legs["serving"] = bench_serving(G, torch)
+        legs["wide_window"] = bench_wide_window(G, torch)
 
     ms_step, calls, bad = bench_prefill(G, wl, args.steps, args.warmup, torch)
     per_call_ms = sum(calls) / len(calls)

@@ -114,6 +114,13 @@ glah_status hybrid_fwd(const glah_desc *desc, const void *q, const void *k, cons
     if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
       return GLAH_EWORKSPACE;
     e = launch_chunked_prefill(a, PART_BOTH);
+  } else if (chunked_supported(a, PART_GLA) && swa_wide_supported(a)) {
+    // windows wider than one chunk: the gated part in the chunked kernels, then
+    // the window part with an online softmax over key chunks, added to o
+    if (ws_bytes < chunked_workspace_bytes(a, PART_GLA) || (!ws && chunked_workspace_bytes(a, PART_GLA)))
+      return GLAH_EWORKSPACE;
+    e = launch_chunked_prefill(a, PART_GLA);
+    if (e == hipSuccess) e = launch_swa_wide(a, true);
   } else {
     if (!recurrent_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
     e = launch_recurrent_prefill(a, PART_BOTH);
@@ -190,6 +197,7 @@ glah_status swa_meta_attn(const glah_desc *desc, const void *q, const void *k, c
       return GLAH_EINVAL;
     a.q = q; a.k = k; a.v = v; a.meta = meta; a.o = o; a.stream = (hipStream_t)stream;
     if (swa_mfma_supported(a)) return finish(launch_swa_mfma(a));
+    if (swa_wide_supported(a)) return finish(launch_swa_wide(a, false));
     if (!recurrent_supported(a, PART_SWA)) return GLAH_ENOTSUP;
     return finish(launch_recurrent_prefill(a, PART_SWA));
   } catch (...) {

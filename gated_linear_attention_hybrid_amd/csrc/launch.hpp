@@ -67,6 +67,11 @@ hipError_t noalloc_scratch(void **ptr);
 bool swa_mfma_supported(const LayerArgs &a);
 hipError_t launch_swa_mfma(const LayerArgs &a);
 
+// Window attention for any window (bf16, d = d_v = 128): online softmax over
+// 64-key chunks on the matrix cores (swa_wide.hip); accumulate: o += o_swa.
+bool swa_wide_supported(const LayerArgs &a);
+hipError_t launch_swa_wide(const LayerArgs &a, bool accumulate);
+
 // Backward of the layer (token-recurrent VALU kernels, any dtype).
 constexpr int kBwdMaxD = 128;        // d_qk and d_v
 constexpr int kBwdMaxF = 128;        // f (f/2 a power of two)

@@ -119,6 +119,9 @@ glah_status gla_prefill(const glah_desc *desc, const void *q, const void *k,
  * swa_meta_attn -- sliding-window softmax attention with meta-memory sinks
  * (Methodology A.2), o = o_swa.  meta is [H][n_meta] fp32 and may be NULL only
  * when n_meta == 0.  Positions start at 0 (no keys before the sequence).
+ * bf16 at d_qk = d_v = 128 runs on the matrix cores for any window: one pass
+ * over the band for window <= 64, an online softmax over 64-key chunks
+ * (started from the sinks) beyond that.
  */
 glah_status swa_meta_attn(const glah_desc *desc, const void *q, const void *k,
                           const void *v, const float *meta, void *o,
@@ -133,6 +136,11 @@ glah_status swa_meta_attn(const glah_desc *desc, const void *q, const void *k,
  *   kcache_out/vcache_out  nullable; receive the ring of the last `window` keys and
  *                       values (slot p % window holds token p; slots of tokens
  *                       before 0 are zero-filled), ready for gla_decode_step
+ * bf16 at d_qk = f = d_v = 128: window <= 64 runs both parts in one fused pass;
+ * a wider window runs the gated part in the same chunked kernels and then the
+ * window part (online softmax over 64-key chunks), which adds its result to o
+ * (bf16 o is then rounded twice: at most one more bf16 ulp).  Other sizes and
+ * fp32 run the token-recurrent kernels (window <= 4096, n_meta <= 64).
  */
 glah_status hybrid_layer_fwd(const glah_desc *desc, const void *q, const void *k,
                              const void *v, const void *gate, const void *wphi_q,

@@ -288,3 +288,63 @@ def test_strong_decay_8k_sampled_heads():
     sg = gpu_f64(st)
     assert row_rel_err(np.stack([sg[b, h] for b, h in heads]).reshape(-1, wl.dv),
                        sexp.reshape(-1, wl.dv)) <= TOL_BF16
+
+
+def test_inter_chunk_readout_margin():
+    """The inter-chunk readout q-bar S takes the fp32 state rounded once to bf16
+    as its matrix-core operand (as q-bar itself is).  With gate = 1 nothing
+    decays, so every row past the first chunk carries the readout of a state
+    built from all earlier tokens.  Each bf16 operand rounding is at most 2^-9
+    relative per term, as is the rounding of the output itself; the typical
+    row (the median past the first chunk) must stay below two such roundings,
+    2^-8, and the worst row within the bf16 tolerance."""
+    wl = WORKLOADS["prefill_2k"]
+    say("gate = 1, 2K x 32 heads, gated part: readout precision margin")
+    x = make_prefill(wl, DEV, gate_log_zero=True)
+    o = G.gla_prefill(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], gate_is_log=True)
+    got = gpu_f64(o)
+    exp = ref(x, wl, parts=oracle.PART_GLA, gate_is_log=True)
+    assert row_rel_err(got, exp) <= TOL_BF16
+    g2, r2 = got[:, :, 64:].reshape(-1, wl.dv), exp[:, :, 64:].reshape(-1, wl.dv)
+    rows = np.max(np.abs(g2 - r2), axis=-1) / np.max(np.abs(r2), axis=-1)
+    assert float(np.median(rows)) <= 2.0 ** -8, float(np.median(rows))
+
+
+@pytest.mark.parametrize("window", [65, 100, 200, 700, 5000])
+def test_wide_windows(window):
+    """Windows wider than one 64-token chunk: the window part runs with an online
+    softmax over key chunks (swa_meta_attn alone, and after the chunked gated
+    part in the hybrid layer, which adds it to o); 5000 >= L is the full causal
+    softmax with sinks.  Ragged length, peaked scores, two batch rows."""
+    wl = base(B=2, H=2, L=1000, window=window, x_std=0.5)
+    say("wide window %d" % window)
+    x = make_prefill(wl, DEV)
+    o = G.swa_meta_attn(x["q"], x["k"], x["v"], x["meta"], window=window)
+    assert_finite(o, "o_swa")
+    assert row_rel_err(gpu_f64(o), ref(x, wl, parts=oracle.PART_SWA)) <= TOL_BF16
+    st = torch.empty((wl.B, wl.H, wl.f, wl.dv), device=DEV)
+    kc = torch.full((wl.B, wl.H, window, wl.d), 3.0, device=DEV, dtype=torch.bfloat16)
+    vc = torch.full((wl.B, wl.H, window, wl.dv), 3.0, device=DEV, dtype=torch.bfloat16)
+    o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], window=window,
+                           state_out=st, kcache_out=kc, vcache_out=vc)
+    assert_finite(o, "o")
+    exp, sexp = ref(x, wl, return_state=True)
+    assert row_rel_err(gpu_f64(o), exp) <= TOL_BF16
+    assert row_rel_err(gpu_f64(st).reshape(-1, wl.dv), sexp.reshape(-1, wl.dv)) <= TOL_BF16
+    torch.cuda.synchronize()
+    for p in range(max(0, wl.L - window), wl.L):  # ring slot p % window holds token p
+        assert torch.equal(kc[:, :, p % window], x["k"][:, :, p])
+        assert torch.equal(vc[:, :, p % window], x["v"][:, :, p])
+    if window > wl.L:  # slots of tokens before 0 are zero-filled
+        assert not kc[:, :, wl.L:].any() and not vc[:, :, wl.L:].any()
+
+
+def test_wide_window_no_sinks_and_short():
+    """No sinks, and sequences shorter than the window (the first chunk alone)."""
+    for L, window in ((300, 129), (40, 100)):
+        wl = base(H=3, L=L, window=window, n_meta=0, x_std=0.7)
+        say("wide window %d, L %d, no sinks" % (window, L))
+        x = make_prefill(wl, DEV)
+        o = G.hybrid_layer_fwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], None, window=window)
+        x["meta"] = torch.zeros((wl.H, 0), device=DEV)
+        assert row_rel_err(gpu_f64(o), ref(x, wl)) <= TOL_BF16
