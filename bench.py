@@ -315,10 +315,12 @@ def bench_delta(G, torch, reps=5, warmup=2, steps=256, sets=12):
     x = make_delta(wl, dev)
     st = torch.empty((wl.B, wl.H, wl.dv, wl.d), device=dev)
     o = torch.empty((wl.B, wl.H, wl.L, wl.dv), dtype=wl.torch_dtype, device=dev)
+    desc = G.make_desc(wl.B, wl.H, wl.L, wl.d, wl.dv, wl.d, dtype=G.GLAH_BF16)
+    ws = torch.empty(max(1, G.gdn_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def call():
-        G.gdn_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state_out=st, o=o, stream=stream)
+        G.gdn_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], state_out=st, o=o, ws=ws, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -336,8 +338,9 @@ def bench_delta(G, torch, reps=5, warmup=2, steps=256, sets=12):
            "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "algorithmic_bytes_per_launch": nbytes},
+           "workspace_bytes": ws.numel(),
            "nonfinite_outputs": int((~torch.isfinite(o.float())).sum().item())}
-    del x, o
+    del x, o, ws
     wd = WORKLOADS["decode_b8"]
     B, H = wd.B, wd.H
     x = make_delta(wd.with_(L=64), dev)

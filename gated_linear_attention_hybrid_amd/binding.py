@@ -28,7 +28,7 @@ GLAH_GATE_LOG_TOKEN, GLAH_GATE_LOG_HEAD = 2, 3  # scalar log-gates: [B,H,L] per 
 EXPORTS = ("glah_status_str", "glah_version", "glah_workspace_bytes", "gla_prefill",
            "swa_meta_attn", "hybrid_layer_fwd", "gla_decode_step", "glah_bwd_workspace_bytes",
            "hybrid_layer_bwd", "gdn_prefill", "gdn_decode_step", "hybrid_layer_fwd_cont",
-           "glah_output_gate", "hybrid_layer_fwd_noalloc")
+           "glah_output_gate", "hybrid_layer_fwd_noalloc", "gdn_workspace_bytes")
 
 
 class GlahError(RuntimeError):
@@ -82,7 +82,9 @@ def load(path: str = LIBRARY):
             lib.hybrid_layer_fwd_cont.restype = i32
             lib.glah_output_gate.argtypes = [dp, vp, vp, vp]
             lib.glah_output_gate.restype = i32
-            lib.gdn_prefill.argtypes = [dp] + [vp] * 8 + [vp]
+            lib.gdn_prefill.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+            lib.gdn_workspace_bytes.argtypes = [dp]
+            lib.gdn_workspace_bytes.restype = sz
             lib.gdn_prefill.restype = i32
             lib.gdn_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
             lib.gdn_decode_step.restype = i32
@@ -449,10 +451,18 @@ def hybrid_layer_bwd(q, k, v, gate, wq, wk, meta, d_o, *, window, scale=0.0, gat
     return out
 
 
-def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=None, stream=None):
+def gdn_workspace_bytes(desc: GlahDesc) -> int:
+    n = load().gdn_workspace_bytes(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlahError("gdn_workspace_bytes", GLAH_EINVAL, "invalid argument")
+    return n
+
+
+def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=None, ws=None, stream=None):
     """Gated delta rule over whole sequences; returns o [B,H,L,dv].  q, k
     [B,H,L,d], v [B,H,L,dv], log_alpha and beta [B,H,L] (the dtype of q); states
-    [B,H,dv,d] fp32."""
+    [B,H,dv,d] fp32; ws a uint8 device buffer of at least gdn_workspace_bytes
+    (allocated here when None)."""
     ck = _Checked()
     B, H, L, d, dv, _, _ = _layer_args(ck, q, k, v, None, None, None, with_gla=False)
     ck.need("log_alpha", log_alpha, (B, H, L), q.dtype)
@@ -461,9 +471,10 @@ def gdn_prefill(q, k, v, log_alpha, beta, *, state_in=None, state_out=None, o=No
     _out(ck, "o", o, (B, H, L, dv), q)
     ck.on_device(q.device)
     desc = make_desc(B, H, L, d, dv, d, dtype=_dtype_code(q))
+    ws, nbytes = _workspace(desc, ws, q.device, need=gdn_workspace_bytes(desc))
     o = _alloc(o, (B, H, L, dv), q)
     st = load().gdn_prefill(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(log_alpha), _p(beta),
-                            _p(state_in), _p(state_out), _p(o), _stream(stream))
+                            _p(state_in), _p(state_out), _p(o), _p(ws), nbytes, _stream(stream))
     _check("gdn_prefill", st)
     return o
 

@@ -19,13 +19,18 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libglahybrid.so")
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "recurrent.hip", "chunked.hip", "chunk_out.hip", "decode.hip", "backward.hip", "delta.hip", "serving.hip", "swa_wide.hip"]
+SOURCES = ["capi.cpp", "recurrent.hip", "chunked.hip", "chunk_out.hip", "decode.hip", "backward.hip", "delta.hip", "serving.hip", "swa_wide.hip", "delta_chunk.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU
 # instructions (ordinary float code is used everywhere instead).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
+
+# Per-source extras.  delta_chunk.hip: matrix-core results in ordinary VGPRs
+# (its recurrence feeds most of them to vector instructions, and results in
+# the accumulator registers would need a copy each).
+EXTRA = {"delta_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -37,7 +42,7 @@ def _hipcc():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

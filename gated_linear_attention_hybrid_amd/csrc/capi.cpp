@@ -363,9 +363,17 @@ glah_status glah_output_gate(const glah_desc *desc, void *o, const void *g, glah
   }
 }
 
+size_t gdn_workspace_bytes(const glah_desc *desc) {
+  LayerArgs a;
+  const glah_status st = check_delta_desc(desc, false, a);
+  if (st == GLAH_ENOTSUP) return 0;
+  if (st != GLAH_OK) return (size_t)-1;
+  return delta_chunk_ws_bytes(a);
+}
+
 glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k, const void *v,
                         const void *log_alpha, const void *beta, const float *state_in,
-                        float *state_out, void *o, glah_stream_t stream) {
+                        float *state_out, void *o, void *ws, size_t ws_bytes, glah_stream_t stream) {
   try {
     LayerArgs a;
     glah_status st = check_delta_desc(desc, false, a);
@@ -377,6 +385,10 @@ glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k, con
     a.q = q; a.k = k; a.v = v; a.gate = log_alpha; a.beta = beta;
     a.state_in = state_in; a.state_out = state_out; a.o = o; a.stream = (hipStream_t)stream;
     if (a.L == 0) return finish(launch_state_passthrough(a));  // f = d_qk: d_v x d_qk floats
+    const size_t need = delta_chunk_ws_bytes(a);
+    if (need && (!ws || ws_bytes < need)) return GLAH_EWORKSPACE;
+    if (!opt(ws)) return GLAH_EINVAL;
+    a.ws = ws; a.ws_bytes = ws_bytes;
     return finish(launch_delta(a, false));
   } catch (...) {
     return GLAH_EHIP;

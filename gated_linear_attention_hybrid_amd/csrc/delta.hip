@@ -413,6 +413,7 @@ bool delta_supported(const LayerArgs &a) {
 
 hipError_t launch_delta(const LayerArgs &a, bool decode) {
   if ((size_t)a.B * a.H == 0 || (!decode && a.L == 0)) return hipSuccess;
+  if (!decode && delta_chunk_supported(a)) return launch_delta_chunk(a);
   return a.bf16 ? dispatch<bf16>(a, decode) : dispatch<float>(a, decode);
 }
 

@@ -92,6 +92,13 @@ hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 // state [B][H][dv][d] fp32.
 bool delta_supported(const LayerArgs &a);
 hipError_t launch_delta(const LayerArgs &a, bool decode);
+// Chunkwise prefill on the matrix cores (delta_chunk.hip): bf16, d = 128,
+// d_v a multiple of 16, at least one 64-token chunk.  Its per-chunk records
+// (T, P, per-token scalars) go to the workspace a.ws of delta_chunk_ws_bytes(a)
+// bytes (0 where the chunkwise path does not apply).
+bool delta_chunk_supported(const LayerArgs &a);
+size_t delta_chunk_ws_bytes(const LayerArgs &a);
+hipError_t launch_delta_chunk(const LayerArgs &a);
 
 // Continuation prefill (serving.hip): window part of the first w - 1 queries
 // reaching into the input ring, and the ring after the call (global positions).

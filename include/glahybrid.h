@@ -294,15 +294,25 @@ glah_status glah_output_gate(const glah_desc *desc, void *o, const void *g,
  *   state_in    nullable; [B][H][d_v][d_qk] fp32 state before token 0 (0 if NULL)
  *   state_out   nullable; [B][H][d_v][d_qk] fp32, receives M_{L-1} (L = 0: the
  *               state before the sequence); may equal state_in
+ *   ws          device workspace of ws_bytes >= gdn_workspace_bytes(desc)
+ *               (may be NULL when that is 0), owned by the caller; the call
+ *               overwrites it
  * Reads B, H, L, d_qk, d_v and dtype of the descriptor; the other fields are
  * ignored.  Supported: d_qk in {32, 64, 128}, any d_v >= 1 (else
- * GLAH_ENOTSUP).  fp32 arithmetic, token-recurrent (each value row of the
- * state is an independent recurrence), bitwise repeatable; no workspace.
+ * GLAH_ENOTSUP); GLAH_EWORKSPACE when ws is missing or too small.  bf16 with
+ * d_qk = 128, d_v a multiple of 16 and L >= 64 runs the chunkwise form on the
+ * matrix cores (bf16 operands, fp32 accumulation and state); every other case
+ * the token-recurrent fp32 form.  Both are bitwise repeatable.
  */
 glah_status gdn_prefill(const glah_desc *desc, const void *q, const void *k,
                         const void *v, const void *log_alpha, const void *beta,
                         const float *state_in, float *state_out, void *o,
-                        glah_stream_t stream);
+                        void *ws, size_t ws_bytes, glah_stream_t stream);
+
+/* Bytes of device workspace gdn_prefill needs for `desc`: per 64-token chunk
+ * of every (b, h), 13568 bytes on the chunkwise path; 0 on the
+ * token-recurrent one.  Returns (size_t)-1 when `desc` is invalid. */
+size_t gdn_workspace_bytes(const glah_desc *desc);
 
 /*
  * gdn_decode_step -- one token of the gated delta rule for every (b, h): the

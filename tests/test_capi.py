@@ -191,7 +191,7 @@ def _gdn_desc(**kw):
 
 def _gdn_prefill(lib, desc, ptrs=None):
     p = [FAKE] * 9 if ptrs is None else ptrs  # q k v a beta state_in state_out o
-    return lib.gdn_prefill(ctypes.byref(desc), *[ctypes.c_void_p(x) for x in p[:8]], None)
+    return lib.gdn_prefill(ctypes.byref(desc), *[ctypes.c_void_p(x) for x in p[:8]], None, 0, None)
 
 
 @pytest.mark.parametrize("bad", [dict(d=0), dict(dv=0), dict(B=-1), dict(H=-1), dict(L=-1), dict(dtype=9)])
@@ -218,7 +218,7 @@ def test_gdn_misaligned_and_null_checks(lib):
     p = [FAKE] * 8
     p[7] = 0  # o
     assert _gdn_prefill(lib, _gdn_desc(), p) == binding.GLAH_EINVAL
-    assert lib.gdn_prefill(None, *[ctypes.c_void_p(FAKE)] * 8, None) == binding.GLAH_EINVAL
+    assert lib.gdn_prefill(None, *[ctypes.c_void_p(FAKE)] * 8, None, 0, None) == binding.GLAH_EINVAL
     d = _gdn_desc()
     args = [ctypes.c_void_p(FAKE)] * 7
     args[5] = ctypes.c_void_p(0)  # state
@@ -253,3 +253,28 @@ def test_output_gate_argument_checks(lib):
     bad = _desc(dtype=5)
     assert lib.glah_output_gate(ctypes.byref(bad), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
                                 None) == binding.GLAH_EINVAL
+
+
+def test_gdn_workspace_bytes(lib):
+    # chunkwise path (bf16, d_qk = 128, d_v a multiple of 16, L >= 64): one
+    # 13568-byte record per 64-token chunk of every (b, h); none otherwise
+    def ws(**kw):
+        return lib.gdn_workspace_bytes(ctypes.byref(_gdn_desc(**kw)))
+    assert ws(B=2, H=3, L=130, d=128, dv=48, dtype=binding.GLAH_BF16) == 2 * 3 * 3 * 13568
+    assert ws(L=64, d=128, dv=128, dtype=binding.GLAH_BF16) == 2 * 13568
+    assert ws(L=63, d=128, dv=128, dtype=binding.GLAH_BF16) == 0
+    assert ws(L=640, d=128, dv=40, dtype=binding.GLAH_BF16) == 0
+    assert ws(L=640, d=64, dv=64, dtype=binding.GLAH_BF16) == 0
+    assert ws(L=640, d=128, dv=128) == 0  # fp32: token-recurrent
+    assert ws(d=256) == 0  # unsupported
+    assert ws(B=-1) == ctypes.c_size_t(-1).value
+    assert lib.gdn_workspace_bytes(None) == ctypes.c_size_t(-1).value
+
+
+def test_gdn_missing_workspace_is_eworkspace(lib):
+    d = _gdn_desc(L=128, d=128, dv=128, dtype=binding.GLAH_BF16)
+    need = lib.gdn_workspace_bytes(ctypes.byref(d))
+    ptrs = [ctypes.c_void_p(FAKE)] * 8
+    assert lib.gdn_prefill(ctypes.byref(d), *ptrs, None, 0, None) == binding.GLAH_EWORKSPACE
+    assert lib.gdn_prefill(ctypes.byref(d), *ptrs, ctypes.c_void_p(FAKE), need - 1, None) == binding.GLAH_EWORKSPACE
+    assert lib.gdn_prefill(ctypes.byref(d), *ptrs, ctypes.c_void_p(FAKE + 8), need, None) == binding.GLAH_EINVAL
