@@ -21,10 +21,14 @@
 //                     once: the cumulative log-decays, the norms, L and P_ts =
 //                     (gamma_t/gamma_s) q^_t . k^_s (s <= t) from the raw score
 //                     products, and T = (I + L)^-1 -- each diagonal 16 x 16
-//                     block by Neumann doubling, (I + N)^-1 = (I + N)(I + N^2)
-//                     (I + N^4)(I + N^8) for the strictly lower N = -L_ii
-//                     (N^16 = 0), the blocks below it by block substitution
-//                     down each block column, T_ij = -X_i sum_{j<=k<i} L_ik T_kj.
+//                     block X_i by forward substitution in fp32 (a lane per
+//                     column), the blocks below it by block substitution down
+//                     each block column, T_ij = -X_i sum_{j<=k<i} L_ik T_kj, on
+//                     the matrix cores.  (A power series for X_i, such as
+//                     Neumann doubling, is exact in exact arithmetic but not
+//                     with bf16 operands: for a key repeated over a block with
+//                     full write strength the powers of L_ii grow like binomial
+//                     coefficients, into the thousands, and must cancel.)
 //                     T and P go to the workspace as matrix-core operands, with
 //                     the per-token scalars gamma/|k|, beta, gamma_C/(gamma |k|),
 //                     gamma/|q| and gamma_C.
@@ -108,26 +112,6 @@ __device__ __forceinline__ s16x4 half_of(bf16x8 x, int u) {
   return u == 0 ? __builtin_shufflevector(s, s, 0, 1, 2, 3) : __builtin_shufflevector(s, s, 4, 5, 6, 7);
 }
 
-// A matrix and its transpose, both in accumulator form.
-struct Pair {
-  f32x4 m, t;
-};
-// (X Y, (X Y)^T) from the pairs of X and Y: X in A form is X^T's accumulator
-// form, Y in B form is Y's; (X Y)^T = Y^T X^T likewise
-__device__ __forceinline__ Pair mul(const Pair &x, const Pair &y) {
-  return {mma16(pk(x.t), pk(y.m), z4()), mma16(pk(y.m), pk(x.t), z4())};
-}
-__device__ __forceinline__ Pair plus_identity(Pair x) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (4 * g + r == n) {
-      x.m[r] += 1.0f;
-      x.t[r] += 1.0f;
-    }
-  return x;
-}
-
 __device__ __forceinline__ void st4(char *base, s16x4 x) { *(s16x4 *)(base + (threadIdx.x & 63) * 8) = x; }
 __device__ __forceinline__ s16x4 ld4(const char *base) { return *(const s16x4 *)(base + (threadIdx.x & 63) * 8); }
 __device__ __forceinline__ void stacc(char *base, f32x4 x) { *(f32x4 *)(base + (threadIdx.x & 63) * 16) = x; }
@@ -172,7 +156,9 @@ struct LdsPrep {
   static constexpr int XA = NL + 16 * kOp16;     // X_i = (I + L_ii)^-1 in A form [4]
   static constexpr int XB = XA + 4 * kOp16;      // X_i in B form [4]
   static constexpr int SC = XB + 4 * kOp16;      // g, beta, 1/|k|, 1/|q| [4][64] fp32
-  static constexpr int BYTES = SC + 4 * 64 * 4;
+  static constexpr int NF = SC + 4 * 64 * 4;     // -L_ii, fp32 row-major [4][16][16]
+  static constexpr int XF = NF + 4 * 256 * 4;    // X_i, fp32 row-major [4][16][16]
+  static constexpr int BYTES = XF + 4 * 256 * 4;
 };
 
 // the score pairs (i, j <= i) of a chunk's 16-token blocks, spread over the
@@ -234,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepParams p) {
   }
   __syncthreads();
 
-  // ---- score pairs: L and P with decay ratios and norms; the diagonal inverses
+  // ---- score pairs: L and P with decay ratios and norms
   const int np = pair_count(blk);
   for (int u = 0; u < 3; ++u) {
     if (u >= np) break;
@@ -270,37 +256,47 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(PrepParams p) {
     if (j < i) {
       st4(smem + LD::NL + (i * 4 + j) * kOp16, pk(NLv));
     } else {
-      // X = (I + L_ii)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -L_ii.
-      // NLv is N^T in accumulator form; N itself from the same (symmetric) raw
-      // product with the roles swapped.
-      Pair N;
-      N.t = NLv;
-      const f32x4 g_r = *(const f32x4 *)(sc + 16 * i + 4 * g);  // rows tau' = 16 i + 4 g + r
-      const f32x4 b_r = *(const f32x4 *)(sc + 64 + 16 * i + 4 * g);
-      const f32x4 nk_r = *(const f32x4 *)(sc + 128 + 16 * i + 4 * g);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 4 * g + r;  // tau' > sigma' = n
-        const float ratio = exp2_fast((g_r[r] - g_t) * kLog2e);
-        N.m[r] = n < rr ? -b_r[r] * ratio * nk_r[r] * nk_t * S[r] : 0.0f;
-      }
-      const Pair N2 = mul(N, N);
-      const Pair N4 = mul(N2, N2);
-      const Pair N8 = mul(N4, N4);
-      const Pair X2 = mul(plus_identity(N), plus_identity(N2));
-      const Pair X4 = mul(X2, plus_identity(N4));
-      const Pair X = mul(X4, plus_identity(N8));
-      const s16x4 xa = pk(X.t);  // X in A form
-      st4(smem + LD::XA + i * kOp16, xa);
-      st4(smem + LD::XB + i * kOp16, pk(X.m));
-      char *const top = rec + Rec::T + opidx(i, i >> 1) * kFrag + lane * 16;
-      *(s16x4 *)(top + (i & 1) * 8) = xa;
-      if ((i & 1) == 0) {
-        const s16x4 zero = {0, 0, 0, 0};
-        *(s16x4 *)(top + 8) = zero;
-        *(s16x4 *)(pop + 8) = zero;
-      }
+      // N = -L_ii for the forward substitution: row tau, columns 4 g .. 4 g + 3
+      *(f32x4 *)(smem + LD::NF + ((i * 16 + n) * 16 + 4 * g) * 4) = NLv;
+      if ((i & 1) == 0) *(s16x4 *)(pop + 8) = (s16x4){0, 0, 0, 0};
     }
+  }
+  __syncthreads();
+
+  // ---- X_blk = (I + L_blk,blk)^-1 = (I - N)^-1 by forward substitution in
+  // fp32: lane (n, g) computes column n (the four lane groups alike), x_t =
+  // [t == n] + sum_{s<t} N_ts x_s
+  {
+    const float *const nf = (const float *)(smem + LD::NF) + blk * 256;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float acc = t == n ? 1.0f : 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < t; s4 += 4) {
+        const f32x4 row = *(const f32x4 *)(nf + t * 16 + s4);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (s4 + jj < t) acc += row[jj] * x[s4 + jj];
+      }
+      x[t] = acc;
+    }
+    float *const xf = (float *)(smem + LD::XF) + blk * 256;
+    if (g == 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) xf[t * 16 + n] = x[t];
+    }
+    // the same wave reads them back (its LDS operations complete in order):
+    // A form, lane (n, g) row n, columns 4 g + r; B form, column n, rows 4 g + r
+    const s16x4 xa = pk(*(const f32x4 *)(xf + n * 16 + 4 * g));
+    f32x4 xbv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xbv[r] = xf[(4 * g + r) * 16 + n];
+    st4(smem + LD::XA + blk * kOp16, xa);
+    st4(smem + LD::XB + blk * kOp16, pk(xbv));
+    char *const top = rec + Rec::T + opidx(blk, blk >> 1) * kFrag + lane * 16;
+    *(s16x4 *)(top + (blk & 1) * 8) = xa;
+    if ((blk & 1) == 0) *(s16x4 *)(top + 8) = (s16x4){0, 0, 0, 0};
   }
   __syncthreads();
 
@@ -409,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void gdn_recur_kernel(RecParams p) {
     if (p.state_in) M[u] = *(const f32x4 *)(p.state_in + (bh * p.dv + col) * (size_t)kDK + 32 * w + 8 * g + 4 * u);
   }
 
-  // chunk c's operands, the rows and the rest apart (c past the last chunk
+  // chunk c's operands, key rows, query rows and the rest apart (c past the last chunk
   // loads the last one again: every load is unconditional, so the wait counts
   // before each use stay exact)
   auto load_rows = [&](int c, ChunkOps &s) {
@@ -419,8 +415,13 @@ __global__ __launch_bounds__(kThreads) void gdn_recur_kernel(RecParams p) {
     for (int i = 0; i < 4; ++i) {
       const unsigned off = (tok0 + 16 * i + n) * (kDK * 2) + 64 * w + 16 * g;
       s.kf[i] = bload(rk, off);
-      s.qf[i] = bload(rq, off);
     }
+  };
+  auto load_qrows = [&](int c, ChunkOps &s) {
+    c = min(c, p.nchunks - 1);
+    const unsigned tok0 = (unsigned)(c * kCT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.qf[i] = bload(rq, (tok0 + 16 * i + n) * (kDK * 2) + 64 * w + 16 * g);
   };
   auto load_rest = [&](int c, ChunkOps &s) {
     c = min(c, p.nchunks - 1);
@@ -464,8 +465,9 @@ __global__ __launch_bounds__(kThreads) void gdn_recur_kernel(RecParams p) {
       for (int pp = 0; pp < 2; ++pp)
         KT[u][pp] = join(pk(mma16(half_of(cur.kf[2 * pp], u), eye, z4())),
                          pk(mma16(half_of(cur.kf[2 * pp + 1], u), eye, z4())));
-    load_rows(c + 3, s);  // the rows are used up: the next ones, apart from the rest
+    load_rows(c + 3, s);  // the key rows are used up: the next ones
     __syncthreads();  // B1: partials, T and scalars in LDS
+    load_qrows(c + 3, s);  // the query rows likewise, spread from the key rows
     // ---- Y of token block w from the partials, summed in slice order
     f32x4 Rs = ldacc(smem + LD::RP + (w * 4) * kFrag), Qs = ldacc(smem + LD::QP + (w * 4) * kFrag);
 #pragma unroll
@@ -492,9 +494,20 @@ __global__ __launch_bounds__(kThreads) void gdn_recur_kernel(RecParams p) {
     D[2] = mfma(lds8(tf + 3 * kFrag), Yb1, mfma(lds8(tf + 2 * kFrag), Yb0, z4()));
     D[3] = mfma(lds8(tf + 5 * kFrag), Yb1, mfma(lds8(tf + 4 * kFrag), Yb0, z4()));
     // ---- o of token block w: (gamma/|q|) Q M0^T + P D
+    // D enters as hi + lo: over a run of similar keys D holds differences whose
+    // sum telescopes, and separately rounded terms would not cancel
     f32x4 O = *(const f32x4 *)(sf + 192 + 16 * w + 4 * g) * Qs;
-    O = mfma(__builtin_bit_cast(bf16x8, cur.p[0]), join(pk(D[0]), pk(D[1])), O);
-    if (w >= 2) O = mfma(__builtin_bit_cast(bf16x8, cur.p[1]), join(pk(D[2]), pk(D[3])), O);
+    {
+      s16x4 dh[4], dl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dh[i] = pk(D[i]);
+        dl[i] = pk(D[i] - unpk(dh[i]));
+      }
+      const bf16x8 p0 = __builtin_bit_cast(bf16x8, cur.p[0]), p1 = __builtin_bit_cast(bf16x8, cur.p[1]);
+      O = mfma(p0, join(dl[0], dl[1]), mfma(p0, join(dh[0], dh[1]), O));
+      if (w >= 2) O = mfma(p1, join(dl[2], dl[3]), mfma(p1, join(dh[2], dh[3]), O));
+    }
     {
       // transposed on the matrix core (exact: bf16 values times the identity)
       // so lane (n, g) holds d_v 16 rt + 4 g .. 4 g + 3 of token 16 w + n: one
@@ -522,12 +535,15 @@ __global__ __launch_bounds__(kThreads) void gdn_recur_kernel(RecParams p) {
   // loads)
   ChunkOps s0, s1, s2;
   load_rows(0, s0);
+  load_qrows(0, s0);
   load_rest(0, s0);
   issue_fence();  // the sets in order, as in the loop
   load_rows(1, s1);
+  load_qrows(1, s1);
   load_rest(1, s1);
   issue_fence();
   load_rows(2, s2);
+  load_qrows(2, s2);
   load_rest(2, s2);
   for (int c = 0;; c += 3) {
     step(c, s0);
