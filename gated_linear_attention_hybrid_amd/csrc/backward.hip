@@ -1375,7 +1375,14 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   }
   if (p.swa && a.L > 0) {
-    if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
+    if (bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, std::is_same<T, bf16>::value)) {
+      WinBwdArgs wa;
+      wa.q = a.q; wa.k = a.k; wa.v = a.v; wa.dout = g.dout; wa.meta = a.meta;
+      wa.lse = p.lse; wa.del = p.del; wa.dq = p.dqs; wa.dk = p.dks; wa.dv = p.dvs; wa.mp = p.mp;
+      wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta; wa.nsb = p.nsb;
+      wa.scale = a.scale;
+      if ((e = launch_bwd_window_mfma(wa, wstream)) != hipSuccess) return e;
+    } else if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
       const unsigned nch = (unsigned)((a.L + kWC - 1) / kWC);
       const size_t lds = sizeof(WinTileLds);
       // dynamic LDS above 64 KiB has to be allowed for each kernel

@@ -87,6 +87,20 @@ bool bwd_supported(const LayerArgs &a, int parts);
 size_t bwd_workspace_bytes(const LayerArgs &a, int parts);
 hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 
+// Window part of the backward on the matrix cores (bwd_window.hip): bf16,
+// d = d_v = 128, window <= 64, n_meta <= 64.  Writes the window part's dq, dk,
+// dv (fp32 [B][H][L][128]), the per-query lse and D = dO . o_swa (fp32
+// [B][H][L]) and the sink-gradient partials of every 16-token block.
+struct WinBwdArgs {
+  const void *q = nullptr, *k = nullptr, *v = nullptr, *dout = nullptr;
+  const float *meta = nullptr;
+  float *lse = nullptr, *del = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *mp = nullptr;
+  int B = 0, H = 0, L = 0, window = 0, n_meta = 0, nsb = 0;
+  float scale = 1.0f;
+};
+bool bwd_window_mfma_supported(int d, int dv, int window, int n_meta, bool bf16);
+hipError_t launch_bwd_window_mfma(const WinBwdArgs &a, hipStream_t stream);
+
 // Gated delta rule (token-recurrent prefill, bandwidth-bound decode step):
 // q, k [B][H][L][d], v and o [B][H][L][dv], log-decay (gate) and beta [B][H][L],
 // state [B][H][dv][d] fp32.
