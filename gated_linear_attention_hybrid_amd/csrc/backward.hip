@@ -1269,9 +1269,16 @@ struct BwdLayout {
 
 size_t up64(size_t n) { return (n + 63) & ~(size_t)63; }
 
+// The state walks write complete feature sums (one d_v slice); the token
+// sweeps one partial sum per 32-column slice of d_v.
+bool use_walk(const LayerArgs &a, int parts) { return (parts & PART_GLA) && bwd_walk_supported(a.f, a.dv, a.bf16); }
+size_t sweep_slices(const LayerArgs &a, int parts) {
+  return use_walk(a, parts) ? 1 : (size_t)(a.dv + kSliceCols - 1) / kSliceCols;
+}
+
 BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t BH = (size_t)a.B * a.H, N = BH * a.L;
-  const size_t nsl = (a.dv + kSliceCols - 1) / kSliceCols, nw = (a.f + 31) / 32;
+  const size_t nsl = sweep_slices(a, parts), nw = (a.f + 31) / 32;
   const size_t nft = (a.L + kFeatTok - 1) / kFeatTok, nsb = (a.L + kSwaTok - 1) / kSwaTok;
   const bool gla = parts & PART_GLA, swa = parts & PART_SWA;
   BwdLayout o;
@@ -1349,7 +1356,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.lf2 = 0;
   while ((1 << p.lf2) < p.f2) ++p.lf2;
   p.window = a.window; p.n_meta = a.n_meta;
-  p.nsl = (a.dv + kSliceCols - 1) / kSliceCols; p.nw = (a.f + 31) / 32;
+  p.nsl = (int)sweep_slices(a, parts); p.nw = (a.f + 31) / 32;
   p.nft = (a.L + kFeatTok - 1) / kFeatTok; p.nsb = (a.L + kSwaTok - 1) / kSwaTok;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
@@ -1414,8 +1421,18 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   }
   if (p.gla && BH > 0) {
     // with no tokens the sweeps still pass dS_final through to dS_0
-    hipLaunchKernelGGL(bwd_sweeps_kernel<T>, dim3(2 * BH * p.nsl), block, 0, a.stream, p);
-    if (!launched()) return e;
+    if (use_walk(a, parts)) {
+      WalkArgs wa;
+      wa.pq = p.pq; wa.pk = p.pk; wa.gam = p.gam; wa.v = a.v; wa.dout = g.dout;
+      wa.state_in = a.state_in; wa.dstate_out = p.dstate_out;
+      wa.dpq = p.dpq; wa.dpk = p.dpk; wa.dvg = p.dvg; wa.tq = p.tq; wa.tk = p.tk; wa.xs = p.xs;
+      wa.dstate_in = g.dstate_in;
+      wa.BH = (int)BH; wa.L = a.L; wa.nft = p.nft;
+      if ((e = launch_bwd_walk(wa, a.stream)) != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(bwd_sweeps_kernel<T>, dim3(2 * BH * p.nsl), block, 0, a.stream, p);
+      if (!launched()) return e;
+    }
     if (a.L > 0) {
       hipLaunchKernelGGL(bwd_tile_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
                          a.stream, p);

@@ -61,10 +61,10 @@ def compare(got, ref, tol, names=OB.NAMES, flat=("gate", "meta", "wq", "wk")):
     return worst
 
 
-def run_case(wl, kind=OB.GATE_LOGITS, with_state=False, seed=3):
+def run_case(wl, kind=OB.GATE_LOGITS, with_state=False, seed=3, gate=None):
     x = make_prefill(wl, DEV)
     dt = wl.torch_dtype
-    g = gate_of(kind, x, wl, dt)
+    g = gate_of(kind, x, wl, dt) if gate is None else gate.to(dt).to(DEV)
     dO = grads_seed((wl.B, wl.H, wl.L, wl.dv), seed, dt, std=1.0)
     s_in = grads_seed((wl.B, wl.H, wl.f, wl.dv), seed + 1, torch.float32, 0.3) if with_state else None
     dS = grads_seed((wl.B, wl.H, wl.f, wl.dv), seed + 2, torch.float32, 0.3) if with_state else None
@@ -133,22 +133,70 @@ def test_backward_bf16_slow_decay():
     compare(got, ref, TOL_BF16)
 
 
-def test_backward_empty_sequence():
+@pytest.mark.parametrize("name", ["tiny_fp32", "prefill_2k"])
+def test_backward_empty_sequence(name):
     """L = 0: the final state is the initial one, so dstate_in = dstate_out and
-    every parameter gradient is zero."""
-    wl = WORKLOADS["tiny_fp32"].with_(B=2, H=2, L=0)
-    say("backward L=0")
+    every parameter gradient is zero (token sweeps at f = 64, the tile walks at
+    bf16 f = d_v = 128)."""
+    wl = WORKLOADS[name].with_(B=2, H=2, L=0)
+    say("backward L=0 %s" % name)
     x = make_prefill(wl.with_(L=1), DEV)
     e = {k: (v[:, :, :0].contiguous() if v.dim() == 4 else v) for k, v in x.items()}
     dS = grads_seed((2, 2, wl.f, wl.dv), 9, torch.float32)
     s_in = grads_seed((2, 2, wl.f, wl.dv), 8, torch.float32)
-    dO = torch.empty((2, 2, 0, wl.dv), device=DEV)
+    dO = torch.empty((2, 2, 0, wl.dv), device=DEV, dtype=wl.torch_dtype)
     got = G.hybrid_layer_bwd(e["q"], e["k"], e["v"], e["gate"], e["wq"], e["wk"], e["meta"], dO,
                              window=wl.window, state_in=s_in, dstate_out=dS, need_dstate_in=True)
     torch.cuda.synchronize()
     assert torch.equal(got["state_in"], dS)
     for n in ("wq", "wk", "meta"):
         assert float(got[n].abs().max()) == 0.0, n
+
+
+@pytest.mark.parametrize("kind,L", [(OB.GATE_LOGITS, 17), (OB.GATE_LOG, 129), (OB.GATE_LOG_TOKEN, 1000),
+                                    (OB.GATE_LOG_HEAD, 64)])
+def test_backward_bf16_state_walks(kind, L):
+    """The 16-token tile walks over the state (bf16, f = d_v = 128): two batches
+    of two heads, every gate layout, a given initial state and final-state
+    gradient, lengths ending inside a 16-token tile and a 64-token tile."""
+    wl = WORKLOADS["prefill_2k"].with_(B=2, H=2, L=L, seed=1501)
+    say("backward bf16 state walks gate=%s L=%d" % (kind, L))
+    got, ref = run_case(wl, kind=kind, with_state=True)
+    compare(got, ref, TOL_BF16)
+
+
+def test_backward_bf16_extreme_gates():
+    """Per-feature log-gates at both ends: whole 16-token tiles of Gamma = e^-12
+    and e^-30 (below the walks' e^-10 floor, which moves any term they touch by
+    at most 4.5e-5 of its undecayed size), a stretch of Gamma = 1 across tile
+    boundaries, and single closed gates inside open stretches.
+
+    The gradient of a closed gate is proportional to the gate (Gamma_t times
+    S_{t-1} . dS_t, about 1e-13 of the others at e^-30), and the path forms it as
+    a running sum of phiq . dphiq - phik . dphik, whose fp32 rounding and floored
+    decays are absolute errors of the sum's size: on the closed tokens the gate
+    gradient is held to the head's largest gate gradient, on every other token
+    to its own row, like every other gradient."""
+    wl = WORKLOADS["prefill_2k"].with_(B=1, H=2, L=300, seed=1502)
+    gen = torch.Generator().manual_seed(77)
+    g = torch.log(torch.rand((1, 2, 300, 128), generator=gen) * 0.5 + 0.5)
+    closed = np.zeros(300, dtype=bool)
+    g[:, :, 32:48] = -12.0
+    g[:, :, 64:80] = -30.0
+    g[:, :, 100:180] = 0.0
+    g[:, :, 120] = -30.0
+    closed[32:48] = closed[64:80] = closed[120] = True
+    g[:, 1, 200:260, :64] = 0.0
+    say("backward bf16 extreme gates")
+    got, ref = run_case(wl, kind=OB.GATE_LOG, with_state=True, gate=g)
+    compare(got, ref, TOL_BF16, names=[n for n in OB.NAMES if n != "gate"])
+    gg, rg = gpu_f64(got["gate"]), ref["gate"]
+    assert_finite(got["gate"], "gate")
+    e_open = row_rel_err(gg[:, :, ~closed], rg[:, :, ~closed])
+    e_head = max(float(np.abs(gg[0, h] - rg[0, h]).max() / np.abs(rg[0, h]).max()) for h in range(2))
+    say("gate gradient: open tokens %.3e, head-scaled %.3e" % (e_open, e_head))
+    assert e_open <= TOL_BF16
+    assert e_head <= TOL_BF16
 
 
 def test_backward_is_bitwise_repeatable():
