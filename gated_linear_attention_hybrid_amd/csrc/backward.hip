@@ -97,6 +97,9 @@ struct BwdParams {
   int nsl, nw, nft, nsb, npt;
   float scale;
   int gate_is_log, gate_mode, gla, swa;
+  // gam holds the in-tile cumsum of the floored log-gate over 16-token tiles
+  // (the tile walks) instead of Gamma (the token sweeps)
+  int gam_cum;
 };
 
 // ---------------------------------------------------------------------------
@@ -254,7 +257,24 @@ __global__ __launch_bounds__(kBT) void bwd_prep_tile_kernel(BwdParams p) {
     __syncthreads();  // W, XT and U are reused by the next map
   }
   const T *g = (const T *)p.gate;
-  if (p.gate_mode == 0) {
+  if (p.gam_cum) {
+    // b_t = sum of max(log Gamma, -10) over the 16-token tile up to t: thread
+    // (feature, tile), the tile's 16 gates loaded before the sum
+    for (int i = tid; i < f * (kPrepTile / 16); i += kBT) {
+      const int r = i % f, j = i / f, tt0 = 16 * j;
+      if (tt0 >= nt) continue;
+      float a[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        a[u] = ld(g + gate_index(p.gate_mode, bh, p.H, L, f, t0 + min(tt0 + u, nt - 1), r));
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        acc += fmaxf(log_gate_from(a[u], p.gate_is_log), -10.0f);
+        if (tt0 + u < nt) p.gam[(row0 + tt0 + u) * f + r] = acc;
+      }
+    }
+  } else if (p.gate_mode == 0) {
     // per-feature gates: quads of the tile's [nt][f] rows, loads first
     constexpr int kGQ = kPrepTile * kBwdMaxF / 4 / kBT;
     const int f4 = f >> 2, ngq = nt * f4;
@@ -1264,21 +1284,26 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
 
 // Workspace layout, in floats; every region starts on a 256-byte boundary.
 struct BwdLayout {
-  size_t pq, pk, gam, tq, tk, ta, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, total;
+  size_t pq, pk, gam, tq, tk, ta, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, wst, total;
 };
 
 size_t up64(size_t n) { return (n + 63) & ~(size_t)63; }
 
 // The state walks write complete feature sums (one d_v slice); the token
 // sweeps one partial sum per 32-column slice of d_v.
-bool use_walk(const LayerArgs &a, int parts) { return (parts & PART_GLA) && bwd_walk_supported(a.f, a.dv, a.bf16); }
+bool use_walk(const LayerArgs &a, int parts) {
+  return (parts & PART_GLA) && bwd_walk_supported(a.f, a.dv, a.L, a.bf16);
+}
 size_t sweep_slices(const LayerArgs &a, int parts) {
   return use_walk(a, parts) ? 1 : (size_t)(a.dv + kSliceCols - 1) / kSliceCols;
 }
+// dv parts of the gated part: the walks sum theirs; the sweeps leave one per
+// 32 features
+size_t row_parts(const LayerArgs &a, int parts) { return use_walk(a, parts) ? 1 : (size_t)(a.f + 31) / 32; }
 
 BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t BH = (size_t)a.B * a.H, N = BH * a.L;
-  const size_t nsl = sweep_slices(a, parts), nw = (a.f + 31) / 32;
+  const size_t nsl = sweep_slices(a, parts), nw = row_parts(a, parts);
   const size_t nft = (a.L + kFeatTok - 1) / kFeatTok, nsb = (a.L + kSwaTok - 1) / kSwaTok;
   const bool gla = parts & PART_GLA, swa = parts & PART_SWA;
   BwdLayout o;
@@ -1297,6 +1322,7 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   o.wqp = take(wp); o.wkp = take(wp);
   o.gp = take(gla ? BH * nft : 0);
   o.mp = take(swa ? BH * nsb * a.n_meta : 0);
+  o.wst = take(use_walk(a, parts) ? bwd_walk_ws_floats((int)BH, a.L) : 0);
   o.total = at;
   return o;
 }
@@ -1356,7 +1382,8 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.lf2 = 0;
   while ((1 << p.lf2) < p.f2) ++p.lf2;
   p.window = a.window; p.n_meta = a.n_meta;
-  p.nsl = (int)sweep_slices(a, parts); p.nw = (a.f + 31) / 32;
+  p.nsl = (int)sweep_slices(a, parts); p.nw = (int)row_parts(a, parts);
+  p.gam_cum = use_walk(a, parts) ? 1 : 0;
   p.nft = (a.L + kFeatTok - 1) / kFeatTok; p.nsb = (a.L + kSwaTok - 1) / kSwaTok;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
@@ -1423,7 +1450,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     // with no tokens the sweeps still pass dS_final through to dS_0
     if (use_walk(a, parts)) {
       WalkArgs wa;
-      wa.pq = p.pq; wa.pk = p.pk; wa.gam = p.gam; wa.v = a.v; wa.dout = g.dout;
+      wa.pq = p.pq; wa.pk = p.pk; wa.gb = p.gam; wa.v = a.v; wa.dout = g.dout; wa.ws = ws + lay.wst;
       wa.state_in = a.state_in; wa.dstate_out = p.dstate_out;
       wa.dpq = p.dpq; wa.dpk = p.dpk; wa.dvg = p.dvg; wa.tq = p.tq; wa.tk = p.tk; wa.xs = p.xs;
       wa.dstate_in = g.dstate_in;

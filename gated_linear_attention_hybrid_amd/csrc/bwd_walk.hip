@@ -1,6 +1,6 @@
-// bwd_walk.hip -- the state sweeps of the gated part's backward in tile form on
-// the gfx950 matrix cores (bf16 values, fp32 feature maps and gates from the
-// backward prologue, d_v = f = 128).
+// bwd_walk.hip -- the state walks of the gated part's backward in tile form on
+// the gfx950 matrix cores (bf16 values, fp32 feature maps from the backward
+// prologue, f = d_v = 128).
 //
 // The gated part ("Lizard" technical summary, gist.science 2507.09025,
 // Methodology A.1): S_t = diag(Gamma_t) S_{t-1} + phik_t v_t^T, o_t = S_t^T
@@ -17,20 +17,36 @@
 //   S <- e^{B} S + sum_s (e^{B - b_s} phik_s) v_s^T
 //   G <- e^{B} G + sum_t (e^{b_t} phiq_t) dO_t^T.
 // Inside a tile the decay between two tokens is split at the tile's middle
-// (e^{b_t - b_s} = e^{b_t - m} e^{m - b_s}, m = B / 2), so with the per-token
-// log-gate floored at -10 no factor leaves e^{+-80}; every other factor is <= 1.
-// Two walks, one wave per block, in one launch:
-//   forward walk  (b, h, 16 features): S^T of its features, dphiq and the
-//                 64-token tile sums of phiq . dphiq, S_{L-1} . dS_final
-//   reverse walk  (b, h, 32 features): G^T of its features, dphik and its tile
-//                 sums, the part of dv from these features, dS_in = the state
-//                 gradient before the sequence, and Gamma_0 (S_in . dS_0)
+// (e^{b_t - b_s} = e^{b_t - m} e^{m - b_s}, m = B / 2); the prologue floors the
+// per-token log-gate at -10 and stores b, so no factor leaves e^{+-80}.
+//
+// Each head's tokens are cut into P segments of whole 64-token tiles so that
+// the walks run P-fold in parallel:
+//   pass 1  each segment's own state from zero, S_loc (forward, segments
+//           0 .. P-2) and G_loc (reverse, segments 1 .. P-1), and its total
+//           log-decay D per feature;
+//   pass 2  the walks, each segment starting from the state combined from the
+//           earlier segments (S_start[p] = e^{D[p-1]} S_start[p-1] + S_loc[p-1])
+//           or the later ones (G_end[p] = e^{D[p+1]} G_end[p+1] + G_loc[p+1]):
+//     forward walk   (b, h, segment, 16 features; one wave): S^T of its
+//                    features, dphiq and the 64-token tile sums of phiq .
+//                    dphiq; the last segment S_{L-1} . dS_final
+//     reverse walk   (b, h, segment; four waves of 32 features): G^T, dphik
+//                    and its tile sums, dv (the four waves' parts summed in
+//                    LDS every tile); the first segment dS_in and Gamma_0
+//                    (S_in . dS_0).
+// The state, the decayed maps and the tile's dO . v products enter the
+// products behind dphiq and dphik as bf16 hi + lo pairs: the gate gradient is a
+// running sum of phiq . dphiq - phik . dphik, differences of nearly equal
+// terms.  dv takes bf16 operands.
 // Lane layouts (n = lane & 15, g = lane >> 4) of the 16x16x16 MFMA as in the
 // other kernels: A row n, K-slots 4g..4g+3; B column n, K-slots 4g..4g+3;
 // accumulator column n, rows 4g..4g+3.  "Layout F" holds element (token 4g + r,
-// feature n) of a tile in lane (n, g), slot r (a B operand over tokens);
-// "layout T" holds (token n, features 4g + j and 16 + 4g + j) (an operand over
-// features, K-slots in the order of two joined 16x16x16 operands).
+// feature n) of a tile in lane (n, g), slot r (a B operand over tokens, or an A
+// operand with the feature as row); the reverse walk turns its layout-F
+// operands into token rows over features with an identity product.
+#include <algorithm>
+
 #include "chunk_common.hpp"
 #include "launch.hpp"
 
@@ -40,7 +56,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-constexpr float kMinLogGate = -10.0f;  // natural log-gate floor (see above)
+constexpr int kWalkWaves = 2048;  // pass-2 waves the segment count aims at
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
@@ -50,25 +66,8 @@ __device__ __forceinline__ f32x4 zf4() { return (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 __device__ __forceinline__ float ex(float x) { return exp2_fast(x * kLog2e); }
 __device__ __forceinline__ float dot4f(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
-// In-tile inclusive cumsum over the tokens of layout F (lane (n, g) holds
-// tokens 4g .. 4g+3 of feature n): b, the tile total B (in every lane).
-__device__ __forceinline__ void cumsum_f(const float *a, float *b, float &B) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  float c0 = a[0], c1 = c0 + a[1], c2 = c1 + a[2], c3 = c2 + a[3];
-  const float t0 = __shfl(c3, n), t1 = __shfl(c3, n + 16), t2 = __shfl(c3, n + 32);
-  const float pre = (g >= 1 ? t0 : 0.0f) + (g >= 2 ? t1 : 0.0f) + (g >= 3 ? t2 : 0.0f);
-  b[0] = pre + c0;
-  b[1] = pre + c1;
-  b[2] = pre + c2;
-  b[3] = pre + c3;
-  B = __shfl(b[3], n + 48);
-}
-
 // x = hi + lo to about 2^-17 of |x|: two bf16 operands whose products with an
-// exact bf16 operand sum (in fp32) to nearly the fp32 product.  The gate
-// gradient is a running sum of phiq . dphiq - phik . dphik, differences of
-// nearly equal terms, so the products behind dphiq and dphik take the state
-// and the decayed maps in this split form.
+// exact bf16 operand sum (in fp32) to nearly the fp32 product.
 __device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
   hi = pack4(x);
   f32x4 h;
@@ -85,80 +84,221 @@ __device__ __forceinline__ bf16x4 eye16() {
   for (int r = 0; r < 4; ++r) e[r] = (bf16)(4 * g + r == n ? 1.0f : 0.0f);
   return e;
 }
+// a layout-F operand (row = feature, K = token) as token rows over features
+__device__ __forceinline__ bf16x4 to_rows(f32x4 x, bf16x4 eye) { return pack4(mma16(pack4(x), eye, zf4())); }
+
+// One head's fp32 [L][128] rows as a buffer: reads past the last row return 0
+// and writes there are dropped (offsets are 32-bit: L < 2^22).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t frows(const float *base, int bh, int L) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (size_t)bh * L * 128), (short)0, L * 512, 0x00020000);
+}
+__device__ __forceinline__ float fld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void fst(__amdgpu_buffer_rsrc_t r, unsigned off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void fst4(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
+}
+// byte offset of (token 16 tau + 4 g + r, column c) in [L][128] fp32 rows
+__device__ __forceinline__ unsigned foff(int tau, int r, int c) {
+  const unsigned g = (threadIdx.x & 63) >> 4;
+  return ((unsigned)(16 * tau + r) + 4u * g) * 512u + (unsigned)c * 4u;
+}
 
 struct WalkParams {
-  const float *pq, *pk, *gam;          // [B H L][128] fp32 (prologue)
+  const float *pq, *pk, *gb;           // [B H L][128] fp32: maps, in-tile cumsum of the log-gate
   const bf16 *v, *dout;                // [B H][L][128]
   const float *state_in, *dstate_out;  // [B H][128][128] or null
-  float *dpq, *dpk, *dvg;              // [N][128], [N][128], [4][N][128]
+  float *dpq, *dpk, *dvg;              // [B H L][128]
   float *tq, *tk, *xs, *dstate_in;     // [BH][nft][128] x 2, [2][BH][128], [BH][128][128]
-  int BH, L, nft;
+  float *sloc, *gloc, *dseg;           // [BH][P][128][128] x 2, [BH][P][128]
+  int BH, L, nft, P, seg;              // seg: 16-token tiles per segment (a multiple of 4)
 };
 
-// ============================== forward walk ================================
-__device__ __forceinline__ void fwd_walk(const WalkParams &p, int blk) {
+// layout-F values of one tile: tokens 16 tau + 4 g + r, column c (0 past the end)
+__device__ __forceinline__ void load_f(__amdgpu_buffer_rsrc_t r, int tau, int c, float *x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = fld(r, foff(tau, i, c));
+}
+// b at the tile's last token (its total B; the last valid token for a ragged tile)
+__device__ __forceinline__ float load_total(__amdgpu_buffer_rsrc_t r, int tau, int c, int L) {
+  return fld(r, (unsigned)min(16 * tau + 15, L - 1) * 512u + (unsigned)c * 4u);
+}
+
+// ================================ pass 1 ====================================
+// forward: S_loc of segment seg from zero, 16 features (ft); D of the segment
+__device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, int ft) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int bh = blk >> 3, ft = blk & 7;
-  const int f = 16 * ft + n;
-  const int L = p.L, ntiles = (L + 15) / 16;
-  const size_t rowN = (size_t)bh * L;
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), ro = head_rsrc(p.dout, bh, L);
+  const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
+  const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
   const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
-  // S^T tiles (s, dt): rows d_v 32 s + 8 g + 4 dt + r, column f
-  f32x4 ST[4][2];
+  f32x4 S[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) S[s][0] = S[s][1] = zf4();
+  bf16x8 xv[4];
+  float lk[4], lb[4], lB;
+  auto load = [&](int tau) {
+    load_vals(rv, (unsigned)(16 * tau + n) * 256, xv);
+    load_f(rk, tau, f, lk);
+    load_f(rb, tau, f, lb);
+    lB = load_total(rb, tau, f, L);
+  };
+  load(t0);
+  float dsum = 0.0f;
+  for (int tau = t0; tau < t1; ++tau) {
+    bf16x8 cv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) cv[s] = xv[s];
+    f32x4 kh;
+    const float B = lB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) kh[r] = lk[r] * ex(B - lb[r]);
+    load(min(tau + 1, t1 - 1));
+    const float eB = ex(B);
+    dsum += B;
+    bf16x4 khh, khl;
+    split4(kh, khh, khl);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
+        S[s][dt] = mma16(vt, khl, mma16(vt, khh, S[s][dt] * eB));
+      }
+  }
+  const size_t base = ((size_t)bh * p.P + seg) * 128 + f;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-      ST[s][dt] = p.state_in ? *(const f32x4 *)(p.state_in + ((size_t)bh * 128 + f) * 128 + 32 * s + 8 * g + 4 * dt)
-                             : zf4();
-  // operands of a tile (rows of v and dO in the value layout, layout F of the
-  // maps and gates), loaded a tile ahead
-  bf16x8 xv[4], xo[4];
-  float lq[4], lk[4], lg[4];
-  auto load = [&](int tau) {
-    tau = min(tau, ntiles - 1);
-    const unsigned base = (unsigned)(16 * tau + n) * 256;
-    load_vals(rv, base, xv);
-    load_vals(ro, base, xo);
+    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt) = S[s][dt];
+  if (g == 0) p.dseg[base] = dsum;
+}
+
+// reverse: G_loc of segment seg from zero, 16 features (ft); D of the last segment
+__device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, int ft) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
+  const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
+  const __amdgpu_buffer_rsrc_t ro = head_rsrc(p.dout, bh, L), rq = frows(p.pq, bh, L), rb = frows(p.gb, bh, L);
+  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
+  f32x4 G[4][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t i = (rowN + min(16 * tau + 4 * g + r, L - 1)) * 128 + f;
-      lq[r] = p.pq[i];
-      lk[r] = p.pk[i];
-      lg[r] = p.gam[i];
-    }
+  for (int s = 0; s < 4; ++s) G[s][0] = G[s][1] = zf4();
+  bf16x8 xo[4];
+  float lq[4], lb[4], lB;
+  auto load = [&](int tau) {
+    load_vals(ro, (unsigned)(16 * tau + n) * 256, xo);
+    load_f(rq, tau, f, lq);
+    load_f(rb, tau, f, lb);
+    lB = load_total(rb, tau, f, L);
   };
-  if (L > 0) load(0);
+  load(t1 - 1);
+  float dsum = 0.0f;
+  for (int tau = t1 - 1; tau >= t0; --tau) {
+    bf16x8 co[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) co[s] = xo[s];
+    f32x4 qb;
+    const float B = lB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qb[r] = lq[r] * ex(lb[r]);
+    load(max(tau - 1, t0));
+    const float eB = ex(B);
+    dsum += B;
+    bf16x4 qh, ql;
+    split4(qb, qh, ql);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x4 ot = pack4(mfma(co[s], sel[dt], zf4()));
+        G[s][dt] = mma16(ot, ql, mma16(ot, qh, G[s][dt] * eB));
+      }
+  }
+  const size_t base = ((size_t)bh * p.P + seg) * 128 + f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.gloc + base * 128 + 32 * s + 8 * g + 4 * dt) = G[s][dt];
+  if (g == 0 && seg == p.P - 1) p.dseg[base] = dsum;
+}
+
+// Blocks of four waves: the forward states of segments 0 .. P-2 (two blocks a
+// segment), then the reverse states of segments 1 .. P-1.
+__global__ __launch_bounds__(256) void bwd_walk_state_kernel(WalkParams p) {
+  const int wave = threadIdx.x >> 6, per = 2 * (p.P - 1);
+  const int nf = p.BH * per;
+  int blk = blockIdx.x;
+  const bool rev = blk >= nf;
+  if (rev) blk -= nf;
+  const int bh = blk / per, r = blk - bh * per, seg = r >> 1, ft = 4 * (r & 1) + wave;
+  if (rev)
+    rev_state(p, bh, seg + 1, ft);
+  else
+    fwd_state(p, bh, seg, ft);
+}
+
+// ================================ pass 2 ====================================
+__device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, int ft) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
+  const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), ro = head_rsrc(p.dout, bh, L);
+  const __amdgpu_buffer_rsrc_t rq = frows(p.pq, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
+  const __amdgpu_buffer_rsrc_t rd = frows(p.dpq, bh, L);
+  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
+  // S^T tiles (s, dt): rows d_v 32 s + 8 g + 4 dt + r, column f; the state
+  // before the segment
+  f32x4 ST[4][2];
+  const size_t srow = ((size_t)bh * 128 + f) * 128 + 8 * g;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) ST[s][dt] = p.state_in ? *(const f32x4 *)(p.state_in + srow + 32 * s + 4 * dt) : zf4();
+  for (int q = 0; q < seg; ++q) {
+    const size_t base = ((size_t)bh * p.P + q) * 128 + f;
+    const float e = ex(p.dseg[base]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        ST[s][dt] = ST[s][dt] * e + *(const f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt);
+  }
+  bf16x8 xv[4], xo[4];
+  float lq[4], lk[4], lb[4], lB;
+  auto load = [&](int tau) {
+    const unsigned rowb = (unsigned)(16 * tau + n) * 256;
+    load_vals(rv, rowb, xv);
+    load_vals(ro, rowb, xo);
+    load_f(rq, tau, f, lq);
+    load_f(rk, tau, f, lk);
+    load_f(rb, tau, f, lb);
+    lB = load_total(rb, tau, f, L);
+  };
+  if (t1 > t0) load(t0);
   float tqa = 0.0f;
-  for (int tau = 0; tau < ntiles; ++tau) {
-    // this tile's operands, then the next tile's loads
+  for (int tau = t0; tau < t1; ++tau) {
     bf16x8 cv[4], co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       cv[s] = xv[s];
       co[s] = xo[s];
     }
-    float a[4], fq[4], fk[4];
+    const float B = lB, mid = 0.5f * B;
+    f32x4 fq, eo, kb, ein, kh;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = 16 * tau + 4 * g + r < L;  // past the end: no decay, no map
-      a[r] = ok ? fmaxf(log2_fast(lg[r]) * kLn2, kMinLogGate) : 0.0f;
-      fq[r] = ok ? lq[r] : 0.0f;
-      fk[r] = ok ? lk[r] : 0.0f;
+      fq[r] = lq[r];
+      eo[r] = ex(lb[r] - mid);
+      kb[r] = lk[r] * ex(mid - lb[r]);
+      ein[r] = ex(lb[r]);
+      kh[r] = lk[r] * ex(B - lb[r]);
     }
-    load(tau + 1);
-    float b[4], B;
-    cumsum_f(a, b, B);
-    const float mid = 0.5f * B, eB = ex(B);
-    f32x4 eo, kb, ein, kh;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      eo[r] = ex(b[r] - mid);
-      kb[r] = fk[r] * ex(mid - b[r]);
-      ein[r] = ex(b[r]);
-      kh[r] = fk[r] * ex(B - b[r]);
-    }
+    load(min(tau + 1, t1 - 1));
+    const float eB = ex(B);
     // M^T (column t, rows s): v_s . dO_t; kept for s <= t it is M in A form
     f32x4 mt = zf4();
 #pragma unroll
@@ -185,11 +325,10 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int blk) {
     dq += inter * ein;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * tau + 4 * g + r;
-      if (t < L) p.dpq[(rowN + t) * 128 + f] = dq[r];
+      fst(rd, foff(tau, r, f), dq[r]);
       tqa += fq[r] * dq[r];
     }
-    if ((tau & 3) == 3 || tau == ntiles - 1) {
+    if ((tau & 3) == 3 || tau == nt - 1) {
       const float ssum = grp_sum(tqa);
       if (g == 0) p.tq[((size_t)bh * p.nft + (tau >> 2)) * 128 + f] = ssum;
       tqa = 0.0f;
@@ -205,105 +344,102 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int blk) {
         ST[s][dt] = mma16(vt, khl, mma16(vt, khh, ST[s][dt] * eB));
       }
   }
-  if (p.dstate_out) {
+  if (seg == p.P - 1 && p.dstate_out) {
     float acc = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        acc += dot4f(ST[s][dt], *(const f32x4 *)(p.dstate_out + ((size_t)bh * 128 + f) * 128 + 32 * s + 8 * g + 4 * dt));
+      for (int dt = 0; dt < 2; ++dt) acc += dot4f(ST[s][dt], *(const f32x4 *)(p.dstate_out + srow + 32 * s + 4 * dt));
     acc = grp_sum(acc);
     if (g == 0) p.xs[(size_t)bh * 128 + f] = acc;
   }
 }
 
-// ============================== reverse walk ================================
-__device__ __forceinline__ void rev_walk(const WalkParams &p, int blk) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int bh = blk >> 2, fs = blk & 3;
-  const int L = p.L, ntiles = (L + 15) / 16;
-  const size_t rowN = (size_t)bh * L, N = (size_t)p.BH * L;
+// LDS of a reverse-walk block: each wave's dv part of a tile, double-buffered
+// (part[buf][wave][s][dt][lane] as f32x4)
+constexpr int kPartBytes = 4 * 4 * 2 * 64 * 16;  // one buffer: 32 KiB
+__device__ __forceinline__ unsigned part_off(int buf, int wave, int s, int dt) {
+  return (unsigned)(buf * kPartBytes + (((wave * 4 + s) * 2 + dt) * 64 + (int)(threadIdx.x & 63)) * 16);
+}
+
+__device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, char *lds) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, fs = threadIdx.x >> 6;
+  const int L = p.L, nt = (L + 15) / 16;
+  const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), ro = head_rsrc(p.dout, bh, L);
+  const __amdgpu_buffer_rsrc_t rq = frows(p.pq, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
+  const __amdgpu_buffer_rsrc_t rd = frows(p.dpk, bh, L), rdv = frows(p.dvg, bh, L);
   const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const bf16x4 eye = eye16();
-  // features of layout F (fa = 0, 1) and of layout T (two quads)
   const int fF[2] = {32 * fs + n, 32 * fs + 16 + n};
-  const int fT[2] = {32 * fs + 4 * g, 32 * fs + 16 + 4 * g};
-  // G^T tiles [fa][s][dt]: rows d_v 32 s + 8 g + 4 dt + r, column fF[fa]
+  // G^T tiles [fa][s][dt]: rows d_v 32 s + 8 g + 4 dt + r, column fF[fa]; the
+  // gradient reaching the state after the segment
   f32x4 GT[2][4][2];
 #pragma unroll
-  for (int fa = 0; fa < 2; ++fa)
+  for (int fa = 0; fa < 2; ++fa) {
+    const size_t srow = ((size_t)bh * 128 + fF[fa]) * 128 + 8 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
-        GT[fa][s][dt] = p.dstate_out ? *(const f32x4 *)(p.dstate_out + ((size_t)bh * 128 + fF[fa]) * 128 + 32 * s +
-                                                        8 * g + 4 * dt)
-                                     : zf4();
+        GT[fa][s][dt] = p.dstate_out ? *(const f32x4 *)(p.dstate_out + srow + 32 * s + 4 * dt) : zf4();
+  }
+  for (int q = p.P - 1; q > seg; --q) {
+#pragma unroll
+    for (int fa = 0; fa < 2; ++fa) {
+      const size_t base = ((size_t)bh * p.P + q) * 128 + fF[fa];
+      const float e = ex(p.dseg[base]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+          GT[fa][s][dt] = GT[fa][s][dt] * e + *(const f32x4 *)(p.gloc + base * 128 + 32 * s + 8 * g + 4 * dt);
+    }
+  }
   bf16x8 xv[4], xo[4];
-  float lq[2][4], lk[2][4], lg[2][4];
-  f32x4 tq4[2], tk4[2], tg4[2];  // layout T: token 16 tau + n, features fT[h] .. + 3
+  float lq[2][4], lk[2][4], lb[2][4], lB[2];
   auto load = [&](int tau) {
-    tau = max(tau, 0);
-    const unsigned base = (unsigned)(16 * tau + n) * 256;
-    load_vals(rv, base, xv);
-    load_vals(ro, base, xo);
+    const unsigned rowb = (unsigned)(16 * tau + n) * 256;
+    load_vals(rv, rowb, xv);
+    load_vals(ro, rowb, xo);
 #pragma unroll
-    for (int fa = 0; fa < 2; ++fa)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t i = (rowN + min(16 * tau + 4 * g + r, L - 1)) * 128 + fF[fa];
-        lq[fa][r] = p.pq[i];
-        lk[fa][r] = p.pk[i];
-        lg[fa][r] = p.gam[i];
-      }
-    const size_t it = (rowN + min(16 * tau + n, L - 1)) * 128;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      tq4[h] = *(const f32x4 *)(p.pq + it + fT[h]);
-      tk4[h] = *(const f32x4 *)(p.pk + it + fT[h]);
-      tg4[h] = *(const f32x4 *)(p.gam + it + fT[h]);
+    for (int fa = 0; fa < 2; ++fa) {
+      load_f(rq, tau, fF[fa], lq[fa]);
+      load_f(rk, tau, fF[fa], lk[fa]);
+      load_f(rb, tau, fF[fa], lb[fa]);
+      lB[fa] = load_total(rb, tau, fF[fa], L);
     }
   };
-  if (L > 0) load(ntiles - 1);
+  if (t1 > t0) load(t1 - 1);
   float tka[2] = {0.0f, 0.0f};
-  for (int tau = ntiles - 1; tau >= 0; --tau) {
+  for (int tau = t1 - 1; tau >= t0; --tau) {
     bf16x8 cv[4], co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       cv[s] = xv[s];
       co[s] = xo[s];
     }
-    // layout F per feature half: log-gates, cumsum, maps
-    float bF[2][4], BF[2], fqF[2][4], fkF[2][4];
+    // per feature half, layout F: the decayed maps
+    f32x4 fk[2], qp[2], kp[2], kh[2], qb[2], eo[2], egk[2];
+    float eB[2];
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
-      float a[4];
+      const float B = lB[fa], mid = 0.5f * B;
+      eB[fa] = ex(B);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = 16 * tau + 4 * g + r < L;
-        a[r] = ok ? fmaxf(log2_fast(lg[fa][r]) * kLn2, kMinLogGate) : 0.0f;
-        fqF[fa][r] = ok ? lq[fa][r] : 0.0f;
-        fkF[fa][r] = ok ? lk[fa][r] : 0.0f;
+        const float b = lb[fa][r], q = lq[fa][r], k = lk[fa][r];
+        const float up = ex(b - mid), dn = ex(mid - b), tail = ex(B - b);
+        fk[fa][r] = k;
+        qp[fa][r] = q * up;
+        kp[fa][r] = k * dn;
+        eo[fa][r] = dn;
+        egk[fa][r] = tail;
+        kh[fa][r] = k * tail;
+        qb[fa][r] = q * ex(b);
       }
-      cumsum_f(a, bF[fa], BF[fa]);
     }
-    // layout T: cumsum over the tokens of the 16-lane row
-    f32x4 qT[2], kT[2], bT[2], BT[2];
-    {
-      const bool ok = 16 * tau + n < L;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = ok ? fmaxf(log2_fast(tg4[h][j]) * kLn2, kMinLogGate) : 0.0f;
-          bT[h][j] = row_scan(a);
-          BT[h][j] = row_bcast15(bT[h][j]);
-          qT[h][j] = ok ? tq4[h][j] : 0.0f;
-          kT[h][j] = ok ? tk4[h][j] : 0.0f;
-        }
-    }
-    load(tau - 1);
+    load(max(tau - 1, t0));
     // M (column t, rows t'): dO_t' . v_t; kept for t' >= t it is M^T in A form
     f32x4 mm = zf4();
 #pragma unroll
@@ -313,22 +449,14 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int blk) {
       if (4 * g + r < n) mm[r] = 0.0f;
     bf16x4 mmh, mml;
     split4(mm, mmh, mml);
-    // dphik per feature half
+    // dphik per feature half (split operands)
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
-      const float mid = 0.5f * BF[fa];
-      f32x4 qp, eo, egk;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        qp[r] = fqF[fa][r] * ex(bF[fa][r] - mid);
-        eo[r] = ex(mid - bF[fa][r]);
-        egk[r] = ex(BF[fa] - bF[fa][r]);
-      }
       bf16x4 qph, qpl;
-      split4(qp, qph, qpl);
+      split4(qp[fa], qph, qpl);
       f32x4 dk = mma16(mmh, qph, zf4());
       dk = mma16(mmh, qpl, dk);
-      dk = mma16(mml, qph, dk) * eo;
+      dk = mma16(mml, qph, dk) * eo[fa];
       f32x4 inter = zf4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -338,12 +466,11 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int blk) {
         inter = mfma(cv[s], join44(h0, h1), inter);
         inter = mfma(cv[s], join44(l0, l1), inter);
       }
-      dk += inter * egk;
+      dk += inter * egk[fa];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tau + 4 * g + r;
-        if (t < L) p.dpk[(rowN + t) * 128 + fF[fa]] = dk[r];
-        tka[fa] += fkF[fa][r] * dk[r];
+        fst(rd, foff(tau, r, fF[fa]), dk[r]);
+        tka[fa] += fk[fa][r] * dk[r];
       }
     }
     if ((tau & 3) == 0) {
@@ -354,98 +481,126 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int blk) {
         tka[fa] = 0.0f;
       }
     }
-    // A (column t, rows t') over this wave's features, kept for t' >= t; and
-    // k-hat^T, both over features in layout T
-    bf16x4 ab;
-    bf16x8 khT;
-    {
-      f32x4 qp[2], kp[2], kh[2];
+    // token rows over this wave's features: the decayed maps of A and k-hat
+    const bf16x8 qr = join44(to_rows(qp[0], eye), to_rows(qp[1], eye));
+    const bf16x8 kr = join44(to_rows(kp[0], eye), to_rows(kp[1], eye));
+    const bf16x8 khr = join44(to_rows(kh[0], eye), to_rows(kh[1], eye));
+    // A (column t, rows t') over the wave's features, kept for t' >= t
+    f32x4 am = mfma(qr, kr, zf4());
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float mid = 0.5f * BT[h][j];
-          qp[h][j] = qT[h][j] * ex(bT[h][j] - mid);
-          kp[h][j] = kT[h][j] * ex(mid - bT[h][j]);
-          kh[h][j] = kT[h][j] * ex(BT[h][j] - bT[h][j]);
-        }
-      f32x4 am = mfma(pack44(qp[0], qp[1]), pack44(kp[0], kp[1]), zf4());
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * g + r < n) am[r] = 0.0f;
-      ab = pack4(am);
-      khT = pack44(kh[0], kh[1]);
-    }
-    // dv^T (rows d_v, column t) and the G update, per d_v tile (s, dt)
-    f32x4 qb[2];  // e^{b} phiq, layout F
-#pragma unroll
-    for (int fa = 0; fa < 2; ++fa)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) qb[fa][r] = fqF[fa][r] * ex(bF[fa][r]);
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < n) am[r] = 0.0f;
+    const bf16x4 ab = pack4(am);
     bf16x4 qbh[2], qbl[2];
     split4(qb[0], qbh[0], qbl[0]);
     split4(qb[1], qbh[1], qbl[1]);
-    const float eB[2] = {ex(BF[0]), ex(BF[1])};
-    const int tv = 16 * tau + n;
+    const int buf = tau & 1;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         // G^T of this d_v tile as an A operand over features (transposed twice
         // on the matrix core: the bf16 values pass unchanged)
-        const bf16x4 g0 = pack4(mma16(pack4(GT[0][s][dt]), eye, zf4()));
-        const bf16x4 g1 = pack4(mma16(pack4(GT[1][s][dt]), eye, zf4()));
+        const bf16x4 g0 = to_rows(GT[0][s][dt], eye);
+        const bf16x4 g1 = to_rows(GT[1][s][dt], eye);
         const bf16x4 ot = pack4(mfma(co[s], sel[dt], zf4()));  // dO^T half: rows d_v, K tokens
         // the two parts in separate accumulators, added on the VALU: a
         // 16x16x16 product accumulating straight onto a 16x16x32 result read
         // stale accumulator rows (the compiler spaces such a mixed pair as if
         // both had one shape)
-        const f32x4 dvt = mfma(join44(g0, g1), khT, zf4()) + mma16(ot, ab, zf4());
-        if (tv < L) *(f32x4 *)(p.dvg + fs * N * 128 + (rowN + tv) * 128 + 32 * s + 8 * g + 4 * dt) = dvt;
+        const f32x4 dvt = mfma(join44(g0, g1), khr, zf4()) + mma16(ot, ab, zf4());
+        *(f32x4 *)(lds + part_off(buf, fs, s, dt)) = dvt;
 #pragma unroll
         for (int fa = 0; fa < 2; ++fa) GT[fa][s][dt] = mma16(ot, qbl[fa], mma16(ot, qbh[fa], GT[fa][s][dt] * eB[fa]));
       }
+    __syncthreads();
+    // this wave's quarter of d_v (s = fs), summed over the four waves' parts
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      f32x4 acc = *(const f32x4 *)(lds + part_off(buf, 0, fs, dt));
+#pragma unroll
+      for (int w = 1; w < 4; ++w) acc += *(const f32x4 *)(lds + part_off(buf, w, fs, dt));
+      fst4(rdv, (unsigned)(16 * tau + n) * 512u + (unsigned)(32 * fs + 8 * g + 4 * dt) * 4u, acc);
+    }
   }
   // G after the first tile = Gamma_0 dS_0: the gradient of the initial state,
   // and Gamma_0 (S_in . dS_0) for the gate gradient at token 0
+  if (seg == 0) {
 #pragma unroll
-  for (int fa = 0; fa < 2; ++fa) {
-    float acc = 0.0f;
+    for (int fa = 0; fa < 2; ++fa) {
+      float acc = 0.0f;
+      const size_t srow = ((size_t)bh * 128 + fF[fa]) * 128 + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const size_t off = ((size_t)bh * 128 + fF[fa]) * 128 + 32 * s + 8 * g + 4 * dt;
-        if (p.dstate_in) *(f32x4 *)(p.dstate_in + off) = GT[fa][s][dt];
-        if (p.state_in) acc += dot4f(GT[fa][s][dt], *(const f32x4 *)(p.state_in + off));
-      }
-    acc = grp_sum(acc);
-    if (g == 0) p.xs[((size_t)p.BH + bh) * 128 + fF[fa]] = acc;
+        for (int dt = 0; dt < 2; ++dt) {
+          const size_t off = srow + 32 * s + 4 * dt;
+          if (p.dstate_in) *(f32x4 *)(p.dstate_in + off) = GT[fa][s][dt];
+          if (p.state_in) acc += dot4f(GT[fa][s][dt], *(const f32x4 *)(p.state_in + off));
+        }
+      acc = grp_sum(acc);
+      if (g == 0) p.xs[((size_t)p.BH + bh) * 128 + fF[fa]] = acc;
+    }
   }
 }
 
-// Both walks in one launch: the reverse walks (4 a head) first, then the
-// forward walks (8 a head); one wave each.
-__global__ __launch_bounds__(64) void bwd_walk_kernel(WalkParams p) {
-  const int nrev = 4 * p.BH;
-  if ((int)blockIdx.x < nrev)
-    rev_walk(p, (int)blockIdx.x);
-  else
-    fwd_walk(p, (int)blockIdx.x - nrev);
+// Blocks of four waves: the reverse walks (one block a head and segment) first,
+// then the forward walks (two blocks a head and segment).  Two waves a SIMD (a
+// few loop-invariant values spill to scratch) and 64 KiB of LDS a block.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_walk_kernel(WalkParams p) {
+  __shared__ __align__(16) char lds[2 * kPartBytes];
+  const int nrev = p.BH * p.P;
+  int blk = blockIdx.x;
+  if (blk < nrev) {
+    rev_walk(p, blk / p.P, blk % p.P, lds);
+  } else {
+    blk -= nrev;
+    const int bh = blk / (2 * p.P), r = blk - bh * 2 * p.P;
+    fwd_walk(p, bh, r >> 1, 4 * (r & 1) + (int)(threadIdx.x >> 6));
+  }
+}
+
+// segments of whole 64-token tiles, at most about kWalkWaves pass-2 waves in all
+int walk_segments(int BH, int L, int *seg16) {
+  const int nt64 = (L + 63) / 64;
+  if (nt64 == 0 || BH <= 0) {
+    *seg16 = 4;
+    return 1;
+  }
+  const int want = std::max(1, std::min(nt64, kWalkWaves / (12 * BH)));
+  const int seg64 = (nt64 + want - 1) / want;
+  *seg16 = 4 * seg64;
+  return (nt64 + seg64 - 1) / seg64;
 }
 
 }  // namespace
 
-bool bwd_walk_supported(int f, int dv, bool bf16) { return bf16 && f == 128 && dv == 128; }
+bool bwd_walk_supported(int f, int dv, int L, bool bf16) { return bf16 && f == 128 && dv == 128 && L < (1 << 22); }
+
+size_t bwd_walk_ws_floats(int BH, int L) {
+  int seg16 = 0;
+  const size_t P = (size_t)walk_segments(BH, L, &seg16);
+  return (size_t)BH * P * (2 * 128 * 128 + 128);
+}
 
 hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream) {
   WalkParams p;
-  p.pq = a.pq; p.pk = a.pk; p.gam = a.gam; p.v = (const bf16 *)a.v; p.dout = (const bf16 *)a.dout;
+  p.pq = a.pq; p.pk = a.pk; p.gb = a.gb; p.v = (const bf16 *)a.v; p.dout = (const bf16 *)a.dout;
   p.state_in = a.state_in; p.dstate_out = a.dstate_out;
   p.dpq = a.dpq; p.dpk = a.dpk; p.dvg = a.dvg; p.tq = a.tq; p.tk = a.tk; p.xs = a.xs; p.dstate_in = a.dstate_in;
   p.BH = a.BH; p.L = a.L; p.nft = a.nft;
   if (p.BH == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_walk_kernel, dim3((unsigned)(12 * p.BH)), dim3(64), 0, stream, p);
+  p.P = walk_segments(p.BH, p.L, &p.seg);
+  const size_t nst = (size_t)p.BH * p.P * 128 * 128;
+  p.sloc = a.ws;
+  p.gloc = a.ws + nst;
+  p.dseg = a.ws + 2 * nst;
+  if (p.P > 1) {
+    hipLaunchKernelGGL(bwd_walk_state_kernel, dim3((unsigned)(4 * p.BH * (p.P - 1))), dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_walk_kernel, dim3((unsigned)(3 * p.BH * p.P)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -102,20 +102,22 @@ bool bwd_window_mfma_supported(int d, int dv, int window, int n_meta, bool bf16)
 hipError_t launch_bwd_window_mfma(const WinBwdArgs &a, hipStream_t stream);
 
 // State walks of the gated part's backward on the matrix cores (bwd_walk.hip):
-// bf16 values, f = d_v = 128.  From the prologue's fp32 feature maps and gates
-// [B H L][128] it writes dphiq, dphik ([B H L][128], complete sums), the dv
-// parts of the four 32-feature groups ([4][B H L][128]), the 64-token tile sums
-// of phiq . dphiq and phik . dphik ([B H][tiles][128]), S_{L-1} . dS_final and
-// Gamma_0 (S_in . dS_0) ([2][B H][128]) and dS_in.
+// bf16 values, f = d_v = 128.  From the prologue's fp32 feature maps and the
+// in-tile cumsum b of the floored log-gate ([B H L][128], 16-token tiles) it
+// writes dphiq, dphik and dv of the gated part ([B H L][128], complete sums),
+// the 64-token tile sums of phiq . dphiq and phik . dphik ([B H][tiles][128]),
+// S_{L-1} . dS_final and Gamma_0 (S_in . dS_0) ([2][B H][128]) and dS_in.  ws
+// holds bwd_walk_ws_floats(B H, L) floats of segment states.
 struct WalkArgs {
-  const float *pq = nullptr, *pk = nullptr, *gam = nullptr;
+  const float *pq = nullptr, *pk = nullptr, *gb = nullptr;
   const void *v = nullptr, *dout = nullptr;
   const float *state_in = nullptr, *dstate_out = nullptr;
   float *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *tq = nullptr, *tk = nullptr, *xs = nullptr;
-  float *dstate_in = nullptr;
+  float *dstate_in = nullptr, *ws = nullptr;
   int BH = 0, L = 0, nft = 0;
 };
-bool bwd_walk_supported(int f, int dv, bool bf16);
+bool bwd_walk_supported(int f, int dv, int L, bool bf16);
+size_t bwd_walk_ws_floats(int BH, int L);
 hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream);
 
 // Gated delta rule (token-recurrent prefill, bandwidth-bound decode step):
