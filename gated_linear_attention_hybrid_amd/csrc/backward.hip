@@ -100,6 +100,7 @@ struct BwdParams {
   // gam holds the in-tile cumsum of the floored log-gate over 16-token tiles
   // (the tile walks) instead of Gamma (the token sweeps)
   int gam_cum;
+  int nwp;  // dW partials per head (wqp, wkp)
 };
 
 // ---------------------------------------------------------------------------
@@ -1256,14 +1257,14 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
     constexpr int kRG = 16;
     float acc = 0.0f;
     for (int b = 0; b < p.B; ++b) {
-      const float *row = src + ((size_t)b * p.H + h) * p.nft * per + r;
-      for (int t0 = 0; t0 < p.nft; t0 += kRG) {
+      const float *row = src + ((size_t)b * p.H + h) * p.nwp * per + r;
+      for (int t0 = 0; t0 < p.nwp; t0 += kRG) {
         float x[kRG];
 #pragma unroll
-        for (int u = 0; u < kRG; ++u) x[u] = row[(size_t)min(t0 + u, p.nft - 1) * per];
+        for (int u = 0; u < kRG; ++u) x[u] = row[(size_t)min(t0 + u, p.nwp - 1) * per];
 #pragma unroll
         for (int u = 0; u < kRG; ++u)
-          if (t0 + u < p.nft) acc += x[u];
+          if (t0 + u < p.nwp) acc += x[u];
       }
     }
     (m ? p.dwk : p.dwq)[e] = acc;
@@ -1384,7 +1385,14 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.window = a.window; p.n_meta = a.n_meta;
   p.nsl = (int)sweep_slices(a, parts); p.nw = (int)row_parts(a, parts);
   p.gam_cum = use_walk(a, parts) ? 1 : 0;
+  const bool feat_mfma = (parts & PART_GLA) && use_walk(a, parts) &&
+                         bwd_feat_mfma_supported(a.d, a.f, a.dv, a.L, a.gate_mode, a.bf16);
   p.nft = (a.L + kFeatTok - 1) / kFeatTok; p.nsb = (a.L + kSwaTok - 1) / kSwaTok;
+  // dW partials: one a block of the matrix-core per-token kernel, else one a
+  // 64-token tile
+  p.nwp = feat_mfma ? (int)(((a.L + 15) / 16 + bwd_feat_span((int)(a.B * a.H), a.L) - 1) /
+                            bwd_feat_span((int)(a.B * a.H), a.L))
+                    : p.nft;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
   p.gla = (parts & PART_GLA) != 0; p.swa = (parts & PART_SWA) != 0;
@@ -1471,7 +1479,15 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     if ((e = hipStreamWaitEvent(a.stream, ss->join, 0)) != hipSuccess) return e;
     lock.unlock();
   }
-  if (a.L > 0 && BH > 0) {
+  if (a.L > 0 && BH > 0 && feat_mfma) {
+    FeatArgs fa;
+    fa.q = a.q; fa.k = a.k; fa.gate = a.gate; fa.wq = a.wq; fa.wk = a.wk;
+    fa.pq = p.pq; fa.pk = p.pk; fa.dpq = p.dpq; fa.dpk = p.dpk; fa.dvg = p.dvg; fa.ta = p.ta;
+    if (p.swa) { fa.dqs = p.dqs; fa.dks = p.dks; fa.dvs = p.dvs; }
+    fa.dq = g.dq; fa.dk = g.dk; fa.dv = g.dv; fa.dg = g.dgate; fa.wqp = p.wqp; fa.wkp = p.wkp;
+    fa.BH = (int)BH; fa.H = a.H; fa.L = a.L; fa.nft = p.nft; fa.gate_is_log = a.gate_is_log;
+    if ((e = launch_bwd_feat_mfma(fa, a.stream)) != hipSuccess) return e;
+  } else if (a.L > 0 && BH > 0) {
     if (p.gla && p.swa)
       hipLaunchKernelGGL((bwd_feature_kernel<T, true, true>), dim3(BH * p.nft), block, 0, a.stream, p);
     else if (p.gla)

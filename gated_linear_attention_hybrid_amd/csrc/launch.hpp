@@ -120,6 +120,25 @@ bool bwd_walk_supported(int f, int dv, int L, bool bf16);
 size_t bwd_walk_ws_floats(int BH, int L);
 hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream);
 
+// Per-token part of the backward on the matrix cores (bwd_feat.hip): bf16,
+// d = f = d_v = 128, one gate per feature.  From the feature maps and their
+// gradients (fp32 [B H L][128]), the gated part's dv, d log Gamma at every
+// 64-token tile's first token and the window part's dq, dk, dv (or null), it
+// writes dq, dk, dv, the gate gradient and one dW partial per block
+// ([B H][blocks][128][64], blocks = ceil(ceil(L / 16) / bwd_feat_span)).
+struct FeatArgs {
+  const void *q = nullptr, *k = nullptr, *gate = nullptr, *wq = nullptr, *wk = nullptr;
+  const float *pq = nullptr, *pk = nullptr, *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *ta = nullptr;
+  const float *dqs = nullptr, *dks = nullptr, *dvs = nullptr;
+  void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
+  float *wqp = nullptr, *wkp = nullptr;
+  int BH = 0, H = 0, L = 0, nft = 0;
+  bool gate_is_log = false;
+};
+bool bwd_feat_mfma_supported(int d, int f, int dv, int L, int gate_mode, bool bf16);
+int bwd_feat_span(int BH, int L);
+hipError_t launch_bwd_feat_mfma(const FeatArgs &a, hipStream_t stream);
+
 // Gated delta rule (token-recurrent prefill, bandwidth-bound decode step):
 // q, k [B][H][L][d], v and o [B][H][L][dv], log-decay (gate) and beta [B][H][L],
 // state [B][H][dv][d] fp32.
