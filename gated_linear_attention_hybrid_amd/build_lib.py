@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libglahybrid.so")
 ARCH = "gfx950"
 
 SOURCES = ["capi.cpp", "recurrent.hip", "chunked.hip", "chunk_out.hip", "decode.hip", "backward.hip", "delta.hip", "serving.hip", "swa_wide.hip", "delta_chunk.hip", "bwd_window.hip",
-           "bwd_walk.hip", "bwd_feat.hip"]
+           "bwd_walk.hip", "bwd_feat.hip",
+           "bwd_prep.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU
 # instructions (ordinary float code is used everywhere instead).

@@ -1445,7 +1445,13 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
       if (!launched()) return e;
     }
   }
-  if (p.gla && a.L > 0) {
+  if (p.gla && a.L > 0 && use_walk(a, parts) && bwd_prep_mfma_supported(a.d, a.f, a.L, a.bf16)) {
+    PrepArgs pa;
+    pa.q = a.q; pa.k = a.k; pa.gate = a.gate; pa.wq = a.wq; pa.wk = a.wk;
+    pa.pq = p.pq; pa.pk = p.pk; pa.gb = p.gam;
+    pa.BH = (int)BH; pa.H = a.H; pa.L = a.L; pa.gate_mode = a.gate_mode; pa.gate_is_log = a.gate_is_log;
+    if ((e = launch_bwd_prep_mfma(pa, a.stream)) != hipSuccess) return e;
+  } else if (p.gla && a.L > 0) {
     if (a.f / 2 % 4 == 0) {
       const unsigned ntl = (unsigned)((a.L + kPrepTile - 1) / kPrepTile);
       hipLaunchKernelGGL(bwd_prep_tile_kernel<T>, dim3(BH * ntl), block, 0, a.stream, p);

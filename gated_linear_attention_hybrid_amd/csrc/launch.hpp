@@ -139,6 +139,18 @@ bool bwd_feat_mfma_supported(int d, int f, int dv, int L, int gate_mode, bool bf
 int bwd_feat_span(int BH, int L);
 hipError_t launch_bwd_feat_mfma(const FeatArgs &a, hipStream_t stream);
 
+// Backward prologue on the matrix cores (bwd_prep.hip): bf16, d = f = 128.
+// Writes phi(q), phi(k) and the in-tile cumsum of the floored log-gate (fp32
+// [B H L][128], 16-token tiles) for the tile walks.
+struct PrepArgs {
+  const void *q = nullptr, *k = nullptr, *gate = nullptr, *wq = nullptr, *wk = nullptr;
+  float *pq = nullptr, *pk = nullptr, *gb = nullptr;
+  int BH = 0, H = 0, L = 0, gate_mode = 0;
+  bool gate_is_log = false;
+};
+bool bwd_prep_mfma_supported(int d, int f, int L, bool bf16);
+hipError_t launch_bwd_prep_mfma(const PrepArgs &a, hipStream_t stream);
+
 // Gated delta rule (token-recurrent prefill, bandwidth-bound decode step):
 // q, k [B][H][L][d], v and o [B][H][L][dv], log-decay (gate) and beta [B][H][L],
 // state [B][H][dv][d] fp32.
