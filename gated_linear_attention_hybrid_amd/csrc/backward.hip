@@ -92,7 +92,7 @@ struct BwdParams {
   float *dvs;                 // [N][dv]
   float *wqp, *wkp;           // [BH][nft][d][f2]
   float *gp;                  // [BH][nft]
-  float *mp;                  // [BH][nsb][n_meta]
+  float *mp;                  // [BH][nmp][n_meta]
   int B, H, L, d, dv, f, f2, lf2, window, n_meta;
   int nsl, nw, nft, nsb, npt;
   float scale;
@@ -101,6 +101,7 @@ struct BwdParams {
   // (the tile walks) instead of Gamma (the token sweeps)
   int gam_cum;
   int nwp;  // dW partials per head (wqp, wkp)
+  int nmp;  // sink-gradient partials per head (mp)
 };
 
 // ---------------------------------------------------------------------------
@@ -920,7 +921,7 @@ __global__ __launch_bounds__(kBT) void bwd_swa_q_kernel(BwdParams p) {
     if (tid < p.n_meta) {
       float s = 0.0f;
       for (int w = 0; w < kBT / 64; ++w) s += MR[w][tid];
-      p.mp[((size_t)bh * p.nsb + blk) * p.n_meta + tid] = s;
+      p.mp[((size_t)bh * p.nmp + blk) * p.n_meta + tid] = s;
     }
   }
 }
@@ -1172,7 +1173,7 @@ __global__ __launch_bounds__(kWT) void bwd_swa_tile_q_kernel(BwdParams p) {
     float acc = 0.0f;
     if (sub == 0)
       for (int r = 0; r < kWT / 16; ++r) acc += S.mp[r][m];
-    if (blk < p.nsb) p.mp[(bh * p.nsb + blk) * p.n_meta + m] = acc;
+    if (blk < p.nmp) p.mp[(bh * p.nmp + blk) * p.n_meta + m] = acc;
   }
 }
 
@@ -1241,45 +1242,64 @@ __global__ __launch_bounds__(kWT) void bwd_swa_tile_kv_kernel(BwdParams p) {
 // Sums of the per-block partials over batch rows and token blocks: dWphi_q,
 // dWphi_k [H][d][f/2], the sink gradients [H][n_meta] and, for a per-head
 // gate, its gradient [H].  Fixed order, one output per thread.
+// Sums of the per-block partials, each in a fixed order: blocks [0, nwb) take
+// four consecutive elements of dWphi_q / dWphi_k a thread; then one block per
+// head sums its sink-gradient partials (thread (part, sink) over every fourth
+// partial, the four parts added in LDS); a last block sums the per-head gate
+// gradient (one gate per head).
 template <class T>
 __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
-  const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
-  const size_t per = (size_t)p.d * p.f2;
-  const size_t nwt = p.gla ? (size_t)p.H * per : 0;
-  const size_t nm = p.swa ? (size_t)p.H * p.n_meta : 0;
-  const size_t ng = (p.gla && p.gate_mode == 2) ? (size_t)p.H : 0;
-  if (idx < 2 * nwt) {
-    const int m = idx >= nwt;
-    const size_t e = idx - m * nwt, h = e / per, r = e - h * per;
+  const size_t per = (size_t)p.d * p.f2;  // a multiple of 4 (d is)
+  const size_t nw4 = p.gla ? 2 * (size_t)p.H * per / 4 : 0;
+  const size_t nwb = (nw4 + kBT - 1) / kBT;
+  const size_t nmb = (p.swa && p.n_meta > 0) ? (size_t)p.H : 0;
+  constexpr int kRG = 16;  // partials loaded (clamped, masked) before they are added
+  if (blockIdx.x < nwb) {
+    const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
+    if (idx >= nw4) return;
+    const size_t nwt = (size_t)p.H * per, e4 = 4 * idx;
+    const int m = e4 >= nwt;
+    const size_t e = e4 - m * nwt, h = e / per, r = e - h * per;
     const float *src = m ? p.wkp : p.wqp;
-    // the partials of kRG tiles load (clamped, masked) before they are added, in
-    // the same order as one tile at a time
-    constexpr int kRG = 16;
-    float acc = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int b = 0; b < p.B; ++b) {
       const float *row = src + ((size_t)b * p.H + h) * p.nwp * per + r;
       for (int t0 = 0; t0 < p.nwp; t0 += kRG) {
-        float x[kRG];
+        f32x4 x[kRG];
 #pragma unroll
-        for (int u = 0; u < kRG; ++u) x[u] = row[(size_t)min(t0 + u, p.nwp - 1) * per];
+        for (int u = 0; u < kRG; ++u) x[u] = *(const f32x4 *)(row + (size_t)min(t0 + u, p.nwp - 1) * per);
 #pragma unroll
         for (int u = 0; u < kRG; ++u)
           if (t0 + u < p.nwp) acc += x[u];
       }
     }
-    (m ? p.dwk : p.dwq)[e] = acc;
-  } else if (idx < 2 * nwt + nm) {
-    const size_t e = idx - 2 * nwt, h = e / p.n_meta, mm = e - h * p.n_meta;
+    *(f32x4 *)((m ? p.dwk : p.dwq) + e) = acc;
+  } else if (blockIdx.x < nwb + nmb) {
+    __shared__ float part[kBT / 64][64];
+    const int h = (int)(blockIdx.x - nwb), mm = threadIdx.x & 63, pt = threadIdx.x >> 6;
+    const int mmc = min(mm, max(p.n_meta - 1, 0));
     float acc = 0.0f;
-    for (int b = 0; b < p.B; ++b)
-      for (int bl = 0; bl < p.nsb; ++bl) acc += p.mp[(((size_t)b * p.H + h) * p.nsb + bl) * p.n_meta + mm];
-    p.dmeta[e] = acc;
-  } else if (idx < 2 * nwt + nm + ng) {
-    const size_t h = idx - 2 * nwt - nm;
-    float acc = 0.0f;
-    for (int b = 0; b < p.B; ++b)
-      for (int tl = 0; tl < p.nft; ++tl) acc += p.gp[((size_t)b * p.H + h) * p.nft + tl];
-    ((T *)p.gg)[h] = from_f32<T>(acc);
+    for (int b = 0; b < p.B; ++b) {
+      const float *col = p.mp + ((size_t)b * p.H + h) * p.nmp * p.n_meta + mmc;
+      for (int t0 = pt; t0 < p.nmp; t0 += 4 * kRG) {
+        float x[kRG];
+#pragma unroll
+        for (int u = 0; u < kRG; ++u) x[u] = col[(size_t)min(t0 + 4 * u, p.nmp - 1) * p.n_meta];
+#pragma unroll
+        for (int u = 0; u < kRG; ++u)
+          if (t0 + 4 * u < p.nmp) acc += x[u];
+      }
+    }
+    part[pt][mm] = acc;
+    __syncthreads();
+    if (pt == 0 && mm < p.n_meta) p.dmeta[(size_t)h * p.n_meta + mm] = ((part[0][mm] + part[1][mm]) + part[2][mm]) + part[3][mm];
+  } else {
+    for (int h = threadIdx.x; h < p.H; h += kBT) {
+      float acc = 0.0f;
+      for (int b = 0; b < p.B; ++b)
+        for (int tl = 0; tl < p.nft; ++tl) acc += p.gp[((size_t)b * p.H + h) * p.nft + tl];
+      ((T *)p.gg)[h] = from_f32<T>(acc);
+    }
   }
 }
 
@@ -1393,6 +1413,10 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.nwp = feat_mfma ? (int)(((a.L + 15) / 16 + bwd_feat_span((int)(a.B * a.H), a.L) - 1) /
                             bwd_feat_span((int)(a.B * a.H), a.L))
                     : p.nft;
+  // the matrix-core window kernels leave one sink partial a 64-token chunk,
+  // the others one a 16-token block
+  const bool win_mfma = (parts & PART_SWA) && bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, a.bf16);
+  p.nmp = win_mfma ? (a.L + 63) / 64 : p.nsb;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
   p.gla = (parts & PART_GLA) != 0; p.swa = (parts & PART_SWA) != 0;
@@ -1417,11 +1441,11 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   }
   if (p.swa && a.L > 0) {
-    if (bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, std::is_same<T, bf16>::value)) {
+    if (win_mfma) {
       WinBwdArgs wa;
       wa.q = a.q; wa.k = a.k; wa.v = a.v; wa.dout = g.dout; wa.meta = a.meta;
       wa.lse = p.lse; wa.del = p.del; wa.dq = p.dqs; wa.dk = p.dks; wa.dv = p.dvs; wa.mp = p.mp;
-      wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta; wa.nsb = p.nsb;
+      wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta; wa.nsb = p.nmp;
       wa.scale = a.scale;
       if ((e = launch_bwd_window_mfma(wa, wstream)) != hipSuccess) return e;
     } else if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
@@ -1502,10 +1526,10 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
       hipLaunchKernelGGL((bwd_feature_kernel<T, false, true>), dim3(BH * p.nft), block, 0, a.stream, p);
     if (!launched()) return e;
   }
-  const size_t nred = (p.gla ? 2 * (size_t)a.H * a.d * p.f2 : 0) + (p.swa ? (size_t)a.H * a.n_meta : 0) +
-                      ((p.gla && a.gate_mode == 2) ? (size_t)a.H : 0);
+  const size_t nwb = p.gla ? (2 * (size_t)a.H * a.d * p.f2 / 4 + kBT - 1) / kBT : 0;
+  const size_t nred = nwb + ((p.swa && a.n_meta > 0) ? (size_t)a.H : 0) + ((p.gla && a.gate_mode == 2) ? 1 : 0);
   if (nred) {
-    hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3((unsigned)((nred + kBT - 1) / kBT)), block, 0, a.stream, p);
+    hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3((unsigned)nred), block, 0, a.stream, p);
     if (!launched()) return e;
   }
   return e;

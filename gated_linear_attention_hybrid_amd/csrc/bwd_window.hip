@@ -221,14 +221,12 @@ __global__ __launch_bounds__(kWNT) void bwd_win_q_kernel(WinBwdQ p) {
       if (live) *(f32x4 *)(p.dq + orow + dcol(s, dt)) = acc * p.scale;
     }
   __syncthreads();
-  // the chunk's sink gradient goes to its first 16-token block, zeros to the
-  // others (the reduction sums every block in a fixed order)
-  if (tid < p.n_meta * 4) {
-    const int m = tid % p.n_meta, sub = tid / p.n_meta, blk = c * 4 + sub;
+  // the chunk's sink gradient (the four waves' parts in a fixed order): one
+  // partial a chunk (nsb = chunks)
+  if (tid < p.n_meta) {
     float acc = 0.0f;
-    if (sub == 0)
-      for (int ww = 0; ww < 4; ++ww) acc += ((const float *)(smem + LD::MP))[ww * 64 + m];
-    if (blk < p.nsb) p.mp[(bh * p.nsb + blk) * p.n_meta + m] = acc;
+    for (int ww = 0; ww < 4; ++ww) acc += ((const float *)(smem + LD::MP))[ww * 64 + tid];
+    p.mp[(bh * p.nsb + c) * p.n_meta + tid] = acc;
   }
 }
 

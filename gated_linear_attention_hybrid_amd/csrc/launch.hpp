@@ -90,7 +90,8 @@ hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 // Window part of the backward on the matrix cores (bwd_window.hip): bf16,
 // d = d_v = 128, window <= 64, n_meta <= 64.  Writes the window part's dq, dk,
 // dv (fp32 [B][H][L][128]), the per-query lse and D = dO . o_swa (fp32
-// [B][H][L]) and the sink-gradient partials of every 16-token block.
+// [B][H][L]) and the sink-gradient partial of every 64-token chunk ([B H][nsb]
+// [n_meta], nsb = chunks).
 struct WinBwdArgs {
   const void *q = nullptr, *k = nullptr, *v = nullptr, *dout = nullptr;
   const float *meta = nullptr;
