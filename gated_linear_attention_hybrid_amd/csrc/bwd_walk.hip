@@ -57,6 +57,12 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 constexpr int kWalkWaves = 2048;  // pass-2 waves the segment count aims at
+// Each state is kept as e^{c} X with c the log-decay gathered since it was last
+// written out in full, per feature: the tile's decay then scales the update's
+// four map values instead of the state's 64 per lane.  Once c would fall
+// below -kReref the state is rescaled and c restarts at 0, so the map factors
+// e^{-c} stay below e^{kReref}.
+constexpr float kReref = 40.0f;
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
@@ -147,33 +153,41 @@ __device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, 
     lB = load_total(rb, tau, f, L);
   };
   load(t0);
-  float dsum = 0.0f;
+  float dsum = 0.0f, c = 0.0f;  // the state is e^{c} S
   for (int tau = t0; tau < t1; ++tau) {
     bf16x8 cv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) cv[s] = xv[s];
+    const float B = lB, cn = c + B;
+    const bool full = __any(cn < -kReref);
+    const float ks = full ? 0.0f : -cn;
     f32x4 kh;
-    const float B = lB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kh[r] = lk[r] * ex(B - lb[r]);
+    for (int r = 0; r < 4; ++r) kh[r] = lk[r] * ex(B - lb[r] + ks);
     load(min(tau + 1, t1 - 1));
-    const float eB = ex(B);
     dsum += B;
     bf16x4 khh, khl;
     split4(kh, khh, khl);
+    if (full) {
+      const float e = ex(cn);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) S[s][0] *= e, S[s][1] *= e;
+    }
+    c = full ? 0.0f : cn;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
-        S[s][dt] = mma16(vt, khl, mma16(vt, khh, S[s][dt] * eB));
+        S[s][dt] = mma16(vt, khl, mma16(vt, khh, S[s][dt]));
       }
   }
   const size_t base = ((size_t)bh * p.P + seg) * 128 + f;
+  const float e = ex(c);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt) = S[s][dt];
+    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt) = S[s][dt] * e;
   if (g == 0) p.dseg[base] = dsum;
 }
 
@@ -196,33 +210,41 @@ __device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, 
     lB = load_total(rb, tau, f, L);
   };
   load(t1 - 1);
-  float dsum = 0.0f;
+  float dsum = 0.0f, c = 0.0f;  // the gradient is e^{c} G
   for (int tau = t1 - 1; tau >= t0; --tau) {
     bf16x8 co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) co[s] = xo[s];
+    const float B = lB, cn = c + B;
+    const bool full = __any(cn < -kReref);
+    const float qs = full ? 0.0f : -cn;
     f32x4 qb;
-    const float B = lB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) qb[r] = lq[r] * ex(lb[r]);
+    for (int r = 0; r < 4; ++r) qb[r] = lq[r] * ex(lb[r] + qs);
     load(max(tau - 1, t0));
-    const float eB = ex(B);
     dsum += B;
     bf16x4 qh, ql;
     split4(qb, qh, ql);
+    if (full) {
+      const float e = ex(cn);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) G[s][0] *= e, G[s][1] *= e;
+    }
+    c = full ? 0.0f : cn;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const bf16x4 ot = pack4(mfma(co[s], sel[dt], zf4()));
-        G[s][dt] = mma16(ot, ql, mma16(ot, qh, G[s][dt] * eB));
+        G[s][dt] = mma16(ot, ql, mma16(ot, qh, G[s][dt]));
       }
   }
   const size_t base = ((size_t)bh * p.P + seg) * 128 + f;
+  const float e = ex(c);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.gloc + base * 128 + 32 * s + 8 * g + 4 * dt) = G[s][dt];
+    for (int dt = 0; dt < 2; ++dt) *(f32x4 *)(p.gloc + base * 128 + 32 * s + 8 * g + 4 * dt) = G[s][dt] * e;
   if (g == 0 && seg == p.P - 1) p.dseg[base] = dsum;
 }
 
@@ -279,7 +301,7 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
     lB = load_total(rb, tau, f, L);
   };
   if (t1 > t0) load(t0);
-  float tqa = 0.0f;
+  float tqa = 0.0f, c = 0.0f;  // the state is e^{c} ST
   for (int tau = t0; tau < t1; ++tau) {
     bf16x8 cv[4], co[4];
 #pragma unroll
@@ -287,18 +309,19 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
       cv[s] = xv[s];
       co[s] = xo[s];
     }
-    const float B = lB, mid = 0.5f * B;
+    const float B = lB, mid = 0.5f * B, cn = c + B;
+    const bool full = __any(cn < -kReref);
+    const float ks = full ? 0.0f : -cn;
     f32x4 fq, eo, kb, ein, kh;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       fq[r] = lq[r];
       eo[r] = ex(lb[r] - mid);
       kb[r] = lk[r] * ex(mid - lb[r]);
-      ein[r] = ex(lb[r]);
-      kh[r] = lk[r] * ex(B - lb[r]);
+      ein[r] = ex(lb[r] + c);
+      kh[r] = lk[r] * ex(B - lb[r] + ks);
     }
     load(min(tau + 1, t1 - 1));
-    const float eB = ex(B);
     // M^T (column t, rows s): v_s . dO_t; kept for s <= t it is M in A form
     f32x4 mt = zf4();
 #pragma unroll
@@ -313,16 +336,16 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
     f32x4 dq = mma16(mh, kbh, zf4());
     dq = mma16(mh, kbl, dq);
     dq = mma16(ml, kbh, dq) * eo;
-    f32x4 inter = zf4();
+    f32x4 ih = zf4(), il = zf4();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x4 h0, l0, h1, l1;
       split4(ST[s][0], h0, l0);
       split4(ST[s][1], h1, l1);
-      inter = mfma(co[s], join44(h0, h1), inter);
-      inter = mfma(co[s], join44(l0, l1), inter);
+      ih = mfma(co[s], join44(h0, h1), ih);
+      il = mfma(co[s], join44(l0, l1), il);
     }
-    dq += inter * ein;
+    dq += (ih + il) * ein;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       fst(rd, foff(tau, r, f), dq[r]);
@@ -333,15 +356,21 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
       if (g == 0) p.tq[((size_t)bh * p.nft + (tau >> 2)) * 128 + f] = ssum;
       tqa = 0.0f;
     }
-    // S^T <- e^{B} S^T + V^T k-hat
+    // S^T <- e^{B} S^T + V^T k-hat (the e^{B} in c, or in a full rescale)
     bf16x4 khh, khl;
     split4(kh, khh, khl);
+    if (full) {
+      const float e = ex(cn);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ST[s][0] *= e, ST[s][1] *= e;
+    }
+    c = full ? 0.0f : cn;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
-        ST[s][dt] = mma16(vt, khl, mma16(vt, khh, ST[s][dt] * eB));
+        ST[s][dt] = mma16(vt, khl, mma16(vt, khh, ST[s][dt]));
       }
   }
   if (seg == p.P - 1 && p.dstate_out) {
@@ -350,7 +379,7 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) acc += dot4f(ST[s][dt], *(const f32x4 *)(p.dstate_out + srow + 32 * s + 4 * dt));
-    acc = grp_sum(acc);
+    acc = grp_sum(acc * ex(c));
     if (g == 0) p.xs[(size_t)bh * 128 + f] = acc;
   }
 }
@@ -411,7 +440,7 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
     }
   };
   if (t1 > t0) load(t1 - 1);
-  float tka[2] = {0.0f, 0.0f};
+  float tka[2] = {0.0f, 0.0f}, c[2] = {0.0f, 0.0f};  // the gradient is e^{c} G^T
   for (int tau = t1 - 1; tau >= t0; --tau) {
     bf16x8 cv[4], co[4];
 #pragma unroll
@@ -419,24 +448,18 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
       cv[s] = xv[s];
       co[s] = xo[s];
     }
-    // per feature half, layout F: the decayed maps
-    f32x4 fk[2], qp[2], kp[2], kh[2], qb[2], eo[2], egk[2];
-    float eB[2];
+    const float cn[2] = {c[0] + lB[0], c[1] + lB[1]};
+    const bool full = __any(cn[0] < -kReref || cn[1] < -kReref);
+    // this tile's layout-F values (the next tile's loads go into the buffers)
+    float cq[2][4], ck[2][4], cb[2][4], cB[2];
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
-      const float B = lB[fa], mid = 0.5f * B;
-      eB[fa] = ex(B);
+      cB[fa] = lB[fa];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float b = lb[fa][r], q = lq[fa][r], k = lk[fa][r];
-        const float up = ex(b - mid), dn = ex(mid - b), tail = ex(B - b);
-        fk[fa][r] = k;
-        qp[fa][r] = q * up;
-        kp[fa][r] = k * dn;
-        eo[fa][r] = dn;
-        egk[fa][r] = tail;
-        kh[fa][r] = k * tail;
-        qb[fa][r] = q * ex(b);
+        cq[fa][r] = lq[fa][r];
+        ck[fa][r] = lk[fa][r];
+        cb[fa][r] = lb[fa][r];
       }
     }
     load(max(tau - 1, t0));
@@ -449,29 +472,49 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
       if (4 * g + r < n) mm[r] = 0.0f;
     bf16x4 mmh, mml;
     split4(mm, mmh, mml);
-    // dphik per feature half (split operands)
+    // per feature half: dphik (split operands), then the decayed maps in the
+    // forms the rest of the tile takes (token rows over features for A and
+    // k-hat, split feature rows for the update); maps meeting G carry its
+    // e^{c}, the update's the e^{-c} of the new c
+    bf16x4 qrw[2], krw[2], khw[2], qbh[2], qbl[2];
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
+      const float B = cB[fa], mid = 0.5f * B, qs = full ? 0.0f : -cn[fa];
+      f32x4 qp, kp, kh, qb, eo, egk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float b = cb[fa][r], up = ex(b - mid), dn = ex(mid - b), tail = ex(B - b + c[fa]);
+        qp[r] = cq[fa][r] * up;
+        kp[r] = ck[fa][r] * dn;
+        eo[r] = dn;
+        egk[r] = tail;
+        kh[r] = ck[fa][r] * tail;
+        qb[r] = cq[fa][r] * ex(b + qs);
+      }
       bf16x4 qph, qpl;
-      split4(qp[fa], qph, qpl);
+      split4(qp, qph, qpl);
       f32x4 dk = mma16(mmh, qph, zf4());
       dk = mma16(mmh, qpl, dk);
-      dk = mma16(mml, qph, dk) * eo[fa];
-      f32x4 inter = zf4();
+      dk = mma16(mml, qph, dk) * eo;
+      f32x4 ih = zf4(), il = zf4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x4 h0, l0, h1, l1;
         split4(GT[fa][s][0], h0, l0);
         split4(GT[fa][s][1], h1, l1);
-        inter = mfma(cv[s], join44(h0, h1), inter);
-        inter = mfma(cv[s], join44(l0, l1), inter);
+        ih = mfma(cv[s], join44(h0, h1), ih);
+        il = mfma(cv[s], join44(l0, l1), il);
       }
-      dk += inter * egk[fa];
+      dk += (ih + il) * egk;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         fst(rd, foff(tau, r, fF[fa]), dk[r]);
-        tka[fa] += fk[fa][r] * dk[r];
+        tka[fa] += ck[fa][r] * dk[r];
       }
+      qrw[fa] = pack4(mma16(qph, eye, zf4()));
+      krw[fa] = to_rows(kp, eye);
+      khw[fa] = to_rows(kh, eye);
+      split4(qb, qbh[fa], qbl[fa]);
     }
     if ((tau & 3) == 0) {
 #pragma unroll
@@ -481,19 +524,14 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
         tka[fa] = 0.0f;
       }
     }
-    // token rows over this wave's features: the decayed maps of A and k-hat
-    const bf16x8 qr = join44(to_rows(qp[0], eye), to_rows(qp[1], eye));
-    const bf16x8 kr = join44(to_rows(kp[0], eye), to_rows(kp[1], eye));
-    const bf16x8 khr = join44(to_rows(kh[0], eye), to_rows(kh[1], eye));
+    const bf16x8 qr = join44(qrw[0], qrw[1]), kr = join44(krw[0], krw[1]), khr = join44(khw[0], khw[1]);
     // A (column t, rows t') over the wave's features, kept for t' >= t
     f32x4 am = mfma(qr, kr, zf4());
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * g + r < n) am[r] = 0.0f;
     const bf16x4 ab = pack4(am);
-    bf16x4 qbh[2], qbl[2];
-    split4(qb[0], qbh[0], qbl[0]);
-    split4(qb[1], qbh[1], qbl[1]);
+    const float er[2] = {full ? ex(cn[0]) : 1.0f, full ? ex(cn[1]) : 1.0f};
     const int buf = tau & 1;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -511,8 +549,13 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
         const f32x4 dvt = mfma(join44(g0, g1), khr, zf4()) + mma16(ot, ab, zf4());
         *(f32x4 *)(lds + part_off(buf, fs, s, dt)) = dvt;
 #pragma unroll
-        for (int fa = 0; fa < 2; ++fa) GT[fa][s][dt] = mma16(ot, qbl[fa], mma16(ot, qbh[fa], GT[fa][s][dt] * eB[fa]));
+        for (int fa = 0; fa < 2; ++fa) {
+          if (full) GT[fa][s][dt] *= er[fa];
+          GT[fa][s][dt] = mma16(ot, qbl[fa], mma16(ot, qbh[fa], GT[fa][s][dt]));
+        }
       }
+#pragma unroll
+    for (int fa = 0; fa < 2; ++fa) c[fa] = full ? 0.0f : cn[fa];
     __syncthreads();
     // this wave's quarter of d_v (s = fs), summed over the four waves' parts
 #pragma unroll
@@ -529,14 +572,16 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
       float acc = 0.0f;
+      const float e = ex(c[fa]);
       const size_t srow = ((size_t)bh * 128 + fF[fa]) * 128 + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const size_t off = srow + 32 * s + 4 * dt;
-          if (p.dstate_in) *(f32x4 *)(p.dstate_in + off) = GT[fa][s][dt];
-          if (p.state_in) acc += dot4f(GT[fa][s][dt], *(const f32x4 *)(p.state_in + off));
+          const f32x4 gt = GT[fa][s][dt] * e;
+          if (p.dstate_in) *(f32x4 *)(p.dstate_in + off) = gt;
+          if (p.state_in) acc += dot4f(gt, *(const f32x4 *)(p.state_in + off));
         }
       acc = grp_sum(acc);
       if (g == 0) p.xs[((size_t)p.BH + bh) * 128 + fF[fa]] = acc;
