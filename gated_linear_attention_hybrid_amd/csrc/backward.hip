@@ -102,6 +102,7 @@ struct BwdParams {
   int gam_cum;
   int nwp;  // dW partials per head (wqp, wkp)
   int nmp;  // sink-gradient partials per head (mp)
+  int win_bf16;  // dqs, dks, dvs hold bf16 (the matrix-core window kernels)
 };
 
 // ---------------------------------------------------------------------------
@@ -679,6 +680,9 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int w = 0; w < kMaxRowWaves; ++w) bdvw[w] = p.dvg + ((size_t)min(w, p.nw - 1) * N + row0) * dv;
   const float *bds = (m ? p.dks : p.dqs) + row0 * d;
   const float *bdvs = p.dvs + row0 * dv;
+  // the same rows when the window part left bf16
+  const bf16 *bds0 = (const bf16 *)(m ? p.dks : p.dqs) + row0 * d;
+  const bf16 *bdvs0 = (const bf16 *)p.dvs + row0 * dv;
   // gates: per feature (stride f), per token (stride 1) or one per head
   const T *bg = g + gate_index(p.gate_mode, bh, p.H, L, f, t0, 0);
   const unsigned gstep = p.gate_mode == 0 ? (unsigned)f : p.gate_mode == 1 ? 1u : 0u;
@@ -718,8 +722,13 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int w = 0; w < kMaxRowWaves; ++w) r.dvw[w] = 0.0f;
     }
     if constexpr (SWA) {
-      r.ds = at(bds, tl * d + mic);
-      r.dvs = at(bdvs, tl * dv + tidv);
+      if (p.win_bf16) {
+        r.ds = to_f32(at((const bf16 *)bds0, tl * d + mic));
+        r.dvs = to_f32(at((const bf16 *)bdvs0, tl * dv + tidv));
+      } else {
+        r.ds = at(bds, tl * d + mic);
+        r.dvs = at(bdvs, tl * dv + tidv);
+      }
     } else {
       r.ds = r.dvs = 0.0f;
     }
@@ -1417,6 +1426,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   // the others one a 16-token block
   const bool win_mfma = (parts & PART_SWA) && bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, a.bf16);
   p.nmp = win_mfma ? (a.L + 63) / 64 : p.nsb;
+  p.win_bf16 = win_mfma ? 1 : 0;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
   p.scale = a.scale; p.gate_is_log = a.gate_is_log ? 1 : 0; p.gate_mode = a.gate_mode;
   p.gla = (parts & PART_GLA) != 0; p.swa = (parts & PART_SWA) != 0;
@@ -1513,7 +1523,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
     FeatArgs fa;
     fa.q = a.q; fa.k = a.k; fa.gate = a.gate; fa.wq = a.wq; fa.wk = a.wk;
     fa.pq = p.pq; fa.pk = p.pk; fa.dpq = p.dpq; fa.dpk = p.dpk; fa.dvg = p.dvg; fa.ta = p.ta;
-    if (p.swa) { fa.dqs = p.dqs; fa.dks = p.dks; fa.dvs = p.dvs; }
+    if (p.swa) { fa.dqs = p.dqs; fa.dks = p.dks; fa.dvs = p.dvs; fa.win_bf16 = p.win_bf16 != 0; }
     fa.dq = g.dq; fa.dk = g.dk; fa.dv = g.dv; fa.dg = g.dgate; fa.wqp = p.wqp; fa.wkp = p.wkp;
     fa.BH = (int)BH; fa.H = a.H; fa.L = a.L; fa.nft = p.nft; fa.gate_is_log = a.gate_is_log;
     if ((e = launch_bwd_feat_mfma(fa, a.stream)) != hipSuccess) return e;

@@ -2,7 +2,8 @@
 // matrix cores: bf16, d = f = d_v = 128, one gate per feature.
 //
 // From the feature maps phi (the prologue's fp32 [B H L][128]), their gradients
-// dphi (the state walks) and the window part's dq, dk, dv (fp32, or none):
+// dphi (the state walks) and the window part's dq, dk, dv (bf16 or fp32, or
+// none):
 //   Hedgehog map ("Lizard" technical summary, gist.science 2507.09025,
 //   Methodology A.1): phi = [softmax(u), softmax(-u)], u = x W (W [d][f/2]).
 //   The gradient of u is du = phi+ (dphi+ - phi+ . dphi+) - phi- (dphi- -
@@ -80,7 +81,7 @@ __device__ __forceinline__ void st8h(__amdgpu_buffer_rsrc_t r, unsigned off, bf1
 struct FeatParams {
   const bf16 *q, *k, *gate, *wq, *wk;
   const float *pq, *pk, *dpq, *dpk, *dvg, *ta;  // [B H L][128] x 5, [B H][tiles][128]
-  const float *dqs, *dks, *dvs;                 // window part [B H L][128] or null
+  const void *dqs, *dks, *dvs;                  // window part [B H L][128] (bf16 or fp32) or null
   bf16 *dq, *dk, *dv, *dg;
   float *wqp, *wkp;                             // [B H][blocks][128][64]
   int H, L, nft, span, nblk, gate_is_log;       // span: 16-token sub-tiles a block (a multiple of 4)
@@ -93,7 +94,7 @@ __device__ __forceinline__ unsigned slot_off(int buf, int m, int hf, int i) {
   return (unsigned)((((buf * 2 + m) * 2 + hf) * 4 + i) * 64 + (int)(threadIdx.x & 63)) * 16u;
 }
 
-template <bool SWA>
+template <bool SWA, bool WB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_feat_mfma_kernel(FeatParams p) {
   __shared__ __align__(16) char sdu[kSlots * 1024];
   __shared__ __align__(16) char sep[kSlots * 1024];
@@ -109,9 +110,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const __amdgpu_buffer_rsrc_t rdp = rows_rsrc(m ? p.dpk : p.dpq, row0 * 512, rowbytes);
   const __amdgpu_buffer_rsrc_t rx = rows_rsrc(m ? p.k : p.q, row0 * 256, hrowbytes);
   const __amdgpu_buffer_rsrc_t rdx = rows_rsrc(m ? p.dk : p.dq, row0 * 256, hrowbytes);
-  const __amdgpu_buffer_rsrc_t rsx = rows_rsrc(SWA ? (m ? p.dks : p.dqs) : p.pq, row0 * 512, rowbytes);
+  // the window part's rows: bf16 (WB) or fp32
+  constexpr unsigned kWs = WB ? 2u : 4u;
+  const __amdgpu_buffer_rsrc_t rsx = rows_rsrc(SWA ? (m ? p.dks : p.dqs) : p.pq, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
   const __amdgpu_buffer_rsrc_t rvg = rows_rsrc(p.dvg, row0 * 512, rowbytes);
-  const __amdgpu_buffer_rsrc_t rvs = rows_rsrc(SWA ? p.dvs : p.dvg, row0 * 512, rowbytes);
+  const __amdgpu_buffer_rsrc_t rvs = rows_rsrc(SWA ? p.dvs : p.dvg, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
+  // four window-part values at element offset e of token row tok
+  auto wld4 = [&](__amdgpu_buffer_rsrc_t r, unsigned tok, unsigned e) -> f32x4 {
+    if constexpr (WB) {
+      const bf16x4 h = ld4h(r, tok * 256u + e * 2u);
+      return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+      return ld4f(r, tok * 512u + e * 4u);
+    }
+  };
   const __amdgpu_buffer_rsrc_t rdv = rows_rsrc(p.dv, row0 * 256, hrowbytes);
   const __amdgpu_buffer_rsrc_t rg = rows_rsrc(p.gate, row0 * 256, hrowbytes);
   const __amdgpu_buffer_rsrc_t rdg = rows_rsrc(p.dg, row0 * 256, hrowbytes);
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int a = 0; a < 2; ++a) {
       const unsigned off = tok * 512u + (unsigned)(32 * wave + 8 * g + 4 * a) * 4u;
       vg[a] = ld4f(rvg, off);
-      vs[a] = SWA ? ld4f(rvs, off) : zf4();
+      vs[a] = SWA ? wld4(rvs, tok, (unsigned)(32 * wave + 8 * g + 4 * a)) : zf4();
     }
     bf16x8 xv[2];
 #pragma unroll
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- phase 2: the window part's dx first (added after dW)
     f32x4 sx[4];
 #pragma unroll
-    for (int et = 0; et < 4; ++et) sx[et] = SWA ? ld4f(rsx, tok * 512u + (unsigned)(64 * hf + 16 * et + 4 * g) * 4u) : zf4();
+    for (int et = 0; et < 4; ++et) sx[et] = SWA ? wld4(rsx, tok, (unsigned)(64 * hf + 16 * et + 4 * g)) : zf4();
     // du of map m (rows over tokens), hi + lo
     bf16x4 duh[4], dul[4];
 #pragma unroll
@@ -295,10 +307,12 @@ hipError_t launch_bwd_feat_mfma(const FeatArgs &a, hipStream_t stream) {
   p.nblk = (int)(((a.L + 15) / 16 + p.span - 1) / p.span);
   if (a.BH == 0 || a.L == 0) return hipSuccess;
   const dim3 grid((unsigned)(a.BH * p.nblk)), block(256);
-  if (a.dqs)
-    hipLaunchKernelGGL(bwd_feat_mfma_kernel<true>, grid, block, 0, stream, p);
+  if (a.dqs && a.win_bf16)
+    hipLaunchKernelGGL((bwd_feat_mfma_kernel<true, true>), grid, block, 0, stream, p);
+  else if (a.dqs)
+    hipLaunchKernelGGL((bwd_feat_mfma_kernel<true, false>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(bwd_feat_mfma_kernel<false>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((bwd_feat_mfma_kernel<false, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -72,7 +72,8 @@ __device__ __forceinline__ unsigned dcol(int s, int dt) {
 struct WinBwdQ {
   const bf16 *q, *k, *v, *dout;
   const float *meta;
-  float *lse, *del, *dq, *mp;
+  float *lse, *del, *mp;
+  bf16 *dq;
   int H, L, nchunks, window, n_meta, nsb;
   float scale;
 };
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kWNT) void bwd_win_q_kernel(WinBwdQ p) {
                                            : z4;
         acc = mfma(join44(lo, hi), dsb[pp], acc);
       }
-      if (live) *(f32x4 *)(p.dq + orow + dcol(s, dt)) = acc * p.scale;
+      if (live) *(bf16x4 *)(p.dq + orow + dcol(s, dt)) = pack4(acc * p.scale);
     }
   __syncthreads();
   // the chunk's sink gradient (the four waves' parts in a fixed order): one
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kWNT) void bwd_win_q_kernel(WinBwdQ p) {
 struct WinBwdK {
   const bf16 *q, *k, *v, *dout;
   const float *lse, *del;
-  float *dk, *dv;
+  bf16 *dk, *dv;
   int L, nchunks, window;
   float scale;
 };
@@ -345,8 +346,8 @@ __global__ __launch_bounds__(kWNT) void bwd_win_k_kernel(WinBwdK p) {
         ak = mfma(join44(qlo, qhi), db[pp], ak);
       }
       if (live) {
-        *(f32x4 *)(p.dv + orow + dcol(s, dt)) = av;
-        *(f32x4 *)(p.dk + orow + dcol(s, dt)) = ak * p.scale;
+        *(bf16x4 *)(p.dv + orow + dcol(s, dt)) = pack4(av);
+        *(bf16x4 *)(p.dk + orow + dcol(s, dt)) = pack4(ak * p.scale);
       }
     }
 }
@@ -363,7 +364,7 @@ hipError_t launch_bwd_window_mfma(const WinBwdArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.B * a.H * nchunks);
   WinBwdQ pq;
   pq.q = (const bf16 *)a.q; pq.k = (const bf16 *)a.k; pq.v = (const bf16 *)a.v; pq.dout = (const bf16 *)a.dout;
-  pq.meta = a.meta; pq.lse = a.lse; pq.del = a.del; pq.dq = a.dq; pq.mp = a.mp;
+  pq.meta = a.meta; pq.lse = a.lse; pq.del = a.del; pq.dq = (bf16 *)a.dq; pq.mp = a.mp;
   pq.H = a.H; pq.L = a.L; pq.nchunks = nchunks; pq.window = a.window; pq.n_meta = a.n_meta; pq.nsb = a.nsb;
   pq.scale = a.scale;
   hipError_t e = hipFuncSetAttribute((const void *)bwd_win_q_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -373,7 +374,7 @@ hipError_t launch_bwd_window_mfma(const WinBwdArgs &a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WinBwdK pk;
   pk.q = pq.q; pk.k = pq.k; pk.v = pq.v; pk.dout = pq.dout; pk.lse = a.lse; pk.del = a.del;
-  pk.dk = a.dk; pk.dv = a.dv; pk.L = a.L; pk.nchunks = nchunks; pk.window = a.window; pk.scale = a.scale;
+  pk.dk = (bf16 *)a.dk; pk.dv = (bf16 *)a.dv; pk.L = a.L; pk.nchunks = nchunks; pk.window = a.window; pk.scale = a.scale;
   e = hipFuncSetAttribute((const void *)bwd_win_k_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LdsWinK::BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_win_k_kernel, dim3(grid), dim3(kWNT), LdsWinK::BYTES, stream, pk);

@@ -89,13 +89,14 @@ hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 
 // Window part of the backward on the matrix cores (bwd_window.hip): bf16,
 // d = d_v = 128, window <= 64, n_meta <= 64.  Writes the window part's dq, dk,
-// dv (fp32 [B][H][L][128]), the per-query lse and D = dO . o_swa (fp32
+// dv (bf16 [B][H][L][128]), the per-query lse and D = dO . o_swa (fp32
 // [B][H][L]) and the sink-gradient partial of every 64-token chunk ([B H][nsb]
 // [n_meta], nsb = chunks).
 struct WinBwdArgs {
   const void *q = nullptr, *k = nullptr, *v = nullptr, *dout = nullptr;
   const float *meta = nullptr;
-  float *lse = nullptr, *del = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *mp = nullptr;
+  float *lse = nullptr, *del = nullptr, *mp = nullptr;
+  void *dq = nullptr, *dk = nullptr, *dv = nullptr;  // bf16
   int B = 0, H = 0, L = 0, window = 0, n_meta = 0, nsb = 0;
   float scale = 1.0f;
 };
@@ -124,13 +125,15 @@ hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream);
 // Per-token part of the backward on the matrix cores (bwd_feat.hip): bf16,
 // d = f = d_v = 128, one gate per feature.  From the feature maps and their
 // gradients (fp32 [B H L][128]), the gated part's dv, d log Gamma at every
-// 64-token tile's first token and the window part's dq, dk, dv (or null), it
+// 64-token tile's first token and the window part's dq, dk, dv (bf16 when
+// win_bf16, else fp32; or null), it
 // writes dq, dk, dv, the gate gradient and one dW partial per block
 // ([B H][blocks][128][64], blocks = ceil(ceil(L / 16) / bwd_feat_span)).
 struct FeatArgs {
   const void *q = nullptr, *k = nullptr, *gate = nullptr, *wq = nullptr, *wk = nullptr;
   const float *pq = nullptr, *pk = nullptr, *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *ta = nullptr;
-  const float *dqs = nullptr, *dks = nullptr, *dvs = nullptr;
+  const void *dqs = nullptr, *dks = nullptr, *dvs = nullptr;
+  bool win_bf16 = false;
   void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
   float *wqp = nullptr, *wkp = nullptr;
   int BH = 0, H = 0, L = 0, nft = 0;
