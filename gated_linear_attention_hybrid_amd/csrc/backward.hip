@@ -1331,10 +1331,29 @@ size_t sweep_slices(const LayerArgs &a, int parts) {
 // 32 features
 size_t row_parts(const LayerArgs &a, int parts) { return use_walk(a, parts) ? 1 : (size_t)(a.f + 31) / 32; }
 
+// The per-token kernel on the matrix cores (per-feature gates, bf16, d = f =
+// d_v = 128, after the walks) and the matrix-core window kernels.
+bool use_feat_mfma(const LayerArgs &a, int parts) {
+  return use_walk(a, parts) && bwd_feat_mfma_supported(a.d, a.f, a.dv, a.L, a.gate_mode, a.bf16);
+}
+bool use_win_mfma(const LayerArgs &a, int parts) {
+  return (parts & PART_SWA) && bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, a.bf16);
+}
+// dW partials per head: one a block of the matrix-core per-token kernel, else
+// one a 64-token tile
+size_t dw_partials(const LayerArgs &a, int parts) {
+  const size_t nft = (a.L + kFeatTok - 1) / kFeatTok;
+  if (!use_feat_mfma(a, parts)) return nft;
+  const size_t span = (size_t)bwd_feat_span(a.B * a.H, a.L);
+  return ((a.L + 15) / 16 + span - 1) / span;
+}
+
 BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t BH = (size_t)a.B * a.H, N = BH * a.L;
   const size_t nsl = sweep_slices(a, parts), nw = row_parts(a, parts);
   const size_t nft = (a.L + kFeatTok - 1) / kFeatTok, nsb = (a.L + kSwaTok - 1) / kSwaTok;
+  // the window part's dq, dk, dv: bf16 from the matrix-core kernels
+  const size_t wsz = use_win_mfma(a, parts) ? 2 : 1;
   const bool gla = parts & PART_GLA, swa = parts & PART_SWA;
   BwdLayout o;
   size_t at = 0;
@@ -1347,8 +1366,9 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   o.dvg = take(gla ? nw * N * a.dv : 0);
   o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
   o.lse = take(swa ? N : 0); o.del = take(swa ? N : 0);
-  o.dqs = take(swa ? N * a.d : 0); o.dks = take(swa ? N * a.d : 0); o.dvs = take(swa ? N * a.dv : 0);
-  const size_t wp = gla ? BH * nft * a.d * (a.f / 2) : 0;
+  o.dqs = take(swa ? N * a.d / wsz : 0); o.dks = take(swa ? N * a.d / wsz : 0);
+  o.dvs = take(swa ? N * a.dv / wsz : 0);
+  const size_t wp = gla ? BH * dw_partials(a, parts) * a.d * (a.f / 2) : 0;
   o.wqp = take(wp); o.wkp = take(wp);
   o.gp = take(gla ? BH * nft : 0);
   o.mp = take(swa ? BH * nsb * a.n_meta : 0);
@@ -1414,17 +1434,12 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.window = a.window; p.n_meta = a.n_meta;
   p.nsl = (int)sweep_slices(a, parts); p.nw = (int)row_parts(a, parts);
   p.gam_cum = use_walk(a, parts) ? 1 : 0;
-  const bool feat_mfma = (parts & PART_GLA) && use_walk(a, parts) &&
-                         bwd_feat_mfma_supported(a.d, a.f, a.dv, a.L, a.gate_mode, a.bf16);
+  const bool feat_mfma = use_feat_mfma(a, parts);
   p.nft = (a.L + kFeatTok - 1) / kFeatTok; p.nsb = (a.L + kSwaTok - 1) / kSwaTok;
-  // dW partials: one a block of the matrix-core per-token kernel, else one a
-  // 64-token tile
-  p.nwp = feat_mfma ? (int)(((a.L + 15) / 16 + bwd_feat_span((int)(a.B * a.H), a.L) - 1) /
-                            bwd_feat_span((int)(a.B * a.H), a.L))
-                    : p.nft;
+  p.nwp = (int)dw_partials(a, parts);
   // the matrix-core window kernels leave one sink partial a 64-token chunk,
   // the others one a 16-token block
-  const bool win_mfma = (parts & PART_SWA) && bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, a.bf16);
+  const bool win_mfma = use_win_mfma(a, parts);
   p.nmp = win_mfma ? (a.L + 63) / 64 : p.nsb;
   p.win_bf16 = win_mfma ? 1 : 0;
   p.npt = (a.L + kPrepTok - 1) / kPrepTok;
