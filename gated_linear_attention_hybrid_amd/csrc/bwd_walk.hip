@@ -289,39 +289,44 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
       for (int dt = 0; dt < 2; ++dt)
         ST[s][dt] = ST[s][dt] * e + *(const f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt);
   }
-  bf16x8 xv[4], xo[4];
-  float lq[4], lk[4], lb[4], lB;
-  auto load = [&](int tau) {
+  // operands two tiles ahead in a ring of two fixed register sets
+  bf16x8 xv[2][4], xo[2][4];
+  float lq[2][4], lk[2][4], lb[2][4], lB[2];
+  auto load = [&](int u, int tau) {
+    tau = min(tau, t1 - 1);
     const unsigned rowb = (unsigned)(16 * tau + n) * 256;
-    load_vals(rv, rowb, xv);
-    load_vals(ro, rowb, xo);
-    load_f(rq, tau, f, lq);
-    load_f(rk, tau, f, lk);
-    load_f(rb, tau, f, lb);
-    lB = load_total(rb, tau, f, L);
+    load_vals(rv, rowb, xv[u]);
+    load_vals(ro, rowb, xo[u]);
+    load_f(rq, tau, f, lq[u]);
+    load_f(rk, tau, f, lk[u]);
+    load_f(rb, tau, f, lb[u]);
+    lB[u] = load_total(rb, tau, f, L);
   };
-  if (t1 > t0) load(t0);
+  if (t1 > t0) {
+    load(0, t0);
+    load(1, t0 + 1);
+  }
   float tqa = 0.0f, c = 0.0f;  // the state is e^{c} ST
-  for (int tau = t0; tau < t1; ++tau) {
+  auto step = [&](int u, int tau) {
     bf16x8 cv[4], co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      cv[s] = xv[s];
-      co[s] = xo[s];
+      cv[s] = xv[u][s];
+      co[s] = xo[u][s];
     }
-    const float B = lB, mid = 0.5f * B, cn = c + B;
+    const float B = lB[u], mid = 0.5f * B, cn = c + B;
     const bool full = __any(cn < -kReref);
     const float ks = full ? 0.0f : -cn;
     f32x4 fq, eo, kb, ein, kh;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      fq[r] = lq[r];
-      eo[r] = ex(lb[r] - mid);
-      kb[r] = lk[r] * ex(mid - lb[r]);
-      ein[r] = ex(lb[r] + c);
-      kh[r] = lk[r] * ex(B - lb[r] + ks);
+      fq[r] = lq[u][r];
+      eo[r] = ex(lb[u][r] - mid);
+      kb[r] = lk[u][r] * ex(mid - lb[u][r]);
+      ein[r] = ex(lb[u][r] + c);
+      kh[r] = lk[u][r] * ex(B - lb[u][r] + ks);
     }
-    load(min(tau + 1, t1 - 1));
+    load(u, tau + 2);
     // M^T (column t, rows s): v_s . dO_t; kept for s <= t it is M in A form
     f32x4 mt = zf4();
 #pragma unroll
@@ -372,6 +377,12 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
         const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
         ST[s][dt] = mma16(vt, khl, mma16(vt, khh, ST[s][dt]));
       }
+  };
+  for (int tau = t0; tau < t1;) {
+    step(0, tau);
+    if (++tau >= t1) break;
+    step(1, tau);
+    ++tau;
   }
   if (seg == p.P - 1 && p.dstate_out) {
     float acc = 0.0f;

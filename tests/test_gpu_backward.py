@@ -231,6 +231,26 @@ def test_backward_full_length_sampled_heads():
         compare(sub, ref, TOL_BF16)
 
 
+def test_backward_8k_sampled_head():
+    """8K tokens x 32 heads: five walk segments of 1664 tokens, long enough that
+    the walks' running exponents are rescaled under the workload's ordinary gates
+    (about one rescale per 800 tokens); the oracle recomputes head 7."""
+    wl = WORKLOADS["prefill_2k"].with_(L=8192, seed=1601)
+    say("backward bf16 L=8192 H=32, head 7 checked")
+    x = make_prefill(wl, DEV)
+    dO = grads_seed((wl.B, wl.H, wl.L, wl.dv), 11, wl.torch_dtype)
+    got = G.hybrid_layer_bwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], dO, window=wl.window)
+    torch.cuda.synchronize()
+    h = 7
+    hx = {k: to_f64(v[:, h:h + 1]) for k, v in x.items() if v.dim() == 4}
+    hw = {k: to_f64(x[k][h:h + 1]) for k in ("wq", "wk", "meta")}
+    ref = OB.layer_bwd(hx["q"], hx["k"], hx["v"], hx["gate"], hw["wq"], hw["wk"], hw["meta"],
+                       to_f64(dO[:, h:h + 1]), window=wl.window)
+    sub = {n: (got[n][h:h + 1] if n in ("wq", "wk", "meta") else got[n][:, h:h + 1])
+           for n in ("q", "k", "v", "gate", "wq", "wk", "meta")}
+    compare(sub, ref, TOL_BF16)
+
+
 def test_backward_graph_replays_match_eager():
     """The window part runs on the library's side stream (forked from and joined
     back into the caller's stream): captured into a graph after an eager call
