@@ -259,20 +259,6 @@ __device__ __forceinline__ void load_gates(const HeadBufs &hb, unsigned base, bf
 #pragma unroll
   for (int s = 0; s < 4; ++s) x[s] = bload(hb.g, base + 2 * feat(g, 8 * s));
 }
-// the gates of fold slots 16h .. 16h + 15 only (fragments 2h, 2h + 1 of load_gates)
-template <bool SG>
-__device__ __forceinline__ void load_gates_half(const HeadBufs &hb, unsigned base, int h, bf16x8 *x) {
-  const unsigned g = (threadIdx.x & 63) >> 4;
-  if constexpr (SG) {
-    const bf16x8 s1 = scalar_gate(hb, base);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) x[s] = s1;
-    return;
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s) x[s] = bload(hb.g, base + 2 * feat(g, 16 * h + 8 * s));
-}
-
 // Unnormalised Hedgehog exponentials of the lane's token: e[4mt + j] =
 // 2^{(u - max u) log2e} (phi+ feature 16g + 4mt + j) and e[16 + 4mt + j] =
 // 2^{(min u - u) log2e} (phi- feature 64 + 16g + 4mt + j), and the reciprocal

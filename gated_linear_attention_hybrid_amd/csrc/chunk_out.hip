@@ -21,17 +21,19 @@
 //                          chunk, with the value operands read straight from
 //                          memory; then u_k = k Wphi_k, phi(k), k~ and the
 //                          k-hat^T fragments; and, in the second phase, the gate
-//                          decay exponents of the phi- features of its tile of
-//                          the NEXT chunk
-//   query wave (w = 4..7): raw-k fragments, window scores and softmax, u_q,
-//                          phi(q), q~, q-bar, intra-chunk scores, weight
-//                          fragments; and, in the first phase, the decay
-//                          exponents of the phi+ features of the NEXT chunk
+//                          decay exponents of every feature of its tile of the
+//                          NEXT chunk
+//   query wave (w = 4..7): first phase: u_q, phi(q), q~, q-bar, the scores of
+//                          all five window bands and the softmax with the sinks
+//                          (the raw keys of a chunk are staged one chunk ahead);
+//                          second phase: the next chunk's raw keys, the
+//                          intra-chunk scores and the weight fragments
 // The decay exponents are shared through LDS, so each is computed once and
 // every wave knows the chunk-wide fold reference when a chunk starts.
-// Per chunk there are two barriers: B1 (raw-k and k~ fragments visible, column
-// phase of the previous chunk and every read of the decay exponents done) and
-// B2 (q-bar, k-hat^T, weights and the next chunk's decay exponents visible).
+// Per chunk there are two barriers: B1 (k~ fragments visible, column phase of
+// the previous chunk and every read of the decay exponents and of the previous
+// chunk's raw keys done) and B2 (q-bar, k-hat^T, weights, the next chunk's raw
+// keys and decay exponents visible).
 #include "chunk_common.hpp"
 
 namespace glah {
@@ -58,14 +60,18 @@ struct Lds8 {
 };
 static_assert(Lds8<true>::BYTES <= 160 * 1024, "LDS budget");
 
+// An empty use of x: the value is computed before this point (the scheduler may
+// otherwise sink pure arithmetic past a barrier).  Emits no instruction.
+template <typename T>
+__device__ __forceinline__ void pin(const T &x) { asm volatile("" ::"v"(x)); }
+
 // Decay exponents (tile_decay) of the chunk, exchanged through LDS: tile t,
 // lane l, fold slots 4q .. 4q+3 at ((t * 8 + q) * 64 + l) * 16 bytes.
-// the half h of the slots (16h .. 16h + 15) from dn[0 .. 15]
-__device__ __forceinline__ void store_dd_half(char *dd, int tile, int h, const float *dn) {
+__device__ __forceinline__ void store_dd(char *dd, int tile, const float *dn) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *(f32x4 *)(dd + ((tile * 8 + 4 * h + q) * 64 + lane) * 16) =
+  for (int q = 0; q < 8; ++q)
+    *(f32x4 *)(dd + ((tile * 8 + q) * 64 + lane) * 16) =
         (f32x4){dn[4 * q], dn[4 * q + 1], dn[4 * q + 2], dn[4 * q + 3]};
 }
 __device__ __forceinline__ void load_dd(const char *dd, int tile, float *dn) {
@@ -255,15 +261,15 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) vcur[T][j] = 0u;
     load_v(c_begin - 1);  // the chunk before the segment (window part); zeros before token 0
-    // The decay exponents of a chunk are computed one chunk ahead: slots 16..31
-    // (the phi- features) here in phase C, slots 0..15 by the query waves
-    bf16x8 xk[4], xg[2];  // this chunk's keys, the next chunk's gates (slots 16..31)
+    // The decay exponents of a chunk are computed one chunk ahead, in phase C
+    // (the key waves wait for the query waves there)
+    bf16x8 xk[4], xg[4];  // this chunk's keys, the next chunk's gates
     load_rows(hb.k, ro + chunk_off(c_begin), xk);
-    load_gates_half<SG>(hb, ro + chunk_off(c_begin), 1, xg);
+    load_gates<SG>(hb, ro + chunk_off(c_begin), xg);
     {
-      float dn[16];
-      tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
-      store_dd_half(smem + LD::DD, tile, 1, dn);
+      float dn[32];
+      tile_decay<32>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
+      store_dd(smem + LD::DD, tile, dn);
     }
     float fdec[2] = {1.0f, 1.0f};  // 2^{B} of the chunk whose column phase is pending
     __syncthreads();               // staged fragments and the first chunk's decay exponents
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         for (int j = 0; j < 4; ++j) vprev[T][j] = vcur[T][j];
       pack_v();  // values of chunk c - 1
       column(c - 1);
-      load_gates_half<SG>(hb, ro1, 1, xg);  // next chunk's gates (decay exponents in phase C)
+      load_gates<SG>(hb, ro1, xg);  // next chunk's gates (decay exponents in phase C)
       f32x4 u[4];
       project(smem + LD::WK + lane * 16, xk, u);
       load_rows(hb.k, ro1, xk);  // next chunk's keys
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::KT + (tile * 4 + s) * kFrag + lane * 16, xr[s]);
-      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
+      __syncthreads();  // B1: k~ fragments visible; column phase, decay and raw-key reads done
 
       // ---- phase C: k-hat^T fragments of this tile, values of this chunk for
       // the next column phase, decay exponents of the next chunk
@@ -409,11 +415,11 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         }
       }
       {
-        float dn[16];
-        tile_decay<16>(xg, gate_is_log, tq + kC < p.L, dn);
-        store_dd_half(smem + LD::DD, tile, 1, dn);
+        float dn[32];
+        tile_decay<32>(xg, gate_is_log, tq + kC < p.L, dn);
+        store_dd(smem + LD::DD, tile, dn);
       }
-      __syncthreads();  // B2: q-bar, k-hat^T, weight fragments and decay exponents visible
+      __syncthreads();  // B2: q-bar, k-hat^T, weights, raw keys and decay exponents visible
     }
 #pragma unroll
     for (int T = 0; T < 4; ++T)
@@ -447,27 +453,19 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::RK + ((slot * 4 + tile) * 4 + s) * kFrag + lane * 16, xk[s]);
     };
-    // q and raw keys of this chunk (the key waves compute the gate decay
-    // exponents, one chunk ahead)
+    // q and raw keys: the raw keys of a chunk are staged one chunk ahead (in the
+    // previous chunk's phase C), so every band of a chunk is scored in its
+    // phase A; the key waves compute the gate decay exponents, one chunk ahead
     bf16x8 xq[4], xb[4];
     const HeadBufs hb = head_bufs(p, bh);
     const unsigned ro = row_off(tile);
-    if (SWA) {  // keys of the chunk before the segment (window part)
+    if (SWA) {  // keys of the chunk before the segment and of its first chunk
       load_rows(hb.k, ro + chunk_off(c_begin - 1), xb);
       stage_rk(xb, (c_begin - 1) & 1);
+      load_rows(hb.k, ro + chunk_off(c_begin), xb);
+      stage_rk(xb, c_begin & 1);
     }
     load_rows(hb.q, ro + chunk_off(c_begin), xq);
-    if (SWA) load_rows(hb.k, ro + chunk_off(c_begin), xb);
-    // decay exponents of slots 0..15 (the phi+ features), one chunk ahead: the
-    // first chunk's here, the next chunk's in phase A, stored after B1
-    bf16x8 xg[2];
-    load_gates_half<SG>(hb, ro + chunk_off(c_begin), 0, xg);
-    {
-      float dn[16];
-      tile_decay<16>(xg, gate_is_log, c_begin * kC + 16 * tile + n < p.L, dn);
-      store_dd_half(smem + LD::DD, tile, 0, dn);
-    }
-    load_gates_half<SG>(hb, ro + chunk_off(c_begin + 1), 0, xg);
     const float sl2 =
         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale * kLog2e)));
     __syncthreads();  // staged fragments and the first chunk's decay exponents
@@ -477,30 +475,7 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       const int pslot = slot ^ 1;
       const unsigned ro1 = ro + chunk_off(c + 1);
       // ---- phase A
-      // band scores sc[i] for key tile tile-4+i: tiles of the previous chunk and
-      // the diagonal at the end of this phase (their keys are in LDS: the own
-      // tile's were staged by this wave), the others after B1
-      f32x4 sc[5];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) sc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      auto band = [&](int i) {
-        const int kt = tile - 4 + i;
-        bf16x8 a[4];
-        issue_fence();  // keep the loads next to their MFMAs
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (kt >= 0)
-            a[s] = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
-          else
-            a[s] = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
-        }
-        issue_fence();
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma(a[s], xq[s], acc);
-        sc[i] = acc;
-      };
-      if (SWA) stage_rk(xb, slot);
+      if (SWA) load_rows(hb.k, ro1, xb);  // next chunk's raw keys, staged in phase C
       f32x4 u[4];
       project(smem + LD::WQ + lane * 16, xq, u);
       float e[32], izp, izn;
@@ -513,25 +488,31 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
         fold(e, izp, izn, dn, r, 1.0f, r.rr2, xr, xs);
       }
       const bool chunk_mode = r.chunk_mode;
-      if (SWA) {
-#pragma unroll
-        for (int i = 0; i < 5; ++i)
-          if (i == 4 || tile - 4 + i < 0) band(i);
-      }
-      float dnx[16];  // next chunk's, stored once every wave has read this chunk's
-      tile_decay<16>(xg, gate_is_log, (c + 1) * kC + 16 * tile + n < p.L, dnx);
-      load_gates_half<SG>(hb, ro + chunk_off(c + 2), 0, xg);
-      __syncthreads();  // B1: raw-k and k~ fragments visible; column phase and decay reads done
-      store_dd_half(smem + LD::DD, tile, 0, dnx);
-
-      // ---- phase C
       f32x4 Wt[5];  // weights^T for key tiles tile-4+i (i = 4: the diagonal tile)
 #pragma unroll
       for (int i = 0; i < 5; ++i) Wt[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
       if (SWA) {
+        // band scores sc[i] for key tile tile-4+i: tiles of the previous chunk
+        // (slot pslot) and of this one (slot slot), all staged before this chunk
+        f32x4 sc[5];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tile - 4 + i >= 0) band(i);
+        for (int i = 0; i < 5; ++i) {
+          const int kt = tile - 4 + i;
+          bf16x8 a[4];
+          issue_fence();  // keep the loads next to their MFMAs
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            if (kt >= 0)
+              a[s] = lds8(smem + LD::RK + ((slot * 4 + kt) * 4 + s) * kFrag + lane * 16);
+            else
+              a[s] = lds8(smem + LD::RK + ((pslot * 4 + kt + 4) * 4 + s) * kFrag + lane * 16);
+          }
+          issue_fence();
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mfma(a[s], xq[s], acc);
+          sc[i] = acc;
+        }
         // query position minus key position: 16(4-i) - j - (4g - n); valid when in
         // [0, window) (one unsigned compare) and the key exists: its position
         // 64c + 16(tile + i - 4) + 4g + j is >= 0 exactly when c > 0 or
@@ -569,6 +550,21 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < 5; ++i) Wt[i] = sc[i] * inv;
       }
+      // the folds and the window softmax belong to this phase: without these
+      // uses the scheduler sinks them past the barrier, into the longer phase
+#pragma unroll
+      for (int i = 0; i < 5; ++i) pin(Wt[i]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        pin(xr[s]);
+        pin(xs[s]);
+      }
+      __syncthreads();  // B1: k~ fragments visible; column phase, decay and raw-key reads done
+
+      // ---- phase C
+      // the next chunk's raw keys go to the slot of the previous chunk, whose
+      // bands were all scored before B1
+      if (SWA) stage_rk(xb, pslot);
       // intra-chunk scores A^T for key tiles kt = tile-4+i, i = 1..4, kt >= 0
       {
         auto kt_frags = [&](int kt, bf16x8 *kf) {
@@ -649,11 +645,8 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) sts8(smem + LD::QB + (tile * 4 + s) * kFrag + lane * 16, xs[s]);
-      // next chunk's queries and raw keys; their first use waits out the key
-      // waves' longer phase A
-      load_rows(hb.q, ro1, xq);
-      if (SWA) load_rows(hb.k, ro1, xb);
-      __syncthreads();  // B2: q-bar, k-hat^T, weight fragments and decay exponents visible
+      load_rows(hb.q, ro1, xq);  // next chunk's queries
+      __syncthreads();  // B2: q-bar, k-hat^T, weights, raw keys and decay exponents visible
     }
   }
 }
