@@ -76,6 +76,8 @@ def load(path: str = LIBRARY):
             lib.gla_decode_step.restype = i32
             lib.glah_bwd_workspace_bytes.argtypes = [dp]
             lib.glah_bwd_workspace_bytes.restype = sz
+            lib.glah_bwd_workspace_bytes_whole.argtypes = [dp]
+            lib.glah_bwd_workspace_bytes_whole.restype = sz
             lib.hybrid_layer_bwd.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
             lib.hybrid_layer_bwd.restype = i32
             lib.hybrid_layer_fwd_cont.argtypes = [dp, ctypes.c_int32] + [vp] * 15 + [sz, vp]
@@ -414,6 +416,14 @@ def bwd_workspace_bytes(desc: GlahDesc) -> int:
     n = load().glah_bwd_workspace_bytes(ctypes.byref(desc))
     if n == ctypes.c_size_t(-1).value:
         raise GlahError("glah_bwd_workspace_bytes", GLAH_EINVAL, "invalid argument")
+    return n
+
+
+def bwd_workspace_bytes_whole(desc: GlahDesc) -> int:
+    """Workspace with which hybrid_layer_bwd runs the whole call at once."""
+    n = load().glah_bwd_workspace_bytes_whole(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise GlahError("glah_bwd_workspace_bytes_whole", GLAH_EINVAL, "invalid argument")
     return n
 
 

@@ -31,6 +31,7 @@
 //
 // Every reduction is done in a fixed order into per-block partials (no atomics),
 // so the gradients are bitwise repeatable.  All arithmetic is fp32.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -103,6 +104,11 @@ struct BwdParams {
   int nwp;  // dW partials per head (wqp, wkp)
   int nmp;  // sink-gradient partials per head (mp)
   int win_bf16;  // dqs, dks, dvs hold bf16 (the matrix-core window kernels)
+  // a call run as sub-problems: add this sub-problem's sums over batch rows to
+  // the per-head outputs instead of writing them; gacc [H] holds the per-head
+  // gate's gradient in fp32 across the rows
+  int accum;
+  float *gacc;
 };
 
 // ---------------------------------------------------------------------------
@@ -541,62 +547,94 @@ __global__ __launch_bounds__(kBT) void bwd_sweeps_kernel(BwdParams p) {
 // from the reverse sweep, the sum past the end = S_{L-1} . dS_final), so the
 // first half of the tiles is summed forward from the start and the second half
 // backward from the end: the exact zero of Gamma_0 without an initial state
-// stays exact, and no running sum spans more than half the sequence.  One
-// thread per (b, h, feature).
+// stays exact, and no running sum spans more than half the sequence.  A block
+// per (b, h, 16 features), each half of the tiles cut into runs, one a thread.
+constexpr int kTsFeat = 16;             // features of a tile-scan block
+constexpr int kTsParts = kBT / kTsFeat;  // threads (runs of tiles) per feature
+
 __global__ __launch_bounds__(kBT) void bwd_tile_scan_kernel(BwdParams p) {
-  const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
-  const int f = p.f, nft = p.nft;
+  // block = (bh, kTsFeat features); the kTsParts threads of a feature take
+  // consecutive runs of tiles of each half: sums of their runs, the runs before
+  // (after) them combined through LDS, then the run scanned again from there
+  const int f = p.f, nft = p.nft, nsl = p.nsl;
   const size_t BH = (size_t)p.B * p.H;
-  if (idx >= BH * f) return;
-  const size_t bh = idx / f, r = idx - bh * f;
-  // tile totals kTS at a time, every load of a group issued (clamped tiles and
-  // slices, masked) before the running sum uses them: one memory round trip
-  // per group instead of one per tile
+  const int ngr = (f + kTsFeat - 1) / kTsFeat;
+  const size_t bh = blockIdx.x / ngr;
+  const int rl = threadIdx.x % kTsFeat, part = threadIdx.x / kTsFeat;
+  const int r = (int)(blockIdx.x % ngr) * kTsFeat + rl;
+  const bool rok = r < f;
+  const int rc = rok ? r : f - 1;  // clamped: loads stay in range, results unused
+  const int half = (nft + 1) / 2;
+  const int cf = (half + kTsParts - 1) / kTsParts, cb = (nft - half + kTsParts - 1) / kTsParts;
+  const int f0 = min(part * cf, half), f1 = min(f0 + cf, half);
+  const int b0 = min(half + part * cb, nft), b1 = min(b0 + cb, nft);
+  // tile totals kTS at a time, every load of a group issued before they are used
   constexpr int kTS = 8;
-  auto totals = [&](int i0, int dir, float (&tot)[kTS]) {
+  auto totals = [&](int i0, int dir, int lo, int hi, float (&tot)[kTS]) {
     float a[kTS][kMaxSlices], b[kTS][kMaxSlices];
 #pragma unroll
     for (int u = 0; u < kTS; ++u)
 #pragma unroll
       for (int sl = 0; sl < kMaxSlices; ++sl) {
         const int i = min(max(i0 + dir * u, 0), nft - 1);
-        const size_t o = (((size_t)min(sl, p.nsl - 1) * BH + bh) * nft + i) * f + r;
+        const size_t o = (((size_t)min(sl, nsl - 1) * BH + bh) * nft + i) * f + rc;
         a[u][sl] = p.tq[o];
         b[u][sl] = p.tk[o];
       }
 #pragma unroll
     for (int u = 0; u < kTS; ++u) {
+      const int i = i0 + dir * u;
       float s = 0.0f;
 #pragma unroll
       for (int sl = 0; sl < kMaxSlices; ++sl)
-        if (sl < p.nsl) s += a[u][sl] - b[u][sl];
-      tot[u] = s;
+        if (sl < nsl) s += a[u][sl] - b[u][sl];
+      tot[u] = (i >= lo && i < hi) ? s : 0.0f;
     }
   };
-  const int half = (nft + 1) / 2;
-  float acc = 0.0f;
-  for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[((BH + bh) * p.nsl + sl) * f + r];
-  for (int i0 = 0; i0 < half; i0 += kTS) {
+  float sf = 0.0f, sb = 0.0f;
+  for (int i0 = f0; i0 < f1; i0 += kTS) {
     float tot[kTS];
-    totals(i0, 1, tot);
+    totals(i0, 1, f0, f1, tot);
+#pragma unroll
+    for (int u = 0; u < kTS; ++u) sf += tot[u];
+  }
+  for (int i0 = b1 - 1; i0 >= b0; i0 -= kTS) {
+    float tot[kTS];
+    totals(i0, -1, b0, b1, tot);
+#pragma unroll
+    for (int u = 0; u < kTS; ++u) sb += tot[u];
+  }
+  __shared__ float runf[kTsParts][kTsFeat], runb[kTsParts][kTsFeat];
+  runf[part][rl] = sf;
+  runb[part][rl] = sb;
+  __syncthreads();
+  // forward half: ta = d log Gamma_0 term minus the totals of the tiles before;
+  // backward half: the dS_final term plus the totals from the tile on
+  float accf = 0.0f, accb = 0.0f;
+  for (int sl = 0; sl < nsl; ++sl) accf += p.xs[((BH + bh) * nsl + sl) * f + rc];
+  if (p.dstate_out)
+    for (int sl = 0; sl < nsl; ++sl) accb += p.xs[(bh * nsl + sl) * f + rc];
+  for (int q = 0; q < part; ++q) accf -= runf[q][rl];
+  for (int q = kTsParts - 1; q > part; --q) accb += runb[q][rl];
+  if (!rok) return;
+  for (int i0 = f0; i0 < f1; i0 += kTS) {
+    float tot[kTS];
+    totals(i0, 1, f0, f1, tot);
 #pragma unroll
     for (int u = 0; u < kTS; ++u)
-      if (i0 + u < half) {
-        p.ta[(bh * nft + i0 + u) * f + r] = acc;
-        acc -= tot[u];
+      if (i0 + u < f1) {
+        p.ta[(bh * nft + i0 + u) * f + r] = accf;
+        accf -= tot[u];
       }
   }
-  acc = 0.0f;
-  if (p.dstate_out)
-    for (int sl = 0; sl < p.nsl; ++sl) acc += p.xs[(bh * p.nsl + sl) * f + r];
-  for (int i0 = nft - 1; i0 >= half; i0 -= kTS) {
+  for (int i0 = b1 - 1; i0 >= b0; i0 -= kTS) {
     float tot[kTS];
-    totals(i0, -1, tot);
+    totals(i0, -1, b0, b1, tot);
 #pragma unroll
     for (int u = 0; u < kTS; ++u)
-      if (i0 - u >= half) {
-        acc += tot[u];
-        p.ta[(bh * nft + i0 - u) * f + r] = acc;
+      if (i0 - u >= b0) {
+        accb += tot[u];
+        p.ta[(bh * nft + i0 - u) * f + r] = accb;
       }
   }
 }
@@ -1282,7 +1320,9 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
           if (t0 + u < p.nwp) acc += x[u];
       }
     }
-    *(f32x4 *)((m ? p.dwk : p.dwq) + e) = acc;
+    float *dst = (m ? p.dwk : p.dwq) + e;
+    if (p.accum) acc += *(const f32x4 *)dst;
+    *(f32x4 *)dst = acc;
   } else if (blockIdx.x < nwb + nmb) {
     __shared__ float part[kBT / 64][64];
     const int h = (int)(blockIdx.x - nwb), mm = threadIdx.x & 63, pt = threadIdx.x >> 6;
@@ -1301,12 +1341,18 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
     }
     part[pt][mm] = acc;
     __syncthreads();
-    if (pt == 0 && mm < p.n_meta) p.dmeta[(size_t)h * p.n_meta + mm] = ((part[0][mm] + part[1][mm]) + part[2][mm]) + part[3][mm];
+    if (pt == 0 && mm < p.n_meta) {
+      float *dst = p.dmeta + (size_t)h * p.n_meta + mm;
+      const float sum = ((part[0][mm] + part[1][mm]) + part[2][mm]) + part[3][mm];
+      *dst = p.accum ? *dst + sum : sum;
+    }
   } else {
     for (int h = threadIdx.x; h < p.H; h += kBT) {
       float acc = 0.0f;
       for (int b = 0; b < p.B; ++b)
         for (int tl = 0; tl < p.nft; ++tl) acc += p.gp[((size_t)b * p.H + h) * p.nft + tl];
+      if (p.accum) acc += p.gacc[h];
+      p.gacc[h] = acc;
       ((T *)p.gg)[h] = from_f32<T>(acc);
     }
   }
@@ -1314,7 +1360,7 @@ __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
 
 // Workspace layout, in floats; every region starts on a 256-byte boundary.
 struct BwdLayout {
-  size_t pq, pk, gam, tq, tk, ta, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, wst, total;
+  size_t pq, pk, gam, tq, tk, ta, dpq, dpk, dvg, xs, lse, del, dqs, dks, dvs, wqp, wkp, gp, mp, wst, gacc, total;
 };
 
 size_t up64(size_t n) { return (n + 63) & ~(size_t)63; }
@@ -1373,6 +1419,7 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   o.gp = take(gla ? BH * nft : 0);
   o.mp = take(swa ? BH * nsb * a.n_meta : 0);
   o.wst = take(use_walk(a, parts) ? bwd_walk_ws_floats((int)BH, a.L) : 0);
+  o.gacc = take(gla && a.gate_mode == 2 ? a.H : 0);
   o.total = at;
   return o;
 }
@@ -1415,8 +1462,9 @@ SideStream *side_stream(hipStream_t main) {
 }
 
 template <class T>
-hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
+hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool accum) {
   BwdParams p = {};
+  p.accum = accum ? 1 : 0;
   p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.wq = a.wq; p.wk = a.wk; p.dout = g.dout;
   p.meta = a.meta; p.state_in = a.state_in; p.dstate_out = g.dstate_out;
   p.gq = g.dq; p.gk = g.dk; p.gv = g.dv; p.gg = g.dgate;
@@ -1428,6 +1476,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
   p.dpq = ws + lay.dpq; p.dpk = ws + lay.dpk; p.dvg = ws + lay.dvg; p.xs = ws + lay.xs;
   p.lse = ws + lay.lse; p.del = ws + lay.del; p.dqs = ws + lay.dqs; p.dks = ws + lay.dks;
   p.dvs = ws + lay.dvs; p.wqp = ws + lay.wqp; p.wkp = ws + lay.wkp; p.gp = ws + lay.gp; p.mp = ws + lay.mp;
+  p.gacc = ws + lay.gacc;
   p.B = a.B; p.H = a.H; p.L = a.L; p.d = a.d; p.dv = a.dv; p.f = a.f; p.f2 = a.f / 2;
   p.lf2 = 0;
   while ((1 << p.lf2) < p.f2) ++p.lf2;
@@ -1524,8 +1573,8 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts) {
       if (!launched()) return e;
     }
     if (a.L > 0) {
-      hipLaunchKernelGGL(bwd_tile_scan_kernel, dim3((unsigned)((BH * (size_t)a.f + kBT - 1) / kBT)), block, 0,
-                         a.stream, p);
+      hipLaunchKernelGGL(bwd_tile_scan_kernel, dim3((unsigned)(BH * (size_t)((a.f + kTsFeat - 1) / kTsFeat))), block,
+                         0, a.stream, p);
       if (!launched()) return e;
     }
   }
@@ -1572,10 +1621,100 @@ bool bwd_supported(const LayerArgs &a, int parts) {
   return true;
 }
 
-size_t bwd_workspace_bytes(const LayerArgs &a, int parts) { return bwd_layout(a, parts).total * sizeof(float); }
+// The backward of every (batch row, head) is independent of the others, so a
+// call can run as a sequence of sub-problems, each with its own share of the
+// workspace: blocks of whole batch rows (every head), or one batch row and a
+// block of heads.  They run head block by head block, batch rows innermost, so
+// the per-head sums over the batch (dWphi, the sink gradients, a per-head
+// gate's gradient) are written by a block's first row and added to by the
+// others.  The plan is the fewest sub-problems whose workspace fits.
+namespace {
+
+struct BwdPlan {
+  bool ok = false;
+  int rows = 0, heads = 0;  // sub-problem shape
+};
+
+LayerArgs bwd_sub_shape(const LayerArgs &a, int rows, int heads) {
+  LayerArgs s = a;
+  s.B = rows;
+  s.H = heads;
+  return s;
+}
+
+size_t bwd_sub_bytes(const LayerArgs &a, int parts, int rows, int heads) {
+  return bwd_layout(bwd_sub_shape(a, rows, heads), parts).total * sizeof(float);
+}
+
+// candidates, fewest sub-problems first: the whole call, blocks of rows, then
+// one row and blocks of heads; the first whose workspace is at most `cap`
+BwdPlan bwd_plan(const LayerArgs &a, int parts, size_t cap) {
+  if (bwd_sub_bytes(a, parts, a.B, a.H) <= cap) return {true, a.B, a.H};
+  if (a.B <= 0 || a.H <= 0) return {};
+  for (int r = a.B - 1; r >= 1; --r)
+    if (a.B % r == 0 && bwd_sub_bytes(a, parts, r, a.H) <= cap) return {true, r, a.H};
+  for (int h = a.H - 1; h >= 1; --h)
+    if (a.H % h == 0 && bwd_sub_bytes(a, parts, 1, h) <= cap) return {true, 1, h};
+  return {};
+}
+
+// the workspace the sizing query reports: the whole call's when it is at most
+// this, else the largest sub-problem's that is
+constexpr size_t kBwdDefaultBytes = 1500000000;
+
+}  // namespace
+
+size_t bwd_workspace_min_bytes(const LayerArgs &a, int parts) {
+  if (a.B <= 0 || a.H <= 0) return bwd_sub_bytes(a, parts, a.B, a.H);
+  return bwd_sub_bytes(a, parts, 1, 1);
+}
+
+size_t bwd_workspace_whole_bytes(const LayerArgs &a, int parts) { return bwd_sub_bytes(a, parts, a.B, a.H); }
+
+size_t bwd_workspace_bytes(const LayerArgs &a, int parts) {
+  const BwdPlan pl = bwd_plan(a, parts, kBwdDefaultBytes);
+  return pl.ok ? bwd_sub_bytes(a, parts, pl.rows, pl.heads) : bwd_workspace_min_bytes(a, parts);
+}
 
 hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts) {
-  return a.bf16 ? bwd_dispatch<bf16>(a, g, parts) : bwd_dispatch<float>(a, g, parts);
+  const BwdPlan pl = bwd_plan(a, parts, a.ws_bytes);
+  if (!pl.ok) return hipErrorInvalidValue;  // the caller checks the minimum
+  auto run = [&](const LayerArgs &s, const BwdArgs &sg, bool accum) {
+    return s.bf16 ? bwd_dispatch<bf16>(s, sg, parts, accum) : bwd_dispatch<float>(s, sg, parts, accum);
+  };
+  if (pl.rows == a.B && pl.heads == a.H) return run(a, g, false);
+  const size_t es = a.bf16 ? 2 : 4, L = (size_t)a.L;
+  const size_t gtok = a.gate_mode == 0 ? (size_t)a.f : 1;  // gate elements per token (modes 0, 1)
+  for (int h0 = 0; h0 < a.H; h0 += pl.heads) {
+    for (int b0 = 0; b0 < a.B; b0 += pl.rows) {
+      const size_t bh0 = (size_t)b0 * a.H + h0;  // first (row, head) of the sub-problem
+      auto at = [&](const void *x, size_t elems, size_t bytes) -> const void * {
+        return x ? (const char *)x + elems * bytes : nullptr;
+      };
+      auto atw = [&](void *x, size_t elems, size_t bytes) -> void * {
+        return x ? (char *)x + elems * bytes : nullptr;
+      };
+      LayerArgs s = bwd_sub_shape(a, pl.rows, pl.heads);
+      s.q = at(a.q, bh0 * L * a.d, es); s.k = at(a.k, bh0 * L * a.d, es); s.v = at(a.v, bh0 * L * a.dv, es);
+      s.gate = a.gate_mode == 2 ? at(a.gate, h0, es) : at(a.gate, bh0 * L * gtok, es);
+      s.wq = at(a.wq, (size_t)h0 * a.d * (a.f / 2), es); s.wk = at(a.wk, (size_t)h0 * a.d * (a.f / 2), es);
+      s.meta = (const float *)at(a.meta, (size_t)h0 * a.n_meta, 4);
+      s.state_in = (const float *)at(a.state_in, bh0 * a.f * a.dv, 4);
+      BwdArgs sg;
+      sg.dout = at(g.dout, bh0 * L * a.dv, es);
+      sg.dstate_out = (const float *)at(g.dstate_out, bh0 * a.f * a.dv, 4);
+      sg.dq = atw(g.dq, bh0 * L * a.d, es); sg.dk = atw(g.dk, bh0 * L * a.d, es);
+      sg.dv = atw(g.dv, bh0 * L * a.dv, es);
+      sg.dgate = a.gate_mode == 2 ? atw(g.dgate, h0, es) : atw(g.dgate, bh0 * L * gtok, es);
+      sg.dwq = (float *)atw(g.dwq, (size_t)h0 * a.d * (a.f / 2), 4);
+      sg.dwk = (float *)atw(g.dwk, (size_t)h0 * a.d * (a.f / 2), 4);
+      sg.dmeta = (float *)atw(g.dmeta, (size_t)h0 * a.n_meta, 4);
+      sg.dstate_in = (float *)atw(g.dstate_in, bh0 * a.f * a.dv, 4);
+      const hipError_t e = run(s, sg, b0 > 0);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace glah

@@ -268,6 +268,13 @@ size_t glah_bwd_workspace_bytes(const glah_desc *desc) {
   return bwd_workspace_bytes(a, PART_BOTH);
 }
 
+size_t glah_bwd_workspace_bytes_whole(const glah_desc *desc) {
+  LayerArgs a;
+  if (!desc || check_desc(desc, Op::kHybrid, a) != GLAH_OK) return (size_t)-1;
+  if (!bwd_supported(a, PART_BOTH)) return 0;
+  return bwd_workspace_whole_bytes(a, PART_BOTH);
+}
+
 glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k, const void *v,
                              const void *gate, const void *wphi_q, const void *wphi_k,
                              const float *meta, const float *state_in, const void *d_o,
@@ -289,7 +296,7 @@ glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k
         !opt(ws))
       return GLAH_EINVAL;
     if (!bwd_supported(a, PART_BOTH)) return GLAH_ENOTSUP;
-    const size_t need = bwd_workspace_bytes(a, PART_BOTH);
+    const size_t need = bwd_workspace_min_bytes(a, PART_BOTH);
     if (ws_bytes < need || (!ws && need)) return GLAH_EWORKSPACE;
     a.q = q; a.k = k; a.v = v; a.gate = gate; a.wq = wphi_q; a.wk = wphi_k; a.meta = meta;
     a.state_in = state_in; a.ws = ws; a.ws_bytes = ws_bytes; a.stream = (hipStream_t)stream;

@@ -84,7 +84,12 @@ struct BwdArgs {
   float *dwq = nullptr, *dwk = nullptr, *dmeta = nullptr, *dstate_in = nullptr;
 };
 bool bwd_supported(const LayerArgs &a, int parts);
+// workspace the sizing query reports (the whole call's, or a sub-problem's when
+// that exceeds 1.5e9 bytes) and the least any call accepts (one row and one head
+// at a time); launch_layer_bwd runs the fewest sub-problems that fit a.ws_bytes
 size_t bwd_workspace_bytes(const LayerArgs &a, int parts);
+size_t bwd_workspace_min_bytes(const LayerArgs &a, int parts);
+size_t bwd_workspace_whole_bytes(const LayerArgs &a, int parts);  // no sub-problems
 hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 
 // Window part of the backward on the matrix cores (bwd_window.hip): bf16,

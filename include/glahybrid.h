@@ -212,11 +212,27 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  *   d_o         [B][H][L][d_v] desc->dtype, the gradient of o
  *   dstate_out  nullable, [B][H][f][d_v] fp32, the gradient of the final state
  *               (NULL = zero)
- *   ws          device workspace of ws_bytes >= glah_bwd_workspace_bytes(desc)
+ *   ws          device workspace of ws_bytes bytes, at least the workspace of one
+ *               batch row and one head (glah_bwd_workspace_bytes of this
+ *               descriptor with B = H = 1; else GLAH_EWORKSPACE).  The gradient
+ *               of every (batch row, head) is independent of the others, so a
+ *               workspace below the whole call's runs the call as the fewest
+ *               sub-problems that fit it (blocks of whole batch rows, else one
+ *               row and a block of heads), in order on `stream`, the per-head
+ *               sums over the batch added up across them.
+ * glah_bwd_workspace_bytes reports the whole call's workspace when it is at
+ * most 1.5e9 bytes, else that of the largest sub-problem within that (at 32K
+ * tokens, 32 heads of 128: blocks of 8 heads, 1.17 GB); (size_t)-1 for an
+ * invalid descriptor, 0 when the sizes are not supported.
  * Supported: d_qk, d_v <= 128 and multiples of 4; f <= 128, a multiple of 4 with
  * f/2 a power of two; window <= 1024; n_meta <= 64 (otherwise GLAH_ENOTSUP).
- * All arithmetic is fp32 (token-recurrent form, no chunking); reductions over
- * tokens and batch rows run in a fixed order, so results are bitwise repeatable.
+ * Arithmetic: bf16 with d_qk = f = d_v = 128 runs on the matrix cores (bf16
+ * operands, split into high and low bf16 halves where the gate gradient needs
+ * more, fp32 accumulation; the window part's dq, dk, dv are rounded to bf16
+ * before they are added to the gated part's; log-gates are floored at -10 as in
+ * the forward); other sizes and fp32 run token-recurrent fp32 kernels.
+ * Reductions over tokens and batch rows run in a fixed order, so results are
+ * bitwise repeatable for a given ws_bytes.
  * Streams: with both parts (f > 0 and window > 0) the window part runs on a
  * side stream of the library (one per device, with two events, created on the
  * first such call and kept until the process ends), forked from `stream` at
@@ -226,6 +242,10 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  * alone.
  */
 size_t glah_bwd_workspace_bytes(const glah_desc *desc);
+/* The workspace with which hybrid_layer_bwd runs the whole call at once (no
+ * sub-problems; the fastest plan, for callers with the memory to spare);
+ * (size_t)-1 for an invalid descriptor, 0 when the sizes are not supported. */
+size_t glah_bwd_workspace_bytes_whole(const glah_desc *desc);
 glah_status hybrid_layer_bwd(const glah_desc *desc, const void *q, const void *k,
                              const void *v, const void *gate, const void *wphi_q,
                              const void *wphi_k, const float *meta,

@@ -174,12 +174,33 @@ def test_backward_argument_checks(lib):
     for missing in ("q", "do", "dq", "dgate", "dwq", "dmeta"):
         assert _bwd(lib, d, need, **{missing: 0}) == binding.GLAH_EINVAL, missing
     assert _bwd(lib, d, need, dq=FAKE + 8) == binding.GLAH_EINVAL
-    assert _bwd(lib, d, need - 1) == binding.GLAH_EWORKSPACE
+    # the least workspace any call takes: one batch row and one head at a time
+    least = lib.glah_bwd_workspace_bytes(ctypes.byref(_desc(H=1)))
+    assert 0 < least < need
+    assert _bwd(lib, d, least - 1) == binding.GLAH_EWORKSPACE
     assert _bwd(lib, d, need, ws=0) == binding.GLAH_EWORKSPACE
     # sizes beyond the backward kernels: valid but unsupported
     for bad in (dict(d=256), dict(dv=66), dict(f=96), dict(f=256), dict(window=2048)):
         assert _bwd(lib, _desc(**bad), 1 << 40) == binding.GLAH_ENOTSUP, bad
     assert lib.glah_bwd_workspace_bytes(ctypes.byref(_desc(f=7))) == ctypes.c_size_t(-1).value
+
+
+def test_backward_workspace_sizing(lib):
+    """The sizing query reports the whole call's workspace up to 1.5e9 bytes, else
+    the largest sub-problem's within that (blocks of heads, or of batch rows)."""
+    gib = 1500000000
+    def ws(B, H, L):
+        d = binding.make_desc(B, H, L, 128, 128, 128, window=64, n_meta=4, dtype=binding.GLAH_BF16)
+        return lib.glah_bwd_workspace_bytes(ctypes.byref(d))
+    def whole(B, H, L):
+        d = binding.make_desc(B, H, L, 128, 128, 128, window=64, n_meta=4, dtype=binding.GLAH_BF16)
+        return lib.glah_bwd_workspace_bytes_whole(ctypes.byref(d))
+    assert ws(1, 32, 2048) < ws(2, 32, 2048) <= gib               # small calls run whole
+    assert whole(1, 32, 2048) == ws(1, 32, 2048) and whole(1, 32, 32768) > gib
+    big = ws(1, 32, 32768)
+    assert big <= gib and big == ws(1, 8, 32768) > ws(1, 4, 32768)  # 32K: blocks of 8 heads
+    assert ws(8, 32, 8192) == ws(1, 32, 8192) <= gib               # batch 8: one row at a time
+    assert ws(1, 1, 1 << 22) > gib                                 # nothing fits: the least
 
 
 def _gdn_desc(**kw):

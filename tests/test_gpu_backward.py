@@ -61,7 +61,7 @@ def compare(got, ref, tol, names=OB.NAMES, flat=("gate", "meta", "wq", "wk")):
     return worst
 
 
-def run_case(wl, kind=OB.GATE_LOGITS, with_state=False, seed=3, gate=None):
+def run_case(wl, kind=OB.GATE_LOGITS, with_state=False, seed=3, gate=None, ws=None):
     x = make_prefill(wl, DEV)
     dt = wl.torch_dtype
     g = gate_of(kind, x, wl, dt) if gate is None else gate.to(dt).to(DEV)
@@ -70,7 +70,7 @@ def run_case(wl, kind=OB.GATE_LOGITS, with_state=False, seed=3, gate=None):
     dS = grads_seed((wl.B, wl.H, wl.f, wl.dv), seed + 2, torch.float32, 0.3) if with_state else None
     got = G.hybrid_layer_bwd(x["q"], x["k"], x["v"], g, x["wq"], x["wk"], x["meta"], dO, window=wl.window,
                              gate_kind=GPU_KIND[kind], state_in=s_in, dstate_out=dS,
-                             need_dstate_in=with_state)
+                             need_dstate_in=with_state, ws=ws)
     torch.cuda.synchronize()
     h = {k: to_f64(v) for k, v in x.items()}
     ref = OB.layer_bwd(h["q"], h["k"], h["v"], to_f64(g), h["wq"], h["wk"], h["meta"], to_f64(dO),
@@ -91,6 +91,36 @@ def test_backward_fp32_no_state_long_window():
     wl = WORKLOADS["tiny_fp32"].with_(B=1, H=3, L=130, window=200)
     say("backward fp32 window > L")
     got, ref = run_case(wl)
+    compare(got, ref, TOL_F32)
+
+
+def sub_problem_workspace(wl, kind, rows, heads):
+    """A workspace that fits sub-problems of `rows` batch rows and `heads` heads
+    but not the whole call: the call then runs as such sub-problems."""
+    def need(B, H):
+        return G.bwd_workspace_bytes(G.make_desc(B, H, wl.L, wl.d, wl.dv, wl.f, window=wl.window,
+                                                 n_meta=wl.n_meta, dtype=G._dtype_code(torch.empty(0, dtype=wl.torch_dtype)),
+                                                 gate_kind=GPU_KIND[kind]))
+    n = need(rows, heads)
+    assert n < need(wl.B, wl.H)
+    return torch.empty(n, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("kind", [OB.GATE_LOGITS, OB.GATE_LOG_HEAD])
+def test_backward_bf16_sub_problems(kind):
+    """Workspace for one batch row and two heads: four sub-problems, the per-head
+    sums over the batch (dWphi, the sinks, a per-head gate) added across rows."""
+    wl = WORKLOADS["prefill_2k"].with_(B=2, H=4, L=300)
+    say("backward bf16 as 1-row 2-head sub-problems, gate kind %d" % kind)
+    got, ref = run_case(wl, kind, with_state=True, ws=sub_problem_workspace(wl, kind, 1, 2))
+    compare(got, ref, TOL_BF16)
+
+
+def test_backward_fp32_sub_problems():
+    """fp32 (token-recurrent kernels), one (row, head) at a time."""
+    wl = WORKLOADS["tiny_fp32"].with_(B=2, H=2, L=77)
+    say("backward fp32 as 1-row 1-head sub-problems")
+    got, ref = run_case(wl, OB.GATE_LOG_HEAD, with_state=True, ws=sub_problem_workspace(wl, OB.GATE_LOG_HEAD, 1, 1))
     compare(got, ref, TOL_F32)
 
 
