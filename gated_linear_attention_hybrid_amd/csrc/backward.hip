@@ -1290,39 +1290,55 @@ __global__ __launch_bounds__(kWT) void bwd_swa_tile_kv_kernel(BwdParams p) {
 // dWphi_k [H][d][f/2], the sink gradients [H][n_meta] and, for a per-head
 // gate, its gradient [H].  Fixed order, one output per thread.
 // Sums of the per-block partials, each in a fixed order: blocks [0, nwb) take
-// four consecutive elements of dWphi_q / dWphi_k a thread; then one block per
+// 64 quads of dWphi_q / dWphi_k, four waves a quad (a quarter of the partials
+// each, added in LDS); then one block per
 // head sums its sink-gradient partials (thread (part, sink) over every fourth
 // partial, the four parts added in LDS); a last block sums the per-head gate
 // gradient (one gate per head).
+constexpr int kRedQuads = 64;  // dW quads (4 elements) a block of the partial sums
+
 template <class T>
 __global__ __launch_bounds__(kBT) void bwd_reduce_kernel(BwdParams p) {
   const size_t per = (size_t)p.d * p.f2;  // a multiple of 4 (d is)
   const size_t nw4 = p.gla ? 2 * (size_t)p.H * per / 4 : 0;
-  const size_t nwb = (nw4 + kBT - 1) / kBT;
+  const size_t nwb = (nw4 + kRedQuads - 1) / kRedQuads;
   const size_t nmb = (p.swa && p.n_meta > 0) ? (size_t)p.H : 0;
   constexpr int kRG = 16;  // partials loaded (clamped, masked) before they are added
   if (blockIdx.x < nwb) {
-    const size_t idx = (size_t)blockIdx.x * kBT + threadIdx.x;
-    if (idx >= nw4) return;
-    const size_t nwt = (size_t)p.H * per, e4 = 4 * idx;
+    // 64 quads a block; wave wv sums its quarter of every batch row's
+    // partials, and the four quarters are added in LDS in a fixed order
+    constexpr int kRQ = kBT / kRedQuads;
+    __shared__ f32x4 wpart[kRQ][kRedQuads];
+    const int l = threadIdx.x % kRedQuads, wv = threadIdx.x / kRedQuads;
+    const size_t idx = (size_t)blockIdx.x * kRedQuads + l;
+    const bool ok = idx < nw4;
+    const size_t nwt = (size_t)p.H * per, e4 = 4 * (ok ? idx : nw4 - 1);
     const int m = e4 >= nwt;
     const size_t e = e4 - m * nwt, h = e / per, r = e - h * per;
     const float *src = m ? p.wkp : p.wqp;
+    const int qn = (p.nwp + kRQ - 1) / kRQ, t_lo = min(wv * qn, p.nwp), t_hi = min(t_lo + qn, p.nwp);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int b = 0; b < p.B; ++b) {
       const float *row = src + ((size_t)b * p.H + h) * p.nwp * per + r;
-      for (int t0 = 0; t0 < p.nwp; t0 += kRG) {
+      for (int t0 = t_lo; t0 < t_hi; t0 += kRG) {
         f32x4 x[kRG];
 #pragma unroll
-        for (int u = 0; u < kRG; ++u) x[u] = *(const f32x4 *)(row + (size_t)min(t0 + u, p.nwp - 1) * per);
+        for (int u = 0; u < kRG; ++u) x[u] = *(const f32x4 *)(row + (size_t)min(t0 + u, t_hi - 1) * per);
 #pragma unroll
         for (int u = 0; u < kRG; ++u)
-          if (t0 + u < p.nwp) acc += x[u];
+          if (t0 + u < t_hi) acc += x[u];
       }
     }
-    float *dst = (m ? p.dwk : p.dwq) + e;
-    if (p.accum) acc += *(const f32x4 *)dst;
-    *(f32x4 *)dst = acc;
+    wpart[wv][l] = acc;
+    __syncthreads();
+    if (wv == 0 && ok) {
+      acc = wpart[0][l];
+#pragma unroll
+      for (int q = 1; q < kRQ; ++q) acc += wpart[q][l];
+      float *dst = (m ? p.dwk : p.dwq) + e;
+      if (p.accum) acc += *(const f32x4 *)dst;
+      *(f32x4 *)dst = acc;
+    }
   } else if (blockIdx.x < nwb + nmb) {
     __shared__ float part[kBT / 64][64];
     const int h = (int)(blockIdx.x - nwb), mm = threadIdx.x & 63, pt = threadIdx.x >> 6;
@@ -1600,7 +1616,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
       hipLaunchKernelGGL((bwd_feature_kernel<T, false, true>), dim3(BH * p.nft), block, 0, a.stream, p);
     if (!launched()) return e;
   }
-  const size_t nwb = p.gla ? (2 * (size_t)a.H * a.d * p.f2 / 4 + kBT - 1) / kBT : 0;
+  const size_t nwb = p.gla ? (2 * (size_t)a.H * a.d * p.f2 / 4 + kRedQuads - 1) / kRedQuads : 0;
   const size_t nred = nwb + ((p.swa && a.n_meta > 0) ? (size_t)a.H : 0) + ((p.gla && a.gate_mode == 2) ? 1 : 0);
   if (nred) {
     hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3((unsigned)nred), block, 0, a.stream, p);

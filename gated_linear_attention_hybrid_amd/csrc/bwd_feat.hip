@@ -39,7 +39,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-constexpr int kFeatBlocks = 2048;  // blocks the span aims at
+constexpr int kFeatBlocks = 512;  // blocks the span aims at (fewer dW partials to sum)
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
