@@ -1425,7 +1425,8 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t nt = gla ? BH * nft * a.f : 0;
   o.tq = take(nsl * nt); o.tk = take(nsl * nt); o.ta = take(nt);
   o.dpq = take(nsl * nf); o.dpk = take(nsl * nf);
-  o.dvg = take(gla ? nw * N * a.dv : 0);
+  // the gated part's dv: bf16 for the matrix-core per-token kernel
+  o.dvg = take(gla ? (use_feat_mfma(a, parts) ? N * a.dv / 2 : nw * N * a.dv) : 0);
   o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
   o.lse = take(swa ? N : 0); o.del = take(swa ? N : 0);
   o.dqs = take(swa ? N * a.d / wsz : 0); o.dks = take(swa ? N * a.d / wsz : 0);
@@ -1582,7 +1583,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
       wa.state_in = a.state_in; wa.dstate_out = p.dstate_out;
       wa.dpq = p.dpq; wa.dpk = p.dpk; wa.dvg = p.dvg; wa.tq = p.tq; wa.tk = p.tk; wa.xs = p.xs;
       wa.dstate_in = g.dstate_in;
-      wa.BH = (int)BH; wa.L = a.L; wa.nft = p.nft;
+      wa.BH = (int)BH; wa.L = a.L; wa.nft = p.nft; wa.dv_bf16 = feat_mfma;
       if ((e = launch_bwd_walk(wa, a.stream)) != hipSuccess) return e;
     } else {
       hipLaunchKernelGGL(bwd_sweeps_kernel<T>, dim3(2 * BH * p.nsl), block, 0, a.stream, p);

@@ -80,7 +80,8 @@ __device__ __forceinline__ void st8h(__amdgpu_buffer_rsrc_t r, unsigned off, bf1
 
 struct FeatParams {
   const bf16 *q, *k, *gate, *wq, *wk;
-  const float *pq, *pk, *dpq, *dpk, *dvg, *ta;  // [B H L][128] x 5, [B H][tiles][128]
+  const float *pq, *pk, *dpq, *dpk, *ta;        // [B H L][128] x 4, [B H][tiles][128]
+  const bf16 *dvg;                              // [B H L][128]: the gated part's dv
   const void *dqs, *dks, *dvs;                  // window part [B H L][128] (bf16 or fp32) or null
   bf16 *dq, *dk, *dv, *dg;
   float *wqp, *wkp;                             // [B H][blocks][128][64]
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the window part's rows: bf16 (WB) or fp32
   constexpr unsigned kWs = WB ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t rsx = rows_rsrc(SWA ? (m ? p.dks : p.dqs) : p.pq, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
-  const __amdgpu_buffer_rsrc_t rvg = rows_rsrc(p.dvg, row0 * 512, rowbytes);
-  const __amdgpu_buffer_rsrc_t rvs = rows_rsrc(SWA ? p.dvs : p.dvg, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
+  const __amdgpu_buffer_rsrc_t rvg = rows_rsrc(p.dvg, row0 * 256, hrowbytes);
+  const __amdgpu_buffer_rsrc_t rvs = rows_rsrc(SWA ? p.dvs : (const void *)p.dvg, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
   // four window-part values at element offset e of token row tok
   auto wld4 = [&](__amdgpu_buffer_rsrc_t r, unsigned tok, unsigned e) -> f32x4 {
     if constexpr (WB) {
@@ -178,8 +179,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x4 vg[2], vs[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const unsigned off = tok * 512u + (unsigned)(32 * wave + 8 * g + 4 * a) * 4u;
-      vg[a] = ld4f(rvg, off);
+      const bf16x4 h = ld4h(rvg, tok * 256u + (unsigned)(32 * wave + 8 * g + 4 * a) * 2u);
+      vg[a] = (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
       vs[a] = SWA ? wld4(rvs, tok, (unsigned)(32 * wave + 8 * g + 4 * a)) : zf4();
     }
     bf16x8 xv[2];
@@ -298,7 +299,7 @@ hipError_t launch_bwd_feat_mfma(const FeatArgs &a, hipStream_t stream) {
   FeatParams p;
   p.q = (const bf16 *)a.q; p.k = (const bf16 *)a.k; p.gate = (const bf16 *)a.gate;
   p.wq = (const bf16 *)a.wq; p.wk = (const bf16 *)a.wk;
-  p.pq = a.pq; p.pk = a.pk; p.dpq = a.dpq; p.dpk = a.dpk; p.dvg = a.dvg; p.ta = a.ta;
+  p.pq = a.pq; p.pk = a.pk; p.dpq = a.dpq; p.dpk = a.dpk; p.dvg = (const bf16 *)a.dvg; p.ta = a.ta;
   p.dqs = a.dqs; p.dks = a.dks; p.dvs = a.dvs;
   p.dq = (bf16 *)a.dq; p.dk = (bf16 *)a.dk; p.dv = (bf16 *)a.dv; p.dg = (bf16 *)a.dg;
   p.wqp = a.wqp; p.wkp = a.wkp;

@@ -121,6 +121,7 @@ struct WalkParams {
   float *tq, *tk, *xs, *dstate_in;     // [BH][nft][128] x 2, [2][BH][128], [BH][128][128]
   float *sloc, *gloc, *dseg;           // [BH][P][128][128] x 2, [BH][P][128]
   int BH, L, nft, P, seg;              // seg: 16-token tiles per segment (a multiple of 4)
+  int dv_bf16;                         // dvg holds bf16 [B H L][128]
 };
 
 // layout-F values of one tile: tokens 16 tau + 4 g + r, column c (0 past the end)
@@ -408,7 +409,12 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
   const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), ro = head_rsrc(p.dout, bh, L);
   const __amdgpu_buffer_rsrc_t rq = frows(p.pq, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
-  const __amdgpu_buffer_rsrc_t rd = frows(p.dpk, bh, L), rdv = frows(p.dvg, bh, L);
+  const __amdgpu_buffer_rsrc_t rd = frows(p.dpk, bh, L);
+  // dv rows: fp32 [L][128], or bf16 [L][128] for the matrix-core per-token kernel
+  const __amdgpu_buffer_rsrc_t rdv =
+      p.dv_bf16 ? __builtin_amdgcn_make_buffer_rsrc((void *)((bf16 *)p.dvg + (size_t)bh * L * 128), (short)0, L * 256,
+                                                    0x00020000)
+                : frows(p.dvg, bh, L);
   const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const bf16x4 eye = eye16();
   const int fF[2] = {32 * fs + n, 32 * fs + 16 + n};
@@ -574,7 +580,12 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
       f32x4 acc = *(const f32x4 *)(lds + part_off(buf, 0, fs, dt));
 #pragma unroll
       for (int w = 1; w < 4; ++w) acc += *(const f32x4 *)(lds + part_off(buf, w, fs, dt));
-      fst4(rdv, (unsigned)(16 * tau + n) * 512u + (unsigned)(32 * fs + 8 * g + 4 * dt) * 4u, acc);
+      if (p.dv_bf16)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(acc)), rdv,
+                                              (int)((unsigned)(16 * tau + n) * 256u + (unsigned)(32 * fs + 8 * g + 4 * dt) * 2u),
+                                              0, 0);
+      else
+        fst4(rdv, (unsigned)(16 * tau + n) * 512u + (unsigned)(32 * fs + 8 * g + 4 * dt) * 4u, acc);
     }
   }
   // G after the first tile = Gamma_0 dS_0: the gradient of the initial state,
@@ -644,7 +655,7 @@ hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream) {
   p.pq = a.pq; p.pk = a.pk; p.gb = a.gb; p.v = (const bf16 *)a.v; p.dout = (const bf16 *)a.dout;
   p.state_in = a.state_in; p.dstate_out = a.dstate_out;
   p.dpq = a.dpq; p.dpk = a.dpk; p.dvg = a.dvg; p.tq = a.tq; p.tk = a.tk; p.xs = a.xs; p.dstate_in = a.dstate_in;
-  p.BH = a.BH; p.L = a.L; p.nft = a.nft;
+  p.BH = a.BH; p.L = a.L; p.nft = a.nft; p.dv_bf16 = a.dv_bf16 ? 1 : 0;
   if (p.BH == 0) return hipSuccess;
   p.P = walk_segments(p.BH, p.L, &p.seg);
   const size_t nst = (size_t)p.BH * p.P * 128 * 128;

@@ -122,6 +122,7 @@ struct WalkArgs {
   float *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *tq = nullptr, *tk = nullptr, *xs = nullptr;
   float *dstate_in = nullptr, *ws = nullptr;
   int BH = 0, L = 0, nft = 0;
+  bool dv_bf16 = false;  // dvg as bf16 [B H L][128] (for the matrix-core per-token kernel)
 };
 bool bwd_walk_supported(int f, int dv, int L, bool bf16);
 size_t bwd_walk_ws_floats(int BH, int L);
@@ -136,7 +137,8 @@ hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream);
 // ([B H][blocks][128][64], blocks = ceil(ceil(L / 16) / bwd_feat_span)).
 struct FeatArgs {
   const void *q = nullptr, *k = nullptr, *gate = nullptr, *wq = nullptr, *wk = nullptr;
-  const float *pq = nullptr, *pk = nullptr, *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *ta = nullptr;
+  const float *pq = nullptr, *pk = nullptr, *dpq = nullptr, *dpk = nullptr, *ta = nullptr;
+  const void *dvg = nullptr;  // bf16 [B H L][128]: the gated part's dv from the walks
   const void *dqs = nullptr, *dks = nullptr, *dvs = nullptr;
   bool win_bf16 = false;
   void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
