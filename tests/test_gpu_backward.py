@@ -106,13 +106,22 @@ def sub_problem_workspace(wl, kind, rows, heads):
     return torch.empty(n, dtype=torch.uint8, device=DEV)
 
 
-@pytest.mark.parametrize("kind", [OB.GATE_LOGITS, OB.GATE_LOG_HEAD])
+@pytest.mark.parametrize("kind", [OB.GATE_LOGITS, OB.GATE_LOG_TOKEN, OB.GATE_LOG_HEAD])
 def test_backward_bf16_sub_problems(kind):
     """Workspace for one batch row and two heads: four sub-problems, the per-head
     sums over the batch (dWphi, the sinks, a per-head gate) added across rows."""
     wl = WORKLOADS["prefill_2k"].with_(B=2, H=4, L=300)
     say("backward bf16 as 1-row 2-head sub-problems, gate kind %d" % kind)
     got, ref = run_case(wl, kind, with_state=True, ws=sub_problem_workspace(wl, kind, 1, 2))
+    compare(got, ref, TOL_BF16)
+
+
+def test_backward_bf16_row_block_sub_problems():
+    """Workspace for two batch rows of every head: two sub-problems of whole rows,
+    the second adding to the per-head sums of the first."""
+    wl = WORKLOADS["prefill_2k"].with_(B=4, H=2, L=200)
+    say("backward bf16 as 2-row sub-problems")
+    got, ref = run_case(wl, OB.GATE_LOG_HEAD, with_state=True, ws=sub_problem_workspace(wl, OB.GATE_LOG_HEAD, 2, 2))
     compare(got, ref, TOL_BF16)
 
 
