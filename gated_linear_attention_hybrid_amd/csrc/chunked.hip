@@ -171,13 +171,13 @@ __global__ __launch_bounds__(kNT) void swa_kernel(ChunkParams p) {
 // <= 0 (no fold reference) and the state is never rescaled.
 // Block = 4 waves, two blocks per CU.  Wave w: token tile w for the row work
 // (u_k, the gate decay exponents, phi(k), k-hat^T fragments transposed on the
-// matrix core, V^T fragments) and d_v columns [32w, 32w + 32) of the state.  Two
-// barriers per chunk: B1a (tile totals visible, previous update done) and B1
-// (k-hat^T and V^T fragments visible).
+// matrix core) and d_v columns dvpair(w, 0..1, 0..15) of the state, whose value
+// operands it reads straight from memory (one dword per token row holds both
+// of a lane's columns).  Two barriers per chunk: B1a (tile totals visible,
+// previous update done) and B1 (k-hat^T fragments visible).
 struct LdsState {
   static constexpr int WK = 0;                   // Wphi_k^T frags [4 mt][4 s]
-  static constexpr int VT = WK + 16 * kFrag;     // V^T half frags [4 tile][8 dv tile]
-  static constexpr int KH = VT + 32 * kHalf;     // k-hat^T frags [8 mt][2 sp]
+  static constexpr int KH = WK + 16 * kFrag;     // k-hat^T frags [8 mt][2 sp]
   static constexpr int T = KH + 16 * kFrag;      // tile decay totals (-log2-gate sums) [4 tile][128]
   static constexpr int BYTES = T + 4 * kF * 4;
 };
@@ -213,7 +213,7 @@ void state_kernel(ChunkParams p) {
   const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const HeadBufs hb = head_bufs(p, bh);
   const unsigned ro = row_off(wave);
-  // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvcol(wave, dt, n)]
+  // state slice: S[mt][dt][j] = S[feat(g, 4mt + j)][dvpair(wave, dt, n)]
   f32x4 S[8][2];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -222,9 +222,20 @@ void state_kernel(ChunkParams p) {
   // base-2 log-decay of the chunks after the current one (features 2n, 2n+1 of
   // the group); the slice total at the end
   float rsum2[2] = {0.0f, 0.0f};
-  bf16x8 xk[4], xv[4], xg[4];
+  // value operands of d_v columns dvpair(wave, dt, n) over token tiles (2sp,
+  // 2sp + 1): dwords of tokens 16T + 4g + j (vraw), packed per column tile
+  uint32_t vraw[4][4];
+  auto load_v = [&](int cc) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vraw[T][j] = __builtin_amdgcn_raw_buffer_load_b32(
+            hb.v, (int)(chunk_off(cc) + (unsigned)(16 * T + 4 * g + j) * (kDV * 2) + 64 * wave + 4 * n), 0, 0);
+  };
+  bf16x8 xk[4], xg[4];
   load_rows(hb.k, ro + chunk_off(c_end - 1), xk);
-  load_vals(hb.v, ro + chunk_off(c_end - 1), xv);
+  load_v(c_end - 1);
   load_gates<SG>(hb, ro + chunk_off(c_end - 1), xg);
   __syncthreads();
 
@@ -250,19 +261,22 @@ void state_kernel(ChunkParams p) {
     hedgehog_exp(u, e, izp, izn);
     __syncthreads();  // B1a: tile totals visible; the previous update done
 
-    // ---- V^T fragments of this tile
-    {
-      char *base = smem + LD::VT + wave * 8 * kHalf + lane * 8;
+    // ---- value operands of this chunk, then the preceding chunk's dwords requested
+    bf16x8 bv[2][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        f32x4 t2[2];
+    for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) t2[dt] = mfma(xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint32_t halves = dt ? 0x07060302u : 0x05040100u;  // high or low halves
+        u32x4 r;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) *(bf16x4 *)(base + (2 * s + dt) * kHalf) = pack4(t2[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const int T = 2 * sp + (e >> 1), hh = e & 1;
+          r[e] = __builtin_amdgcn_perm(vraw[T][2 * hh + 1], vraw[T][2 * hh], halves);
+        }
+        bv[sp][dt] = __builtin_bit_cast(bf16x8, r);
       }
-    }
-    load_vals(hb.v, ro1, xv);  // preceding chunk's values
+    load_v(c - 1);  // preceding chunk's values
     // ---- k-hat = phi_k 2^{B - b + R} with B - b = (B - P_w) - b_loc <= 0
     float base[2];  // B - P_w + R, then R += B
     {
@@ -309,18 +323,10 @@ void state_kernel(ChunkParams p) {
           *(bf16x4 *)(smem + LD::KH + ((2 * m2 + d2) * 2 + sp) * kFrag + lane * 16 + hf * 8) = pack4(t2[d2]);
       }
     }
-    __syncthreads();  // B1: k-hat^T and V^T fragments visible
+    __syncthreads();  // B1: k-hat^T fragments visible
 
     // ---- S += k-hat^T V (columns of this wave), fragments of a group of 4 state
     // tiles requested together
-    bf16x8 bv[2][2];
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const char *vb = smem + LD::VT + ((2 * sp) * 8 + 2 * wave + dt) * kHalf + lane * 8;
-        bv[sp][dt] = join44(*(const bf16x4 *)vb, *(const bf16x4 *)(vb + 8 * kHalf));
-      }
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {  // grp = 2 sp + (mt / 4)
       const int sp = grp >> 1, mb = 4 * (grp & 1);
@@ -342,7 +348,7 @@ void state_kernel(ChunkParams p) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvcol(wave, dt, n)] = S[mt][dt][j];
+      for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvpair(wave, dt, n)] = S[mt][dt][j];
   if (wave == 0) {
     float *dd = p.seg_decay + (bh * NS + seg) * (size_t)kF;
     *(float2 *)(dd + feat(g, 2 * n)) = make_float2(rsum2[0], rsum2[1]);
