@@ -157,14 +157,9 @@ __device__ __forceinline__ float row_bcast(float x, int src) {
 // feature index of fold slot i (0..31) of lane group g: phi+ half then phi- half
 __device__ __forceinline__ int feat(int g, int i) { return 64 * (i >> 4) + 16 * g + (i & 15); }
 
-// d_v column held by lane n, column-tile dt, of wave w (8 contiguous per lane group)
-__device__ __forceinline__ int dvcol(int w, int dt, int n) {
-  return 32 * w + 8 * (n >> 2) + 4 * dt + (n & 3);
-}
-
-// d_v column held by lane n, column-tile dt, of wave w in the output pass: the
-// two column tiles of a lane are adjacent columns, so one dword of a value row
-// feeds both
+// d_v column held by lane n, column-tile dt, of wave w (state pass and output
+// pass): the two column tiles of a lane are adjacent columns, so one dword of a
+// value row feeds both
 __device__ __forceinline__ int dvpair(int w, int dt, int n) { return 32 * w + 2 * n + dt; }
 
 // 0/1 selection operand: as the B operand of a 16x16x32 MFMA, output column n
