@@ -41,10 +41,10 @@ PREFILL_FLOPS_PER_TOKEN_HEAD = 2 * (2 * 128 * 64 + 65 * 128 + 128 * 128 + 128 * 
 # weights x V 96, state update 128, the two projections 128, window bands 80,
 # intra tiles 40 = 600 MFMAs; state pass (7/8 of the tokens): projection 64 +
 # update 128 = 192 per chunk.  Transposes on the matrix core (0/1 selection
-# operands, no arithmetic work) are counted apart: 32 per output-pass chunk, 64
-# per state-pass chunk.
+# operands, no arithmetic work) are counted apart: 32 per output-pass chunk, 32
+# per state-pass chunk (the k-hat^T fragments).
 PREFILL_EXECUTED_FLOPS_PER_TOKEN_HEAD = (600 * 16384 + 192 * 16384 * 7 // 8) // 64
-PREFILL_TRANSPOSE_FLOPS_PER_TOKEN_HEAD = (32 * 16384 + 64 * 16384 * 7 // 8) // 64
+PREFILL_TRANSPOSE_FLOPS_PER_TOKEN_HEAD = (32 * 16384 + 32 * 16384 * 7 // 8) // 64
 
 
 # backward at d = f = d_v = 128 (bf16): q, k, v, gate and dO read once, dq, dk,
