@@ -25,9 +25,14 @@
 // Window part.  P_tj = e^{s_tj - lse_t}, with the sinks' e^{t_m} inside the
 // normaliser; D_t = dO_t . o_swa,t; ds_tj = P_tj (dO_t . v_j - D_t); a query
 // kernel gives dq, lse, D and the sink gradient -sum_t P_tm D_t; a key kernel
-// gives dk_j = scale sum_t ds_tj q_t and dv_j = sum_t P_tj dO_t.  The two
-// window kernels run on a side stream beside the prologue and the sweeps; the
-// per-token kernel, which adds their dq, dk and dv, waits for them.
+// gives dk_j = scale sum_t ds_tj q_t and dv_j = sum_t P_tj dO_t.  On the
+// matrix-core path (bf16, one gate per feature, window <= 64) the window
+// kernels run after the state walks, which write the gated part's dv to the
+// output rows: the key kernel adds its dv there and writes dq and dk there, and
+// the per-token kernel adds the gated part's dq and dk in place.  Otherwise
+// they run on a side stream beside the prologue and the sweeps, into the
+// workspace, and the per-token kernel, which adds their dq, dk and dv, waits
+// for them.
 //
 // Every reduction is done in a fixed order into per-block partials (no atomics),
 // so the gradients are bitwise repeatable.  All arithmetic is fp32.
@@ -1393,13 +1398,18 @@ size_t sweep_slices(const LayerArgs &a, int parts) {
 // 32 features
 size_t row_parts(const LayerArgs &a, int parts) { return use_walk(a, parts) ? 1 : (size_t)(a.f + 31) / 32; }
 
-// The per-token kernel on the matrix cores (per-feature gates, bf16, d = f =
-// d_v = 128, after the walks) and the matrix-core window kernels.
-bool use_feat_mfma(const LayerArgs &a, int parts) {
-  return use_walk(a, parts) && bwd_feat_mfma_supported(a.d, a.f, a.dv, a.L, a.gate_mode, a.bf16);
-}
+// The matrix-core window kernels, and the per-token kernel on the matrix cores
+// (per-feature gates, bf16, d = f = d_v = 128, after the walks).  With the
+// latter the window part, when it runs, is the matrix-core one and goes first:
+// it writes its dq, dk, dv into the output rows, the reverse walk adds the
+// gated part's dv to them and the per-token kernel its dq and dk, so neither
+// part's gradients pass through the workspace.
 bool use_win_mfma(const LayerArgs &a, int parts) {
   return (parts & PART_SWA) && bwd_window_mfma_supported(a.d, a.dv, a.window, a.n_meta, a.bf16);
+}
+bool use_feat_mfma(const LayerArgs &a, int parts) {
+  return use_walk(a, parts) && bwd_feat_mfma_supported(a.d, a.f, a.dv, a.L, a.gate_mode, a.bf16) &&
+         (!(parts & PART_SWA) || use_win_mfma(a, parts));
 }
 // dW partials per head: one a block of the matrix-core per-token kernel, else
 // one a 64-token tile
@@ -1414,9 +1424,11 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t BH = (size_t)a.B * a.H, N = BH * a.L;
   const size_t nsl = sweep_slices(a, parts), nw = row_parts(a, parts);
   const size_t nft = (a.L + kFeatTok - 1) / kFeatTok, nsb = (a.L + kSwaTok - 1) / kSwaTok;
-  // the window part's dq, dk, dv: bf16 from the matrix-core kernels
+  // the window part's dq, dk, dv: bf16 from the matrix-core kernels, none when
+  // they go straight to the output rows
   const size_t wsz = use_win_mfma(a, parts) ? 2 : 1;
-  const bool gla = parts & PART_GLA, swa = parts & PART_SWA;
+  const bool gla = parts & PART_GLA, swa = parts & PART_SWA, feat_mfma = use_feat_mfma(a, parts);
+  const size_t nws = swa && !feat_mfma ? N : 0;
   BwdLayout o;
   size_t at = 0;
   auto take = [&](size_t n) { const size_t r = at; at += up64(n); return r; };
@@ -1425,12 +1437,12 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   const size_t nt = gla ? BH * nft * a.f : 0;
   o.tq = take(nsl * nt); o.tk = take(nsl * nt); o.ta = take(nt);
   o.dpq = take(nsl * nf); o.dpk = take(nsl * nf);
-  // the gated part's dv: bf16 for the matrix-core per-token kernel
-  o.dvg = take(gla ? (use_feat_mfma(a, parts) ? N * a.dv / 2 : nw * N * a.dv) : 0);
+  // the gated part's dv (none when the reverse walk writes the finished dv)
+  o.dvg = take(gla && !feat_mfma ? nw * N * a.dv : 0);
   o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
   o.lse = take(swa ? N : 0); o.del = take(swa ? N : 0);
-  o.dqs = take(swa ? N * a.d / wsz : 0); o.dks = take(swa ? N * a.d / wsz : 0);
-  o.dvs = take(swa ? N * a.dv / wsz : 0);
+  o.dqs = take(nws * a.d / wsz); o.dks = take(nws * a.d / wsz);
+  o.dvs = take(nws * a.dv / wsz);
   const size_t wp = gla ? BH * dw_partials(a, parts) * a.d * (a.f / 2) : 0;
   o.wqp = take(wp); o.wkp = take(wp);
   o.gp = take(gla ? BH * nft : 0);
@@ -1517,11 +1529,13 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
   const dim3 block(kBT);
   hipError_t e = hipSuccess;
   auto launched = [&]() { if (e == hipSuccess) e = hipGetLastError(); return e == hipSuccess; };
-  // the window part on the side stream when both parts run (forked from and
-  // joined back to the caller's stream), else on the caller's stream
+  // the window part on the side stream when both parts run and meet only in
+  // the per-token kernel (forked from and joined back to the caller's stream),
+  // else on the caller's stream: with the matrix-core per-token kernel it goes
+  // first and the reverse walk adds to its dv
   std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
   SideStream *ss = nullptr;
-  if (p.gla && p.swa && a.L > 0 && BH > 0) {
+  if (p.gla && p.swa && !feat_mfma && a.L > 0 && BH > 0) {
     lock.lock();
     ss = side_stream(a.stream);
     if (!ss) lock.unlock();
@@ -1531,35 +1545,45 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
     if ((e = hipEventRecord(ss->fork, a.stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
   }
-  if (p.swa && a.L > 0) {
+  // the window part: on the side stream, or (matrix-core per-token kernel)
+  // after the walks, adding its dv to theirs in the output rows
+  auto launch_window = [&]() -> hipError_t {
+    if (!p.swa || a.L <= 0) return hipSuccess;
     if (win_mfma) {
       WinBwdArgs wa;
       wa.q = a.q; wa.k = a.k; wa.v = a.v; wa.dout = g.dout; wa.meta = a.meta;
-      wa.lse = p.lse; wa.del = p.del; wa.dq = p.dqs; wa.dk = p.dks; wa.dv = p.dvs; wa.mp = p.mp;
+      wa.lse = p.lse; wa.del = p.del; wa.mp = p.mp;
+      if (feat_mfma) {
+        wa.dq = g.dq; wa.dk = g.dk; wa.dv = g.dv; wa.add_dv = p.gla;
+      } else {
+        wa.dq = p.dqs; wa.dk = p.dks; wa.dv = p.dvs;
+      }
       wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta; wa.nsb = p.nmp;
       wa.scale = a.scale;
-      if ((e = launch_bwd_window_mfma(wa, wstream)) != hipSuccess) return e;
-    } else if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
+      return launch_bwd_window_mfma(wa, wstream);
+    }
+    if (std::is_same<T, bf16>::value && a.d == kWD && a.dv == kWD && a.window <= kWC && a.n_meta <= 16) {
       const unsigned nch = (unsigned)((a.L + kWC - 1) / kWC);
       const size_t lds = sizeof(WinTileLds);
       // dynamic LDS above 64 KiB has to be allowed for each kernel
-      e = hipFuncSetAttribute((const void *)bwd_swa_tile_q_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)bwd_swa_tile_kv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-      if (e != hipSuccess) return e;
+      hipError_t we = hipFuncSetAttribute((const void *)bwd_swa_tile_q_kernel,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (we == hipSuccess)
+        we = hipFuncSetAttribute((const void *)bwd_swa_tile_kv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds);
+      if (we != hipSuccess) return we;
       hipLaunchKernelGGL(bwd_swa_tile_q_kernel, dim3(BH * nch), dim3(kWT), lds, wstream, p);
-      if (!launched()) return e;
+      if ((we = hipGetLastError()) != hipSuccess) return we;
       hipLaunchKernelGGL(bwd_swa_tile_kv_kernel, dim3(BH * nch), dim3(kWT), lds, wstream, p);
-      if (!launched()) return e;
-    } else {
-      hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
-      if (!launched()) return e;
-      hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
-      if (!launched()) return e;
+      return hipGetLastError();
     }
-  }
+    hipLaunchKernelGGL(bwd_swa_q_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
+    hipError_t we = hipGetLastError();
+    if (we != hipSuccess) return we;
+    hipLaunchKernelGGL(bwd_swa_kv_kernel<T>, dim3(BH * p.nsb), block, 0, wstream, p);
+    return hipGetLastError();
+  };
+  if (!feat_mfma && (e = launch_window()) != hipSuccess) return e;
   if (p.gla && a.L > 0 && use_walk(a, parts) && bwd_prep_mfma_supported(a.d, a.f, a.L, a.bf16)) {
     PrepArgs pa;
     pa.q = a.q; pa.k = a.k; pa.gate = a.gate; pa.wq = a.wq; pa.wk = a.wk;
@@ -1583,7 +1607,8 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
       wa.state_in = a.state_in; wa.dstate_out = p.dstate_out;
       wa.dpq = p.dpq; wa.dpk = p.dpk; wa.dvg = p.dvg; wa.tq = p.tq; wa.tk = p.tk; wa.xs = p.xs;
       wa.dstate_in = g.dstate_in;
-      wa.BH = (int)BH; wa.L = a.L; wa.nft = p.nft; wa.dv_bf16 = feat_mfma;
+      wa.dv = g.dv; wa.dv_mode = feat_mfma ? (p.swa ? 2 : 1) : 0;
+      wa.BH = (int)BH; wa.L = a.L; wa.nft = p.nft;
       if ((e = launch_bwd_walk(wa, a.stream)) != hipSuccess) return e;
     } else {
       hipLaunchKernelGGL(bwd_sweeps_kernel<T>, dim3(2 * BH * p.nsl), block, 0, a.stream, p);
@@ -1595,6 +1620,7 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
       if (!launched()) return e;
     }
   }
+  if (feat_mfma && (e = launch_window()) != hipSuccess) return e;
   if (ss) {  // the per-token kernel reads the window part's outputs
     if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(a.stream, ss->join, 0)) != hipSuccess) return e;
@@ -1603,9 +1629,9 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
   if (a.L > 0 && BH > 0 && feat_mfma) {
     FeatArgs fa;
     fa.q = a.q; fa.k = a.k; fa.gate = a.gate; fa.wq = a.wq; fa.wk = a.wk;
-    fa.pq = p.pq; fa.pk = p.pk; fa.dpq = p.dpq; fa.dpk = p.dpk; fa.dvg = p.dvg; fa.ta = p.ta;
-    if (p.swa) { fa.dqs = p.dqs; fa.dks = p.dks; fa.dvs = p.dvs; fa.win_bf16 = p.win_bf16 != 0; }
-    fa.dq = g.dq; fa.dk = g.dk; fa.dv = g.dv; fa.dg = g.dgate; fa.wqp = p.wqp; fa.wkp = p.wkp;
+    fa.pq = p.pq; fa.pk = p.pk; fa.dpq = p.dpq; fa.dpk = p.dpk; fa.ta = p.ta;
+    fa.swa = p.swa;
+    fa.dq = g.dq; fa.dk = g.dk; fa.dg = g.dgate; fa.wqp = p.wqp; fa.wkp = p.wkp;
     fa.BH = (int)BH; fa.H = a.H; fa.L = a.L; fa.nft = p.nft; fa.gate_is_log = a.gate_is_log;
     if ((e = launch_bwd_feat_mfma(fa, a.stream)) != hipSuccess) return e;
   } else if (a.L > 0 && BH > 0) {

@@ -2,14 +2,14 @@
 // matrix cores: bf16, d = f = d_v = 128, one gate per feature.
 //
 // From the feature maps phi (the prologue's fp32 [B H L][128]), their gradients
-// dphi (the state walks) and the window part's dq, dk, dv (bf16 or fp32, or
-// none):
+// dphi (the state walks) and, when the window part runs, its dq and dk already
+// in the output rows (bf16; each is read and then overwritten by the same lane):
 //   Hedgehog map ("Lizard" technical summary, gist.science 2507.09025,
 //   Methodology A.1): phi = [softmax(u), softmax(-u)], u = x W (W [d][f/2]).
 //   The gradient of u is du = phi+ (dphi+ - phi+ . dphi+) - phi- (dphi- -
 //   phi- . dphi-) (the softmax Jacobian of each half), so
 //     dx = du W^T (+ the window part),  dW += x^T du,
-//   dv = the gated part's dv + the window part's, and the gate gradient from
+//   and the gate gradient from
 //   d log Gamma_t = d log Gamma at the 64-token tile's first token minus the sum
 //   over the tile's earlier tokens of phiq . dphiq - phik . dphik (per
 //   feature), times d log Gamma / d gate.
@@ -25,7 +25,7 @@
 //            turned to feature rows by an identity product, hi + lo); the gate
 //            gradient of features [32 w, 32 w + 32) (a scan over the tokens of
 //            the sub-tile).
-// dv of columns [32 w, 32 w + 32) is summed in phase 1.
+// dv is not touched here: the reverse state walk writes the finished dv.
 // The LDS halves are double-buffered: one barrier a sub-tile.  dW leaves as one
 // fp32 partial a block ([B H][blocks][d][f/2]).
 #include <algorithm>
@@ -74,16 +74,11 @@ __device__ __forceinline__ bf16x4 ld4h(__amdgpu_buffer_rsrc_t r, unsigned off) {
 __device__ __forceinline__ void st4h(__amdgpu_buffer_rsrc_t r, unsigned off, bf16x4 x) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, (int)off, 0, 0);
 }
-__device__ __forceinline__ void st8h(__amdgpu_buffer_rsrc_t r, unsigned off, bf16x8 x) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
-}
 
 struct FeatParams {
   const bf16 *q, *k, *gate, *wq, *wk;
   const float *pq, *pk, *dpq, *dpk, *ta;        // [B H L][128] x 4, [B H][tiles][128]
-  const bf16 *dvg;                              // [B H L][128]: the gated part's dv
-  const void *dqs, *dks, *dvs;                  // window part [B H L][128] (bf16 or fp32) or null
-  bf16 *dq, *dk, *dv, *dg;
+  bf16 *dq, *dk, *dg;                           // dq, dk hold the window part on entry (SWA)
   float *wqp, *wkp;                             // [B H][blocks][128][64]
   int H, L, nft, span, nblk, gate_is_log;       // span: 16-token sub-tiles a block (a multiple of 4)
 };
@@ -95,7 +90,7 @@ __device__ __forceinline__ unsigned slot_off(int buf, int m, int hf, int i) {
   return (unsigned)((((buf * 2 + m) * 2 + hf) * 4 + i) * 64 + (int)(threadIdx.x & 63)) * 16u;
 }
 
-template <bool SWA, bool WB>
+template <bool SWA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_feat_mfma_kernel(FeatParams p) {
   __shared__ __align__(16) char sdu[kSlots * 1024];
   __shared__ __align__(16) char sep[kSlots * 1024];
@@ -110,22 +105,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const __amdgpu_buffer_rsrc_t rph = rows_rsrc(m ? p.pk : p.pq, row0 * 512, rowbytes);
   const __amdgpu_buffer_rsrc_t rdp = rows_rsrc(m ? p.dpk : p.dpq, row0 * 512, rowbytes);
   const __amdgpu_buffer_rsrc_t rx = rows_rsrc(m ? p.k : p.q, row0 * 256, hrowbytes);
+  // dx rows: the window part's on entry (SWA), the whole gradient on exit
   const __amdgpu_buffer_rsrc_t rdx = rows_rsrc(m ? p.dk : p.dq, row0 * 256, hrowbytes);
-  // the window part's rows: bf16 (WB) or fp32
-  constexpr unsigned kWs = WB ? 2u : 4u;
-  const __amdgpu_buffer_rsrc_t rsx = rows_rsrc(SWA ? (m ? p.dks : p.dqs) : p.pq, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
-  const __amdgpu_buffer_rsrc_t rvg = rows_rsrc(p.dvg, row0 * 256, hrowbytes);
-  const __amdgpu_buffer_rsrc_t rvs = rows_rsrc(SWA ? p.dvs : (const void *)p.dvg, row0 * 128 * kWs, (unsigned)L * 128u * kWs);
-  // four window-part values at element offset e of token row tok
-  auto wld4 = [&](__amdgpu_buffer_rsrc_t r, unsigned tok, unsigned e) -> f32x4 {
-    if constexpr (WB) {
-      const bf16x4 h = ld4h(r, tok * 256u + e * 2u);
-      return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-    } else {
-      return ld4f(r, tok * 512u + e * 4u);
-    }
-  };
-  const __amdgpu_buffer_rsrc_t rdv = rows_rsrc(p.dv, row0 * 256, hrowbytes);
   const __amdgpu_buffer_rsrc_t rg = rows_rsrc(p.gate, row0 * 256, hrowbytes);
   const __amdgpu_buffer_rsrc_t rdg = rows_rsrc(p.dg, row0 * 256, hrowbytes);
   const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
@@ -173,16 +154,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ph[i] = xph[i];
       dp[i] = xdp[i];
     }
-    // this sub-tile's dv (columns 32 wave + 8 g .. + 7) and the phase-2
-    // operands, loaded now: x rows (value layout, columns 32 s + 8 g .. + 7 for
-    // s = 2 hf, 2 hf + 1), the gates
-    f32x4 vg[2], vs[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const bf16x4 h = ld4h(rvg, tok * 256u + (unsigned)(32 * wave + 8 * g + 4 * a) * 2u);
-      vg[a] = (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-      vs[a] = SWA ? wld4(rvs, tok, (unsigned)(32 * wave + 8 * g + 4 * a)) : zf4();
-    }
+    // the phase-2 operands, loaded now: x rows (value layout, columns
+    // 32 s + 8 g .. + 7 for s = 2 hf, 2 hf + 1), the gates
     bf16x8 xv[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) xv[a] = bload(rx, tok * 256u + 16u * g + 64u * (2 * hf + a));
@@ -213,12 +186,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *(f32x4 *)(sdu + slot_off(buf, m, hf, i)) = ph[i] * (dp[i] - sum) * sg;
       *(f32x4 *)(sep + slot_off(buf, m, hf, i)) = e[i];
     }
-    st8h(rdv, tok * 256u + (unsigned)(32 * wave + 8 * g) * 2u, pack44(vg[0] + vs[0], vg[1] + vs[1]));
     __syncthreads();
     // ---- phase 2: the window part's dx first (added after dW)
     f32x4 sx[4];
 #pragma unroll
-    for (int et = 0; et < 4; ++et) sx[et] = SWA ? wld4(rsx, tok, (unsigned)(64 * hf + 16 * et + 4 * g)) : zf4();
+    for (int et = 0; et < 4; ++et) {
+      if (SWA) {
+        const bf16x4 h = ld4h(rdx, tok * 256u + (unsigned)(64 * hf + 16 * et + 4 * g) * 2u);
+        sx[et] = (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      } else {
+        sx[et] = zf4();
+      }
+    }
     // du of map m (rows over tokens), hi + lo
     bf16x4 duh[4], dul[4];
 #pragma unroll
@@ -299,21 +278,18 @@ hipError_t launch_bwd_feat_mfma(const FeatArgs &a, hipStream_t stream) {
   FeatParams p;
   p.q = (const bf16 *)a.q; p.k = (const bf16 *)a.k; p.gate = (const bf16 *)a.gate;
   p.wq = (const bf16 *)a.wq; p.wk = (const bf16 *)a.wk;
-  p.pq = a.pq; p.pk = a.pk; p.dpq = a.dpq; p.dpk = a.dpk; p.dvg = (const bf16 *)a.dvg; p.ta = a.ta;
-  p.dqs = a.dqs; p.dks = a.dks; p.dvs = a.dvs;
-  p.dq = (bf16 *)a.dq; p.dk = (bf16 *)a.dk; p.dv = (bf16 *)a.dv; p.dg = (bf16 *)a.dg;
+  p.pq = a.pq; p.pk = a.pk; p.dpq = a.dpq; p.dpk = a.dpk; p.ta = a.ta;
+  p.dq = (bf16 *)a.dq; p.dk = (bf16 *)a.dk; p.dg = (bf16 *)a.dg;
   p.wqp = a.wqp; p.wkp = a.wkp;
   p.H = a.H; p.L = a.L; p.nft = a.nft; p.gate_is_log = a.gate_is_log ? 1 : 0;
   p.span = bwd_feat_span(a.BH, a.L);
   p.nblk = (int)(((a.L + 15) / 16 + p.span - 1) / p.span);
   if (a.BH == 0 || a.L == 0) return hipSuccess;
   const dim3 grid((unsigned)(a.BH * p.nblk)), block(256);
-  if (a.dqs && a.win_bf16)
-    hipLaunchKernelGGL((bwd_feat_mfma_kernel<true, true>), grid, block, 0, stream, p);
-  else if (a.dqs)
-    hipLaunchKernelGGL((bwd_feat_mfma_kernel<true, false>), grid, block, 0, stream, p);
+  if (a.swa)
+    hipLaunchKernelGGL(bwd_feat_mfma_kernel<true>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_feat_mfma_kernel<false, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL(bwd_feat_mfma_kernel<false>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

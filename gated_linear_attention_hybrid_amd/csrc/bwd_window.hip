@@ -17,11 +17,14 @@
 //                 D, and forms dq^T = K^T ds^T
 //   key kernel    wave w owns key tile w; with the query kernel's lse and D it
 //                 recomputes P for the five query tiles that reach it (this and
-//                 the next chunk), and forms dv^T = dO^T P and dk^T = Q^T ds
+//                 the next chunk), and forms dv^T = dO^T P and dk^T = Q^T ds;
+//                 dv is either written or added to the bf16 dv already in its
+//                 rows (the gated part's)
 // Every product is a 16x16x32 bf16 MFMA with fp32 accumulation; P and ds enter
-// as bf16 operands.  The transposed operands (K^T, Q^T, dO^T) are made on the
-// matrix core from the token rows (a product with 0/1 selection operands) and
-// staged in LDS as half fragments.
+// as bf16 operands.  The token rows are staged in LDS once; the transposed
+// operands (K^T, Q^T, dO^T: four tokens of one feature per lane) are read from
+// those rows with gfx950's transposing LDS read, so a block needs 65 KiB and
+// two blocks share a compute unit.
 #include "chunk_common.hpp"
 #include "launch.hpp"
 
@@ -34,32 +37,40 @@ constexpr int kWNT = 256;  // four waves
 struct LdsWinQ {
   static constexpr int KR = 0;                // key rows [8 tiles][4 s] (previous chunk tiles 0-3, this chunk 0-3)
   static constexpr int VR = KR + 32 * kFrag;  // value rows, same
-  static constexpr int KT = VR + 32 * kFrag;  // K^T half fragments [8 tiles][8 (s, dt)]
-  static constexpr int MP = KT + 64 * kHalf;  // sink gradient partials [4 waves][64]
+  static constexpr int MP = VR + 32 * kFrag;  // sink gradient partials [4 waves][64]
   static constexpr int BYTES = MP + 4 * 64 * 4;
 };
 
 struct LdsWinK {
   static constexpr int QR = 0;                // query rows [8 tiles][4 s] (this chunk tiles 0-3, next chunk 0-3)
   static constexpr int OR = QR + 32 * kFrag;  // dO rows, same
-  static constexpr int QT = OR + 32 * kFrag;  // Q^T half fragments [8 tiles][8 (s, dt)]
-  static constexpr int OT = QT + 64 * kHalf;  // dO^T half fragments
-  static constexpr int LS = OT + 64 * kHalf;  // lse and D of the 128 queries [2][128] fp32
+  static constexpr int LS = OR + 32 * kFrag;  // lse and D of the 128 queries [2][128] fp32
   static constexpr int BYTES = LS + 2 * 128 * 4;
 };
 
-// Transposed half fragments of one 16-token tile from its rows in the value
-// layout (lane (n, g) holding x[token n][32 s + 8 g + j]): for d tile (s, dt)
-// lane (n, g) gets x[token 4 g + r][32 s + 8 (n / 4) + 4 dt + n % 4], r = 0..3,
-// the A operand of a 16x16x16 product over tokens whose row n is that feature.
-__device__ __forceinline__ void stage_transposed(char *dst, const bf16x8 *xv, const bf16x8 *sel) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-      *(bf16x4 *)(dst + (2 * s + dt) * kHalf + lane * 8) =
-          pack4(mfma(xv[s], sel[dt], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}));
+// Blocks are dealt to the 8 XCDs in turn (block b to XCD b % 8).  Number the
+// chunks so that each XCD takes a contiguous run of them: a block reads the rows
+// of its neighbouring chunk too, which its neighbour then finds in the same L2.
+__device__ __forceinline__ unsigned xcd_run(unsigned b, unsigned grid) {
+  const unsigned x = b & 7, per = grid >> 3, rem = grid & 7;
+  return x * per + min(x, rem) + (b >> 3);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_ptr;
+
+// Transposed half fragment of d tile (s, dt) of row tile tl, from token rows
+// staged as load_rows lays them (fragment (tl, s'), lane (n, g) holding
+// x[token 16 tl + n][32 g + 8 s' + j]): lane (n, g) gets
+// x[token 16 tl + 4 g + r][32 s + 8 (n / 4) + 4 dt + n % 4], r = 0..3, the A
+// operand of a 16x16x16 product over tokens whose row n is that feature.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane row element i % 4 of the
+// 8-byte chunks addressed by lanes 4 r + i / 4 of that row (r = 0..3), so lane
+// (m, g) addresses token 4 g + m / 4, features 32 s + 8 (m % 4) + 4 dt + 0..3.
+__device__ __forceinline__ bf16x4 tr_half(const char *rows, int tl, int s, int dt) {
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const char *p = rows + (tl * 4 + (m & 3)) * kFrag + (4 * g + (m >> 2) + 16 * s) * 16 + 8 * dt;
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(char *)p));
 }
 
 // Output row of d tile (s, dt) held by lane (n, g) in slot r of an accumulator
@@ -84,31 +95,29 @@ __global__ __launch_bounds__(kWNT) void bwd_win_q_kernel(WinBwdQ p) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const size_t bh = blockIdx.x / p.nchunks;
-  const int c = blockIdx.x % p.nchunks;
+  const unsigned blk = xcd_run(blockIdx.x, gridDim.x);
+  const size_t bh = blk / p.nchunks;
+  const int c = blk % p.nchunks;
   const int h = (int)(bh % p.H);
   const unsigned Lu = (unsigned)p.L;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(p.q, bh, p.L), rk = head_rsrc(p.k, bh, p.L),
                                rv = head_rsrc(p.v, bh, p.L), ro = head_rsrc(p.dout, bh, p.L);
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const unsigned rw = row_off(w);
 
-  // stage key and value rows and K^T of tile w of the previous chunk (ci = 0)
-  // and of this chunk (ci = 1); rows before 0 read zeros (offsets wrap past the
-  // range) and are masked below
+  // stage key and value rows of tile w of the previous chunk (ci = 0) and of
+  // this chunk (ci = 1); rows before 0 read zeros (offsets wrap past the range)
+  // and are masked below
 #pragma unroll
   for (int ci = 0; ci < 2; ++ci) {
-    bf16x8 xk[4], xv[4], xkv[4];
+    bf16x8 xk[4], xv[4];
     load_rows(rk, rw + chunk_off(c - 1 + ci), xk);
     load_rows(rv, rw + chunk_off(c - 1 + ci), xv);
-    load_vals(rk, rw + chunk_off(c - 1 + ci), xkv);
     const int tl = 4 * ci + w;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       sts8(smem + LD::KR + (tl * 4 + s) * kFrag + lane * 16, xk[s]);
       sts8(smem + LD::VR + (tl * 4 + s) * kFrag + lane * 16, xv[s]);
     }
-    stage_transposed(smem + LD::KT + tl * 8 * kHalf, xkv, sel);
   }
   bf16x8 xq[4], xo[4];
   load_rows(rq, rw + chunk_off(c), xq);
@@ -214,9 +223,8 @@ __global__ __launch_bounds__(kWNT) void bwd_win_q_kernel(WinBwdQ p) {
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp) {
         const int k0 = w + 2 * pp, k1 = k0 + 1;
-        const bf16x4 lo = *(const bf16x4 *)(smem + LD::KT + (k0 * 8 + 2 * s + dt) * kHalf + lane * 8);
-        const bf16x4 hi = k1 < 8 && pp < 2 ? *(const bf16x4 *)(smem + LD::KT + (k1 * 8 + 2 * s + dt) * kHalf + lane * 8)
-                                           : z4;
+        const bf16x4 lo = tr_half(smem + LD::KR, k0, s, dt);
+        const bf16x4 hi = k1 < 8 && pp < 2 ? tr_half(smem + LD::KR, k1, s, dt) : z4;
         acc = mfma(join44(lo, hi), dsb[pp], acc);
       }
       if (live) *(bf16x4 *)(p.dq + orow + dcol(s, dt)) = pack4(acc * p.scale);
@@ -235,7 +243,7 @@ struct WinBwdK {
   const bf16 *q, *k, *v, *dout;
   const float *lse, *del;
   bf16 *dk, *dv;
-  int L, nchunks, window;
+  int L, nchunks, window, add_dv;  // add_dv: dv += this part (else dv = it)
   float scale;
 };
 
@@ -245,31 +253,27 @@ __global__ __launch_bounds__(kWNT) void bwd_win_k_kernel(WinBwdK p) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const size_t bh = blockIdx.x / p.nchunks;
-  const int c = blockIdx.x % p.nchunks;
+  const unsigned blk = xcd_run(blockIdx.x, gridDim.x);
+  const size_t bh = blk / p.nchunks;
+  const int c = blk % p.nchunks;
   const unsigned Lu = (unsigned)p.L;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(p.q, bh, p.L), rk = head_rsrc(p.k, bh, p.L),
                                rv = head_rsrc(p.v, bh, p.L), ro = head_rsrc(p.dout, bh, p.L);
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const unsigned rw = row_off(w);
 
-  // stage query and dO rows and their transposes of tile w of this chunk
-  // (ci = 0) and of the next one (ci = 1); rows past the end read zeros
+  // stage query and dO rows of tile w of this chunk (ci = 0) and of the next
+  // one (ci = 1); rows past the end read zeros
 #pragma unroll
   for (int ci = 0; ci < 2; ++ci) {
-    bf16x8 xq[4], xo[4], xqv[4], xov[4];
+    bf16x8 xq[4], xo[4];
     load_rows(rq, rw + chunk_off(c + ci), xq);
     load_rows(ro, rw + chunk_off(c + ci), xo);
-    load_vals(rq, rw + chunk_off(c + ci), xqv);
-    load_vals(ro, rw + chunk_off(c + ci), xov);
     const int tl = 4 * ci + w;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       sts8(smem + LD::QR + (tl * 4 + s) * kFrag + lane * 16, xq[s]);
       sts8(smem + LD::OR + (tl * 4 + s) * kFrag + lane * 16, xo[s]);
     }
-    stage_transposed(smem + LD::QT + tl * 8 * kHalf, xqv, sel);
-    stage_transposed(smem + LD::OT + tl * 8 * kHalf, xov, sel);
   }
   if (tid < 128) {
     const int t = c * kC + tid;
@@ -282,11 +286,21 @@ __global__ __launch_bounds__(kWNT) void bwd_win_k_kernel(WinBwdK p) {
   bf16x8 xk[4], xv[4];
   load_rows(rk, rw + chunk_off(c), xk);
   load_rows(rv, rw + chunk_off(c), xv);
+  const int jk = c * kC + 16 * w + n;  // this lane's key
+  const bool live = jk < p.L;
+  const unsigned orow = (bh * Lu + (unsigned)min(jk, p.L - 1)) * kD;
+  // the dv already in the output rows, to add to (loaded early)
+  bf16x4 dvo[4][2];
+  if (p.add_dv) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) dvo[s][dt] = *(const bf16x4 *)(p.dv + orow + dcol(s, dt));
+  }
   __syncthreads();
 
   // S and dP for query tiles w .. w + 4 (index in [0, 8)): lane (n, g) holds
   // key n of tile w and queries 16 qt + 4 g + r
-  const int jk = c * kC + 16 * w + n;  // this lane's key
   const float *lse = (const float *)(smem + LD::LS), *del = lse + 128;
   f32x4 pw[6], ds[6];
 #pragma unroll
@@ -326,8 +340,6 @@ __global__ __launch_bounds__(kWNT) void bwd_win_k_kernel(WinBwdK p) {
   }
   // dv^T = dO^T P, dk^T = Q^T ds: d tile (s, dt), lane (n, g) holds key n
   const bf16x4 z4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
-  const bool live = jk < p.L;
-  const unsigned orow = (bh * Lu + (unsigned)min(jk, p.L - 1)) * kD;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -337,15 +349,18 @@ __global__ __launch_bounds__(kWNT) void bwd_win_k_kernel(WinBwdK p) {
       for (int pp = 0; pp < 3; ++pp) {
         const int q0 = w + 2 * pp, q1 = q0 + 1;
         const bool h1 = q1 < 8 && pp < 2;
-        const int o0 = (q0 * 8 + 2 * s + dt) * kHalf + lane * 8, o1 = (q1 * 8 + 2 * s + dt) * kHalf + lane * 8;
-        const bf16x4 olo = *(const bf16x4 *)(smem + LD::OT + o0);
-        const bf16x4 ohi = h1 ? *(const bf16x4 *)(smem + LD::OT + o1) : z4;
-        const bf16x4 qlo = *(const bf16x4 *)(smem + LD::QT + o0);
-        const bf16x4 qhi = h1 ? *(const bf16x4 *)(smem + LD::QT + o1) : z4;
+        const bf16x4 olo = tr_half(smem + LD::OR, q0, s, dt);
+        const bf16x4 ohi = h1 ? tr_half(smem + LD::OR, q1, s, dt) : z4;
+        const bf16x4 qlo = tr_half(smem + LD::QR, q0, s, dt);
+        const bf16x4 qhi = h1 ? tr_half(smem + LD::QR, q1, s, dt) : z4;
         av = mfma(join44(olo, ohi), pb[pp], av);
         ak = mfma(join44(qlo, qhi), db[pp], ak);
       }
       if (live) {
+        if (p.add_dv) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) av[r] += (float)dvo[s][dt][r];
+        }
         *(bf16x4 *)(p.dv + orow + dcol(s, dt)) = pack4(av);
         *(bf16x4 *)(p.dk + orow + dcol(s, dt)) = pack4(ak * p.scale);
       }
@@ -374,7 +389,7 @@ hipError_t launch_bwd_window_mfma(const WinBwdArgs &a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WinBwdK pk;
   pk.q = pq.q; pk.k = pq.k; pk.v = pq.v; pk.dout = pq.dout; pk.lse = a.lse; pk.del = a.del;
-  pk.dk = (bf16 *)a.dk; pk.dv = (bf16 *)a.dv; pk.L = a.L; pk.nchunks = nchunks; pk.window = a.window; pk.scale = a.scale;
+  pk.dk = (bf16 *)a.dk; pk.dv = (bf16 *)a.dv; pk.add_dv = a.add_dv ? 1 : 0; pk.L = a.L; pk.nchunks = nchunks; pk.window = a.window; pk.scale = a.scale;
   e = hipFuncSetAttribute((const void *)bwd_win_k_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LdsWinK::BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_win_k_kernel, dim3(grid), dim3(kWNT), LdsWinK::BYTES, stream, pk);

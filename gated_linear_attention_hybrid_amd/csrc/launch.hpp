@@ -102,6 +102,7 @@ struct WinBwdArgs {
   const float *meta = nullptr;
   float *lse = nullptr, *del = nullptr, *mp = nullptr;
   void *dq = nullptr, *dk = nullptr, *dv = nullptr;  // bf16
+  bool add_dv = false;  // add dv to the bf16 values already there
   int B = 0, H = 0, L = 0, window = 0, n_meta = 0, nsb = 0;
   float scale = 1.0f;
 };
@@ -121,8 +122,9 @@ struct WalkArgs {
   const float *state_in = nullptr, *dstate_out = nullptr;
   float *dpq = nullptr, *dpk = nullptr, *dvg = nullptr, *tq = nullptr, *tk = nullptr, *xs = nullptr;
   float *dstate_in = nullptr, *ws = nullptr;
+  void *dv = nullptr;  // bf16 [B H L][128] (dv_mode 1)
   int BH = 0, L = 0, nft = 0;
-  bool dv_bf16 = false;  // dvg as bf16 [B H L][128] (for the matrix-core per-token kernel)
+  int dv_mode = 0;  // the gated part's dv: 0 to dvg (fp32), 1 to dv (bf16)
 };
 bool bwd_walk_supported(int f, int dv, int L, bool bf16);
 size_t bwd_walk_ws_floats(int BH, int L);
@@ -138,10 +140,8 @@ hipError_t launch_bwd_walk(const WalkArgs &a, hipStream_t stream);
 struct FeatArgs {
   const void *q = nullptr, *k = nullptr, *gate = nullptr, *wq = nullptr, *wk = nullptr;
   const float *pq = nullptr, *pk = nullptr, *dpq = nullptr, *dpk = nullptr, *ta = nullptr;
-  const void *dvg = nullptr;  // bf16 [B H L][128]: the gated part's dv from the walks
-  const void *dqs = nullptr, *dks = nullptr, *dvs = nullptr;
-  bool win_bf16 = false;
-  void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dg = nullptr;
+  bool swa = false;  // dq and dk hold the window part's gradient (bf16) on entry
+  void *dq = nullptr, *dk = nullptr, *dg = nullptr;
   float *wqp = nullptr, *wkp = nullptr;
   int BH = 0, H = 0, L = 0, nft = 0;
   bool gate_is_log = false;

@@ -222,22 +222,27 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  *               sums over the batch added up across them.
  * glah_bwd_workspace_bytes reports the whole call's workspace when it is at
  * most 1.5e9 bytes, else that of the largest sub-problem within that (at 32K
- * tokens, 32 heads of 128: blocks of 8 heads, 1.00 GB); (size_t)-1 for an
- * invalid descriptor, 0 when the sizes are not supported.
+ * tokens, 32 heads of 128: blocks of 16 heads, 1.41 GB; the whole call takes
+ * 2.77 GB); (size_t)-1 for an invalid descriptor, 0 when the sizes are not
+ * supported.
  * Supported: d_qk, d_v <= 128 and multiples of 4; f <= 128, a multiple of 4 with
  * f/2 a power of two; window <= 1024; n_meta <= 64 (otherwise GLAH_ENOTSUP).
  * Arithmetic: bf16 with d_qk = f = d_v = 128 runs on the matrix cores (bf16
  * operands, split into high and low bf16 halves where the gate gradient needs
- * more, fp32 accumulation; the window part's dq, dk, dv are rounded to bf16
- * before they are added to the gated part's; log-gates are floored at -10 as in
- * the forward); other sizes and fp32 run token-recurrent fp32 kernels.
+ * more, fp32 accumulation; one part's dq, dk, dv are rounded to bf16 before the
+ * other's are added to them; log-gates are floored at -10 as in the forward);
+ * other sizes and fp32 run token-recurrent fp32 kernels.  With one gate per
+ * feature and the window part on the matrix cores (window <= 64), the parts'
+ * gradients meet in the output rows: dq, dk, dv are written more than once
+ * during the call and hold the gradient only when it has finished.
  * Reductions over tokens and batch rows run in a fixed order, so results are
  * bitwise repeatable for a given ws_bytes.
- * Streams: with both parts (f > 0 and window > 0) the window part runs on a
- * side stream of the library (one per device, with two events, created on the
- * first such call and kept until the process ends), forked from `stream` at
- * the call and joined back into it before the call's last kernels, so all of
- * the call's work is ordered on `stream` as usual.  When `stream` is being
+ * Streams: the bf16 path of the previous paragraph runs on `stream` alone.  In
+ * the other cases with both parts (f > 0 and window > 0) the window part runs
+ * on a side stream of the library (one per device, with two events, created on
+ * the first such call and kept until the process ends), forked from `stream`
+ * at the call and joined back into it before the call's last kernels, so all
+ * of the call's work is ordered on `stream` as usual.  When `stream` is being
  * captured into a graph before the side stream exists, the call uses `stream`
  * alone.
  */

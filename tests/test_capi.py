@@ -198,8 +198,8 @@ def test_backward_workspace_sizing(lib):
     assert ws(1, 32, 2048) < ws(2, 32, 2048) <= gib               # small calls run whole
     assert whole(1, 32, 2048) == ws(1, 32, 2048) and whole(1, 32, 32768) > gib
     big = ws(1, 32, 32768)
-    assert big <= gib and big == ws(1, 8, 32768) > ws(1, 4, 32768)  # 32K: blocks of 8 heads
-    assert ws(8, 32, 8192) == ws(1, 32, 8192) <= gib               # batch 8: one row at a time
+    assert big <= gib and big == ws(1, 16, 32768) > ws(1, 8, 32768)  # 32K: blocks of 16 heads
+    assert ws(8, 32, 8192) == ws(2, 32, 8192) <= gib < whole(4, 32, 8192)  # batch 8: two rows at a time
     assert ws(1, 1, 1 << 22) > gib                                 # nothing fits: the least
 
 
