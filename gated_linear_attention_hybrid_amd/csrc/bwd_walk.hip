@@ -256,12 +256,19 @@ __device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, 
 
 // Blocks of four waves: the forward states of segments 0 .. P-2 (two blocks a
 // segment), then the reverse states of segments 1 .. P-1.
+// Blocks are dealt to the 8 XCDs in turn; when the counts allow, the two
+// blocks of a segment and direction (which read the same value or dO rows) are
+// numbered onto one XCD, each XCD taking a contiguous run of segments.
 __global__ __launch_bounds__(256) void bwd_walk_state_kernel(WalkParams p) {
   const int wave = threadIdx.x >> 6, per = 2 * (p.P - 1);
   const int nf = p.BH * per;
   int blk = blockIdx.x;
   const bool rev = blk >= nf;
   if (rev) blk -= nf;
+  if (nf % 16 == 0) {
+    const int x = blk & 7, l = blk >> 3;
+    blk = 2 * (x * (nf / 16) + (l >> 1)) + (l & 1);
+  }
   const int bh = blk / per, r = blk - bh * per, seg = r >> 1, ft = 4 * (r & 1) + wave;
   if (rev)
     rev_state(p, bh, seg + 1, ft);
@@ -622,7 +629,10 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
 
 // Blocks of four waves: the reverse walks (one block a head and segment) first,
 // then the forward walks (two blocks a head and segment).  Two waves a SIMD (a
-// few loop-invariant values spill to scratch) and 64 KiB of LDS a block.
+// few loop-invariant values spill to scratch) and 64 KiB of LDS a block.  When
+// the counts allow, the two forward blocks of a segment, which walk the same
+// value and dO rows in step, are numbered onto one XCD (blocks are dealt to the
+// 8 XCDs in turn; each XCD takes a contiguous run of segments).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_walk_kernel(WalkParams p) {
   __shared__ __align__(16) char lds[2 * kPartBytes];
   const int nrev = p.BH * p.P;
@@ -631,6 +641,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rev_walk(p, blk / p.P, blk % p.P, lds);
   } else {
     blk -= nrev;
+    if (nrev % 8 == 0) {
+      const int x = blk & 7, l = blk >> 3;
+      blk = 2 * (x * (nrev / 8) + (l >> 1)) + (l & 1);
+    }
     const int bh = blk / (2 * p.P), r = blk - bh * 2 * p.P;
     fwd_walk(p, bh, r >> 1, 4 * (r & 1) + (int)(threadIdx.x >> 6));
   }
