@@ -1440,7 +1440,9 @@ BwdLayout bwd_layout(const LayerArgs &a, int parts) {
   // the gated part's dv (none when the reverse walk writes the finished dv)
   o.dvg = take(gla && !feat_mfma ? nw * N * a.dv : 0);
   o.xs = take(gla ? 2 * BH * nsl * a.f : 0);
-  o.lse = take(swa ? N : 0); o.del = take(swa ? N : 0);
+  // lse and D of the window part (the matrix-core kernel keeps them in LDS)
+  const size_t nld = swa && !use_win_mfma(a, parts) ? N : 0;
+  o.lse = take(nld); o.del = take(nld);
   o.dqs = take(nws * a.d / wsz); o.dks = take(nws * a.d / wsz);
   o.dvs = take(nws * a.dv / wsz);
   const size_t wp = gla ? BH * dw_partials(a, parts) * a.d * (a.f / 2) : 0;
@@ -1552,13 +1554,13 @@ hipError_t bwd_dispatch(const LayerArgs &a, const BwdArgs &g, int parts, bool ac
     if (win_mfma) {
       WinBwdArgs wa;
       wa.q = a.q; wa.k = a.k; wa.v = a.v; wa.dout = g.dout; wa.meta = a.meta;
-      wa.lse = p.lse; wa.del = p.del; wa.mp = p.mp;
+      wa.mp = p.mp;
       if (feat_mfma) {
         wa.dq = g.dq; wa.dk = g.dk; wa.dv = g.dv; wa.add_dv = p.gla;
       } else {
         wa.dq = p.dqs; wa.dk = p.dks; wa.dv = p.dvs;
       }
-      wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta; wa.nsb = p.nmp;
+      wa.B = a.B; wa.H = a.H; wa.L = a.L; wa.window = a.window; wa.n_meta = a.n_meta;
       wa.scale = a.scale;
       return launch_bwd_window_mfma(wa, wstream);
     }

@@ -94,16 +94,15 @@ hipError_t launch_layer_bwd(const LayerArgs &a, const BwdArgs &g, int parts);
 
 // Window part of the backward on the matrix cores (bwd_window.hip): bf16,
 // d = d_v = 128, window <= 64, n_meta <= 64.  Writes the window part's dq, dk,
-// dv (bf16 [B][H][L][128]), the per-query lse and D = dO . o_swa (fp32
-// [B][H][L]) and the sink-gradient partial of every 64-token chunk ([B H][nsb]
-// [n_meta], nsb = chunks).
+// dv (bf16 [B][H][L][128]; dv optionally added to the values already there)
+// and the sink-gradient partial of every 64-token chunk ([B H][chunks][n_meta]).
 struct WinBwdArgs {
   const void *q = nullptr, *k = nullptr, *v = nullptr, *dout = nullptr;
   const float *meta = nullptr;
-  float *lse = nullptr, *del = nullptr, *mp = nullptr;
+  float *mp = nullptr;
   void *dq = nullptr, *dk = nullptr, *dv = nullptr;  // bf16
   bool add_dv = false;  // add dv to the bf16 values already there
-  int B = 0, H = 0, L = 0, window = 0, n_meta = 0, nsb = 0;
+  int B = 0, H = 0, L = 0, window = 0, n_meta = 0;
   float scale = 1.0f;
 };
 bool bwd_window_mfma_supported(int d, int dv, int window, int n_meta, bool bf16);
