@@ -290,20 +290,24 @@ def test_backward_8k_sampled_head():
     compare(sub, ref, TOL_BF16)
 
 
-def test_backward_graph_replays_match_eager():
-    """The window part runs on the library's side stream (forked from and joined
-    back into the caller's stream): captured into a graph after an eager call
-    has created that stream, every replay, with eager work in between, must give
-    the eager call's gradients bit for bit."""
+@pytest.mark.parametrize("kind", [OB.GATE_LOGITS, OB.GATE_LOG_TOKEN])
+def test_backward_graph_replays_match_eager(kind):
+    """Captured into a graph, every replay, with eager work in between, must
+    give the eager call's gradients bit for bit.  With one gate per feature the
+    call runs on the caller's stream alone (the parts' gradients meet in the
+    output rows); with per-token gates the window part runs on the library's
+    side stream, forked from and joined back into the caller's stream (the
+    capture follows an eager call that has created that stream)."""
     wl = WORKLOADS["prefill_2k"].with_(H=2, L=300)
-    say("backward graph capture and replays")
+    say("backward graph capture and replays, gate %s" % kind)
     x = make_prefill(wl, DEV)
+    g = gate_of(kind, x, wl, wl.torch_dtype)
     dO = grads_seed((wl.B, wl.H, wl.L, wl.dv), 8, wl.torch_dtype)
     names = ("q", "k", "v", "gate", "wq", "wk", "meta")
 
     def call():
-        return G.hybrid_layer_bwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], dO,
-                                  window=wl.window)
+        return G.hybrid_layer_bwd(x["q"], x["k"], x["v"], g, x["wq"], x["wk"], x["meta"], dO,
+                                  window=wl.window, gate_kind=GPU_KIND[kind])
 
     ref = call()
     torch.cuda.synchronize()
