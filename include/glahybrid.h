@@ -237,8 +237,8 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  * during the call and hold the gradient only when it has finished.
  * Reductions over tokens and batch rows run in a fixed order, so results are
  * bitwise repeatable for a given ws_bytes.
- * Streams: the bf16 path of the previous paragraph runs on `stream` alone.  In
- * the other cases with both parts (f > 0 and window > 0) the window part runs
+ * Streams: that path (bf16, d_qk = f = d_v = 128, one gate per feature, window
+ * <= 64) runs on `stream` alone.  In the other cases the window part runs
  * on a side stream of the library (one per device, with two events, created on
  * the first such call and kept until the process ends), forked from `stream`
  * at the call and joined back into it before the call's last kernels, so all
