@@ -270,6 +270,28 @@ def test_backward_full_length_sampled_heads():
         compare(sub, ref, TOL_BF16)
 
 
+def test_backward_window_runs_ragged_sampled_heads():
+    """32 heads of 2389 tokens (38 chunks, the last of 21 tokens) and a window of
+    37: the window kernel walks runs of 5 chunks, the last run holds 3, so the
+    ring, the halo chunk before and after each run and the run that ends the
+    sequence all run at the benchmark's head count; the oracle recomputes heads
+    0 and 17."""
+    wl = WORKLOADS["prefill_2k"].with_(L=64 * 37 + 21, window=37, seed=1701)
+    say("backward bf16 L=%d H=32 window 37, heads 0 and 17 checked" % wl.L)
+    x = make_prefill(wl, DEV)
+    dO = grads_seed((wl.B, wl.H, wl.L, wl.dv), 12, wl.torch_dtype)
+    got = G.hybrid_layer_bwd(x["q"], x["k"], x["v"], x["gate"], x["wq"], x["wk"], x["meta"], dO, window=wl.window)
+    torch.cuda.synchronize()
+    for h in (0, 17):
+        hx = {k: to_f64(v[:, h:h + 1]) for k, v in x.items() if v.dim() == 4}
+        hw = {k: to_f64(x[k][h:h + 1]) for k in ("wq", "wk", "meta")}
+        ref = OB.layer_bwd(hx["q"], hx["k"], hx["v"], hx["gate"], hw["wq"], hw["wk"], hw["meta"],
+                           to_f64(dO[:, h:h + 1]), window=wl.window)
+        sub = {n: (got[n][h:h + 1] if n in ("wq", "wk", "meta") else got[n][:, h:h + 1])
+               for n in ("q", "k", "v", "gate", "wq", "wk", "meta")}
+        compare(sub, ref, TOL_BF16)
+
+
 def test_backward_8k_sampled_head():
     """8K tokens x 32 heads: five walk segments of 1664 tokens, long enough that
     the walks' running exponents are rescaled under the workload's ordinary gates
