@@ -17,7 +17,8 @@
 // Parallel structure over one head: the sequence is cut into P segments.
 //   state_kernel         end state of every slice of the segments 0..P-2 from a
 //                        zero state, and its total log-decay
-//   segment_scan_kernel  the state after every slice (fp32, sequential in q)
+//   segment_scan_kernel  the state after every segment's last slice (fp32,
+//                        sequential over the slices)
 //   chunk_out_kernel     the outputs, one block per segment, starting from the
 //                        state after the segment's preceding slice
 //   swa_kernel           window attention alone, one block per chunk
@@ -357,9 +358,11 @@ void state_kernel(ChunkParams p) {
 
 // State after every state slice: S_(0) = e^{D_0} S_in + dS_0,
 // S_(q) = e^{D_q} S_(q-1) + dS_q.  Thread = one state element of one head; the
-// slots are overwritten in place (slot q receives S_(q)).
+// slots are overwritten in place, but only the last slice of each segment (q =
+// R - 1, 2R - 1, ...) receives S_(q): the output pass reads no other (the
+// kernel is bound by HBM, so the other stores are skipped).
 __global__ __launch_bounds__(kNT) void segment_scan_kernel(float *seg_state, const float *seg_decay,
-                                                           const float *state_in, int BH, int NS) {
+                                                           const float *state_in, int BH, int NS, int R) {
   const size_t idx = (size_t)blockIdx.x * kNT + threadIdx.x;
   const size_t per = (size_t)kF * kDV;
   if (idx >= (size_t)BH * per) return;
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(kNT) void segment_scan_kernel(float *seg_state, con
     float *slot = seg_state + (bh * NS + q) * per;
     const float dec = exp2_fast(seg_decay[(bh * NS + q) * kF + f]);  // base-2 log-decay
     s = dec * s + slot[e];
-    slot[e] = s;
+    if ((q + 1) % R == 0) slot[e] = s;
   }
 }
 
@@ -482,7 +485,7 @@ hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
     if (e != hipSuccess) return e;
     const size_t elems = (size_t)bh * kF * kDV;
     hipLaunchKernelGGL(segment_scan_kernel, dim3((unsigned)((elems + kNT - 1) / kNT)), dim3(kNT), 0,
-                       a.stream, p.seg_state, (const float *)p.seg_decay, a.state_in, bh, NS);
+                       a.stream, p.seg_state, (const float *)p.seg_decay, a.state_in, bh, NS, s.R);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
