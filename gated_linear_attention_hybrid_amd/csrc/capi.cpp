@@ -113,7 +113,8 @@ glah_status hybrid_fwd(const glah_desc *desc, const void *q, const void *k, cons
   if (chunked_supported(a, PART_BOTH)) {
     if (ws_bytes < chunked_workspace_bytes(a, PART_BOTH) || (!ws && chunked_workspace_bytes(a, PART_BOTH)))
       return GLAH_EWORKSPACE;
-    e = launch_chunked_prefill(a, PART_BOTH);
+    e = launch_chunked_prefill(a, PART_BOTH, kcache_out != nullptr);  // the ring from the output pass
+    if (e == hipSuccess) return finish(e);
   } else if (chunked_supported(a, PART_GLA) && swa_wide_supported(a)) {
     // windows wider than one chunk: the gated part in the chunked kernels, then
     // the window part with an online softmax over key chunks, added to o

@@ -13,6 +13,8 @@ struct ChunkParams {
   const float *state_in;  // [BH][F][DV] state before token 0 (segment 0), or null
   float *state_out;       // [BH][F][DV] written by the last segment, or null
   bf16 *o;
+  bf16 *kc, *vc;          // [BH][window][128]: the ring of the last `window` keys and
+                          // values, written by each head's last segment, or null
   float *seg_state;       // [BH][NS][F][DV]: end state of state slice q from zero (state
                           // pass), overwritten by the scan with the state after slice q
   float *seg_decay;       // [BH][NS][F]: total base-2 log-decay of state slice q

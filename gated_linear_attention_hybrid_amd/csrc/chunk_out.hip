@@ -436,6 +436,20 @@ __global__ __launch_bounds__(kNT8) void chunk_out_kernel(ChunkParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) dst[feat(g, 4 * mt + j) * kDV + dvpair(tile, dt, n)] = S[mt][dt][j];
     }
+    if (p.kc && seg == p.P - 1) {
+      // the ring of the last `window` keys and values for decoding: slot
+      // t % window holds token t of [L - window, L), zeros for tokens before 0
+      // (16-byte pieces, 16 a row; the key waves are threads 0..255)
+      const int w = p.window, L = p.L;
+      const bf16x8 z8 = {};
+      for (int i = threadIdx.x; i < w * 32; i += 256) {
+        const int slot = i >> 5, part = i & 31, piece = part & 15;
+        const int t = L - w + ((slot - (L - w)) % w + w) % w;
+        const bf16 *src = (part < 16 ? p.k : p.v) + (bh * (size_t)L + (size_t)max(t, 0)) * kD + 8 * piece;
+        bf16 *dst = (part < 16 ? p.kc : p.vc) + (bh * (size_t)w + slot) * kD + 8 * piece;
+        *(bf16x8 *)dst = t >= 0 ? *(const bf16x8 *)src : z8;
+      }
+    }
   } else {
     // ============================== query waves ==============================
     // meta-memory sinks of this head, base 2

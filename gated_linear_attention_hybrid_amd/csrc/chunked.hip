@@ -411,6 +411,7 @@ ChunkParams make_params(const LayerArgs &a, int P, int seg_chunks, int nchunks) 
   p.gate = (const bf16 *)a.gate; p.wq = (const bf16 *)a.wq; p.wk = (const bf16 *)a.wk;
   p.meta = a.meta; p.state_in = a.state_in; p.state_out = a.state_out; p.o = (bf16 *)a.o;
   p.seg_state = nullptr; p.seg_decay = nullptr;
+  p.kc = nullptr; p.vc = nullptr;
   p.B = a.B; p.H = a.H; p.L = a.L; p.window = a.window; p.n_meta = a.n_meta;
   p.nchunks = nchunks; p.P = P; p.seg_chunks = seg_chunks;
   p.R = 1; p.sub_chunks = seg_chunks;
@@ -463,11 +464,15 @@ hipError_t noalloc_scratch(void **ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_chunked_prefill(const LayerArgs &a, int parts) {
+hipError_t launch_chunked_prefill(const LayerArgs &a, int parts, bool ring) {
   if ((size_t)a.B * a.H * a.L == 0) return hipSuccess;
   const int bh = a.B * a.H;
   const SegPlan s = plan_segments(a);
   ChunkParams p = make_params(a, s.P, s.seg_chunks, s.nchunks);
+  if (ring) {
+    p.kc = (bf16 *)a.kcache;
+    p.vc = (bf16 *)a.vcache;
+  }
   p.R = s.R;
   p.sub_chunks = s.sub_chunks;
   if (s.P > 1) {

@@ -54,7 +54,9 @@ hipError_t launch_decode128(const LayerArgs &a, int parts);
 // Chunkwise MFMA path (bf16, d = f = d_v = 128).
 bool chunked_supported(const LayerArgs &a, int parts);
 size_t chunked_workspace_bytes(const LayerArgs &a, int parts);
-hipError_t launch_chunked_prefill(const LayerArgs &a, int parts);
+// ring: also write the decode ring (a.kcache, a.vcache) of the last `window` keys
+// and values (the bf16 matrix-core path, from each head's last segment)
+hipError_t launch_chunked_prefill(const LayerArgs &a, int parts, bool ring = false);
 
 // Device scratch of hybrid_layer_fwd_noalloc (chunked.hip): a static device
 // array of kNoAllocScratchBytes per device; *ptr receives the current device's
