@@ -226,17 +226,24 @@ def test_empty_sequence_passes_the_state(dtype):
         assert not kc.any() and not vc.any()
 
 
-def test_window_cache_out_mfma():
-    wl = base(H=2, L=200)
-    say("window cache out (MFMA path)")
+@pytest.mark.parametrize("L", [200, 40, 2000])
+def test_window_cache_out_mfma(L):
+    """The decode ring written by each head's last output-pass block: one segment
+    (L = 200), fewer tokens than the window (slots of tokens before 0 are
+    zeros), and seven segments (L = 2000)."""
+    wl = base(H=2, L=L)
+    say("window cache out (MFMA path), L=%d" % L)
     x = make_prefill(wl, DEV)
     kc = torch.full((wl.B, wl.H, wl.window, wl.d), 3.0, device=DEV, dtype=torch.bfloat16)
     vc = torch.full((wl.B, wl.H, wl.window, wl.dv), 3.0, device=DEV, dtype=torch.bfloat16)
     run_hybrid(x, wl, kcache_out=kc, vcache_out=vc)
     torch.cuda.synchronize()
     for p in range(wl.L - wl.window, wl.L):
-        assert torch.equal(kc[:, :, p % wl.window], x["k"][:, :, p])
-        assert torch.equal(vc[:, :, p % wl.window], x["v"][:, :, p])
+        if p < 0:
+            assert not kc[:, :, p % wl.window].any() and not vc[:, :, p % wl.window].any()
+        else:
+            assert torch.equal(kc[:, :, p % wl.window], x["k"][:, :, p])
+            assert torch.equal(vc[:, :, p % wl.window], x["v"][:, :, p])
 
 
 def test_deterministic():
