@@ -140,30 +140,59 @@ __device__ __forceinline__ float load_total(__amdgpu_buffer_rsrc_t r, int tau, i
 }
 
 // ================================ pass 1 ====================================
+// The four waves of a pass-1 block walk the same 16-token tiles, so a tile of
+// value (or dO) rows is read once a block and shared through LDS: wave w loads
+// rows 4w .. 4w + 3 (16 bytes a lane) into a buffer in the row-operand
+// fragment layout (fragment (c & 3), lane (row + 16 (c >> 2)) holding row
+// `row`, columns 8c .. 8c + 7), and every wave reads its transposed half
+// fragments from it with gfx950's transposing LDS read.  Two buffers: one
+// barrier a tile.
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_ptr;
+constexpr int kRowTileBytes = 16 * 128 * 2;
+__device__ __forceinline__ u32x4 tile_piece_load(__amdgpu_buffer_rsrc_t r, int tau) {
+  const int lane = threadIdx.x & 63, row = 4 * (int)(threadIdx.x >> 6) + (lane >> 4), c = lane & 15;
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)((unsigned)(16 * tau + row) * 256u + (unsigned)c * 16u), 0, 0);
+}
+__device__ __forceinline__ void tile_piece_store(char *buf, u32x4 x) {
+  const int lane = threadIdx.x & 63, row = 4 * (int)(threadIdx.x >> 6) + (lane >> 4), c = lane & 15;
+  *(u32x4 *)(buf + (c & 3) * 1024 + (row + 16 * (c >> 2)) * 16) = x;
+}
+// Transposed half fragment (s, dt) of a staged tile: lane (n, g) gets
+// x[token 4 g + r][32 s + 8 (n / 4) + 4 dt + n % 4], r = 0..3 (the A operand of a
+// 16x16x16 product over tokens, as a selection product of the value-layout
+// rows gives it).  ds_read_b64_tr_b16 hands lane i of each 16-lane row element
+// i % 4 of the 8-byte chunks addressed by lanes 4 r + i / 4 of that row.
+__device__ __forceinline__ bf16x4 tile_tr_half(const char *buf, int s, int dt) {
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const char *p = buf + (m & 3) * 1024 + (4 * g + (m >> 2) + 16 * s) * 16 + 8 * dt;
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(char *)p));
+}
+
 // forward: S_loc of segment seg from zero, 16 features (ft); D of the segment
-__device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, int ft) {
+__device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, int ft, char *lds) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
   const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   f32x4 S[4][2];
 #pragma unroll
   for (int s = 0; s < 4; ++s) S[s][0] = S[s][1] = zf4();
-  bf16x8 xv[4];
   float lk[4], lb[4], lB;
   auto load = [&](int tau) {
-    load_vals(rv, (unsigned)(16 * tau + n) * 256, xv);
     load_f(rk, tau, f, lk);
     load_f(rb, tau, f, lb);
     lB = load_total(rb, tau, f, L);
   };
+  u32x4 vraw = tile_piece_load(rv, t0);
   load(t0);
+  tile_piece_store(lds + (t0 & 1) * kRowTileBytes, vraw);
+  if (t0 + 1 < t1) vraw = tile_piece_load(rv, t0 + 1);
   float dsum = 0.0f, c = 0.0f;  // the state is e^{c} S
   for (int tau = t0; tau < t1; ++tau) {
-    bf16x8 cv[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) cv[s] = xv[s];
+    __syncthreads();  // value rows of tile tau staged; the other buffer free
+    if (tau + 1 < t1) tile_piece_store(lds + ((tau + 1) & 1) * kRowTileBytes, vraw);
+    if (tau + 2 < t1) vraw = tile_piece_load(rv, tau + 2);
+    const char *vb = lds + (tau & 1) * kRowTileBytes;
     const float B = lB, cn = c + B;
     const bool full = __any(cn < -kReref);
     const float ks = full ? 0.0f : -cn;
@@ -184,7 +213,7 @@ __device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, 
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
+        const bf16x4 vt = tile_tr_half(vb, s, dt);
         S[s][dt] = mma16(vt, khl, mma16(vt, khh, S[s][dt]));
       }
   }
@@ -198,29 +227,30 @@ __device__ __forceinline__ void fwd_state(const WalkParams &p, int bh, int seg, 
 }
 
 // reverse: G_loc of segment seg from zero, 16 features (ft); D of the last segment
-__device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, int ft) {
+__device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, int ft, char *lds) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
   const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
   const __amdgpu_buffer_rsrc_t ro = head_rsrc(p.dout, bh, L), rq = frows(p.pq, bh, L), rb = frows(p.gb, bh, L);
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   f32x4 G[4][2];
 #pragma unroll
   for (int s = 0; s < 4; ++s) G[s][0] = G[s][1] = zf4();
-  bf16x8 xo[4];
   float lq[4], lb[4], lB;
   auto load = [&](int tau) {
-    load_vals(ro, (unsigned)(16 * tau + n) * 256, xo);
     load_f(rq, tau, f, lq);
     load_f(rb, tau, f, lb);
     lB = load_total(rb, tau, f, L);
   };
+  u32x4 oraw = tile_piece_load(ro, t1 - 1);
   load(t1 - 1);
+  tile_piece_store(lds + ((t1 - 1) & 1) * kRowTileBytes, oraw);
+  if (t1 - 2 >= t0) oraw = tile_piece_load(ro, t1 - 2);
   float dsum = 0.0f, c = 0.0f;  // the gradient is e^{c} G
   for (int tau = t1 - 1; tau >= t0; --tau) {
-    bf16x8 co[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) co[s] = xo[s];
+    __syncthreads();  // dO rows of tile tau staged; the other buffer free
+    if (tau - 1 >= t0) tile_piece_store(lds + ((tau - 1) & 1) * kRowTileBytes, oraw);
+    if (tau - 2 >= t0) oraw = tile_piece_load(ro, tau - 2);
+    const char *ob = lds + (tau & 1) * kRowTileBytes;
     const float B = lB, cn = c + B;
     const bool full = __any(cn < -kReref);
     const float qs = full ? 0.0f : -cn;
@@ -241,7 +271,7 @@ __device__ __forceinline__ void rev_state(const WalkParams &p, int bh, int seg, 
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const bf16x4 ot = pack4(mfma(co[s], sel[dt], zf4()));
+        const bf16x4 ot = tile_tr_half(ob, s, dt);
         G[s][dt] = mma16(ot, ql, mma16(ot, qh, G[s][dt]));
       }
   }
@@ -270,10 +300,11 @@ __global__ __launch_bounds__(256) void bwd_walk_state_kernel(WalkParams p) {
     blk = 2 * (x * (nf / 16) + (l >> 1)) + (l & 1);
   }
   const int bh = blk / per, r = blk - bh * per, seg = r >> 1, ft = 4 * (r & 1) + wave;
+  __shared__ __align__(16) char lds[2 * kRowTileBytes];
   if (rev)
-    rev_state(p, bh, seg + 1, ft);
+    rev_state(p, bh, seg + 1, ft, lds);
   else
-    fwd_state(p, bh, seg, ft);
+    fwd_state(p, bh, seg, ft, lds);
 }
 
 // ================================ pass 2 ====================================
