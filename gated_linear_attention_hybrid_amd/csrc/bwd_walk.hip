@@ -308,14 +308,23 @@ __global__ __launch_bounds__(256) void bwd_walk_state_kernel(WalkParams p) {
 }
 
 // ================================ pass 2 ====================================
-__device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, int ft) {
+// a value-layout operand (lane (n, g): token n, columns 32 s + 8 g .. + 7) read
+// from a staged tile
+__device__ __forceinline__ bf16x8 tile_val(const char *buf, int s) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  return *(const bf16x8 *)(buf + g * 1024 + (n + 16 * s) * 16);
+}
+
+// The forward walks of a segment's block (four waves, 16 features each) share
+// the value and dO rows of each tile through LDS as pass 1 does (two buffers of
+// both tiles, one barrier a tile).
+__device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, int ft, char *lds) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int f = 16 * ft + n, L = p.L, nt = (L + 15) / 16;
   const int t0 = seg * p.seg, t1 = min(t0 + p.seg, nt);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(p.v, bh, L), ro = head_rsrc(p.dout, bh, L);
   const __amdgpu_buffer_rsrc_t rq = frows(p.pq, bh, L), rk = frows(p.pk, bh, L), rb = frows(p.gb, bh, L);
   const __amdgpu_buffer_rsrc_t rd = frows(p.dpq, bh, L);
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   // S^T tiles (s, dt): rows d_v 32 s + 8 g + 4 dt + r, column f; the state
   // before the segment
   f32x4 ST[4][2];
@@ -333,30 +342,47 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
       for (int dt = 0; dt < 2; ++dt)
         ST[s][dt] = ST[s][dt] * e + *(const f32x4 *)(p.sloc + base * 128 + 32 * s + 8 * g + 4 * dt);
   }
-  // operands two tiles ahead in a ring of two fixed register sets
-  bf16x8 xv[2][4], xo[2][4];
+  // layout-F operands two tiles ahead in a ring of two fixed register sets; the
+  // value and dO rows through LDS (buffer tau & 1: value tile, then dO tile)
   float lq[2][4], lk[2][4], lb[2][4], lB[2];
   auto load = [&](int u, int tau) {
     tau = min(tau, t1 - 1);
-    const unsigned rowb = (unsigned)(16 * tau + n) * 256;
-    load_vals(rv, rowb, xv[u]);
-    load_vals(ro, rowb, xo[u]);
     load_f(rq, tau, f, lq[u]);
     load_f(rk, tau, f, lk[u]);
     load_f(rb, tau, f, lb[u]);
     lB[u] = load_total(rb, tau, f, L);
   };
+  u32x4 vraw = {0u, 0u, 0u, 0u}, oraw = {0u, 0u, 0u, 0u};
   if (t1 > t0) {
+    vraw = tile_piece_load(rv, t0);
+    oraw = tile_piece_load(ro, t0);
     load(0, t0);
     load(1, t0 + 1);
+    tile_piece_store(lds + (t0 & 1) * 2 * kRowTileBytes, vraw);
+    tile_piece_store(lds + (t0 & 1) * 2 * kRowTileBytes + kRowTileBytes, oraw);
+    if (t0 + 1 < t1) {
+      vraw = tile_piece_load(rv, t0 + 1);
+      oraw = tile_piece_load(ro, t0 + 1);
+    }
   }
   float tqa = 0.0f, c = 0.0f;  // the state is e^{c} ST
   auto step = [&](int u, int tau) {
+    __syncthreads();  // rows of tile tau staged; the other buffer free
+    if (tau + 1 < t1) {
+      char *nb = lds + ((tau + 1) & 1) * 2 * kRowTileBytes;
+      tile_piece_store(nb, vraw);
+      tile_piece_store(nb + kRowTileBytes, oraw);
+    }
+    if (tau + 2 < t1) {
+      vraw = tile_piece_load(rv, tau + 2);
+      oraw = tile_piece_load(ro, tau + 2);
+    }
+    const char *vb = lds + (tau & 1) * 2 * kRowTileBytes, *ob = vb + kRowTileBytes;
     bf16x8 cv[4], co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      cv[s] = xv[u][s];
-      co[s] = xo[u][s];
+      cv[s] = tile_val(vb, s);
+      co[s] = tile_val(ob, s);
     }
     const float B = lB[u], mid = 0.5f * B, cn = c + B;
     const bool full = __any(cn < -kReref);
@@ -418,7 +444,7 @@ __device__ __forceinline__ void fwd_walk(const WalkParams &p, int bh, int seg, i
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const bf16x4 vt = pack4(mfma(cv[s], sel[dt], zf4()));
+        const bf16x4 vt = tile_tr_half(vb, s, dt);
         ST[s][dt] = mma16(vt, khl, mma16(vt, khh, ST[s][dt]));
       }
   };
@@ -677,7 +703,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       blk = 2 * (x * (nrev / 8) + (l >> 1)) + (l & 1);
     }
     const int bh = blk / (2 * p.P), r = blk - bh * 2 * p.P;
-    fwd_walk(p, bh, r >> 1, 4 * (r & 1) + (int)(threadIdx.x >> 6));
+    fwd_walk(p, bh, r >> 1, 4 * (r & 1) + (int)(threadIdx.x >> 6), lds);
   }
 }
 
