@@ -485,7 +485,6 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
                 : frows(p.dvg, bh, L);
   // this lane's eight dv columns of a bf16 token row
   const unsigned dvcol = (unsigned)(32 * fs + 8 * g) * 2u;
-  const bf16x8 sel[2] = {select_operand(0), select_operand(1)};
   const bf16x4 eye = eye16();
   const int fF[2] = {32 * fs + n, 32 * fs + 16 + n};
   // G^T tiles [fa][s][dt]: rows d_v 32 s + 8 g + 4 dt + r, column fF[fa]; the
@@ -512,12 +511,8 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
           GT[fa][s][dt] = GT[fa][s][dt] * e + *(const f32x4 *)(p.gloc + base * 128 + 32 * s + 8 * g + 4 * dt);
     }
   }
-  bf16x8 xv[4], xo[4];
   float lq[2][4], lk[2][4], lb[2][4], lB[2];
   auto load = [&](int tau) {
-    const unsigned rowb = (unsigned)(16 * tau + n) * 256;
-    load_vals(rv, rowb, xv);
-    load_vals(ro, rowb, xo);
 #pragma unroll
     for (int fa = 0; fa < 2; ++fa) {
       load_f(rq, tau, fF[fa], lq[fa]);
@@ -526,14 +521,40 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
       lB[fa] = load_total(rb, tau, fF[fa], L);
     }
   };
-  if (t1 > t0) load(t1 - 1);
+  // the value and dO rows of a tile through LDS, after the dv parts (buffer
+  // tau & 1: value tile, then dO tile): tile tau - 1 is stored during tile tau,
+  // before the tile's barrier, and read after it
+  char *const rows = lds + 2 * kPartBytes;
+  u32x4 vraw = {0u, 0u, 0u, 0u}, oraw = {0u, 0u, 0u, 0u};
+  if (t1 > t0) {
+    vraw = tile_piece_load(rv, t1 - 1);
+    oraw = tile_piece_load(ro, t1 - 1);
+    load(t1 - 1);
+    tile_piece_store(rows + ((t1 - 1) & 1) * 2 * kRowTileBytes, vraw);
+    tile_piece_store(rows + ((t1 - 1) & 1) * 2 * kRowTileBytes + kRowTileBytes, oraw);
+    if (t1 - 2 >= t0) {
+      vraw = tile_piece_load(rv, t1 - 2);
+      oraw = tile_piece_load(ro, t1 - 2);
+    }
+  }
+  __syncthreads();
   float tka[2] = {0.0f, 0.0f}, c[2] = {0.0f, 0.0f};  // the gradient is e^{c} G^T
   for (int tau = t1 - 1; tau >= t0; --tau) {
+    const char *vb = rows + (tau & 1) * 2 * kRowTileBytes, *ob = vb + kRowTileBytes;
     bf16x8 cv[4], co[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      cv[s] = xv[s];
-      co[s] = xo[s];
+      cv[s] = tile_val(vb, s);
+      co[s] = tile_val(ob, s);
+    }
+    if (tau - 1 >= t0) {
+      char *nb = rows + ((tau - 1) & 1) * 2 * kRowTileBytes;
+      tile_piece_store(nb, vraw);
+      tile_piece_store(nb + kRowTileBytes, oraw);
+    }
+    if (tau - 2 >= t0) {
+      vraw = tile_piece_load(rv, tau - 2);
+      oraw = tile_piece_load(ro, tau - 2);
     }
     const float cn[2] = {c[0] + lB[0], c[1] + lB[1]};
     const bool full = __any(cn[0] < -kReref || cn[1] < -kReref);
@@ -628,7 +649,7 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
         // on the matrix core: the bf16 values pass unchanged)
         const bf16x4 g0 = to_rows(GT[0][s][dt], eye);
         const bf16x4 g1 = to_rows(GT[1][s][dt], eye);
-        const bf16x4 ot = pack4(mfma(co[s], sel[dt], zf4()));  // dO^T half: rows d_v, K tokens
+        const bf16x4 ot = tile_tr_half(ob, s, dt);  // dO^T half: rows d_v, K tokens
         // the two parts in separate accumulators, added on the VALU: a
         // 16x16x16 product accumulating straight onto a 16x16x32 result read
         // stale accumulator rows (the compiler spaces such a mixed pair as if
@@ -686,12 +707,13 @@ __device__ __forceinline__ void rev_walk(const WalkParams &p, int bh, int seg, c
 
 // Blocks of four waves: the reverse walks (one block a head and segment) first,
 // then the forward walks (two blocks a head and segment).  Two waves a SIMD (a
-// few loop-invariant values spill to scratch) and 64 KiB of LDS a block.  When
+// few loop-invariant values spill to scratch) and 80 KiB of LDS a block (the
+// reverse walks' dv parts, both roles' staged value and dO rows).  When
 // the counts allow, the two forward blocks of a segment, which walk the same
 // value and dO rows in step, are numbered onto one XCD (blocks are dealt to the
 // 8 XCDs in turn; each XCD takes a contiguous run of segments).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_walk_kernel(WalkParams p) {
-  __shared__ __align__(16) char lds[2 * kPartBytes];
+  __shared__ __align__(16) char lds[2 * kPartBytes + 4 * kRowTileBytes];
   const int nrev = p.BH * p.P;
   int blk = blockIdx.x;
   if (blk < nrev) {
