@@ -56,11 +56,13 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-// Pass-2 waves the segment count aims at: 576 blocks of four waves, an eighth
-// more than fit at once at two waves per SIMD.  Measured at 32K tokens, 16 and
-// 32 heads, this beats filling the chip exactly (2048 waves) by 5-7%: the
-// forward-walk blocks finish first and the extra blocks fill their places.
-constexpr int kWalkWaves = 2304;
+// Pass-2 waves the segment count aims at: 768 blocks of four waves, half again
+// as many as fit at once at two waves per SIMD.  Measured at 32K tokens, 16 and
+// 32 heads (segments of 2048 and 4096 tokens), this beats 2048, 2304, 2688,
+// 3456, 4096 and 4608 waves by 1-10%: shorter segments shorten the serial tile
+// chains, and the forward-walk blocks, which finish first, leave their places
+// to the rest.
+constexpr int kWalkWaves = 3072;
 // Each state is kept as e^{c} X with c the log-decay gathered since it was last
 // written out in full, per feature: the tile's decay then scales the update's
 // four map values instead of the state's 64 per lane.  Once c would fall
