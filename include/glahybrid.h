@@ -222,8 +222,8 @@ glah_status gla_decode_step(const glah_desc *desc, const void *q_t,
  *               sums over the batch added up across them.
  * glah_bwd_workspace_bytes reports the whole call's workspace when it is at
  * most 1.5e9 bytes, else that of the largest sub-problem within that (at 32K
- * tokens, 32 heads of 128: blocks of 16 heads, 1.41 GB; the whole call takes
- * 2.77 GB); (size_t)-1 for an invalid descriptor, 0 when the sizes are not
+ * tokens, 32 heads of 128: blocks of 16 heads, 1.42 GB; the whole call takes
+ * 2.78 GB); (size_t)-1 for an invalid descriptor, 0 when the sizes are not
  * supported.
  * Supported: d_qk, d_v <= 128 and multiples of 4; f <= 128, a multiple of 4 with
  * f/2 a power of two; window <= 1024; n_meta <= 64 (otherwise GLAH_ENOTSUP).
